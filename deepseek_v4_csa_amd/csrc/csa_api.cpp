@@ -1,0 +1,189 @@
+// C ABI of the CSA forward path: host-side validation, then launches on the caller's
+// stream.  Every check that the host can make happens before anything is enqueued;
+// device data (cu_seqlens, ids) is a documented precondition and is never read here.
+#include "../../include/csa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa_status_t fail(csa_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+csa_status_t ok() {
+  g_err[0] = '\0';
+  return CSA_OK;
+}
+
+csa_status_t hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(CSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Layout checks shared by every entry point ("RuntimeError when no segment has compressed
+// keys" in the csa.py THD excerpt of the page "[Bug] DSV4 unfused CSA indexer loss uses a
+// compressed-only teacher ..." becomes CSA_ERR_INVALID for total_k == 0).
+csa_status_t check_layout(const csa_layout_t *L, const char *fn, csa::LaunchLayout *out) {
+  if (!L) return fail(CSA_ERR_INVALID, "%s: layout is NULL", fn);
+  if (L->num_seqs < 1) return fail(CSA_ERR_INVALID, "%s: num_seqs=%d < 1", fn, L->num_seqs);
+  if (L->total_q < 0) return fail(CSA_ERR_INVALID, "%s: total_q=%d < 0", fn, L->total_q);
+  if (L->total_k < 1)
+    return fail(CSA_ERR_INVALID, "%s: total_k=%d: no segment has compressed keys", fn, L->total_k);
+  if (L->max_seqlen_q < 1 || L->max_seqlen_k < 1)
+    return fail(CSA_ERR_INVALID, "%s: max_seqlen_q=%d / max_seqlen_k=%d must be >= 1", fn,
+                L->max_seqlen_q, L->max_seqlen_k);
+  if (L->max_seqlen_q > L->total_q && L->total_q > 0)
+    return fail(CSA_ERR_INVALID, "%s: max_seqlen_q=%d > total_q=%d", fn, L->max_seqlen_q, L->total_q);
+  if (L->max_seqlen_k > L->total_k)
+    return fail(CSA_ERR_INVALID, "%s: max_seqlen_k=%d > total_k=%d", fn, L->max_seqlen_k, L->total_k);
+  if (L->compress_ratio < 1)
+    return fail(CSA_ERR_INVALID, "%s: compress_ratio=%d < 1", fn, L->compress_ratio);
+  if (!L->cu_seqlens_q || !L->cu_seqlens_k)
+    return fail(CSA_ERR_INVALID, "%s: cu_seqlens_q / cu_seqlens_k is NULL", fn);
+  out->dev.cu_q = L->cu_seqlens_q;
+  out->dev.cu_k = L->cu_seqlens_k;
+  out->dev.off = L->q_causal_offsets;
+  out->dev.num_seqs = L->num_seqs;
+  out->dev.ratio = L->compress_ratio;
+  out->num_seqs = L->num_seqs;
+  out->total_q = L->total_q;
+  out->total_k = L->total_k;
+  out->max_seqlen_q = L->max_seqlen_q;
+  out->max_seqlen_k = L->max_seqlen_k;
+  return CSA_OK;
+}
+
+bool dtype_ok(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+
+int k_eff_of(const csa_layout_t *L, int topk) { return topk < L->max_seqlen_k ? topk : L->max_seqlen_k; }
+
+}  // namespace
+
+extern "C" {
+
+const char *csa_last_error(void) { return g_err; }
+
+int32_t csa_k_eff(const csa_layout_t *L, int32_t topk) {
+  if (!L || topk < 0 || L->max_seqlen_k < 1) return -1;
+  return k_eff_of(L, topk);
+}
+
+csa_status_t csa_indexer_score(const csa_layout_t *L, const void *q_idx, const void *k_idx,
+                               const float *weights, csa_dtype_t dt, int32_t Hi, int32_t Di,
+                               float idx_scale, float *scores, int64_t ld_scores, void *stream) {
+  const char *fn = "csa_indexer_score";
+  csa::LaunchLayout LL;
+  csa_status_t st = check_layout(L, fn, &LL);
+  if (st != CSA_OK) return st;
+  if (!q_idx || !k_idx || !weights || !scores)
+    return fail(CSA_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+  if (Hi < 1 || Di < 1) return fail(CSA_ERR_INVALID, "%s: Hi=%d, Di=%d must be >= 1", fn, Hi, Di);
+  if (ld_scores < L->max_seqlen_k)
+    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld < max_seqlen_k=%d", fn, (long long)ld_scores,
+                L->max_seqlen_k);
+  if (!csa::indexer_supported(dt == CSA_BF16, Hi, Di))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d Hi=%d Di=%d", fn, (int)dt, Hi, Di);
+  if (L->total_q == 0) return ok();
+  return hip_status(csa::launch_indexer_score(LL, q_idx, k_idx, weights, dt == CSA_BF16, Hi, Di,
+                                              idx_scale, scores, ld_scores,
+                                              static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+csa_status_t csa_topk(const csa_layout_t *L, const float *scores, int64_t ld_scores, int32_t topk,
+                      int32_t *ids, void *stream) {
+  const char *fn = "csa_topk";
+  csa::LaunchLayout LL;
+  csa_status_t st = check_layout(L, fn, &LL);
+  if (st != CSA_OK) return st;
+  if (!scores || !ids) return fail(CSA_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  if (topk < 1) return fail(CSA_ERR_INVALID, "%s: topk=%d < 1", fn, topk);
+  if (ld_scores < L->max_seqlen_k)
+    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld < max_seqlen_k=%d", fn, (long long)ld_scores,
+                L->max_seqlen_k);
+  const int k_eff = k_eff_of(L, topk);
+  if (!csa::topk_supported(L->max_seqlen_k, k_eff))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: max_seqlen_k=%d exceeds the supported 16384", fn,
+                L->max_seqlen_k);
+  if (L->total_q == 0) return ok();
+  return hip_status(csa::launch_topk(LL, scores, ld_scores, k_eff, ids, static_cast<hipStream_t>(stream)), fn);
+}
+
+csa_status_t csa_sparse_attn_fwd(const csa_layout_t *L, const void *q, const void *kv,
+                                 const void *ckv, const float *sink, const int32_t *ids,
+                                 int32_t k_eff, int32_t window, csa_dtype_t dt, int32_t H,
+                                 int32_t D, float softmax_scale, void *out, float *lse,
+                                 float *lse_nc, float *cmass, void *stream) {
+  const char *fn = "csa_sparse_attn_fwd";
+  csa::LaunchLayout LL;
+  csa_status_t st = check_layout(L, fn, &LL);
+  if (st != CSA_OK) return st;
+  if (!q || !kv || !ckv || !sink || !out || !lse || !lse_nc)
+    return fail(CSA_ERR_INVALID, "%s: a required tensor pointer is NULL", fn);
+  if (k_eff < 0 || k_eff > L->max_seqlen_k)
+    return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [0, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
+  if (k_eff > 0 && !ids) return fail(CSA_ERR_INVALID, "%s: ids is NULL with k_eff=%d", fn, k_eff);
+  if (window < 0) return fail(CSA_ERR_INVALID, "%s: window=%d < 0", fn, window);
+  if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+  if (H < 1 || D < 1) return fail(CSA_ERR_INVALID, "%s: H=%d, D=%d must be >= 1", fn, H, D);
+  if (!csa::attn_supported(dt == CSA_BF16, H, D, k_eff))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d H=%d D=%d k_eff=%d", fn, (int)dt, H, D, k_eff);
+  if (L->total_q == 0) return ok();
+  return hip_status(csa::launch_sparse_attn(LL, q, kv, ckv, sink, ids, k_eff, window, dt == CSA_BF16, H,
+                                            D, softmax_scale, out, lse, lse_nc, cmass,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, const float *scores,
+                                    int64_t ld_scores, const int32_t *ids, int32_t k_eff,
+                                    const float *cmass, const void *q, const void *ckv,
+                                    const float *lse_nc, csa_dtype_t dt, int32_t H, int32_t D,
+                                    float softmax_scale, int32_t per_token_loss, float *teacher,
+                                    int64_t ld_teacher, float *kl_row, float *loss, void *stream) {
+  const char *fn = "csa_indexer_teacher_kl";
+  csa::LaunchLayout LL;
+  csa_status_t st = check_layout(L, fn, &LL);
+  if (st != CSA_OK) return st;
+  if (!scores || !kl_row || !loss) return fail(CSA_ERR_INVALID, "%s: scores/kl_row/loss is NULL", fn);
+  if (ld_scores < L->max_seqlen_k)
+    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld < max_seqlen_k=%d", fn, (long long)ld_scores,
+                L->max_seqlen_k);
+  if (sparse_loss) {
+    if (k_eff < 1 || k_eff > L->max_seqlen_k)
+      return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [1, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
+    if (!ids || !cmass) return fail(CSA_ERR_INVALID, "%s: sparse loss needs ids and cmass", fn);
+    if (teacher && ld_teacher < k_eff)
+      return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < k_eff=%d", fn, (long long)ld_teacher, k_eff);
+  } else {
+    if (!q || !ckv || !lse_nc) return fail(CSA_ERR_INVALID, "%s: dense loss needs q, ckv and lse_nc", fn);
+    if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+    if (H < 1 || D < 1) return fail(CSA_ERR_INVALID, "%s: H=%d, D=%d must be >= 1", fn, H, D);
+    if (teacher && ld_teacher < L->max_seqlen_k)
+      return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < max_seqlen_k=%d", fn, (long long)ld_teacher,
+                  L->max_seqlen_k);
+    if (!csa::dense_teacher_supported(dt == CSA_BF16, H, D, L->max_seqlen_k))
+      return fail(CSA_ERR_UNSUPPORTED, "%s: no dense kernel for dtype=%d H=%d D=%d max_seqlen_k=%d", fn,
+                  (int)dt, H, D, L->max_seqlen_k);
+  }
+  return hip_status(csa::launch_teacher_kl(LL, sparse_loss != 0, scores, ld_scores, ids, k_eff, cmass, q,
+                                           ckv, lse_nc, dt == CSA_BF16, H, D, softmax_scale,
+                                           per_token_loss != 0, teacher, ld_teacher, kl_row, loss,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Device helpers shared by the CSA kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- bf16 <-> f32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// round-to-nearest-even (lowers to v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- MFMA wrappers
+// 16x16x32 bf16: lane l supplies A[l%16][(l/16)*8 + e] and B[(l/16)*8 + e][l%16],
+// e = 0..7; receives C[(l/16)*4 + i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// 16x16x4 fp32: lane l supplies A[l%16][l/16] and B[l/16][l%16]; same C layout.
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- wave reductions
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) { return __shfl_xor(v, m, WAVE); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+  return v;
+}
+// reductions over the 16 lanes of a lane group (lanes with the same l/16)
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+// reductions over the 4 lane groups holding the same l%16
+__device__ __forceinline__ float across_groups_max(float v) {
+  v = fmaxf(v, shfl_xor(v, 16));
+  v = fmaxf(v, shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float across_groups_sum(float v) {
+  v += shfl_xor(v, 16);
+  v += shfl_xor(v, 32);
+  return v;
+}
+
+// ---------------------------------------------------------------- row geometry
+struct LayoutDev {
+  const int32_t *cu_q;
+  const int32_t *cu_k;
+  const int32_t *off;  // may be null: bottom-right default
+  int32_t num_seqs;
+  int32_t ratio;
+};
+
+// segment s with cu_q[s] <= t < cu_q[s+1] (binary search; cu_q is non-decreasing,
+// empty segments are skipped because the search finds the last s with cu_q[s] <= t)
+__device__ __forceinline__ int segment_of(const int32_t *cu_q, int nseq, int t) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (__ldg(cu_q + mid) <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct RowGeo {
+  int seg, q_start, q_len, k_base, s_k, n_valid;
+};
+
+__device__ __forceinline__ int n_valid_of(int local, int off, int ratio, int s_k) {
+  int i = local + 1 + off;
+  int n = i > 0 ? i / ratio : 0;
+  return n < s_k ? n : s_k;
+}
+
+__device__ __forceinline__ RowGeo row_geo(const LayoutDev &L, int t) {
+  RowGeo g;
+  g.seg = segment_of(L.cu_q, L.num_seqs, t);
+  g.q_start = __ldg(L.cu_q + g.seg);
+  g.q_len = __ldg(L.cu_q + g.seg + 1) - g.q_start;
+  g.k_base = __ldg(L.cu_k + g.seg);
+  g.s_k = __ldg(L.cu_k + g.seg + 1) - g.k_base;
+  int off = L.off ? __ldg(L.off + g.seg) : g.s_k * L.ratio - g.q_len;
+  g.n_valid = n_valid_of(t - g.q_start, off, L.ratio, g.s_k);
+  return g;
+}
+
+__device__ __forceinline__ int seg_offset(const LayoutDev &L, int s, int q_len, int s_k) {
+  return L.off ? __ldg(L.off + s) : s_k * L.ratio - q_len;
+}
+
+}  // namespace csa

@@ -1,0 +1,324 @@
+// Paper-equivalent indexer teacher, KL(teacher || indexer softmax) and the loss.
+//
+// Page "[Bug] DSV4 unfused CSA indexer loss uses a compressed-only teacher ...":
+//   "Paper reference": t_j = sum_h exp(c_hj)/Z_h, L1-normalised over the compressed set,
+//   Z_h keeping the sink and window terms;
+//   proposal comment (discussion thread): l_h = log(exp(u_h) + sum_{j in C} exp(c_hj)),
+//   p_hj = exp(c_hj - l_h); C = top-k intersected with the causally valid entries
+//   (sparse loss) or every causally visible entry (dense loss);
+//   dsa.py excerpt: L1 clamp 1e-10, KL with log(x + 1e-10) on both sides (kept as
+//   written per the review comment "KL numerical contract");
+//   dsa_kernels.py excerpt: the sparse predictor is the softmax of the indexer scores
+//   gathered at the top-k ids, -1 slots excluded.
+//
+// Sparse mode: the attention pass already produced cmass[t, j] = sum_h exp(c_hj -
+// lse_h) with lse_h = l_h (its compressed set is C), so the teacher is cmass / sum.
+// One wave per row.  Dense mode: c_hj is recomputed here for every visible key (MFMA,
+// one workgroup per row, keys streamed through LDS in two passes: exact l_h first,
+// then the head-summed probabilities).  kl_row is then reduced to the loss by a
+// single-workgroup kernel in a fixed order (deterministic, no atomics).
+#include "common.h"
+#include "../launch.h"
+
+namespace csa {
+
+constexpr float EPS = 1e-10f;
+
+// ---------------------------------------------------------------- sparse
+__global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
+    LayoutDev L, int T, const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ ids,
+    int k_eff, const float *__restrict__ cmass, float *__restrict__ teacher, int64_t ldt,
+    float *__restrict__ kl_row) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const RowGeo geo = row_geo(L, t);
+  const int32_t *idr = ids + (int64_t)t * k_eff;
+  const float *cm = cmass + (int64_t)t * k_eff;
+  const float *sr = scores + (int64_t)t * ld;
+  if (geo.n_valid == 0) {
+    if (teacher)
+      for (int j = lane; j < k_eff; j += 64) teacher[(int64_t)t * ldt + j] = 0.f;
+    if (lane == 0) kl_row[t] = 0.f;
+    return;
+  }
+  // predictor statistics and teacher mass over the valid slots.  The KL of two nearly
+  // equal distributions is a second-order quantity, so the normalisations, the
+  // predictor log-probabilities and the log-ratios are finished in fp64: an fp32 error
+  // in either normaliser shifts the KL by about that relative error.
+  float mx = -__builtin_inff();
+  double msum = 0.0;
+  for (int j = lane; j < k_eff; j += 64) {
+    const int id = idr[j];
+    if (id >= 0) {
+      mx = fmaxf(mx, sr[id - geo.k_base]);
+      msum += (double)cm[j];
+    }
+  }
+  mx = wave_max(mx);
+  msum = wave_sum_f64(msum);
+  double es = 0.0;
+  for (int j = lane; j < k_eff; j += 64) {
+    const int id = idr[j];
+    if (id >= 0) es += exp((double)sr[id - geo.k_base] - (double)mx);
+  }
+  es = wave_sum_f64(es);
+  const double lse_i = (double)mx + log(es);
+  const double inv_m = 1.0 / fmax(msum, (double)EPS);
+  double kl = 0.0;
+  for (int j = lane; j < k_eff; j += 64) {
+    const int id = idr[j];
+    double tj = 0.0;
+    if (id >= 0) {
+      tj = (double)cm[j] * inv_m;
+      const double pj = exp((double)sr[id - geo.k_base] - lse_i);
+      kl += tj * (log(tj + (double)EPS) - log(pj + (double)EPS));
+    }
+    if (teacher) teacher[(int64_t)t * ldt + j] = (float)tj;
+  }
+  kl = wave_sum_f64(kl);
+  if (lane == 0) kl_row[t] = (float)kl;
+}
+
+// ---------------------------------------------------------------- dense
+constexpr int DN_CHUNK = 32;
+
+template <int D> struct DenseCfg {
+  static constexpr int RS = D * 2 + 16;
+  static constexpr int PIECES = D * 2 / 16;
+};
+
+template <int D, int HG>
+__global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
+    LayoutDev L, const float *__restrict__ scores, int64_t ld, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ ckv, const float *__restrict__ lse_nc, int H, float scale_log2,
+    float *__restrict__ teacher, int64_t ldt, float *__restrict__ kl_row) {
+  using C = DenseCfg<D>;
+  constexpr int NT = 64 * HG;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char *rows = smem;                                                   // [DN_CHUNK][RS]
+  float *mj = reinterpret_cast<float *>(smem + DN_CHUNK * C::RS);      // [n_valid]
+  __shared__ float part[HG][DN_CHUNK];
+  __shared__ float red[2 * 16];
+
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, hl = lane & 15;
+  const int h = 16 * w + hl;
+  const bool h_ok = h < H;
+  const RowGeo geo = row_geo(L, t);
+  const int n = geo.n_valid;
+  if (n == 0) {
+    if (teacher)
+      for (int j = tid; j < ldt; j += NT) teacher[(int64_t)t * ldt + j] = 0.f;
+    if (tid == 0) kl_row[t] = 0.f;
+    return;
+  }
+  // q^T fragment (16 heads of this wave)
+  u32x4 qf[D / 32];
+  {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok ? h : 0)) * D + g * (D / 4));
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) qf[c] = h_ok ? p[c] : u32x4{0, 0, 0, 0};
+  }
+  const uint16_t *kseg = ckv + (int64_t)geo.k_base * D;
+  const int nch = (n + DN_CHUNK - 1) / DN_CHUNK;
+  auto stage = [&](int ci) {
+    for (int p = tid; p < DN_CHUNK * C::PIECES; p += NT) {
+      const int r = p / C::PIECES, pc = p - r * C::PIECES;
+      const int j = ci * DN_CHUNK + r;
+      u32x4 v = {0, 0, 0, 0};
+      if (j < n) v = reinterpret_cast<const u32x4 *>(kseg + (int64_t)j * D)[pc];
+      *reinterpret_cast<u32x4 *>(rows + r * C::RS + pc * 16) = v;
+    }
+  };
+  auto s_tile = [&](int row0) {
+    const char *base = rows + (row0 + hl) * C::RS + g * (D / 4) * 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) acc = mfma16x16x32(*reinterpret_cast<const u32x4 *>(base + 16 * c), qf[c], acc);
+    return acc;
+  };
+
+  // pass 1: l_h = log2(2^{u_h} + sum_j 2^{c_hj})   (base-2 logits)
+  const float u2 = h_ok ? lse_nc[(int64_t)t * H + h] * LOG2E : -__builtin_inff();
+  float m = g == 0 ? u2 : -__builtin_inff();
+  float l = (g == 0 && u2 > -__builtin_inff()) ? 1.f : 0.f;
+  for (int ci = 0; ci < nch; ++ci) {
+    stage(ci);
+    __syncthreads();
+    float s[8];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const f32x4 st = s_tile(16 * tau);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = ci * DN_CHUNK + 16 * tau + 4 * g + i;
+        s[4 * tau + i] = (j < n && h_ok) ? st[i] * scale_log2 : -__builtin_inff();
+      }
+    }
+    float cmx = s[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cmx = fmaxf(cmx, s[e]);
+    const float mn = fmaxf(m, cmx);
+    if (mn > -__builtin_inff()) {
+      float acc = l * exp2f(m - mn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += exp2f(s[e] - mn);
+      l = acc;
+      m = mn;
+    }
+    __syncthreads();
+  }
+  const float M = across_groups_max(m);
+  const float Ls = across_groups_sum(M > -__builtin_inff() ? l * exp2f(m - M) : 0.f);
+  const float ell2 = Ls > 0.f ? M + __log2f(Ls) : -__builtin_inff();
+  const bool any = ell2 > -__builtin_inff();
+
+  // pass 2: m_j = sum_h 2^{c_hj - l_h}
+  for (int ci = 0; ci < nch; ++ci) {
+    stage(ci);
+    __syncthreads();
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const f32x4 st = s_tile(16 * tau);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = ci * DN_CHUNK + 16 * tau + 4 * g + i;
+        const float p = (j < n && h_ok && any) ? exp2f(st[i] * scale_log2 - ell2) : 0.f;
+        const float sh = group16_sum(p);
+        if (hl == 0) part[w][16 * tau + 4 * g + i] = sh;
+      }
+    }
+    __syncthreads();
+    if (tid < DN_CHUNK) {
+      const int j = ci * DN_CHUNK + tid;
+      if (j < n) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < HG; ++ww) sum += part[ww][tid];
+        mj[j] = sum;
+      }
+    }
+    __syncthreads();
+  }
+
+  // predictor over j < n, teacher normalisation, KL (finished in fp64, see above)
+  const float *sr = scores + (int64_t)t * ld;
+  __shared__ double dred[2 * 16];
+  float mx = -__builtin_inff();
+  double msum = 0.0;
+  for (int j = tid; j < n; j += NT) { mx = fmaxf(mx, sr[j]); msum += (double)mj[j]; }
+  mx = wave_max(mx);
+  msum = wave_sum_f64(msum);
+  if (lane == 0) { red[w] = mx; dred[w] = msum; }
+  __syncthreads();
+  mx = red[0]; msum = dred[0];
+  for (int ww = 1; ww < HG; ++ww) { mx = fmaxf(mx, red[ww]); msum += dred[ww]; }
+  __syncthreads();
+  double es = 0.0;
+  for (int j = tid; j < n; j += NT) es += exp((double)sr[j] - (double)mx);
+  es = wave_sum_f64(es);
+  if (lane == 0) dred[16 + w] = es;
+  __syncthreads();
+  es = 0.0;
+  for (int ww = 0; ww < HG; ++ww) es += dred[16 + ww];
+  const double lse_i = (double)mx + log(es);
+  const double inv_m = 1.0 / fmax(msum, (double)EPS);
+  double kl = 0.0;
+  for (int j = tid; j < n; j += NT) {
+    const double tj = (double)mj[j] * inv_m;
+    const double pj = exp((double)sr[j] - lse_i);
+    kl += tj * (log(tj + (double)EPS) - log(pj + (double)EPS));
+    if (teacher) teacher[(int64_t)t * ldt + j] = (float)tj;
+  }
+  if (teacher)
+    for (int j = n + tid; j < ldt; j += NT) teacher[(int64_t)t * ldt + j] = 0.f;
+  kl = wave_sum_f64(kl);
+  __shared__ double kred[16];
+  __syncthreads();
+  if (lane == 0) kred[w] = kl;
+  __syncthreads();
+  if (tid == 0) {
+    double s = 0.0;
+    for (int ww = 0; ww < HG; ++ww) s += kred[ww];
+    kl_row[t] = (float)s;
+  }
+}
+
+// ---------------------------------------------------------------- loss
+__global__ __launch_bounds__(1024) void loss_reduce_kernel(const float *__restrict__ kl_row, int T,
+                                                           int per_token, float *__restrict__ loss) {
+  __shared__ double part[16];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < T; i += 1024) s += (double)kl_row[i];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < 16; ++i) tot += part[i];
+    loss[0] = (float)(per_token ? tot : (T > 0 ? tot / (double)T : 0.0));
+  }
+}
+
+bool dense_teacher_supported(bool bf16, int H, int D, int max_seqlen_k) {
+  if (!bf16 || H < 1 || H > 128 || max_seqlen_k > 8192) return false;
+  if (!(D == 64 || D == 128 || D == 192 || D == 256 || D == 512)) return false;
+  // dynamic LDS: one staged key chunk plus the row's head-summed masses
+  return (size_t)DN_CHUNK * (D * 2 + 16) + (size_t)max_seqlen_k * sizeof(float) <= 65536;
+}
+
+template <int D>
+static hipError_t launch_dense(const LaunchLayout &LL, const float *scores, int64_t ld, const void *q,
+                               const void *ckv, const float *lse_nc, int H, float scale,
+                               float *teacher, int64_t ldt, float *kl_row, hipStream_t st) {
+  const int hg = (H + 15) / 16;
+  const size_t lds = DN_CHUNK * DenseCfg<D>::RS + (size_t)LL.max_seqlen_k * sizeof(float);
+  const float sl2 = scale * LOG2E;
+#define CSA_DN_CASE(G)                                                                              \
+  if (hg <= G) {                                                                                    \
+    hipLaunchKernelGGL((teacher_kl_dense_kernel<D, G>), dim3((unsigned)LL.total_q), dim3(64 * G), \
+                       lds, st, LL.dev, scores, ld, static_cast<const uint16_t *>(q),               \
+                       static_cast<const uint16_t *>(ckv), lse_nc, H, sl2, teacher, ldt, kl_row);   \
+    return hipGetLastError();                                                                       \
+  }
+  CSA_DN_CASE(1)
+  CSA_DN_CASE(2)
+  CSA_DN_CASE(4)
+  CSA_DN_CASE(8)
+#undef CSA_DN_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_teacher_kl(const LaunchLayout &LL, bool sparse, const float *scores, int64_t ld,
+                             const int32_t *ids, int k_eff, const float *cmass, const void *q,
+                             const void *ckv, const float *lse_nc, bool bf16, int H, int D,
+                             float scale, bool per_token, float *teacher, int64_t ld_teacher,
+                             float *kl_row, float *loss, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (LL.total_q > 0) {
+    if (sparse) {
+      hipLaunchKernelGGL(teacher_kl_sparse_kernel, dim3((unsigned)((LL.total_q + 3) / 4)), dim3(256), 0,
+                         st, LL.dev, LL.total_q, scores, ld, ids, k_eff, cmass, teacher, ld_teacher,
+                         kl_row);
+      e = hipGetLastError();
+    } else {
+      (void)bf16;
+      switch (D) {
+        case 64: e = launch_dense<64>(LL, scores, ld, q, ckv, lse_nc, H, scale, teacher, ld_teacher, kl_row, st); break;
+        case 128: e = launch_dense<128>(LL, scores, ld, q, ckv, lse_nc, H, scale, teacher, ld_teacher, kl_row, st); break;
+        case 192: e = launch_dense<192>(LL, scores, ld, q, ckv, lse_nc, H, scale, teacher, ld_teacher, kl_row, st); break;
+        case 256: e = launch_dense<256>(LL, scores, ld, q, ckv, lse_nc, H, scale, teacher, ld_teacher, kl_row, st); break;
+        case 512: e = launch_dense<512>(LL, scores, ld, q, ckv, lse_nc, H, scale, teacher, ld_teacher, kl_row, st); break;
+        default: return hipErrorInvalidValue;
+      }
+    }
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, st, kl_row, LL.total_q,
+                     per_token ? 1 : 0, loss);
+  return hipGetLastError();
+}
+
+}  // namespace csa

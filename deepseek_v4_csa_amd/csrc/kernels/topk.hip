@@ -1,0 +1,175 @@
+// Per-row top-k with lowest-index ties, ascending global ids and -1 padding.
+//
+// K_t = min(k_eff, n_valid(t)) largest scores among the causally visible columns
+// (k = min(index_topk, n_compressed): csa.py excerpts of the page "[Bug] DSV4 unfused
+// CSA indexer loss uses a compressed-only teacher ..."; picks beyond the causal limit
+// are -1 in its sparse-attention excerpt); ids are global, cu_k[s] + j (page
+// "Megatron-LM pull request 8539", item 1).
+//
+// One workgroup (256 threads) per row; the row's visible scores sit in registers as
+// order-preserving uint32 keys.  The k-th largest key is found by radix selection on
+// (key - row_min_key), starting at the highest set bit of (max - min) so the first
+// 8-bit digit already spreads the values over the histogram (the raw top byte of
+// same-sign floats of similar magnitude would put them all in one or two bins).
+// Ties at the threshold are resolved by index order with a block prefix count, and
+// the selected ids are compacted in ascending order.
+#include "common.h"
+#include "../launch.h"
+
+namespace csa {
+
+constexpr int TK_THREADS = 256;
+constexpr int TK_WAVES = TK_THREADS / 64;
+
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// exclusive prefix count of `flag` over the block in thread order; returns the rank
+// and writes the block total.  Uses two LDS slots per wave and two barriers.
+__device__ __forceinline__ int block_rank(bool flag, int *wsum, int &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t m = __ballot(flag);
+  const int in_wave = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+  if (lane == 0) wsum[w] = __popcll(m);
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < TK_WAVES; ++i) {
+    const int c = wsum[i];
+    before += i < w ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  return before + in_wave;
+}
+
+template <int VPT>
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const float *__restrict__ scores,
+                                                          int64_t ld, int k_eff, int32_t *__restrict__ ids) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t red[2 * TK_WAVES];
+  __shared__ int wsum[TK_WAVES];
+  __shared__ uint32_t sel_digit, sel_above;
+
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const RowGeo g = row_geo(L, t);
+  const int n = g.n_valid;
+  int32_t *out = ids + (int64_t)t * k_eff;
+  if (n <= k_eff) {  // every visible key is selected
+    for (int j = tid; j < k_eff; j += TK_THREADS) out[j] = j < n ? g.k_base + j : -1;
+    return;
+  }
+  const float *row = scores + (int64_t)t * ld;
+
+  uint32_t key[VPT];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int j = v * TK_THREADS + tid;
+    key[v] = j < n ? ordered_key(row[j]) : 0u;
+    if (j < n) { kmin = min(kmin, key[v]); kmax = max(kmax, key[v]); }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
+  }
+  if (lane == 0) { red[w] = kmin; red[TK_WAVES + w] = kmax; }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TK_WAVES; ++i) { kmin = min(kmin, red[i]); kmax = max(kmax, red[TK_WAVES + i]); }
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) key[v] -= kmin;  // relative keys (garbage where j >= n)
+
+  // radix selection of the k-th largest relative key
+  const uint32_t range = kmax - kmin;
+  uint32_t thr = 0;       // known high bits of the threshold (relative key)
+  int need = k_eff;       // elements still to take among those matching `thr`
+  int cur = range ? 32 - __builtin_clz(range) : 0;   // bits above `cur` are all equal
+  while (cur > 0) {
+    const int width = cur < 8 ? cur : 8;
+    const int sh = cur - width;
+    hist[tid] = 0;  // TK_THREADS == 256 bins
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      const int j = v * TK_THREADS + tid;
+      const bool in_play = j < n && (cur >= 32 || (key[v] >> cur) == thr);
+      if (in_play) atomicAdd(&hist[(key[v] >> sh) & ((1u << width) - 1u)], 1u);
+    }
+    __syncthreads();
+    if (w == 0) {
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      uint32_t suf = mine;  // sum over lanes >= lane
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_down((int)suf, o, 64);
+        if (lane + o < 64) suf += y;
+      }
+      uint32_t above = suf - mine;  // bins held by higher lanes
+      if (above < (uint32_t)need && suf >= (uint32_t)need) {
+        uint32_t d;
+        if (above + c3 >= (uint32_t)need) d = 3;
+        else if ((above += c3) + c2 >= (uint32_t)need) d = 2;
+        else if ((above += c2) + c1 >= (uint32_t)need) d = 1;
+        else { above += c1; d = 0; }
+        sel_digit = 4 * lane + d;
+        sel_above = above;
+      }
+    }
+    __syncthreads();
+    thr = (thr << width) | sel_digit;
+    need -= (int)sel_above;
+    cur = sh;
+    __syncthreads();
+  }
+
+  // compaction in index order: key > thr, or key == thr among the first `need` ties
+  int base = 0, tie_base = 0;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    if (v * TK_THREADS >= n) break;  // block-uniform
+    const int j = v * TK_THREADS + tid;
+    const bool valid = j < n;
+    const bool gt = valid && key[v] > thr;
+    const bool eq = valid && key[v] == thr;
+    int eq_total;
+    const int eq_rank = block_rank(eq, wsum, eq_total);
+    const bool sel = gt || (eq && tie_base + eq_rank < need);
+    int sel_total;
+    const int pos = block_rank(sel, wsum, sel_total);
+    if (sel && base + pos < k_eff) out[base + pos] = g.k_base + j;
+    base += sel_total;
+    tie_base += eq_total;
+  }
+}
+
+bool topk_supported(int max_seqlen_k, int k_eff) { return max_seqlen_k <= 16384 && k_eff >= 0; }
+
+hipError_t launch_topk(const LaunchLayout &LL, const float *scores, int64_t ld, int k_eff,
+                       int32_t *ids, hipStream_t st) {
+  if (LL.total_q == 0 || k_eff == 0) return hipSuccess;
+  const int per = (LL.max_seqlen_k + TK_THREADS - 1) / TK_THREADS;
+  dim3 grid((unsigned)LL.total_q), block(TK_THREADS);
+#define CSA_TOPK_CASE(V)                                                                         \
+  if (per <= V) {                                                                                \
+    hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, st, LL.dev, scores, ld, k_eff, ids);     \
+    return hipGetLastError();                                                                    \
+  }
+  CSA_TOPK_CASE(1)
+  CSA_TOPK_CASE(2)
+  CSA_TOPK_CASE(4)
+  CSA_TOPK_CASE(8)
+  CSA_TOPK_CASE(16)
+  CSA_TOPK_CASE(32)
+  CSA_TOPK_CASE(64)
+#undef CSA_TOPK_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace csa

@@ -1,0 +1,38 @@
+// Internal launch interface between the C-ABI layer (csa_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "kernels/common.h"
+
+namespace csa {
+
+struct LaunchLayout {
+  LayoutDev dev;
+  int num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k;
+};
+
+hipError_t launch_indexer_score(const LaunchLayout &L, const void *q_idx, const void *k_idx,
+                                const float *weights, bool bf16, int Hi, int Di, float idx_scale,
+                                float *scores, int64_t ld, hipStream_t st);
+
+hipError_t launch_topk(const LaunchLayout &L, const float *scores, int64_t ld, int k_eff,
+                       int32_t *ids, hipStream_t st);
+
+hipError_t launch_sparse_attn(const LaunchLayout &L, const void *q, const void *kv,
+                              const void *ckv, const float *sink, const int32_t *ids, int k_eff,
+                              int window, bool bf16, int H, int D, float scale, void *out,
+                              float *lse, float *lse_nc, float *cmass, hipStream_t st);
+
+hipError_t launch_teacher_kl(const LaunchLayout &L, bool sparse, const float *scores, int64_t ld,
+                             const int32_t *ids, int k_eff, const float *cmass, const void *q,
+                             const void *ckv, const float *lse_nc, bool bf16, int H, int D,
+                             float scale, bool per_token, float *teacher, int64_t ld_teacher,
+                             float *kl_row, float *loss, hipStream_t st);
+
+// shape support tables (host side, used by validation before any launch)
+bool indexer_supported(bool bf16, int Hi, int Di);
+bool topk_supported(int max_seqlen_k, int k_eff);
+bool attn_supported(bool bf16, int H, int D, int k_eff);
+bool dense_teacher_supported(bool bf16, int H, int D, int max_seqlen_k);
+
+}  // namespace csa

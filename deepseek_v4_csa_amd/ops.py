@@ -1,0 +1,216 @@
+"""Thin Python binding of libcsa.so (include/csa.h): argument marshalling only.
+
+Every function here has the name of a C entry point, takes torch tensors already on the
+GPU, passes their device pointers and the current HIP stream, and raises RuntimeError
+with the library's message when the call returns a non-OK status.  No arithmetic of
+the method runs in Python; there is no CPU fallback: if the library is missing or the
+tensors are not on a GPU the call fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+_lib = None
+
+CSA_F32, CSA_BF16 = 0, 1
+
+
+class _CLayout(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("total_k", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32),
+        ("compress_ratio", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_k", ctypes.c_void_p),
+        ("q_causal_offsets", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = ("csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
+           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libcsa.so (after torch, so the process keeps a single HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m deepseek_v4_csa_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    LP = ctypes.POINTER(_CLayout)
+    lib.csa_last_error.restype = ctypes.c_char_p
+    lib.csa_last_error.argtypes = []
+    lib.csa_k_eff.restype = I32
+    lib.csa_k_eff.argtypes = [LP, I32]
+    lib.csa_indexer_score.restype = ctypes.c_int
+    lib.csa_indexer_score.argtypes = [LP, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, P]
+    lib.csa_topk.restype = ctypes.c_int
+    lib.csa_topk.argtypes = [LP, P, I64, I32, P, P]
+    lib.csa_sparse_attn_fwd.restype = ctypes.c_int
+    lib.csa_sparse_attn_fwd.argtypes = [LP, P, P, P, P, P, I32, I32, ctypes.c_int, I32, I32, F32,
+                                        P, P, P, P, P]
+    lib.csa_indexer_teacher_kl.restype = ctypes.c_int
+    lib.csa_indexer_teacher_kl.argtypes = [LP, I32, P, I64, P, I32, P, P, P, P, ctypes.c_int, I32,
+                                           I32, F32, I32, P, I64, P, P, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().csa_last_error().decode()
+        raise RuntimeError(f"libcsa status {status}: {msg}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise RuntimeError("libcsa takes GPU tensors only")
+    if not t.is_contiguous():
+        raise RuntimeError("libcsa takes contiguous tensors only")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    if t.dtype == torch.float32:
+        return CSA_F32
+    raise RuntimeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+@dataclass
+class Layout:
+    """Packed layout: device int32 cu_seqlens (and offsets) plus host sizes."""
+    cu_q: torch.Tensor
+    cu_k: torch.Tensor
+    ratio: int
+    total_q: int
+    total_k: int
+    max_seqlen_q: int
+    max_seqlen_k: int
+    offsets: torch.Tensor | None = None
+
+    @property
+    def num_seqs(self) -> int:
+        return self.cu_q.numel() - 1
+
+    @classmethod
+    def from_lengths(cls, seg_q, seg_k, ratio, device="cuda", offsets=None):
+        cq = [0]
+        ck = [0]
+        for a, b in zip(seg_q, seg_k):
+            cq.append(cq[-1] + int(a))
+            ck.append(ck[-1] + int(b))
+        mk = lambda v: torch.tensor(v, dtype=torch.int32, device=device)
+        return cls(mk(cq), mk(ck), int(ratio), cq[-1], ck[-1], max(int(a) for a in seg_q),
+                   max(int(b) for b in seg_k), None if offsets is None else mk(list(offsets)))
+
+    def c(self) -> _CLayout:
+        return _CLayout(self.num_seqs, int(self.total_q), int(self.total_k), int(self.max_seqlen_q),
+                        int(self.max_seqlen_k), int(self.ratio), _ptr(self.cu_q), _ptr(self.cu_k),
+                        _ptr(self.offsets) if self.offsets is not None else None)
+
+
+def k_eff(layout: Layout, topk: int) -> int:
+    return int(load().csa_k_eff(ctypes.byref(layout.c()), int(topk)))
+
+
+def csa_indexer_score(layout: Layout, q_idx, k_idx, weights, idx_scale: float, scores=None):
+    T, Hi, Di = q_idx.shape
+    if scores is None:
+        scores = torch.empty((T, layout.max_seqlen_k), dtype=torch.float32, device=q_idx.device)
+    _check(load().csa_indexer_score(ctypes.byref(layout.c()), _ptr(q_idx), _ptr(k_idx), _ptr(weights),
+                                    _dtype(q_idx), Hi, Di, float(idx_scale), _ptr(scores),
+                                    scores.stride(0), _stream()))
+    return scores
+
+
+def csa_topk(layout: Layout, scores, topk: int, ids=None):
+    ke = k_eff(layout, topk)
+    if ids is None:
+        ids = torch.empty((scores.shape[0], ke), dtype=torch.int32, device=scores.device)
+    _check(load().csa_topk(ctypes.byref(layout.c()), _ptr(scores), scores.stride(0), int(topk),
+                           _ptr(ids), _stream()))
+    return ids
+
+
+def csa_sparse_attn_fwd(layout: Layout, q, kv, ckv, sink, ids, window: int, softmax_scale: float,
+                        out=None, lse=None, lse_nc=None, cmass=None, want_cmass=True):
+    T, H, D = q.shape
+    k_eff_ = ids.shape[1]
+    dev = q.device
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse
+    lse_nc = torch.empty((T, H), dtype=torch.float32, device=dev) if lse_nc is None else lse_nc
+    if want_cmass and cmass is None:
+        cmass = torch.empty((T, k_eff_), dtype=torch.float32, device=dev)
+    _check(load().csa_sparse_attn_fwd(ctypes.byref(layout.c()), _ptr(q), _ptr(kv), _ptr(ckv), _ptr(sink),
+                                      _ptr(ids), k_eff_, int(window), _dtype(q), H, D,
+                                      float(softmax_scale), _ptr(out), _ptr(lse), _ptr(lse_nc),
+                                      _ptr(cmass) if want_cmass else None, _stream()))
+    return out, lse, lse_nc, cmass
+
+
+def csa_indexer_teacher_kl(layout: Layout, sparse_loss: bool, scores, ids, cmass, q, ckv, lse_nc,
+                           softmax_scale: float, per_token: bool = False, want_teacher: bool = False,
+                           teacher=None, kl_row=None, loss=None):
+    T = scores.shape[0]
+    dev = scores.device
+    H = q.shape[1] if q is not None else 1
+    D = q.shape[2] if q is not None else 1
+    k_eff_ = ids.shape[1] if ids is not None else 0
+    if want_teacher and teacher is None:
+        width = k_eff_ if sparse_loss else layout.max_seqlen_k
+        teacher = torch.empty((T, width), dtype=torch.float32, device=dev)
+    kl_row = torch.empty((T,), dtype=torch.float32, device=dev) if kl_row is None else kl_row
+    loss = torch.empty((1,), dtype=torch.float32, device=dev) if loss is None else loss
+    dt = _dtype(q) if q is not None else CSA_BF16
+    _check(load().csa_indexer_teacher_kl(
+        ctypes.byref(layout.c()), 1 if sparse_loss else 0, _ptr(scores), scores.stride(0),
+        _ptr(ids) if ids is not None else None, k_eff_, _ptr(cmass) if cmass is not None else None,
+        _ptr(q) if q is not None else None, _ptr(ckv) if ckv is not None else None,
+        _ptr(lse_nc) if lse_nc is not None else None, dt, H, D, float(softmax_scale),
+        1 if per_token else 0, _ptr(teacher) if teacher is not None else None,
+        teacher.stride(0) if teacher is not None else 0, _ptr(kl_row), _ptr(loss), _stream()))
+    return teacher, kl_row, loss
+
+
+def layout_of_inputs(inp) -> Layout:
+    """Layout of a deepseek_v4_csa_amd.inputs.Inputs (device tensors already built)."""
+    wl = inp.wl
+    return Layout(inp.cu_q, inp.cu_k, wl.ratio, wl.total_q, wl.total_k, wl.max_seqlen_q,
+                  wl.max_seqlen_k, inp.offsets)
+
+
+def forward(inp, want_teacher=False):
+    """The whole path on one Inputs: the four calls on the current stream."""
+    wl = inp.wl
+    L = layout_of_inputs(inp)
+    scores = csa_indexer_score(L, inp.q_idx, inp.k_idx, inp.weights, inp.idx_scale)
+    ids = csa_topk(L, scores, wl.topk)
+    out, lse, lse_nc, cmass = csa_sparse_attn_fwd(L, inp.q, inp.kv, inp.ckv, inp.sink, ids, wl.window,
+                                                  inp.scale, want_cmass=wl.sparse_loss)
+    teacher, kl_row, loss = csa_indexer_teacher_kl(L, wl.sparse_loss, scores, ids, cmass, inp.q, inp.ckv,
+                                                   lse_nc, inp.scale, want_teacher=want_teacher)
+    return dict(scores=scores, ids=ids, out=out, lse=lse, lse_nc=lse_nc, cmass=cmass,
+                teacher=teacher, kl_row=kl_row, loss=loss)

@@ -1,0 +1,187 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) compressed-sparse-attention (CSA) forward path.
+ *
+ * The path has four calls, run in this order on one HIP stream:
+ *   csa_indexer_score      Lightning-Indexer scores with the compressed causal mask
+ *   csa_topk               per-row top-k with global ids
+ *   csa_sparse_attn_fwd    sliding-window + top-k attention with a per-head sink;
+ *                          also emits lse, the sink+window log-mass and the head-summed
+ *                          compressed probabilities (cmass) the teacher needs
+ *   csa_indexer_teacher_kl paper-equivalent teacher, KL(teacher || indexer softmax)
+ *                          and the loss reduction
+ *
+ * Sources cited below by tag:
+ *  [I5776]  page "[Bug] DSV4 unfused CSA indexer loss uses a compressed-only teacher
+ *           instead of the full CSA attention distribution" (Megatron-LM issue 5776),
+ *           its Megatron-LM code excerpts (csa.py, dsa.py, dsa_kernels.py) and its
+ *           discussion thread (proposal comment, review comment).
+ *  [PR8539] page "Megatron-LM pull request 8539" (cuDNN frontend 1.26 defaults):
+ *           item 1 (global top-k ids), item 2 (bottom-right causal offsets).
+ *
+ * Conventions shared by every call
+ *  - Every tensor pointer is DEVICE memory allocated and owned by the caller (the
+ *    library allocates nothing, frees nothing and keeps no pointer after a call
+ *    returns).  Tensors are dense row-major; the shapes below are in elements.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues
+ *    kernels on it and returns: no host synchronisation, no device->host copy.
+ *  - Misuse that the host can see (null pointers, sizes out of range, an unsupported
+ *    shape or dtype) is rejected BEFORE anything is enqueued, with CSA_ERR_INVALID or
+ *    CSA_ERR_UNSUPPORTED; a launch failure returns CSA_ERR_HIP.  csa_last_error()
+ *    then returns a message (thread-local, valid until the next call on the thread).
+ *  - Device-side data is a precondition and is not validated (that would need a sync):
+ *    cu_seqlens_q/k non-decreasing, starting at 0 and ending at total_q / total_k;
+ *    ids either -1 or a valid global key row.
+ *  - A packed (THD) batch of num_seqs segments is described by csa_layout_t; a BSHD
+ *    batch of b sequences of length S is the special case cu_seqlens_q = [0,S,..,bS]
+ *    (one code path for both).
+ *  - Row geometry (per query row t of segment s), used by every call:
+ *      r = t - cu_q[s],  i = r + 1 + off[s]  (1-based absolute position),
+ *      S_k(s) = cu_k[s+1] - cu_k[s],
+ *      n_valid(t) = clamp(floor(i / compress_ratio), 0, S_k(s))
+ *    i.e. query position i sees compressed keys j < i // ratio ([I5776], csa.py SBHD
+ *    causal-mask excerpt), aligned bottom-right per segment ([PR8539], item 2).
+ *  - k_eff = min(topk, max_seqlen_k) ([I5776], csa.py excerpts: k = min(index_topk,
+ *    n_compressed) for SBHD, min(index_topk, max_seqlen_compressed) for THD).
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID = 1,      /* bad argument visible on the host */
+  CSA_ERR_UNSUPPORTED = 2,  /* valid request without a kernel (shape / dtype) */
+  CSA_ERR_HIP = 3           /* a HIP launch failed */
+} csa_status_t;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype_t;
+
+typedef struct {
+  int32_t num_seqs;          /* B >= 1: sequences (BSHD) or documents (THD) */
+  int32_t total_q;           /* T >= 0: query rows (rows of q, kv, q_idx, weights) */
+  int32_t total_k;           /* T_k >= 1: compressed key rows (rows of ckv, k_idx) */
+  int32_t max_seqlen_q;      /* host copy of max_s (cu_q[s+1]-cu_q[s]), >= 1 */
+  int32_t max_seqlen_k;      /* host copy of max_s S_k(s), >= 1 */
+  int32_t compress_ratio;    /* >= 1 */
+  const int32_t *cu_seqlens_q;     /* device [B+1] */
+  const int32_t *cu_seqlens_k;     /* device [B+1]: compressed-key row boundaries
+                                      ([I5776] THD excerpt: cumsum(seg_len_q // ratio)) */
+  const int32_t *q_causal_offsets; /* device [B] per-segment offsets, or NULL for the
+                                      bottom-right default S_k(s)*ratio - seg_len_q(s)
+                                      ([PR8539], item 2).  A query chunk scored against
+                                      its key prefix passes off = chunk start. */
+} csa_layout_t;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *csa_last_error(void);
+
+/* k_eff = min(topk, L->max_seqlen_k), the width of ids/cmass; -1 if L or topk is bad. */
+int32_t csa_k_eff(const csa_layout_t *L, int32_t topk);
+
+/*
+ * csa_indexer_score -- Lightning-Indexer scores.
+ *   scores[t, j] = sum_h ws[t,h] * max(0, q_idx[t,h,:] . k_idx[cu_k[s]+j, :])  j < n_valid(t)
+ *   scores[t, j] = -inf                                    n_valid(t) <= j < max_seqlen_k
+ * with ws[t,h] = fp32(weights[t,h] * idx_scale) rounded to fp32 ([I5776], csa.py SBHD
+ * excerpt: weights.float() * indexer.softmax_scale).  The ReLU/weighted-head-sum form
+ * is the Lightning-Indexer score; the pages only show the scale folding and the
+ * per-indexer-head intermediate [Sq, B, H_index, Sk], which this call never stores.
+ * One k_idx row is shared by every indexer head.
+ *   q_idx   [T, Hi, Di]  dtype dt        k_idx [T_k, Di] dtype dt
+ *   weights [T, Hi] fp32                 scores [T, ld_scores] fp32, ld_scores >= max_seqlen_k;
+ *                                        columns >= max_seqlen_k are not written.
+ * Supported: dt = CSA_BF16 with Di in {32, 64, 128}; dt = CSA_F32 with Di in {32, 64, 128};
+ * 1 <= Hi <= 128.  Arithmetic: exact products, fp32 accumulation (MFMA), fp32 epilogue.
+ */
+csa_status_t csa_indexer_score(const csa_layout_t *L, const void *q_idx, const void *k_idx,
+                               const float *weights, csa_dtype_t dt, int32_t Hi, int32_t Di,
+                               float idx_scale, float *scores, int64_t ld_scores, void *stream);
+
+/*
+ * csa_topk -- per-row top-k selection.
+ *   K_t = min(k_eff, n_valid(t)) columns j < n_valid(t) with the largest scores[t, j];
+ *   ties go to the lower j.  ids[t, 0..K_t) = cu_k[s] + j in ascending order (global
+ *   ids: [PR8539] item 1, b*S_k + local for BSHD; flat packed ids for THD), and
+ *   ids[t, K_t..k_eff) = -1 ([I5776], csa.py sparse-attention excerpt: picks beyond the
+ *   causal limit become -1).  Only columns j < n_valid(t) are read.
+ *   scores [T, ld_scores] fp32 (finite or -inf; no NaN);  ids [T, k_eff] int32.
+ * Supported: max_seqlen_k <= 16384, 1 <= topk.
+ */
+csa_status_t csa_topk(const csa_layout_t *L, const float *scores, int64_t ld_scores,
+                      int32_t topk, int32_t *ids, void *stream);
+
+/*
+ * csa_sparse_attn_fwd -- sliding-window + top-k compressed attention with a sink.
+ * For query row t of segment s and head h ([I5776] "Paper reference", Z_h equation;
+ * csa.py sparse-attention excerpt: window ids concatenated with the top-k ids, the
+ * sink passed as fp32, softmax_scale on the q.k products):
+ *   window rows   Wset(t) = { t' : max(cu_q[s], t - window + 1) <= t' <= t }
+ *                 (the window ids are not defined on the pages; this reading takes the
+ *                 `window` most recent rows of the segment, the query row included)
+ *   w_ht' = scale * q[t,h,:] . kv[t',:],  c_hj = scale * q[t,h,:] . ckv[ids[t,j],:]
+ *   Z_h = exp(sink[h]) + sum_W exp(w) + sum_{j: ids[t,j] >= 0} exp(c)
+ *   out[t,h,:] = (sum_W exp(w) kv[t',:] + sum_j exp(c) ckv[ids[t,j],:]) / Z_h
+ * One KV row per position is both key and value and is shared by every head; the sink
+ * is a raw logit that carries no value.  Also written:
+ *   lse[t,h]    = log Z_h
+ *   lse_nc[t,h] = u_h = log(exp(sink[h]) + sum_W exp(w))   ([I5776] proposal comment)
+ *   cmass[t,j]  = sum_h exp(c_hj - lse[t,h]) for ids[t,j] >= 0, else 0
+ *   q [T, H, D], kv [T, D], ckv [T_k, D]: dtype dt;   out [T, H, D]: dtype dt
+ *   sink [H] fp32;  ids [T, k_eff] int32;  lse, lse_nc [T, H] fp32;
+ *   cmass [T, k_eff] fp32 or NULL (then not computed).
+ * Supported: dt = CSA_BF16 with D in {64, 128, 192, 256, 512}, dt = CSA_F32 with
+ * D in {64, 128}; 1 <= H <= 128; 0 <= window; 0 <= k_eff <= 4096.
+ * A row with no key at all and sink = -inf gets out = 0, lse = lse_nc = -inf.
+ */
+csa_status_t csa_sparse_attn_fwd(const csa_layout_t *L, const void *q, const void *kv,
+                                 const void *ckv, const float *sink, const int32_t *ids,
+                                 int32_t k_eff, int32_t window, csa_dtype_t dt, int32_t H,
+                                 int32_t D, float softmax_scale, void *out, float *lse,
+                                 float *lse_nc, float *cmass, void *stream);
+
+/*
+ * csa_indexer_teacher_kl -- paper-equivalent teacher, KL and loss.
+ * Support C_t: sparse_loss != 0: the valid top-k slots of ids[t, :];
+ *              sparse_loss == 0: every causally visible key j < n_valid(t)
+ *              ([I5776] proposal comment: top-k intersected with the causally valid
+ *              entries for the sparse loss, all causally visible entries for the dense).
+ * Teacher ([I5776] "Paper reference", t_j equation; proposal comment, l_h and p_hj):
+ *   l_h = log(exp(lse_nc[t,h]) + sum_{j in C} exp(c_hj)),  m_j = sum_h exp(c_hj - l_h),
+ *   teacher_j = m_j / max(sum_{j in C} m_j, 1e-10)
+ *   sparse: m_j = cmass[t, j] (the attention's own l_h);  dense: c_hj = softmax_scale *
+ *   q[t,h,:] . ckv[cu_k[s]+j,:] recomputed here for every j < n_valid(t).
+ * Predictor p = softmax of scores[t, .] over C (sparse: the scores at the local columns
+ * ids - cu_k[s]; dense: columns 0..n_valid(t)-1) ([I5776], dsa_kernels.py excerpt).
+ *   kl_row[t] = sum_{j in C} teacher_j * (log(teacher_j + 1e-10) - log(p_j + 1e-10))
+ *   ([I5776], dsa.py excerpt; review comment "KL numerical contract"); 0 if n_valid(t)=0.
+ *   loss[0] = sum_t kl_row[t] / total_q  (every physical row is in the divisor), or the
+ *   plain sum if per_token_loss != 0.  The reduction is deterministic (no atomics).
+ * Arguments:
+ *   scores [T, ld_scores] fp32 (from csa_indexer_score);  ids [T, k_eff] int32;
+ *   sparse: cmass [T, k_eff] fp32 (q, ckv, lse_nc may be NULL);
+ *   dense:  q [T, H, D], ckv [T_k, D] (dtype dt), lse_nc [T, H] fp32 (cmass may be NULL);
+ *   teacher: NULL, or [T, ld_teacher] fp32 receiving the teacher (sparse: slot j at
+ *            column j, 0 at -1 slots, ld_teacher >= k_eff; dense: column j < n_valid,
+ *            0 beyond, ld_teacher >= max_seqlen_k);
+ *   kl_row [T] fp32;  loss [1] fp32.
+ * Supported (dense): dt = CSA_BF16 with D in {64, 128, 192, 256, 512}, 1 <= H <= 128,
+ * max_seqlen_k <= 8192 (any dtype in sparse mode, where q and ckv are not read).
+ */
+csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss,
+                                    const float *scores, int64_t ld_scores,
+                                    const int32_t *ids, int32_t k_eff, const float *cmass,
+                                    const void *q, const void *ckv, const float *lse_nc,
+                                    csa_dtype_t dt, int32_t H, int32_t D, float softmax_scale,
+                                    int32_t per_token_loss, float *teacher, int64_t ld_teacher,
+                                    float *kl_row, float *loss, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */
