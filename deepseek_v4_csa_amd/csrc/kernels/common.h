@@ -58,12 +58,20 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
   return v;
 }
-// reductions over the 16 lanes of a lane group (lanes with the same l/16)
+// reductions over the 16 lanes of a lane group (lanes with the same l/16), on DPP:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
   return v;
 }
+// 2^x on the hardware unit (no denormal range fix-up: results below 2^-126 flush to 0)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // reductions over the 4 lane groups holding the same l%16
 __device__ __forceinline__ float across_groups_max(float v) {
   v = fmaxf(v, shfl_xor(v, 16));
@@ -122,4 +130,59 @@ __device__ __forceinline__ int seg_offset(const LayoutDev &L, int s, int q_len, 
   return L.off ? __ldg(L.off + s) : s_k * L.ratio - q_len;
 }
 
+}  // namespace csa
+
+namespace csa {
+// ---------------------------------------------------------------- LDS transposing read
+// ds_read_b64_tr_b16 (gfx950): within each 16-lane group, lane j supplies the address of
+// 4 consecutive bf16 X[j][0..3]; lane i receives X[4k + i/4][i%4], k = 0..3.  When lane j
+// points at row R + j/4, columns C + 4*(j%4) of a row-major bf16 tile, lane i receives
+// column C + i of rows R..R+3 -- a 4x16 transpose, the K-major operand layout of MFMA.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ uint2 lds_read_tr16(const char *lds_ptr) {
+  lds_v4i16 *p = (lds_v4i16 *)(const_cast<char *>(lds_ptr));
+  v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+  return __builtin_bit_cast(uint2, v);
+}
+}  // namespace csa
+
+namespace csa {
+// ---------------------------------------------------------------- buffer loads
+// A raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes return
+// zeros instead of touching memory (the hardware range check of gfx9 raw buffers).
+constexpr uint32_t BUF_OOB = 0x7fffffffu;  // an offset past every resource used here
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// lane shuffle through the LDS crossbar with a precomputed byte address (lane * 4)
+__device__ __forceinline__ float bperm(int addr, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, v)));
+}
+}  // namespace csa
+
+namespace csa {
+// ---------------------------------------------------------------- LDS DMA
+// buffer_load_dwordx4 ... lds (gfx950): lane i's 16 bytes from rsrc+voffset land at
+// lds_base + 16*i; an out-of-range offset reads zeros.  Completion is tracked by vmcnt,
+// which the kernels wait on explicitly before reading the tile.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, (int)voff, 0, 0, 0);
+}
+// s_waitcnt with only vmcnt constrained (expcnt 7 and lgkmcnt 15 = no wait); N <= 15
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 15, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 }  // namespace csa

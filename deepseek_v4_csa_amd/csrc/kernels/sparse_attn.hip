@@ -286,6 +286,304 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
   }
 }
 
+// ============================================================================
+// Gather-optimised variant (bf16; 16 heads per wave; k_eff <= 32*KC, KC <= 8).
+//
+// One wave per (query row, group of 16 heads), independent waves (no barriers).
+// Row gathers are the cost that matters here: a load instruction whose 64 lanes touch
+// 16 different rows (the MFMA register layout) sustains about a third of the rate of
+// one whose lanes cover 4 whole rows.  So rows are fetched row-coalesced with direct
+// buffer->LDS loads (16 lanes x 16 bytes per 256-byte row, no VGPRs involved) into a
+// per-wave double-buffered LDS tile, while the previous tile is consumed:
+//   S^T = K Q^T     K operand read from the tile (16-byte LDS reads)
+//   O^T += V^T P^T  V^T operand read from the same tile with the transposing LDS read
+// The 16-byte pieces of row R are stored XOR-swizzled (position = piece ^ swz(R)) so
+// that both read patterns are free of bank conflicts.  An online softmax carries the
+// per-head running max (identical in the 4 lane groups of a head, raised only when a
+// logit exceeds it by 2^8) and a per-lane partial sum; the compressed logits stay in
+// registers so that cmass = sum_h exp(c - lse) is formed once lse is final.
+// ============================================================================
+__device__ __forceinline__ int row_swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+template <int D, int KC>
+__global__ __launch_bounds__(256) void sparse_attn_dma_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
+    const uint16_t *__restrict__ ckv, const float *__restrict__ sink,
+    const int32_t *__restrict__ ids, int k_eff, int window, int H, int total_q, int total_k,
+    float sl2, uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ lse_nc,
+    float *__restrict__ cmass) {
+  constexpr int NC = D / 32;          // MFMA K-chunks per row
+  constexpr int ROWB = D * 2;         // bytes per KV row
+  constexpr int PIECES = D / 8;       // 16-byte pieces per row
+  constexpr int RPI = 64 / PIECES;    // rows per direct-to-LDS load instruction
+  constexpr int NI = 32 / RPI;        // load instructions per 32-row step
+  constexpr int TILE = 32 * ROWB;     // one 32-row tile
+  constexpr int IDS = 32 * KC;        // id slots staged in LDS
+  constexpr float NINF = -__builtin_inff();
+  constexpr float RESCALE = 8.f;
+  static_assert(NI <= 15, "vmcnt");
+  __shared__ __attribute__((aligned(16))) char lds_all[4][2 * TILE + IDS * 4];
+  // the wave index is uniform: readfirstlane lets every per-query value live in SGPRs
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const int hgc = (H + 15) >> 4;            // waves per query (1, 2 or 4)
+  const int t = blockIdx.x * (4 / hgc) + w / hgc;
+  if (t >= total_q) return;                 // no block-level barrier below
+  const int hgrp = w % hgc;
+  char *tiles = lds_all[w];
+  int *ids_l = reinterpret_cast<int *>(tiles + 2 * TILE);
+  const int h = 16 * hgrp + r16;
+  const bool h_ok = h < H;
+  const bool group_full = 16 * (hgrp + 1) <= H;
+  const RowGeo geo = row_geo(L, t);
+  const int w_lo = max(geo.q_start, t - window + 1);
+  const int nw = window > 0 ? t - w_lo + 1 : 0;
+  const int nwc = (nw + 31) >> 5;
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)total_q * ROWB);
+  const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * ROWB);
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // bpermute addresses
+
+  // Masked rows read zeros or keep stale tile contents; the tiles start zeroed so those
+  // are always finite (their probabilities are exactly 0).
+#pragma unroll
+  for (int i = 0; i < 2 * TILE / 1024; ++i) reinterpret_cast<u32x4 *>(tiles)[i * 64 + lane] = u32x4{0, 0, 0, 0};
+  // ids in LDS ordered [step][row-in-instruction][instruction]: a lane's ids of one step
+  // are contiguous
+#pragma unroll
+  for (int s0 = 0; s0 < IDS; s0 += 64) {
+    const int s = s0 + lane;
+    if (s < IDS) {
+      const int rs = s & 31;
+      ids_l[(s & ~31) + (rs % RPI) * NI + rs / RPI] = s < k_eff ? ids[(int64_t)t * k_eff + s] : -1;
+    }
+  }
+  // MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
+  u32x4 qf[NC];
+  {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok ? h : 0)) * D) + g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = h_ok ? p[4 * c] : u32x4{0, 0, 0, 0};
+  }
+  // per-lane LDS offsets (relative to a tile)
+  const int gg = lane / PIECES, pp = lane % PIECES;   // load: row-in-instruction, piece position
+  int kro[NC];                                         // K operand: row r16, piece 4c+g
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kro[c] = r16 * ROWB + 16 * ((4 * c + g) ^ row_swz(r16));
+  const int rho = 4 * g + (r16 >> 2);                  // V^T operand: rows rho (+16)
+  int tro[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    tro[dt] = rho * ROWB + 16 * ((2 * dt + ((r16 & 3) >> 1)) ^ row_swz(rho)) + 8 * (r16 & 1);
+
+  auto dma_window = [&](int c, char *base) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int R = i * RPI + gg, slot = 32 * c + R;
+      const uint32_t off = slot < nw ? (uint32_t)(w_lo + slot) * ROWB + 16 * (pp ^ row_swz(R)) : BUF_OOB;
+      dma16(rkv, base + i * 1024, off);
+    }
+  };
+  auto dma_comp = [&](int c, char *base) {
+    int idr[NI];
+    if (c < KC) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) idr[i] = ids_l[c * 32 + gg * NI + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) idr[i] = -1;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int R = i * RPI + gg;
+      const uint32_t off = idr[i] >= 0 ? (uint32_t)idr[i] * ROWB + 16 * (pp ^ row_swz(R)) : BUF_OOB;
+      dma16(rck, base + i * 1024, off);
+    }
+  };
+
+  const float a2 = h_ok ? sink[h] * LOG2E : NINF;
+  float m = a2;                                        // shared by the 4 lane groups of a head
+  float l = (g == 0 && a2 > NINF) ? 1.f : 0.f;         // per-lane partial sum
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one 32-row step on the tile at `base`; bm = row validity bits; leaves this lane's
+  // unscaled masked logits in raw
+  auto step = [&](const char *base, uint32_t bm, float(&raw)[8]) {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const u32x4 k0 = *reinterpret_cast<const u32x4 *>(base + kro[c]);
+      const u32x4 k1 = *reinterpret_cast<const u32x4 *>(base + 16 * ROWB + kro[c]);
+      acc0 = mfma16x16x32(k0, qf[c], acc0);
+      acc1 = mfma16x16x32(k1, qf[c], acc1);
+    }
+    if (group_full && bm == 0xffffffffu) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { raw[i] = acc0[i]; raw[4 + i] = acc1[i]; }
+    } else {
+      const uint32_t m0 = h_ok ? (bm >> (4 * g)) : 0u, m1 = h_ok ? (bm >> (16 + 4 * g)) : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        raw[i] = ((m0 >> i) & 1) ? acc0[i] : NINF;
+        raw[4 + i] = ((m1 >> i) & 1) ? acc1[i] : NINF;
+      }
+    }
+    // Common path without cross-lane traffic: each lane tests its logits against the
+    // shared reference max; only a logit 2^8 above it makes the wave agree on a new
+    // per-head max and rescale.
+    float cmx = fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
+                      fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
+    if (__builtin_expect(__ballot(cmx * sl2 > m + RESCALE) != 0, 0)) {
+      cmx = fmaxf(cmx, bperm(x16, cmx));
+      cmx = fmaxf(cmx, bperm(x32, cmx));
+      const float cand = cmx * sl2;
+      const float mn = cand > m + RESCALE ? cand : m;
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
+      m = mn;
+    }
+    const float nms = m == NINF ? 0.f : -m;
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(fmaf(raw[e], sl2, nms)); l += p[e]; }
+    const u32x4 pb = {pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]),
+                      pack2_bf16(p[6], p[7])};
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const uint2 x0 = lds_read_tr16(base + tro[dt]);
+      const uint2 x1 = lds_read_tr16(base + 16 * ROWB + tro[dt]);
+      const u32x4 a = {x0.x, x0.y, x1.x, x1.y};
+      o[dt] = mfma16x16x32(a, pb, o[dt]);
+    }
+  };
+  // row validity of compressed step c: bit R set iff the id of row R is >= 0
+  auto comp_mask = [&](int c) -> uint32_t {
+    const int R = lane & 31;
+    const bool v = ids_l[c * 32 + (R % RPI) * NI + R / RPI] >= 0;
+    return (uint32_t)__ballot(v);
+  };
+  auto win_mask = [&](int c) -> uint32_t {
+    const int n = nw - 32 * c;
+    return n >= 32 ? 0xffffffffu : (n > 0 ? (1u << n) - 1u : 0u);
+  };
+
+  // Pipeline: step n reads tile n&1 while step n+1's rows stream into the other tile.
+  // Before a tile is overwritten every earlier LDS read has returned (lgkmcnt 0); before
+  // a tile is read its NI loads have landed (vmcnt NI: only the next step's NI loads may
+  // still be in flight).  Past the last step the prefetch reads out of range (zeros).
+  float raw[8];
+  int n = 0;  // global step index
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // the zeroing and id stores have executed
+  if (nwc > 0) dma_window(0, tiles); else dma_comp(0, tiles);
+  for (int c = 0; c < nwc; ++c, ++n) {
+    char *cur = tiles + (n & 1) * TILE, *nxt = tiles + ((n + 1) & 1) * TILE;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    if (c + 1 < nwc) dma_window(c + 1, nxt); else dma_comp(0, nxt);
+    wait_vmcnt<NI>();
+    step(cur, win_mask(c), raw);
+  }
+  const float m_nc = m, l_nc = l;
+
+  float sk[KC][8];  // unscaled compressed logits (-inf when masked)
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk[c][e] = NINF;
+    if (32 * c < k_eff) {
+      char *cur = tiles + (n & 1) * TILE, *nxt = tiles + ((n + 1) & 1) * TILE;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      dma_comp(32 * (c + 1) < k_eff ? c + 1 : KC, nxt);
+      wait_vmcnt<NI>();
+      const uint32_t bm = comp_mask(c);
+      if (bm) step(cur, bm, sk[c]);
+      ++n;
+    }
+  }
+
+  // ---- final statistics (the 4 lane groups of a head share m; sums are partial)
+  const float Ls = across_groups_sum(l);
+  const float Lnc = across_groups_sum(l_nc);
+  const float lse2 = Ls > 0.f ? m + __log2f(Ls) : NINF;
+  const float lse2_nc = Lnc > 0.f ? m_nc + __log2f(Lnc) : NINF;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  if (h_ok && g == 0) {
+    lse[(int64_t)t * H + h] = lse2 * LN2;
+    lse_nc[(int64_t)t * H + h] = lse2_nc * LN2;
+  }
+  // O through the LDS tile so every lane stores 16 contiguous bytes: rows of the tile
+  // are heads (D bf16 each)
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  {
+    char *ob = tiles;  // 16 heads x ROWB bytes (<= one tile)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      uint2 pk = {pack2_bf16(o[dt][0] * inv, o[dt][1] * inv), pack2_bf16(o[dt][2] * inv, o[dt][3] * inv)};
+      *reinterpret_cast<uint2 *>(ob + r16 * ROWB + (dt * 16 + 4 * g) * 2) = pk;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    const int nh = min(16, H - 16 * hgrp);   // heads of this group that exist
+    uint16_t *obase = out + ((int64_t)t * H + 16 * hgrp) * D;
+#pragma unroll
+    for (int k = 0; k < 16 * ROWB / 1024; ++k) {
+      const int byte = k * 1024 + lane * 16;
+      if (byte < nh * ROWB)
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(obase) + byte) = *reinterpret_cast<const u32x4 *>(ob + byte);
+    }
+  }
+  if (cmass != nullptr && hgc == 1) {
+    const float nl = (lse2 == NINF || !h_ok) ? NINF : -lse2;   // exp2(-inf) = 0 for dead heads
+    float *crow = cmass + (int64_t)t * k_eff;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (32 * c >= k_eff) break;
+      float sums[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sums[e] = group16_sum(fast_exp2(fmaf(sk[c][e], sl2, nl)));
+      // lane r16 = tau of group g writes slots 32c + 16*tau + 4g + (0..3)
+      const int slot0 = 32 * c + 16 * r16 + 4 * g;
+      if (r16 < 2) {
+        const f32x4 v = r16 ? f32x4{sums[4], sums[5], sums[6], sums[7]} : f32x4{sums[0], sums[1], sums[2], sums[3]};
+        if (slot0 + 4 <= k_eff) {
+          *reinterpret_cast<f32x4 *>(crow + slot0) = v;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (slot0 + i < k_eff) crow[slot0 + i] = v[i];
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_dma(const LaunchLayout &LL, const void *q, const void *kv, const void *ckv,
+                             const float *sink, const int32_t *ids, int k_eff, int window, int H,
+                             float scale, void *out, float *lse, float *lse_nc, float *cmass,
+                             hipStream_t st) {
+  const int hgc = (H + 15) / 16;
+  const int qpw = 4 / hgc;
+  dim3 grid((unsigned)((LL.total_q + qpw - 1) / qpw));
+  const float sl2 = scale * LOG2E;
+#define CSA_DMA_CASE(K)                                                                              \
+  if (k_eff <= 32 * K) {                                                                             \
+    hipLaunchKernelGGL((sparse_attn_dma_kernel<D, K>), grid, dim3(256), 0, st, LL.dev,               \
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),          \
+                       static_cast<const uint16_t *>(ckv), sink, ids, k_eff, window, H, LL.total_q,  \
+                       LL.total_k, sl2, static_cast<uint16_t *>(out), lse, lse_nc, cmass);           \
+    return hipGetLastError();                                                                        \
+  }
+  CSA_DMA_CASE(1)
+  CSA_DMA_CASE(2)
+  CSA_DMA_CASE(4)
+  CSA_DMA_CASE(8)
+#undef CSA_DMA_CASE
+  return hipErrorInvalidValue;
+}
+
 template <typename IN, int D>
 static hipError_t launch_d(const LaunchLayout &LL, const void *q, const void *kv, const void *ckv,
                            const float *sink, const int32_t *ids, int k_eff, int window, int H,
@@ -322,6 +620,15 @@ hipError_t launch_sparse_attn(const LaunchLayout &LL, const void *q, const void 
                               float *lse, float *lse_nc, float *cmass, hipStream_t st) {
   if (LL.total_q == 0) return hipSuccess;
 #define CSA_ARGS LL, q, kv, ckv, sink, ids, k_eff, window, H, scale, out, lse, lse_nc, cmass, st
+  // gather-optimised variant: one wave per 16 heads, cmass from kept logits
+  // (buffer offsets are 32-bit: both KV tensors must stay below 2 GiB)
+  if (bf16 && H <= 16 && k_eff >= 1 && k_eff <= 256 && (int64_t)LL.total_q * D * 2 < (1ll << 31) &&
+      (int64_t)LL.total_k * D * 2 < (1ll << 31)) {
+    switch (D) {
+      case 64: return launch_dma<64>(CSA_ARGS);
+      case 128: return launch_dma<128>(CSA_ARGS);
+    }
+  }
   if (bf16) {
     switch (D) {
       case 64: return launch_d<uint16_t, 64>(CSA_ARGS);
