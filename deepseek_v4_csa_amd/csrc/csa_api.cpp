@@ -166,6 +166,7 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, 
     if (k_eff < 1 || k_eff > L->max_seqlen_k)
       return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [1, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
     if (!ids || !cmass) return fail(CSA_ERR_INVALID, "%s: sparse loss needs ids and cmass", fn);
+    if (k_eff > 4096) return fail(CSA_ERR_UNSUPPORTED, "%s: k_eff=%d above the supported 4096", fn, k_eff);
     if (teacher && ld_teacher < k_eff)
       return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < k_eff=%d", fn, (long long)ld_teacher, k_eff);
   } else {

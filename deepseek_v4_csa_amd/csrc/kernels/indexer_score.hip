@@ -158,6 +158,192 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_score_kernel(
   }
 }
 
+// ============================================================================
+// LDS-staged variant (bf16, Hi*Di*2 in {1, 2, 4} KiB).  One workgroup = 16 tokens x a
+// 256-key chunk of one segment; wave w owns the 64-key tile 4*chunk + w.
+//
+// q_idx of the 16 tokens is one contiguous block of 16 rows; it is copied into LDS by
+// buffer-load-to-LDS, each wave instruction moving 1 KiB of one row, so the reads are
+// fully coalesced.  In LDS, 16-byte chunk q of token r sits at slot r*CPR + (q ^ r): a
+// 1 KiB piece of a row maps onto itself under the XOR (r < 16), so lane i of the copy
+// fetches chunk (q0 + i) ^ r and lands at slot q0 + i; when the MFMA A operand is read
+// (lane (r, g) wants chunk h*Di/8 + 4c + g of token r) the 16 lanes of a group hit 16
+// different 16-byte bank groups.
+//
+// Per head: Di/32 MFMAs per 16-key N-tile (the key tile stays in registers), then the
+// ReLU x fp32(w * s_idx) epilogue folded into the (token, key) accumulator; the MFMAs of
+// head h+1 are issued before the epilogue of head h.  Key tiles entirely above the
+// causal limit of the 16 tokens are only filled with -inf.  Workgroup ids are mapped so
+// that the chunks of one token block go to one XCD, one after the other, and share its
+// L2 copy of the block's q_idx.
+// ============================================================================
+constexpr int IXL_TOK = 16;
+
+// max(x, 0) in one integer max on the bit pattern: a float with the sign bit set is a
+// negative int32 (-> +0), a non-negative float keeps its bits
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+template <int DI, int HI>
+__global__ __launch_bounds__(256) void indexer_score_lds_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
+    const float *__restrict__ weights, float idx_scale, float *__restrict__ scores, int64_t ld,
+    int max_sk, int total_q, int nqb, int nch) {
+  constexpr int RB = HI * DI * 2;   // bytes of one token's q_idx row
+  constexpr int CPR = RB / 16;      // 16-byte chunks per row
+  constexpr int PPR = RB / 1024;    // 1 KiB pieces per row
+  constexpr int NCD = DI / 32;
+  static_assert(RB % 1024 == 0 && (IXL_TOK * PPR) % 4 == 0, "row of whole KiB pieces");
+  __shared__ __attribute__((aligned(16))) u32x4 qs[IXL_TOK * CPR];
+  __shared__ __attribute__((aligned(16))) float ws[HI * IXL_TOK];
+
+  const int id = blockIdx.x;
+  const int chunk = (id >> 3) % nch;
+  const int blk = (id & 7) + 8 * ((id >> 3) / nch);
+  const int seg = blk / nqb, qb = blk - seg * nqb;
+  if (seg >= L.num_seqs) return;
+  const int q_start = __ldg(L.cu_q + seg);
+  const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
+  const int t0 = qb * IXL_TOK;
+  if (t0 >= q_len) return;
+  const int k_base = __ldg(L.cu_k + seg);
+  const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
+  const int off = seg_offset(L, seg, q_len, s_k);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nv_last = n_valid_of(min(t0 + IXL_TOK, q_len) - 1, off, L.ratio, s_k);
+  const int jw = (chunk * 4 + w) * 64;  // first key of this wave's tile
+
+  int nv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nv[i] = n_valid_of(t0 + 4 * g + i, off, L.ratio, s_k);
+  auto store_tile = [&](const f32x4 (&acc)[4], bool masked_only) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      if (t >= q_len) continue;
+      float *dst = scores + (int64_t)(q_start + t) * ld;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int j = jw + 16 * n + r16;
+        if (j < max_sk) dst[j] = (!masked_only && j < nv[i]) ? acc[n][i] : -__builtin_inff();
+      }
+    }
+  };
+  const f32x4 zero4[4] = {};
+  if (chunk * 256 >= nv_last) {  // the whole chunk is above the causal limit (uniform)
+    if (jw < max_sk) store_tile(zero4, true);
+    return;
+  }
+
+  // q_idx rows t0 .. t0+15 -> LDS (rows past the end of the buffer read as zeros)
+  {
+    const int rows_left = min(IXL_TOK, total_q - (q_start + t0));
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(q_idx + (int64_t)(q_start + t0) * (RB / 2), (uint32_t)(rows_left * RB));
+#pragma unroll
+    for (int k = 0; k < IXL_TOK * PPR / 4; ++k) {
+      const int m = k * 4 + w;           // wave instruction index: row r, piece p
+      const int r = m / PPR, q0 = (m - r * PPR) * 64;
+      dma16(rq, reinterpret_cast<char *>(qs) + (size_t)(r * CPR + q0) * 16,
+            (uint32_t)(r * RB + (((q0 + lane) ^ r) << 4)));
+    }
+  }
+  const bool live = jw < nv_last;  // this wave's tile has keys below the causal limit
+  u32x4 kb[4][NCD];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int j = min(jw + 16 * n + r16, s_k - 1);
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(k_idx + (int64_t)(k_base + max(j, 0)) * DI) + g;
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) kb[n][c] = live ? kp[4 * c] : u32x4{0, 0, 0, 0};
+  }
+  // fp32(w * s_idx), head-major: one 16-byte LDS read gives a lane its 4 tokens
+  for (int e = tid; e < HI * IXL_TOK; e += 256) {
+    const int tt = e / HI, h = e - tt * HI;
+    const int t = t0 + tt;
+    ws[h * IXL_TOK + tt] = t < q_len ? weights[(int64_t)(q_start + t) * HI + h] * idx_scale : 0.f;
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  if (!live) {
+    if (jw < max_sk) store_tile(zero4, true);
+    return;
+  }
+
+  const char *qrow = reinterpret_cast<const char *>(qs) + r16 * RB;
+  auto a_frag = [&](int h, int c) -> u32x4 {
+    const int q = h * (DI / 8) + 4 * c + g;
+    return *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
+  };
+  auto head_mfma = [&](const u32x4 (&qa)[NCD], f32x4 (&d)[4]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) d[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCD; ++c)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) d[n] = mfma16x16x32(qa[c], kb[n][c], d[n]);
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float *wsp = ws + 4 * g;
+  u32x4 qa[NCD], qn[NCD];
+#pragma unroll
+  for (int c = 0; c < NCD; ++c) qa[c] = a_frag(0, c);
+  f32x4 dc[4], dn[4];
+  head_mfma(qa, dc);
+#pragma unroll
+  for (int c = 0; c < NCD; ++c) qn[c] = a_frag(HI > 1 ? 1 : 0, c);
+  f32x4 wv = *reinterpret_cast<const f32x4 *>(wsp), wvn = wv;
+#pragma unroll
+  for (int h = 0; h < HI; ++h) {
+    if (h + 1 < HI) {
+      wvn = *reinterpret_cast<const f32x4 *>(wsp + (h + 1) * IXL_TOK);
+      head_mfma(qn, dn);
+      if (h + 2 < HI) {
+#pragma unroll
+        for (int c = 0; c < NCD; ++c) qn[c] = a_frag(h + 2, c);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[n][i] = fmaf(wv[i], relu_bits(dc[n][i]), acc[n][i]);
+      asm volatile("" : "+v"(acc[n]));  // the epilogue of head h stays in iteration h
+    }
+    if (h + 1 < HI) {
+#pragma unroll
+      for (int m = 0; m < 4 * NCD; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 32 / (4 * NCD), 0);  // then VALU
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) dc[n] = dn[n];
+    wv = wvn;
+  }
+  store_tile(acc, false);
+}
+
+template <int DI, int HI>
+static hipError_t launch_lds(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+                             const float *weights, float idx_scale, float *scores, int64_t ld,
+                             hipStream_t st) {
+  const int nqb = (LL.max_seqlen_q + IXL_TOK - 1) / IXL_TOK;
+  const int nch = (LL.max_seqlen_k + 255) / 256;
+  const int64_t nblk = (int64_t)LL.num_seqs * nqb;
+  const int64_t grid = 8 * (int64_t)nch * ((nblk + 7) / 8);
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((indexer_score_lds_kernel<DI, HI>), dim3((unsigned)grid), dim3(256), 0, st, LL.dev,
+                     static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
+                     weights, idx_scale, scores, ld, LL.max_seqlen_k, LL.total_q, nqb, nch);
+  return hipGetLastError();
+}
+
 template <typename IN, int DI>
 static hipError_t launch_t(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
                            const float *weights, int Hi, float idx_scale, float *scores,
@@ -175,6 +361,14 @@ static hipError_t launch_t(const LaunchLayout &LL, const void *q_idx, const void
 hipError_t launch_indexer_score(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
                                 const float *weights, bool bf16, int Hi, int Di, float idx_scale,
                                 float *scores, int64_t ld, hipStream_t st) {
+  if (bf16) {
+    if (Di == 64 && Hi == 8) return launch_lds<64, 8>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
+    if (Di == 64 && Hi == 16) return launch_lds<64, 16>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
+    if (Di == 64 && Hi == 32) return launch_lds<64, 32>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
+    if (Di == 128 && Hi == 4) return launch_lds<128, 4>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
+    if (Di == 128 && Hi == 8) return launch_lds<128, 8>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
+    if (Di == 128 && Hi == 16) return launch_lds<128, 16>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
+  }
   if (bf16) {
     switch (Di) {
       case 32: return launch_t<uint16_t, 32>(LL, q_idx, k_idx, weights, Hi, idx_scale, scores, ld, st);

@@ -24,57 +24,98 @@ namespace csa {
 
 constexpr float EPS = 1e-10f;
 
+// log(1 + x) for x > -1: |x| < 1/2 by the series 2 atanh(u), u = x / (2 + x) (|u| < 1/3,
+// terms through u^15: truncation below 3e-9 relative); otherwise the hardware log of 1 + x,
+// where 1 + x is exact enough (relative error ~1e-7 of the result).
+__device__ __forceinline__ float log1p_kl(float x) {
+  if (fabsf(x) < 0.5f) {
+    const float u = x / (2.f + x);
+    const float u2 = u * u;
+    float p = 1.f / 15.f;
+    p = fmaf(p, u2, 1.f / 13.f);
+    p = fmaf(p, u2, 1.f / 11.f);
+    p = fmaf(p, u2, 1.f / 9.f);
+    p = fmaf(p, u2, 1.f / 7.f);
+    p = fmaf(p, u2, 1.f / 5.f);
+    p = fmaf(p, u2, 1.f / 3.f);
+    p = fmaf(p, u2, 1.f);
+    return 2.f * u * p;
+  }
+  return __log2f(1.f + x) * LN2;
+}
+
 // ---------------------------------------------------------------- sparse
+// One wave per row; slot j = v*64 + lane (v < SPL), so every load is issued up front and
+// coalesced except the score gather (one dependent load per slot).  The KL of two nearly
+// equal distributions is a second-order quantity, so the normalisers and the log-ratios
+// are finished in fp64: an fp32 error in either normaliser shifts the KL by about that
+// relative error.  log(t+eps) - log(p+eps) is taken as one log of the ratio.
+template <int SPL>
 __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
     LayoutDev L, int T, const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ ids,
     int k_eff, const float *__restrict__ cmass, float *__restrict__ teacher, int64_t ldt,
     float *__restrict__ kl_row) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + w;
   if (t >= T) return;
   const RowGeo geo = row_geo(L, t);
   const int32_t *idr = ids + (int64_t)t * k_eff;
   const float *cm = cmass + (int64_t)t * k_eff;
   const float *sr = scores + (int64_t)t * ld;
+  float *te = teacher ? teacher + (int64_t)t * ldt : nullptr;
   if (geo.n_valid == 0) {
-    if (teacher)
-      for (int j = lane; j < k_eff; j += 64) teacher[(int64_t)t * ldt + j] = 0.f;
+    if (te)
+      for (int j = lane; j < k_eff; j += 64) te[j] = 0.f;
     if (lane == 0) kl_row[t] = 0.f;
     return;
   }
-  // predictor statistics and teacher mass over the valid slots.  The KL of two nearly
-  // equal distributions is a second-order quantity, so the normalisations, the
-  // predictor log-probabilities and the log-ratios are finished in fp64: an fp32 error
-  // in either normaliser shifts the KL by about that relative error.
-  float mx = -__builtin_inff();
-  double msum = 0.0;
-  for (int j = lane; j < k_eff; j += 64) {
-    const int id = idr[j];
-    if (id >= 0) {
-      mx = fmaxf(mx, sr[id - geo.k_base]);
-      msum += (double)cm[j];
-    }
+  int id[SPL];
+  float c[SPL], sc[SPL];
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    const int j = v * 64 + lane;
+    id[v] = j < k_eff ? idr[j] : -1;
+    c[v] = j < k_eff ? cm[j] : 0.f;
   }
-  mx = wave_max(mx);
-  msum = wave_sum_f64(msum);
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    sc[v] = id[v] >= 0 ? sr[id[v] - geo.k_base] : -__builtin_inff();
+    mx = fmaxf(mx, sc[v]);
+  }
+  double ms = 0.0;
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) ms += id[v] >= 0 ? (double)c[v] : 0.0;
+  mx = __builtin_amdgcn_readfirstlane(wave_max(mx));
+  ms = wave_sum_f64(ms);
+  // Predictor terms in fp32 (an independent relative error d_j in e_j moves the KL only
+  // through sum_j (t_j - p_j) d_j), the normalisations in fp64.
+  float e[SPL];
   double es = 0.0;
-  for (int j = lane; j < k_eff; j += 64) {
-    const int id = idr[j];
-    if (id >= 0) es += exp((double)sr[id - geo.k_base] - (double)mx);
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    e[v] = id[v] >= 0 ? fast_exp2((sc[v] - mx) * LOG2E) : 0.f;
+    es += (double)e[v];
   }
   es = wave_sum_f64(es);
-  const double lse_i = (double)mx + log(es);
-  const double inv_m = 1.0 / fmax(msum, (double)EPS);
+  const double inv_es = 1.0 / es;
+  const double inv_m = 1.0 / fmax(ms, (double)EPS);
+  // log(t+eps) - log(p+eps) = log1p(x), x = (t - p) / (p + eps): the difference t - p is
+  // taken in fp64, the rest in fp32, so x and log1p(x) err by ~1e-7 of |x| -- the KL
+  // moves by ~1e-7 * sum_j t_j |x_j|, far below its tolerance.
   double kl = 0.0;
-  for (int j = lane; j < k_eff; j += 64) {
-    const int id = idr[j];
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    const int j = v * 64 + lane;
     double tj = 0.0;
-    if (id >= 0) {
-      tj = (double)cm[j] * inv_m;
-      const double pj = exp((double)sr[id - geo.k_base] - lse_i);
-      kl += tj * (log(tj + (double)EPS) - log(pj + (double)EPS));
+    if (id[v] >= 0) {
+      tj = (double)c[v] * inv_m;
+      const double pj = (double)e[v] * inv_es;
+      const float x = (float)(tj - pj) / ((float)pj + EPS);
+      kl += tj * (double)log1p_kl(x);
     }
-    if (teacher) teacher[(int64_t)t * ldt + j] = (float)tj;
+    if (te && j < k_eff) te[j] = (float)tj;
   }
   kl = wave_sum_f64(kl);
   if (lane == 0) kl_row[t] = (float)kl;
@@ -299,10 +340,17 @@ hipError_t launch_teacher_kl(const LaunchLayout &LL, bool sparse, const float *s
   hipError_t e = hipSuccess;
   if (LL.total_q > 0) {
     if (sparse) {
-      hipLaunchKernelGGL(teacher_kl_sparse_kernel, dim3((unsigned)((LL.total_q + 3) / 4)), dim3(256), 0,
-                         st, LL.dev, LL.total_q, scores, ld, ids, k_eff, cmass, teacher, ld_teacher,
-                         kl_row);
-      e = hipGetLastError();
+      const int spl = (k_eff + 63) / 64;
+      const dim3 grid((unsigned)((LL.total_q + 3) / 4));
+#define CSA_TKS_CASE(V)                                                                              \
+      if (spl <= V) {                                                                                \
+        hipLaunchKernelGGL(teacher_kl_sparse_kernel<V>, grid, dim3(256), 0, st, LL.dev, LL.total_q,  \
+                           scores, ld, ids, k_eff, cmass, teacher, ld_teacher, kl_row);              \
+        e = hipGetLastError();                                                                       \
+      } else
+      CSA_TKS_CASE(1) CSA_TKS_CASE(2) CSA_TKS_CASE(4) CSA_TKS_CASE(8) CSA_TKS_CASE(16)
+      CSA_TKS_CASE(32) CSA_TKS_CASE(64) { return hipErrorInvalidValue; }
+#undef CSA_TKS_CASE
     } else {
       (void)bf16;
       switch (D) {

@@ -149,11 +149,122 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   }
 }
 
+// One wave per row (rows up to 64*VPL visible keys): the same selection as above with
+// wave-level primitives only -- a per-wave LDS histogram, a shuffle scan over the 256
+// bins, ballot/mbcnt ranks for the compaction -- so there is no workgroup barrier.
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_wave_kernel(LayoutDev L, int T, const float *__restrict__ scores,
+                                                        int64_t ld, int k_eff, int32_t *__restrict__ ids) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][256];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + w;
+  if (t >= T) return;
+  uint32_t *hist = hist_all[w];
+  const RowGeo g = row_geo(L, t);
+  const int n = g.n_valid;
+  int32_t *out = ids + (int64_t)t * k_eff;
+  if (n <= k_eff) {  // every visible key is selected
+    for (int j = lane; j < k_eff; j += 64) out[j] = j < n ? g.k_base + j : -1;
+    return;
+  }
+  const float *row = scores + (int64_t)t * ld;
+  uint32_t key[VPL];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int j = v * 64 + lane;
+    key[v] = j < n ? ordered_key(row[j]) : 0u;
+    kmin = j < n ? min(kmin, key[v]) : kmin;
+    kmax = j < n ? max(kmax, key[v]) : kmax;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
+  }
+  // wave-reduced values are uniform: keep them (and the loop control below) in SGPRs
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) key[v] -= kmin;   // relative keys (garbage where j >= n)
+  const uint32_t range = kmax - kmin;
+  uint32_t thr = 0;
+  int need = k_eff;
+  int cur = range ? 32 - __builtin_clz(range) : 0;
+  while (cur > 0) {
+    const int width = cur < 8 ? cur : 8;
+    const int sh = cur - width;
+    reinterpret_cast<u32x4 *>(hist)[lane] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int j = v * 64 + lane;
+      const bool in_play = j < n && (cur >= 32 || (key[v] >> cur) == thr);
+      if (in_play) atomicAdd(&hist[(key[v] >> sh) & ((1u << width) - 1u)], 1u);
+    }
+    const u32x4 cb = reinterpret_cast<const u32x4 *>(hist)[lane];
+    const uint32_t mine = cb[0] + cb[1] + cb[2] + cb[3];
+    uint32_t suf = mine;  // sum over lanes >= lane
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_down((int)suf, o, 64);
+      if (lane + o < 64) suf += y;
+    }
+    uint32_t above = suf - mine;
+    const bool here = above < (uint32_t)need && suf >= (uint32_t)need;
+    uint32_t d = 0;
+    if (above + cb[3] >= (uint32_t)need) d = 3;
+    else if ((above += cb[3]) + cb[2] >= (uint32_t)need) d = 2;
+    else if ((above += cb[2]) + cb[1] >= (uint32_t)need) d = 1;
+    else { above += cb[1]; d = 0; }
+    const int src = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(here)));
+    const uint32_t digit = __builtin_amdgcn_readlane(4 * lane + d, src);
+    const uint32_t ab = __builtin_amdgcn_readlane(above, src);
+    thr = (thr << width) | digit;
+    need -= (int)ab;
+    cur = sh;
+  }
+  // compaction in index order: key > thr, or key == thr among the first `need` ties
+  int base = 0, tie_base = 0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    if (v * 64 >= n) break;
+    const int j = v * 64 + lane;
+    const bool valid = j < n;
+    const bool gt = valid && key[v] > thr;
+    const bool eq = valid && key[v] == thr;
+    const uint64_t be = __ballot(eq);
+    const int eq_rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0));
+    const bool sel = gt || (eq && tie_base + eq_rank < need);
+    const uint64_t bs = __ballot(sel);
+    const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0));
+    if (sel && pos < k_eff) out[pos] = g.k_base + j;
+    base += __popcll(bs);
+    tie_base += __popcll(be);
+  }
+}
+
 bool topk_supported(int max_seqlen_k, int k_eff) { return max_seqlen_k <= 16384 && k_eff >= 0; }
 
 hipError_t launch_topk(const LaunchLayout &LL, const float *scores, int64_t ld, int k_eff,
                        int32_t *ids, hipStream_t st) {
   if (LL.total_q == 0 || k_eff == 0) return hipSuccess;
+  if (LL.max_seqlen_k <= 64 * 64) {  // one wave per row
+    const int vpl = (LL.max_seqlen_k + 63) / 64;
+    const dim3 wgrid((unsigned)((LL.total_q + 3) / 4));
+#define CSA_TOPKW_CASE(V)                                                                            \
+    if (vpl <= V) {                                                                                  \
+      hipLaunchKernelGGL(topk_wave_kernel<V>, wgrid, dim3(256), 0, st, LL.dev, LL.total_q, scores, ld, \
+                         k_eff, ids);                                                                \
+      return hipGetLastError();                                                                      \
+    }
+    CSA_TOPKW_CASE(4)
+    CSA_TOPKW_CASE(8)
+    CSA_TOPKW_CASE(16)
+    CSA_TOPKW_CASE(32)
+    CSA_TOPKW_CASE(64)
+#undef CSA_TOPKW_CASE
+  }
   const int per = (LL.max_seqlen_k + TK_THREADS - 1) / TK_THREADS;
   dim3 grid((unsigned)LL.total_q), block(TK_THREADS);
 #define CSA_TOPK_CASE(V)                                                                         \

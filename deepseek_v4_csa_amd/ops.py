@@ -214,3 +214,50 @@ def forward(inp, want_teacher=False):
                                                    lse_nc, inp.scale, want_teacher=want_teacher)
     return dict(scores=scores, ids=ids, out=out, lse=lse, lse_nc=lse_nc, cmass=cmass,
                 teacher=teacher, kl_row=kl_row, loss=loss)
+
+
+class Prepared:
+    """The four calls of one forward step with every ctypes argument built once.
+
+    Marshalling only: the same C entry points with the same arguments as the functions
+    above, but the pointers, strides, layout struct and stream handle are converted a
+    single time, so a host loop can enqueue steps far faster than the GPU runs them.
+    The tensors given here must stay alive and in place while the object is used.
+    """
+
+    def __init__(self, layout: Layout, inp, scores, ids, out, lse, lse_nc, cmass, kl_row, loss,
+                 sparse_loss: bool, topk: int, window: int, teacher=None):
+        lib = load()
+        self._lib = lib
+        self._L = layout.c()
+        Lp = ctypes.byref(self._L)
+        st = _stream()
+        T, Hi, Di = inp.q_idx.shape
+        _, H, D = inp.q.shape
+        k_eff_ = ids.shape[1]
+        self._keep = (inp, scores, ids, out, lse, lse_nc, cmass, kl_row, loss, teacher)
+        self.args_score = (Lp, _ptr(inp.q_idx), _ptr(inp.k_idx), _ptr(inp.weights), _dtype(inp.q_idx),
+                           Hi, Di, ctypes.c_float(inp.idx_scale), _ptr(scores),
+                           ctypes.c_int64(scores.stride(0)), st)
+        self.args_topk = (Lp, _ptr(scores), ctypes.c_int64(scores.stride(0)), int(topk), _ptr(ids), st)
+        self.args_attn = (Lp, _ptr(inp.q), _ptr(inp.kv), _ptr(inp.ckv), _ptr(inp.sink), _ptr(ids), k_eff_,
+                          int(window), _dtype(inp.q), H, D, ctypes.c_float(inp.scale), _ptr(out), _ptr(lse),
+                          _ptr(lse_nc), _ptr(cmass) if cmass is not None else None, st)
+        self.args_tkl = (Lp, 1 if sparse_loss else 0, _ptr(scores), ctypes.c_int64(scores.stride(0)),
+                         _ptr(ids), k_eff_, _ptr(cmass) if cmass is not None else None, _ptr(inp.q),
+                         _ptr(inp.ckv), _ptr(lse_nc), _dtype(inp.q), H, D, ctypes.c_float(inp.scale), 0,
+                         _ptr(teacher) if teacher is not None else None,
+                         ctypes.c_int64(teacher.stride(0) if teacher is not None else 0),
+                         _ptr(kl_row), _ptr(loss), st)
+
+    def csa_indexer_score(self):
+        _check(self._lib.csa_indexer_score(*self.args_score))
+
+    def csa_topk(self):
+        _check(self._lib.csa_topk(*self.args_topk))
+
+    def csa_sparse_attn_fwd(self):
+        _check(self._lib.csa_sparse_attn_fwd(*self.args_attn))
+
+    def csa_indexer_teacher_kl(self):
+        _check(self._lib.csa_indexer_teacher_kl(*self.args_tkl))
