@@ -69,14 +69,17 @@ def work_model(wl):
     }
 
 
-def traffic_of(kernel_src, wl_name, kernel):
-    """HBM bytes per launch from a committed counter summary, if it was taken on the
-    current source of the kernel; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{wl_name}_traffic.json")
+def traffic_of(wl_name, kernel):
+    """HBM bytes per launch of ``kernel`` from the committed counter table of the
+    workload (FETCH_SIZE / WRITE_SIZE scaled by a copy of known size), if it was taken
+    on the current source of the kernel; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"csa_path_{wl_name}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
-    d = json.load(open(path))
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    d = json.load(open(path)).get("kernels", {}).get(kernel)
+    if not d:
+        return None
+    sha = hashlib.sha256(open(os.path.join(ROOT, d["source"]), "rb").read()).hexdigest()
     if d.get("source_sha256") != sha:
         return None
     return d.get("hbm_bytes_per_launch")
@@ -177,10 +180,9 @@ def main():
     wm = work_model(wl)
 
     att_ms = per_kernel_ms["sparse_attn"]
-    src = os.path.join(ROOT, "deepseek_v4_csa_amd", "csrc", "kernels", "sparse_attn.hip")
     roof = {"kernel": "sparse_attn", "bound": "hbm",
             "achieved": wm["attn_bytes"] / (att_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "traffic": traffic_of(src, wl.name, "sparse_attn")}
+            "traffic": traffic_of(wl.name, "sparse_attn")}
     roof["frac"] = roof["achieved"] / roof["peak"]
     idx_peak = FP32_MFMA_PEAK_TFLOPS if wl.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
     kernels = {
