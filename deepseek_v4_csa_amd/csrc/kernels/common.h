@@ -145,6 +145,32 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char *lds_ptr) {
   v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
   return __builtin_bit_cast(uint2, v);
 }
+// The same read issued as inline assembly.  The compiler then does not treat it as an
+// LDS access that might alias buffer-to-LDS loads still in flight (for the builtin it
+// inserts a full vmcnt wait, which would also wait for the next tile's prefetch).  The
+// result is not tracked either: the caller waits on lgkmcnt with lds_tr16_wait before use.
+__device__ __forceinline__ uint2 lds_read_tr16_nowait(const char *lds_ptr) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const lds_v4i16 *)(lds_ptr);
+  uint2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a) : "memory");
+  return r;
+}
+// the same with a constant byte offset added in the instruction's offset field
+template <int OFF> __device__ __forceinline__ uint2 lds_read_tr16_nowait_off(uint32_t lds_addr) {
+  uint2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const void *lds_ptr) {
+  return (uint32_t)(uintptr_t)(const lds_v4i16 *)(lds_ptr);
+}
+// lgkmcnt(0), then every given value is re-defined after the wait (empty volatile asm
+// with a read-write operand), so no instruction using them can be scheduled earlier.
+template <int N> __device__ __forceinline__ void lds_tr16_wait(uint2 (&v)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
 }  // namespace csa
 
 namespace csa {

@@ -159,25 +159,28 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_score_kernel(
 }
 
 // ============================================================================
-// LDS-staged variant (bf16, Hi*Di*2 in {1, 2, 4} KiB).  One workgroup = 16 tokens x a
-// 256-key chunk of one segment; wave w owns the 64-key tile 4*chunk + w.
+// LDS-staged variant (bf16; Di = 64 with Hi*Di*2 in {1, 2, 4} KiB, or Di = 128 with
+// Hi <= 8).  One workgroup (8 waves) = two 16-token blocks of one segment, paired
+// heaviest with lightest (blocks p and nqb-1-p), so that every workgroup has about the
+// same number of key tiles below the causal limit; the 64-key tiles of both blocks are
+// dealt round-robin to the 8 waves.
 //
-// q_idx of the 16 tokens is one contiguous block of 16 rows; it is copied into LDS by
-// buffer-load-to-LDS, each wave instruction moving 1 KiB of one row, so the reads are
-// fully coalesced.  In LDS, 16-byte chunk q of token r sits at slot r*CPR + (q ^ r): a
-// 1 KiB piece of a row maps onto itself under the XOR (r < 16), so lane i of the copy
-// fetches chunk (q0 + i) ^ r and lands at slot q0 + i; when the MFMA A operand is read
-// (lane (r, g) wants chunk h*Di/8 + 4c + g of token r) the 16 lanes of a group hit 16
-// different 16-byte bank groups.
+// q_idx of a block is one contiguous run of 16 rows, read from HBM once: it is copied
+// into LDS by buffer-load-to-LDS, each wave instruction moving 1 KiB of one row, so the
+// reads are fully coalesced.  In LDS, 16-byte chunk q of token r sits at slot
+// r*CPR + (q ^ r): a 1 KiB piece of a row maps onto itself under the XOR (r < 16), so
+// lane i of the copy fetches chunk (q0 + i) ^ r and lands at slot q0 + i; when the MFMA
+// A operand is read (lane (r, g) wants chunk h*Di/8 + 4c + g of token r) the 16 lanes of
+// a group hit 16 different 16-byte bank groups.
 //
-// Per head: Di/32 MFMAs per 16-key N-tile (the key tile stays in registers), then the
-// ReLU x fp32(w * s_idx) epilogue folded into the (token, key) accumulator; the MFMAs of
-// head h+1 are issued before the epilogue of head h.  Key tiles entirely above the
-// causal limit of the 16 tokens are only filled with -inf.  Workgroup ids are mapped so
-// that the chunks of one token block go to one XCD, one after the other, and share its
-// L2 copy of the block's q_idx.
+// Per tile and head: Di/32 MFMAs per 16-key N-tile (the key tile sits in registers, the
+// next one is prefetched), then the ReLU x fp32(w * s_idx) epilogue folded into the
+// (token, key) accumulator; the MFMAs of head h+1 are issued between the epilogue
+// instructions of head h.  Tiles entirely above the causal limit are only filled with
+// -inf.
 // ============================================================================
 constexpr int IXL_TOK = 16;
+constexpr int IXL_WAVES = 8;
 
 // max(x, 0) in one integer max on the bit pattern: a float with the sign bit set is a
 // negative int32 (-> +0), a non-negative float keeps its bits
@@ -186,161 +189,235 @@ __device__ __forceinline__ float relu_bits(float x) {
 }
 
 template <int DI, int HI>
-__global__ __launch_bounds__(256) void indexer_score_lds_kernel(
+__global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
     LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const float *__restrict__ weights, float idx_scale, float *__restrict__ scores, int64_t ld,
-    int max_sk, int total_q, int nqb, int nch) {
+    int max_sk, int total_q) {
   constexpr int RB = HI * DI * 2;   // bytes of one token's q_idx row
   constexpr int CPR = RB / 16;      // 16-byte chunks per row
   constexpr int PPR = RB / 1024;    // 1 KiB pieces per row
+  constexpr int CH = DI / 8;        // 16-byte chunks per head
   constexpr int NCD = DI / 32;
-  static_assert(RB % 1024 == 0 && (IXL_TOK * PPR) % 4 == 0, "row of whole KiB pieces");
-  __shared__ __attribute__((aligned(16))) u32x4 qs[IXL_TOK * CPR];
-  __shared__ __attribute__((aligned(16))) float ws[HI * IXL_TOK];
+  constexpr int NTHR = 64 * IXL_WAVES;
+  static_assert(RB % 1024 == 0 && (2 * IXL_TOK * PPR) % IXL_WAVES == 0, "row of whole KiB pieces");
+  static_assert(CH == 8 || CH == 16, "Di of 64 or 128");
+  __shared__ __attribute__((aligned(16))) u32x4 qs[2][IXL_TOK * CPR];
+  __shared__ __attribute__((aligned(16))) float ws[2][HI * IXL_TOK];
 
-  const int id = blockIdx.x;
-  const int chunk = (id >> 3) % nch;
-  const int blk = (id & 7) + 8 * ((id >> 3) / nch);
-  const int seg = blk / nqb, qb = blk - seg * nqb;
-  if (seg >= L.num_seqs) return;
+  const int seg = blockIdx.x % L.num_seqs;
+  const int pair = blockIdx.x / L.num_seqs;
   const int q_start = __ldg(L.cu_q + seg);
   const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
-  const int t0 = qb * IXL_TOK;
-  if (t0 >= q_len) return;
+  const int nqb = (q_len + IXL_TOK - 1) / IXL_TOK;
+  if (2 * pair >= nqb) return;
+  const int nblk = (nqb - 1 - pair > pair) ? 2 : 1;
+  const int tb0 = (nqb - 1 - pair) * IXL_TOK, tb1 = pair * IXL_TOK;  // first token of block 0 / 1
   const int k_base = __ldg(L.cu_k + seg);
   const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
   const int off = seg_offset(L, seg, q_len, s_k);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nv_last = n_valid_of(min(t0 + IXL_TOK, q_len) - 1, off, L.ratio, s_k);
-  const int jw = (chunk * 4 + w) * 64;  // first key of this wave's tile
+  const int ntiles = (max_sk + 63) / 64;   // tiles of one output row
+  auto nlive_of = [&](int t0) {             // tiles with a key below the causal limit
+    return (n_valid_of(min(t0 + IXL_TOK, q_len) - 1, off, L.ratio, s_k) + 63) / 64;
+  };
+  const int nl0 = nlive_of(tb0), nl1 = nblk > 1 ? nlive_of(tb1) : 0;
 
-  int nv[4];
+  auto store_tile = [&](int t0, int jw, const f32x4 (&acc)[4], bool masked_only) {
+    const int nv_first = n_valid_of(t0, off, L.ratio, s_k);
+    if (!masked_only && t0 + IXL_TOK <= q_len && jw + 64 <= nv_first && jw + 64 <= max_sk) {
+      // every key of the tile is below the causal limit of all 16 tokens
 #pragma unroll
-  for (int i = 0; i < 4; ++i) nv[i] = n_valid_of(t0 + 4 * g + i, off, L.ratio, s_k);
-  auto store_tile = [&](const f32x4 (&acc)[4], bool masked_only) {
+      for (int i = 0; i < 4; ++i) {
+        float *dst = scores + (int64_t)(q_start + t0 + 4 * g + i) * ld + jw + r16;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) dst[16 * n] = acc[n][i];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + 4 * g + i;
       if (t >= q_len) continue;
+      const int nv = n_valid_of(t, off, L.ratio, s_k);
       float *dst = scores + (int64_t)(q_start + t) * ld;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int j = jw + 16 * n + r16;
-        if (j < max_sk) dst[j] = (!masked_only && j < nv[i]) ? acc[n][i] : -__builtin_inff();
+        if (j < max_sk) dst[j] = (!masked_only && j < nv) ? acc[n][i] : -__builtin_inff();
       }
     }
   };
   const f32x4 zero4[4] = {};
-  if (chunk * 256 >= nv_last) {  // the whole chunk is above the causal limit (uniform)
-    if (jw < max_sk) store_tile(zero4, true);
-    return;
-  }
-
-  // q_idx rows t0 .. t0+15 -> LDS (rows past the end of the buffer read as zeros)
+  // tiles above the causal limit: (block, tile) pairs dealt round-robin over the waves
   {
-    const int rows_left = min(IXL_TOK, total_q - (q_start + t0));
-    const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(q_idx + (int64_t)(q_start + t0) * (RB / 2), (uint32_t)(rows_left * RB));
-#pragma unroll
-    for (int k = 0; k < IXL_TOK * PPR / 4; ++k) {
-      const int m = k * 4 + w;           // wave instruction index: row r, piece p
-      const int r = m / PPR, q0 = (m - r * PPR) * 64;
-      dma16(rq, reinterpret_cast<char *>(qs) + (size_t)(r * CPR + q0) * 16,
-            (uint32_t)(r * RB + (((q0 + lane) ^ r) << 4)));
+    const int nf0 = ntiles - nl0, nf = nf0 + (nblk > 1 ? ntiles - nl1 : 0);
+    for (int v = w; v < nf; v += IXL_WAVES) {
+      if (v < nf0) store_tile(tb0, (nl0 + v) * 64, zero4, true);
+      else store_tile(tb1, (nl1 + v - nf0) * 64, zero4, true);
     }
   }
-  const bool live = jw < nv_last;  // this wave's tile has keys below the causal limit
-  u32x4 kb[4][NCD];
+  const int nlive = nl0 + nl1;
+  if (nlive == 0) return;  // uniform: no barrier is skipped by part of the workgroup
+
+  // q_idx rows of both blocks -> LDS (rows past the end of the buffer read as zeros)
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int j = min(jw + 16 * n + r16, s_k - 1);
-    const u32x4 *kp = reinterpret_cast<const u32x4 *>(k_idx + (int64_t)(k_base + max(j, 0)) * DI) + g;
+  for (int bk = 0; bk < 2; ++bk) {
+    if (bk < nblk) {
+      const int t0 = bk ? tb1 : tb0;
+      const int rows_left = min(IXL_TOK, total_q - (q_start + t0));
+      const __amdgpu_buffer_rsrc_t rq =
+          make_rsrc(q_idx + (int64_t)(q_start + t0) * (RB / 2), (uint32_t)(rows_left * RB));
 #pragma unroll
-    for (int c = 0; c < NCD; ++c) kb[n][c] = live ? kp[4 * c] : u32x4{0, 0, 0, 0};
+      for (int k = 0; k < IXL_TOK * PPR / IXL_WAVES + (IXL_TOK * PPR % IXL_WAVES ? 1 : 0); ++k) {
+        const int m = k * IXL_WAVES + w;   // wave instruction index: row r, piece p
+        if (m < IXL_TOK * PPR) {
+          const int r = m / PPR, q0 = (m - r * PPR) * 64;
+          dma16(rq, reinterpret_cast<char *>(qs[bk]) + (size_t)(r * CPR + q0) * 16,
+                (uint32_t)(r * RB + (((q0 + lane) ^ r) << 4)));
+        }
+      }
+    }
+  }
+  // live tile u of this workgroup: block 0 tiles first, then block 1
+  auto tile_of = [&](int u, int &bk, int &tile) {
+    bk = u >= nl0;
+    tile = bk ? u - nl0 : u;
+  };
+  // key tile fragments (MFMA B operand: lane column r16 = key, piece 4c+g); keys past
+  // the segment are clamped to its last key (their scores are masked)
+  auto load_k = [&](int tile, u32x4 (&kb)[4][NCD]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int j = min(tile * 64 + 16 * n + r16, s_k - 1);
+      const u32x4 *kp = reinterpret_cast<const u32x4 *>(k_idx + (int64_t)(k_base + j) * DI) + g;
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) kb[n][c] = kp[4 * c];
+    }
+  };
+  u32x4 kb[4][NCD], kbn[4][NCD];
+  if (w < nlive) {
+    int bk, tile;
+    tile_of(w, bk, tile);
+    load_k(tile, kbn);
   }
   // fp32(w * s_idx), head-major: one 16-byte LDS read gives a lane its 4 tokens
-  for (int e = tid; e < HI * IXL_TOK; e += 256) {
-    const int tt = e / HI, h = e - tt * HI;
-    const int t = t0 + tt;
-    ws[h * IXL_TOK + tt] = t < q_len ? weights[(int64_t)(q_start + t) * HI + h] * idx_scale : 0.f;
+  for (int e = tid; e < 2 * HI * IXL_TOK; e += NTHR) {
+    const int bk = e >= HI * IXL_TOK, e2 = e - bk * HI * IXL_TOK;
+    const int tt = e2 / HI, h = e2 - tt * HI;
+    const int t = (bk ? tb1 : tb0) + tt;
+    ws[bk][h * IXL_TOK + tt] =
+        (bk < nblk && t < q_len) ? weights[(int64_t)(q_start + t) * HI + h] * idx_scale : 0.f;
   }
   wait_vmcnt<0>();
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
-  if (!live) {
-    if (jw < max_sk) store_tile(zero4, true);
-    return;
+
+  // LDS address of A chunk (head h, piece c): chunk index h*CH + 4c + g, swizzled by
+  // XOR with r16.  For CH = 16 the XOR only touches the piece bits; for CH = 8 it also
+  // flips bit 0 of h when r16 >= 8, which is folded into two per-parity base offsets
+  // so that h always ends up in the instruction's immediate offset.
+  int abase[2][NCD];
+#pragma unroll
+  for (int c = 0; c < NCD; ++c) {
+    const int x = 4 * c + g;
+    if constexpr (CH == 16) {
+      abase[0][c] = abase[1][c] = r16 * RB + ((x ^ r16) << 4);
+    } else {
+      const int hb = r16 >> 3, b0 = r16 * RB + ((x ^ (r16 & 7)) << 4);
+      abase[0][c] = b0 + 128 * hb;   // even h: h ^ hb = h + hb
+      abase[1][c] = b0 - 128 * hb;   // odd h:  h ^ hb = h - hb
+    }
   }
 
-  const char *qrow = reinterpret_cast<const char *>(qs) + r16 * RB;
-  auto a_frag = [&](int h, int c) -> u32x4 {
-    const int q = h * (DI / 8) + 4 * c + g;
-    return *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
-  };
-  auto head_mfma = [&](const u32x4 (&qa)[NCD], f32x4 (&d)[4]) {
+  for (int u = w; u < nlive; u += IXL_WAVES) {
+    int bk, tile;
+    tile_of(u, bk, tile);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) d[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int c = 0; c < NCD; ++c)
+      for (int c = 0; c < NCD; ++c) kb[n][c] = kbn[n][c];
+    if (u + IXL_WAVES < nlive) {
+      int bk2, tile2;
+      tile_of(u + IXL_WAVES, bk2, tile2);
+      load_k(tile2, kbn);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    const char *qb = reinterpret_cast<const char *>(qs[bk]);
+    const float *wsp = ws[bk] + 4 * g;
+    auto a_frag = [&](int h, u32x4 (&qa)[NCD]) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) d[n] = mfma16x16x32(qa[c], kb[n][c], d[n]);
-  };
-  f32x4 acc[4];
+      for (int c = 0; c < NCD; ++c)
+        qa[c] = *reinterpret_cast<const u32x4 *>(qb + abase[h & 1][c] + h * CH * 16);
+    };
+    auto head_mfma = [&](const u32x4 (&qa)[NCD], f32x4 (&d)[4]) {
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float *wsp = ws + 4 * g;
-  u32x4 qa[NCD], qn[NCD];
+      for (int n = 0; n < 4; ++n) d[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < NCD; ++c) qa[c] = a_frag(0, c);
-  f32x4 dc[4], dn[4];
-  head_mfma(qa, dc);
+      for (int c = 0; c < NCD; ++c)
 #pragma unroll
-  for (int c = 0; c < NCD; ++c) qn[c] = a_frag(HI > 1 ? 1 : 0, c);
-  f32x4 wv = *reinterpret_cast<const f32x4 *>(wsp), wvn = wv;
+        for (int n = 0; n < 4; ++n) d[n] = mfma16x16x32(qa[c], kb[n][c], d[n]);
+    };
+    f32x4 acc[4];
 #pragma unroll
-  for (int h = 0; h < HI; ++h) {
-    if (h + 1 < HI) {
-      wvn = *reinterpret_cast<const f32x4 *>(wsp + (h + 1) * IXL_TOK);
-      head_mfma(qn, dn);
-      if (h + 2 < HI) {
+    for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto epilogue = [&](const f32x4 (&d)[4], const f32x4 &wv) {
 #pragma unroll
-        for (int c = 0; c < NCD; ++c) qn[c] = a_frag(h + 2, c);
+      for (int n = 0; n < 4; ++n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[n][i] = fmaf(wv[i], relu_bits(d[n][i]), acc[n][i]);
+        asm volatile("" : "+v"(acc[n]));  // the epilogue of head h stays in its iteration
       }
-    }
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[n][i] = fmaf(wv[i], relu_bits(dc[n][i]), acc[n][i]);
-      asm volatile("" : "+v"(acc[n]));  // the epilogue of head h stays in iteration h
-    }
-    if (h + 1 < HI) {
+    };
+    auto interleave = [&]() {
 #pragma unroll
       for (int m = 0; m < 4 * NCD; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 32 / (4 * NCD), 0);  // then VALU
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    // two register sets alternate between "MFMAs in flight" and "epilogue"
+    u32x4 qa0[NCD], qa1[NCD];
+    f32x4 d0[4], d1[4];
+    a_frag(0, qa0);
+    head_mfma(qa0, d0);
+    if (HI > 1) a_frag(1, qa1);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) dc[n] = dn[n];
-    wv = wvn;
+    for (int h = 0; h < HI; h += 2) {
+      const f32x4 w0 = *reinterpret_cast<const f32x4 *>(wsp + h * IXL_TOK);
+      if (h + 1 < HI) {
+        head_mfma(qa1, d1);
+        if (h + 2 < HI) a_frag(h + 2, qa0);
+      }
+      epilogue(d0, w0);
+      if (h + 1 < HI) interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      if (h + 1 < HI) {
+        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(wsp + (h + 1) * IXL_TOK);
+        if (h + 2 < HI) {
+          head_mfma(qa0, d0);
+          if (h + 3 < HI) a_frag(h + 3, qa1);
+        }
+        epilogue(d1, w1);
+        if (h + 2 < HI) interleave();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    store_tile(bk ? tb1 : tb0, tile * 64, acc, false);
   }
-  store_tile(acc, false);
 }
 
 template <int DI, int HI>
 static hipError_t launch_lds(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
                              const float *weights, float idx_scale, float *scores, int64_t ld,
                              hipStream_t st) {
-  const int nqb = (LL.max_seqlen_q + IXL_TOK - 1) / IXL_TOK;
-  const int nch = (LL.max_seqlen_k + 255) / 256;
-  const int64_t nblk = (int64_t)LL.num_seqs * nqb;
-  const int64_t grid = 8 * (int64_t)nch * ((nblk + 7) / 8);
+  const int npair = ((LL.max_seqlen_q + IXL_TOK - 1) / IXL_TOK + 1) / 2;
+  const int64_t grid = (int64_t)LL.num_seqs * npair;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((indexer_score_lds_kernel<DI, HI>), dim3((unsigned)grid), dim3(256), 0, st, LL.dev,
-                     static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
-                     weights, idx_scale, scores, ld, LL.max_seqlen_k, LL.total_q, nqb, nch);
+  hipLaunchKernelGGL((indexer_score_lds_kernel<DI, HI>), dim3((unsigned)grid), dim3(64 * IXL_WAVES), 0, st,
+                     LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
+                     weights, idx_scale, scores, ld, LL.max_seqlen_k, LL.total_q);
   return hipGetLastError();
 }
 
@@ -367,7 +444,6 @@ hipError_t launch_indexer_score(const LaunchLayout &LL, const void *q_idx, const
     if (Di == 64 && Hi == 32) return launch_lds<64, 32>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
     if (Di == 128 && Hi == 4) return launch_lds<128, 4>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
     if (Di == 128 && Hi == 8) return launch_lds<128, 8>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
-    if (Di == 128 && Hi == 16) return launch_lds<128, 16>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
   }
   if (bf16) {
     switch (Di) {

@@ -23,6 +23,9 @@
 //                 up to a reduction over the 4 lane groups g = l/16.
 //   O^T += V^T P^T : A = V^T read from LDS column-wise, B = P^T built from two S^T
 //                 tiles: MFMA k index 8g+e <-> chunk row (e<4 ? 4g+e : 16+4g+e-4).
+#include <algorithm>
+#include <utility>
+
 #include "common.h"
 #include "../launch.h"
 
@@ -303,7 +306,14 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
 // logit exceeds it by 2^8) and a per-lane partial sum; the compressed logits stay in
 // registers so that cmass = sum_h exp(c - lse) is formed once lse is final.
 // ============================================================================
-__device__ __forceinline__ int row_swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// 16-byte piece p of tile row R is stored at piece position p ^ row_swz<D>(R).  With 64
+// LDS banks of 4 bytes (256 bytes per bank row), this keeps conflict-free: the K-operand
+// reads (16 lanes = rows 0..15, one piece each), the transposing V reads (32 lanes =
+// 8 rows x 2 pieces x 2 halves) and the O staging writes.
+template <int D> __device__ __forceinline__ int row_swz(int r) {
+  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
 
 template <int D, int KC>
 __global__ __launch_bounds__(256) void sparse_attn_dma_kernel(
@@ -368,18 +378,18 @@ __global__ __launch_bounds__(256) void sparse_attn_dma_kernel(
   const int gg = lane / PIECES, pp = lane % PIECES;   // load: row-in-instruction, piece position
   int kro[NC];                                         // K operand: row r16, piece 4c+g
 #pragma unroll
-  for (int c = 0; c < NC; ++c) kro[c] = r16 * ROWB + 16 * ((4 * c + g) ^ row_swz(r16));
+  for (int c = 0; c < NC; ++c) kro[c] = r16 * ROWB + 16 * ((4 * c + g) ^ row_swz<D>(r16));
   const int rho = 4 * g + (r16 >> 2);                  // V^T operand: rows rho (+16)
   int tro[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-    tro[dt] = rho * ROWB + 16 * ((2 * dt + ((r16 & 3) >> 1)) ^ row_swz(rho)) + 8 * (r16 & 1);
+    tro[dt] = rho * ROWB + 16 * ((2 * dt + ((r16 & 3) >> 1)) ^ row_swz<D>(rho)) + 8 * (r16 & 1);
 
   auto dma_window = [&](int c, char *base) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int R = i * RPI + gg, slot = 32 * c + R;
-      const uint32_t off = slot < nw ? (uint32_t)(w_lo + slot) * ROWB + 16 * (pp ^ row_swz(R)) : BUF_OOB;
+      const uint32_t off = slot < nw ? (uint32_t)(w_lo + slot) * ROWB + 16 * (pp ^ row_swz<D>(R)) : BUF_OOB;
       dma16(rkv, base + i * 1024, off);
     }
   };
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(256) void sparse_attn_dma_kernel(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int R = i * RPI + gg;
-      const uint32_t off = idr[i] >= 0 ? (uint32_t)idr[i] * ROWB + 16 * (pp ^ row_swz(R)) : BUF_OOB;
+      const uint32_t off = idr[i] >= 0 ? (uint32_t)idr[i] * ROWB + 16 * (pp ^ row_swz<D>(R)) : BUF_OOB;
       dma16(rck, base + i * 1024, off);
     }
   };
@@ -522,16 +532,19 @@ __global__ __launch_bounds__(256) void sparse_attn_dma_kernel(
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       uint2 pk = {pack2_bf16(o[dt][0] * inv, o[dt][1] * inv), pack2_bf16(o[dt][2] * inv, o[dt][3] * inv)};
-      *reinterpret_cast<uint2 *>(ob + r16 * ROWB + (dt * 16 + 4 * g) * 2) = pk;
+      // dims dt*16 + 4g .. +3 = half (g & 1) of piece 2dt + (g >> 1), swizzled like the tiles
+      *reinterpret_cast<uint2 *>(ob + r16 * ROWB + 16 * ((2 * dt + (g >> 1)) ^ row_swz<D>(r16)) + 8 * (g & 1)) = pk;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     const int nh = min(16, H - 16 * hgrp);   // heads of this group that exist
     uint16_t *obase = out + ((int64_t)t * H + 16 * hgrp) * D;
 #pragma unroll
     for (int k = 0; k < 16 * ROWB / 1024; ++k) {
-      const int byte = k * 1024 + lane * 16;
+      const int byte = k * 1024 + lane * 16;       // LDS: row hr, piece position pos
+      const int hr = byte / ROWB, pos = (byte % ROWB) >> 4;
       if (byte < nh * ROWB)
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(obase) + byte) = *reinterpret_cast<const u32x4 *>(ob + byte);
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(obase) + hr * ROWB + 16 * (pos ^ row_swz<D>(hr))) =
+            *reinterpret_cast<const u32x4 *>(ob + byte);
     }
   }
   if (cmass != nullptr && hgc == 1) {
@@ -559,6 +572,364 @@ __global__ __launch_bounds__(256) void sparse_attn_dma_kernel(
   }
 }
 
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{}), inlined
+template <class F, int... Cs>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, Cs...>) {
+  (f(std::integral_constant<int, Cs>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F &f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ============================================================================
+// Persistent pipelined variant (bf16; H <= 16; 1 <= k_eff <= 32*KC, KC <= 8; window > 0).
+//
+// Same per-query arithmetic and swizzled LDS tiles as the kernel above, but each wave
+// walks a strided list of query rows (t, t + W, t + 2W, ... for W waves in the grid)
+// as one continuous stream of 32-row steps, with two tiles and a prefetch distance of
+// two steps: as soon as step n has read its tile (K operand, then the transposing V
+// reads), the rows of step n+2 are requested into that same tile, so every load has a
+// whole step to land and the request is issued behind the step's PV MFMAs.  Step n+2
+// may belong to the next query (its first or second step), whose ids are fetched during
+// the current query's first step and written to the other ids buffer at its second.
+//
+// Every step requests exactly NI loads (out-of-range ones past the end of the stream),
+// so "at most NI vector-memory operations outstanding" at the top of a step means the
+// tile of this step has landed: loads complete in order, and any other memory operation
+// issued in between (output stores, q and id loads) only makes that wait stricter.
+//
+// Compressed probabilities are kept in fp32 (rescaled with O when the running max is
+// raised), so at the end cmass[j] = sum_h p_hj / L_h needs no second exponential.
+// ============================================================================
+template <int D, int KC>
+__global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
+    const uint16_t *__restrict__ ckv, const float *__restrict__ sink,
+    const int32_t *__restrict__ ids, int k_eff, int window, int H, int total_q, int total_k,
+    float sl2, uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ lse_nc,
+    float *__restrict__ cmass) {
+  constexpr int NC = D / 32;          // MFMA K-chunks per row
+  constexpr int ROWB = D * 2;         // bytes per KV row
+  constexpr int PIECES = D / 8;       // 16-byte pieces per row
+  constexpr int RPI = 64 / PIECES;    // rows per direct-to-LDS load instruction
+  constexpr int NI = 32 / RPI;        // load instructions per 32-row step
+  constexpr int TILE = 32 * ROWB;     // one 32-row tile
+  constexpr int IDS = 32 * KC;        // id slots per query
+  constexpr int IPL = (IDS + 63) / 64;  // id slots per lane
+  constexpr float NINF = -__builtin_inff();
+  constexpr float RESCALE = 8.f;
+  static_assert(NI <= 15, "vmcnt");
+  __shared__ __attribute__((aligned(16))) char lds_all[4][2 * TILE + 2 * IDS * 4];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const int nwaves = gridDim.x * 4;
+  int t = blockIdx.x * 4 + w;
+  if (t >= total_q) return;           // no block-level barrier below
+  char *tiles = lds_all[w];
+  int *ids_lds = reinterpret_cast<int *>(tiles + 2 * TILE);   // [2][IDS]
+  const int h = r16;
+  const bool h_ok = h < H;
+  const bool group_full = H >= 16;
+  const int ncc = (k_eff + 31) >> 5;  // compressed steps per query
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)total_q * ROWB);
+  const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * ROWB);
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // bpermute addresses
+  const int gg = lane / PIECES, pp = lane % PIECES;   // load: row-in-instruction, piece position
+  // K operand: row r16, piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3))
+  const int ksw = row_swz<D>(r16);
+  const int kbase = r16 * ROWB + 16 * (g ^ (ksw & 3)), kx = ksw >> 2;
+  // V^T operand: rows rho (+16), piece (2dt + hb) ^ swz = 2 (dt ^ (swz >> 1)) + (hb ^ (swz & 1))
+  const int rho = 4 * g + (r16 >> 2);
+  const int vsw = row_swz<D>(rho);
+  const int vbase = rho * ROWB + 16 * (((r16 & 3) >> 1) ^ (vsw & 1)) + 8 * (r16 & 1), vx = vsw >> 1;
+
+  // Masked rows read zeros or keep stale tile contents (rows of earlier steps, always
+  // finite); their probabilities are exactly 0.
+#pragma unroll
+  for (int i = 0; i < 2 * TILE / 1024; ++i) reinterpret_cast<u32x4 *>(tiles)[i * 64 + lane] = u32x4{0, 0, 0, 0};
+
+  struct Geo { int w_lo, nw, nwc; };
+  auto geo_of = [&](int tq) {
+    const RowGeo rg = row_geo(L, tq);
+    Geo o;
+    o.w_lo = max(rg.q_start, tq - window + 1);
+    o.nw = tq - o.w_lo + 1;
+    o.nwc = (o.nw + 31) >> 5;
+    return o;
+  };
+  auto load_ids = [&](int tq, int (&r)[IPL]) {
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) {
+      const int sl = i * 64 + lane;
+      r[i] = sl < k_eff ? ids[(int64_t)tq * k_eff + sl] : -1;
+    }
+  };
+  // LDS order [step][row-in-instruction][instruction]: a lane's ids of one step are contiguous
+  auto store_ids = [&](int buf, const int (&r)[IPL]) {
+    int *dst = ids_lds + buf * IDS;
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) {
+      const int sl = i * 64 + lane;
+      if (sl < IDS) {
+        const int rs = sl & 31;
+        dst[(sl & ~31) + (rs % RPI) * NI + rs / RPI] = r[i];
+      }
+    }
+  };
+  // MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
+  auto load_q = [&](int tq, u32x4 (&f)[NC]) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)tq * H + (h_ok ? h : 0)) * D) + g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) f[c] = h_ok ? p[4 * c] : u32x4{0, 0, 0, 0};
+  };
+  // the NI row loads of step s of a query (window steps first, then compressed steps)
+  // into `base`; valid = false requests NI out-of-range loads
+  auto dma_step = [&](bool valid, const Geo &G, int buf, int s, char *base) {
+    int pps = pp, ggs = gg;
+    asm volatile("" : "+v"(pps), "+v"(ggs));
+    if (valid && s < G.nwc) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int R = i * RPI + ggs, slot = 32 * s + R;
+        const uint32_t off = slot < G.nw ? (uint32_t)(G.w_lo + slot) * ROWB + 16 * (pps ^ row_swz<D>(R)) : BUF_OOB;
+        dma16(rkv, base + i * 1024, off);
+      }
+    } else {
+      int idr[NI];
+      if (valid) {
+        const int *il = ids_lds + buf * IDS + (s - G.nwc) * 32 + ggs * NI;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) idr[i] = il[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) idr[i] = -1;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int R = i * RPI + ggs;
+        const uint32_t off = idr[i] >= 0 ? (uint32_t)idr[i] * ROWB + 16 * (pps ^ row_swz<D>(R)) : BUF_OOB;
+        dma16(rck, base + i * 1024, off);
+      }
+    }
+  };
+
+  // ---- stream start: the first query's ids and q, then its first two tiles
+  u32x4 qf[NC];
+  int buf = 0;
+  {
+    int r[IPL];
+    load_ids(t, r);
+    load_q(t, qf);
+    store_ids(0, r);
+  }
+  Geo G = geo_of(t);
+  int tn = t + nwaves;
+  bool has_next = tn < total_q;
+  Geo Gn = {0, 0, 0};
+  if (has_next) Gn = geo_of(tn);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // zeroing and id stores have executed
+  dma_step(true, G, 0, 0, tiles);
+  {
+    const bool own = 1 < G.nwc + ncc;   // always true with a window
+    dma_step(own || has_next, own ? G : Gn, own ? 0 : 1, own ? 1 : 0, tiles + TILE);
+  }
+  int n = 0;  // stream step index: step n reads tile n & 1
+
+  for (;;) {
+    const int nsteps = G.nwc + ncc;
+    int idn[IPL];
+    bool ids_done = !has_next;
+
+    const float a2 = h_ok ? sink[h] * LOG2E : NINF;
+    float m = a2;                                        // shared by the 4 lane groups of a head
+    float l = (g == 0 && a2 > NINF) ? 1.f : 0.f;         // per-lane partial sum
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float pk[KC][8];  // compressed probabilities exp2(sl2*s - m), kept for cmass
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[c][e] = 0.f;
+
+    // Top of step s: its tile has landed (at most the NI loads of step n+1 outstanding)
+    // and every LDS access of step n-1 has returned; the next query's ids are fetched at
+    // s = 0 and written to the other buffer at s = 1 (they are first needed by a request
+    // issued at s >= 1: the next query's first step is a window step).
+    auto top = [&](int s) __attribute__((always_inline)) {
+      wait_vmcnt<NI>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      if (s == 0 && has_next) load_ids(tn, idn);
+      if (s == 1 && !ids_done) {
+        store_ids(buf ^ 1, idn);
+        ids_done = true;
+      }
+    };
+    // the rows of stream step n+2 into the tile step n has just finished reading
+    auto request = [&](int s) __attribute__((always_inline)) {
+      char *dst = tiles + (n & 1) * TILE;
+      const int s2 = s + 2;
+      if (s2 < nsteps) dma_step(true, G, buf, s2, dst);
+      else dma_step(has_next, Gn, buf ^ 1, s2 - nsteps, dst);
+    };
+
+    // one 32-row step on the tile at `base`; bm = row validity bits; leaves this lane's
+    // compressed step CI keeps its fp32 probabilities in pk[CI] (CI < 0: window step)
+    auto step = [&](auto ci, int s, uint32_t bm) __attribute__((always_inline)) {
+      constexpr int CI = decltype(ci)::value;
+      float raw[8];
+      const char *base = tiles + (n & 1) * TILE;
+      // the per-lane address terms are re-derived every step (opaque copies), so that
+      // the compiler does not keep all the operand addresses live across the loop
+      int kxs = kx, vxs = vx;
+      asm volatile("" : "+v"(kxs), "+v"(vxs));
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const char *kp = base + kbase + 64 * (c ^ kxs);
+        const u32x4 k0 = *reinterpret_cast<const u32x4 *>(kp);
+        const u32x4 k1 = *reinterpret_cast<const u32x4 *>(kp + 16 * ROWB);
+        acc0 = mfma16x16x32(k0, qf[c], acc0);
+        acc1 = mfma16x16x32(k1, qf[c], acc1);
+      }
+      if (group_full && bm == 0xffffffffu) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { raw[i] = acc0[i]; raw[4 + i] = acc1[i]; }
+      } else {
+        const uint32_t m0 = h_ok ? (bm >> (4 * g)) : 0u, m1 = h_ok ? (bm >> (16 + 4 * g)) : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          raw[i] = ((m0 >> i) & 1) ? acc0[i] : NINF;
+          raw[4 + i] = ((m1 >> i) & 1) ? acc1[i] : NINF;
+        }
+      }
+      // Common path without cross-lane traffic: each lane tests its logits against the
+      // shared reference max; only a logit 2^8 above it makes the wave agree on a new
+      // per-head max and rescale.
+      float cmx = fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
+                        fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
+      if (__builtin_expect(__ballot(cmx * sl2 > m + RESCALE) != 0, 0)) {
+        cmx = fmaxf(cmx, bperm(x16, cmx));
+        cmx = fmaxf(cmx, bperm(x32, cmx));
+        const float cand = cmx * sl2;
+        const float mn = cand > m + RESCALE ? cand : m;
+        const float alpha = fast_exp2(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk[c][e] *= alpha;
+        m = mn;
+      }
+      const float nms = m == NINF ? 0.f : -m;
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(fmaf(raw[e], sl2, nms)); l += p[e]; }
+      if constexpr (CI >= 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pk[CI][e] = p[e];
+      }
+      const u32x4 pb = {pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]),
+                        pack2_bf16(p[6], p[7])};
+      // V^T operands in two halves of D/32 d-tiles (fewer registers in flight)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint2 xv[D / 16];
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+          const int dt = hf * (D / 32) + k;
+          const uint32_t va = lds_addr_of(base + vbase + 32 * (dt ^ vxs));
+          xv[2 * k] = lds_read_tr16_nowait_off<0>(va);
+          xv[2 * k + 1] = lds_read_tr16_nowait_off<16 * ROWB>(va);
+        }
+        lds_tr16_wait(xv);
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+          const int dt = hf * (D / 32) + k;
+          const u32x4 a = {xv[2 * k].x, xv[2 * k].y, xv[2 * k + 1].x, xv[2 * k + 1].y};
+          o[dt] = mfma16x16x32(a, pb, o[dt]);
+        }
+      }
+      request(s);   // the tile is free: its LDS reads have all returned
+    };
+
+    for (int s = 0; s < G.nwc; ++s, ++n) {
+      top(s);
+      const int nwin = G.nw - 32 * s;
+      step(std::integral_constant<int, -1>{}, s, nwin >= 32 ? 0xffffffffu : (1u << nwin) - 1u);
+    }
+    const float m_nc = m, l_nc = l;
+    // compressed steps, unrolled so that step c writes pk[c] with constant indices
+    auto comp_step = [&](auto ci) __attribute__((always_inline)) {
+      constexpr int C = decltype(ci)::value;
+      if (C < ncc) {
+        const int s = G.nwc + C;
+        top(s);
+        // row validity of compressed step C: bit R set iff the id of row R is >= 0
+        const int R = lane & 31;
+        const uint32_t bm = (uint32_t)__ballot(ids_lds[buf * IDS + C * 32 + (R % RPI) * NI + R / RPI] >= 0);
+        step(ci, s, bm);
+        ++n;
+      }
+    };
+    static_for<KC>(comp_step);
+    if (!ids_done) store_ids(buf ^ 1, idn);   // (only if this query had a single step)
+    // the next query's q rows stream in during this query's epilogue
+    if (has_next) load_q(tn, qf);
+
+    // ---- final statistics (the 4 lane groups of a head share m; sums are partial)
+    const float Ls = across_groups_sum(l);
+    const float Lnc = across_groups_sum(l_nc);
+    const float lse2 = Ls > 0.f ? m + __log2f(Ls) : NINF;
+    const float lse2_nc = Lnc > 0.f ? m_nc + __log2f(Lnc) : NINF;
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    if (h_ok) {
+      if (g == 0) {
+        lse[(int64_t)t * H + h] = lse2 * LN2;
+        lse_nc[(int64_t)t * H + h] = lse2_nc * LN2;
+      }
+      // O straight from the accumulator: lane (head r16, group g) holds dims 16dt+4g..+3
+      uint16_t *orow = out + ((int64_t)t * H + h) * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<uint2 *>(orow + 16 * dt) =
+            uint2{pack2_bf16(o[dt][0] * inv, o[dt][1] * inv), pack2_bf16(o[dt][2] * inv, o[dt][3] * inv)};
+    }
+    if (cmass != nullptr) {
+      float *crow = cmass + (int64_t)t * k_eff;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        if (c >= ncc) break;
+        float sums[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sums[e] = group16_sum(pk[c][e] * inv);
+        // lane r16 = tau of group g writes slots 32c + 16*tau + 4g + (0..3)
+        const int slot0 = 32 * c + 16 * r16 + 4 * g;
+        if (r16 < 2) {
+          const f32x4 v = r16 ? f32x4{sums[4], sums[5], sums[6], sums[7]} : f32x4{sums[0], sums[1], sums[2], sums[3]};
+          if (slot0 + 4 <= k_eff) {
+            *reinterpret_cast<f32x4 *>(crow + slot0) = v;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (slot0 + i < k_eff) crow[slot0 + i] = v[i];
+          }
+        }
+      }
+    }
+    if (!has_next) break;
+    t = tn;
+    G = Gn;
+    buf ^= 1;
+    tn = t + nwaves;
+    has_next = tn < total_q;
+    if (has_next) Gn = geo_of(tn);
+  }
+  wait_vmcnt<0>();   // the stream's trailing out-of-range requests
+}
+
 template <int D>
 static hipError_t launch_dma(const LaunchLayout &LL, const void *q, const void *kv, const void *ckv,
                              const float *sink, const int32_t *ids, int k_eff, int window, int H,
@@ -566,8 +937,30 @@ static hipError_t launch_dma(const LaunchLayout &LL, const void *q, const void *
                              hipStream_t st) {
   const int hgc = (H + 15) / 16;
   const int qpw = 4 / hgc;
-  dim3 grid((unsigned)((LL.total_q + qpw - 1) / qpw));
   const float sl2 = scale * LOG2E;
+  if (hgc == 1 && window > 0) {
+    // persistent: two workgroups of 4 waves per CU, each wave walking a strided list of rows
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t need = (LL.total_q + 3) / 4;
+    dim3 pgrid((unsigned)std::min<int64_t>(need, 2 * (int64_t)ncu));
+#define CSA_PIPE_CASE(K)                                                                             \
+    if (k_eff <= 32 * K) {                                                                           \
+      hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, K>), pgrid, dim3(256), 0, st, LL.dev,           \
+                         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),        \
+                         static_cast<const uint16_t *>(ckv), sink, ids, k_eff, window, H,            \
+                         LL.total_q, LL.total_k, sl2, static_cast<uint16_t *>(out), lse, lse_nc,     \
+                         cmass);                                                                     \
+      return hipGetLastError();                                                                      \
+    }
+    CSA_PIPE_CASE(1)
+    CSA_PIPE_CASE(2)
+    CSA_PIPE_CASE(4)
+    CSA_PIPE_CASE(8)
+#undef CSA_PIPE_CASE
+    return hipErrorInvalidValue;
+  }
+  dim3 grid((unsigned)((LL.total_q + qpw - 1) / qpw));
 #define CSA_DMA_CASE(K)                                                                              \
   if (k_eff <= 32 * K) {                                                                             \
     hipLaunchKernelGGL((sparse_attn_dma_kernel<D, K>), grid, dim3(256), 0, st, LL.dev,               \
