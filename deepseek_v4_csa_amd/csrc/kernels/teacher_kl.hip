@@ -87,8 +87,8 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
   double ms = 0.0;
 #pragma unroll
   for (int v = 0; v < SPL; ++v) ms += id[v] >= 0 ? (double)c[v] : 0.0;
-  mx = __builtin_amdgcn_readfirstlane(wave_max(mx));
-  ms = wave_sum_f64(ms);
+  mx = wave_max_dpp(mx);
+  ms = wave_sum_f64_dpp(ms);
   // Predictor terms in fp32 (an independent relative error d_j in e_j moves the KL only
   // through sum_j (t_j - p_j) d_j), the normalisations in fp64.
   float e[SPL];
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
     e[v] = id[v] >= 0 ? fast_exp2((sc[v] - mx) * LOG2E) : 0.f;
     es += (double)e[v];
   }
-  es = wave_sum_f64(es);
+  es = wave_sum_f64_dpp(es);
   const double inv_es = 1.0 / es;
   const double inv_m = 1.0 / fmax(ms, (double)EPS);
   // log(t+eps) - log(p+eps) = log1p(x), x = (t - p) / (p + eps): the difference t - p is
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
     }
     if (te && j < k_eff) te[j] = (float)tj;
   }
-  kl = wave_sum_f64(kl);
+  kl = wave_sum_f64_dpp(kl);
   if (lane == 0) kl_row[t] = (float)kl;
 }
 
@@ -292,14 +292,13 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float *__restri
   __shared__ double part[16];
   double s = 0.0;
   for (int i = threadIdx.x; i < T; i += 1024) s += (double)kl_row[i];
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  s = wave_sum_f64_dpp(s);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int i = 0; i < 16; ++i) tot += part[i];
-    loss[0] = (float)(per_token ? tot : (T > 0 ? tot / (double)T : 0.0));
+  if (threadIdx.x < 64) {
+    double v = threadIdx.x < 16 ? part[threadIdx.x] : 0.0;
+    v = wave_sum_f64_dpp(v);
+    if (threadIdx.x == 0) loss[0] = (float)(per_token ? v : (T > 0 ? v / (double)T : 0.0));
   }
 }
 
