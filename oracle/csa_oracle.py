@@ -155,17 +155,20 @@ def k_eff_of(L: Layout, topk: int) -> int:
 # --------------------------------------------------------------------------------------
 # Step 1: Lightning-Indexer scores
 # --------------------------------------------------------------------------------------
-def indexer_weight_scale(w_row, idx_scale) -> np.ndarray:
-    """fp32(weights) * fp32(indexer softmax scale), rounded to fp32.
+def indexer_weight_scale(w_row, idx_scale, exact: bool = False) -> np.ndarray:
+    """fp32(weights) * fp32(indexer softmax scale), rounded to fp32 (exact=True keeps the
+    float64 product; only the finite-difference pins of the backward use it).
 
     [I5776, csa.py SBHD excerpt]: the indexer scale is folded into the per-head weights as
     ``weights.float() * indexer.softmax_scale`` before the loss call.  READING: the
     product is formed in fp32 (the SBHD form; the review comment notes that the
     rounding point can change selection near a tie)."""
+    if exact:
+        return np.asarray(w_row, dtype=np.float64) * float(np.float32(idx_scale))
     return (np.asarray(w_row, dtype=np.float32) * np.float32(idx_scale)).astype(np.float32)
 
 
-def indexer_scores_row(q_idx_t, w_t, k_idx_seg, idx_scale, n_valid) -> np.ndarray:
+def indexer_scores_row(q_idx_t, w_t, k_idx_seg, idx_scale, n_valid, exact_ws: bool = False) -> np.ndarray:
     """Scores I[t, j] for all local keys j of the row's segment.
 
     READING (the pages do not print the score formula; they show the weight/scale folding
@@ -180,7 +183,7 @@ def indexer_scores_row(q_idx_t, w_t, k_idx_seg, idx_scale, n_valid) -> np.ndarra
     """
     q = np.asarray(q_idx_t, dtype=np.float64)
     k = np.asarray(k_idx_seg, dtype=np.float64)
-    ws = indexer_weight_scale(w_t, idx_scale).astype(np.float64)
+    ws = indexer_weight_scale(w_t, idx_scale, exact_ws).astype(np.float64)
     s_k = k.shape[0]
     out = np.full(s_k, NEG_INF)
     if n_valid > 0:
@@ -488,3 +491,111 @@ def run_all(P: Problem):
     rows = [run_row(P, t) for t in range(P.layout.total_q)]
     loss = reduce_loss([r.kl for r in rows], P.layout.total_q, P.per_token)
     return rows, loss
+
+
+# --------------------------------------------------------------------------------------
+# Next step after the path: the indexer-loss backward
+# --------------------------------------------------------------------------------------
+# [I5776, proposal comment and its follow-up review]: the loss keeps a custom backward that
+# recomputes what it needs from saved tensors and returns gradients only for the indexer
+# q, weights and k; every teacher-side input (hence the teacher itself) is detached, and
+# the top-k selection is a fixed, non-differentiable choice.  [PR8539, item 1 and test
+# plan]: the sparse path's ids are global, and a batch of two rows-sets must give the
+# same gradients as two single runs scaled for the row-mean loss.
+
+def kl_grad_scores(teacher, pred) -> np.ndarray:
+    """dKL/ds over the support, teacher held fixed.
+
+    KL = sum_j t_j (log(t_j + eps) - log(p_j + eps)) with p = softmax(s):
+        dKL/dp_j = -t_j / (p_j + eps),   dp_j/ds_k = p_j (delta_jk - p_k)
+        => dKL/ds_k = p_k R - r_k,   r_j = t_j p_j / (p_j + eps),   R = sum_j r_j
+    (with eps -> 0 this is the familiar p - t)."""
+    t = np.asarray(teacher, dtype=np.float64)
+    p = np.asarray(pred, dtype=np.float64)
+    r = t * p / (p + EPS_LOG)
+    return p * np.sum(r) - r
+
+
+def indexer_grads_row(q_idx_t, w_t, k_idx_seg, idx_scale, cols, g_cols, exact_ws: bool = False):
+    """Gradients of sum_c g_c * I[t, cols[c]] (I from ``indexer_scores_row``) with respect
+    to q_idx[t] ([Hi, Di]), w[t] ([Hi]) and the key rows k_idx_seg[cols] ([n, Di]).
+
+    With d_hj = q_idx[t, h] . k_j, a_hj = [d_hj > 0] and ws_h = w_h * s_idx:
+        dq[h]  = ws_h * sum_j g_j a_hj k_j
+        dw[h]  = s_idx * sum_j g_j max(d_hj, 0)
+        dk[j]  = g_j * sum_h ws_h a_hj q[h]
+    READING: the weight gradient treats ws = w * s_idx as exact (the fp32 rounding of the
+    forward product has derivative 1 almost everywhere)."""
+    q = np.asarray(q_idx_t, dtype=np.float64)
+    cols = np.asarray(cols, dtype=np.int64)
+    k = np.asarray(k_idx_seg, dtype=np.float64)[cols]
+    g = np.asarray(g_cols, dtype=np.float64)
+    ws = indexer_weight_scale(w_t, idx_scale, exact_ws).astype(np.float64)
+    d = k @ q.T                                   # [n, Hi]
+    a = (d > 0.0).astype(np.float64)
+    ga = g[:, None] * a                           # [n, Hi]
+    dq = ws[:, None] * (ga.T @ k)                 # [Hi, Di]
+    dw = float(np.float32(idx_scale)) * (g @ np.maximum(d, 0.0))
+    dk = (ga * ws[None, :]) @ q                   # [n, Di]
+    return dq, dw, dk
+
+
+def loss_support(P: Problem, r: RowResult):
+    """The support C of row r as local columns, with the teacher and predictor on it."""
+    g = r.geom
+    if g.n_valid == 0:
+        return np.zeros(0, dtype=np.int64), np.zeros(0), np.zeros(0)
+    if P.sparse_loss:
+        valid = r.ids >= 0
+        return r.ids[valid] - g.k_base, r.teacher[valid], r.pred[valid]
+    return np.arange(g.n_valid, dtype=np.int64), r.teacher, r.pred
+
+
+def indexer_loss_backward(P: Problem, rows=None, grad_loss: float = 1.0):
+    """dLoss/dq_idx [T, Hi, Di], dLoss/dweights [T, Hi], dLoss/dk_idx [T_k, Di] for the
+    reduced loss of ``run_all`` (mean over physical rows, or the per-token sum), with the
+    teacher and the selection held fixed.  rows: RowResults of every row (recomputed if
+    None)."""
+    L = P.layout
+    T = L.total_q
+    if rows is None:
+        rows = [run_row(P, t) for t in range(T)]
+    scale = float(grad_loss) if P.per_token else float(grad_loss) / float(T)
+    dq = np.zeros(P.q_idx.shape, dtype=np.float64)
+    dw = np.zeros(P.weights.shape, dtype=np.float64)
+    dk = np.zeros(P.k_idx.shape, dtype=np.float64)
+    for r in rows:
+        cols, tch, prd = loss_support(P, r)
+        if cols.size == 0:
+            continue
+        gs = scale * kl_grad_scores(tch, prd)
+        g = r.geom
+        seg_k = slice(g.k_base, int(L.cu_k[g.seg + 1]))
+        dq_t, dw_t, dk_c = indexer_grads_row(P.q_idx[r.t], P.weights[r.t], P.k_idx[seg_k],
+                                             P.idx_scale, cols, gs)
+        dq[r.t] = dq_t
+        dw[r.t] = dw_t
+        np.add.at(dk, g.k_base + cols, dk_c)
+    return dq, dw, dk
+
+
+def indexer_loss_fixed(P: Problem, rows, q_idx=None, weights=None, k_idx=None, exact_ws: bool = True) -> float:
+    """The reduced loss as a function of the indexer inputs alone: the teacher and the
+    support of every row are taken from ``rows`` and held fixed, the scores recomputed
+    from (q_idx, weights, k_idx).  Used to pin ``indexer_loss_backward`` by finite
+    differences."""
+    L = P.layout
+    q_idx = P.q_idx if q_idx is None else q_idx
+    weights = P.weights if weights is None else weights
+    k_idx = P.k_idx if k_idx is None else k_idx
+    kls = []
+    for r in rows:
+        cols, tch, _ = loss_support(P, r)
+        if cols.size == 0:
+            kls.append(0.0)
+            continue
+        g = r.geom
+        seg_k = slice(g.k_base, int(L.cu_k[g.seg + 1]))
+        sc = indexer_scores_row(q_idx[r.t], weights[r.t], k_idx[seg_k], P.idx_scale, g.n_valid, exact_ws)
+        kls.append(kl_row(tch, predictor(sc[cols])))
+    return reduce_loss(kls, L.total_q, P.per_token)
