@@ -26,6 +26,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "topk.hip"),
     os.path.join(CSRC, "kernels", "sparse_attn.hip"),
     os.path.join(CSRC, "kernels", "teacher_kl.hip"),
+    os.path.join(CSRC, "kernels", "indexer_bwd.hip"),
 ]
 
 # packed-fp32 VALU ops are disabled for every device pass; the host pass warns that it

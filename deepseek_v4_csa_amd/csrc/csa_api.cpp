@@ -187,4 +187,43 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, 
                     fn);
 }
 
+csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, const void *q_idx,
+                                  const void *k_idx, const float *weights, csa_dtype_t dt, int32_t Hi,
+                                  int32_t Di, float idx_scale, const float *scores, int64_t ld_scores,
+                                  const int32_t *ids, int32_t k_eff, const float *teacher,
+                                  int64_t ld_teacher, float grad_loss, int32_t per_token_loss,
+                                  float *grad_scores, int64_t ld_grad, float *dq_idx, float *dweights,
+                                  float *dk_idx, void *stream) {
+  const char *fn = "csa_indexer_loss_bwd";
+  csa::LaunchLayout LL;
+  csa_status_t st = check_layout(L, fn, &LL);
+  if (st != CSA_OK) return st;
+  if (!q_idx || !k_idx || !weights || !scores || !teacher || !grad_scores || !dq_idx || !dweights || !dk_idx)
+    return fail(CSA_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+  if (Hi < 1 || Di < 1) return fail(CSA_ERR_INVALID, "%s: Hi=%d, Di=%d must be >= 1", fn, Hi, Di);
+  if (ld_scores < L->max_seqlen_k || ld_grad < L->max_seqlen_k)
+    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld / ld_grad=%lld < max_seqlen_k=%d", fn,
+                (long long)ld_scores, (long long)ld_grad, L->max_seqlen_k);
+  if (sparse_loss) {
+    if (k_eff < 1 || k_eff > L->max_seqlen_k)
+      return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [1, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
+    if (!ids) return fail(CSA_ERR_INVALID, "%s: sparse loss needs ids", fn);
+    if (ld_teacher < k_eff)
+      return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < k_eff=%d", fn, (long long)ld_teacher, k_eff);
+  } else if (ld_teacher < L->max_seqlen_k) {
+    return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < max_seqlen_k=%d", fn, (long long)ld_teacher,
+                L->max_seqlen_k);
+  }
+  if (!csa::indexer_bwd_supported(dt == CSA_BF16, Hi, Di, k_eff, sparse_loss != 0, L->max_seqlen_k))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d Hi=%d Di=%d k_eff=%d", fn, (int)dt, Hi,
+                Di, k_eff);
+  const float gscale = per_token_loss ? grad_loss : (L->total_q > 0 ? grad_loss / (float)L->total_q : 0.f);
+  return hip_status(csa::launch_indexer_loss_bwd(LL, sparse_loss != 0, q_idx, k_idx, weights, Hi, Di,
+                                                  idx_scale, scores, ld_scores, ids, k_eff, teacher,
+                                                  ld_teacher, gscale, grad_scores, ld_grad, dq_idx,
+                                                  dweights, dk_idx, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

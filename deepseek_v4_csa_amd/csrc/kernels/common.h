@@ -34,6 +34,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+// 16x16x16 bf16: lane l supplies A[l%16][(l/16)*4 + e] and B[(l/16)*4 + e][l%16],
+// e = 0..3 (4 bf16 in two dwords); same C layout.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16x16x16(uint2 a, uint2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16_t, a),
+                                                   __builtin_bit_cast(v4i16_t, b), c, 0, 0, 0);
+}
 // 16x16x4 fp32: lane l supplies A[l%16][l/16] and B[l/16][l%16]; same C layout.
 __device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -229,6 +236,16 @@ __device__ __forceinline__ float bperm(int addr, float v) {
 }  // namespace csa
 
 namespace csa {
+// Row tiles of D bf16 (D*2 bytes per row) staged in LDS: 16-byte piece p of tile row R is
+// stored at piece position p ^ row_swz<D>(R).  With 64 LDS banks of 4 bytes (256 bytes
+// per bank row), this keeps conflict-free the row-operand reads (16 lanes = rows 0..15,
+// one piece each), the transposing reads (32 lanes = 8 rows x 2 pieces x 2 halves) and
+// the row-staging writes.
+template <int D> __device__ __forceinline__ int row_swz(int r) {
+  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
+
 // ---------------------------------------------------------------- LDS DMA
 // buffer_load_dwordx4 ... lds (gfx950): lane i's 16 bytes from rsrc+voffset land at
 // lds_base + 16*i; an out-of-range offset reads zeros.  Completion is tracked by vmcnt,

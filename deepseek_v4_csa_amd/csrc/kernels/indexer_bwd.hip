@@ -1,0 +1,467 @@
+// Indexer-loss backward: gradients for the indexer q, weights and k.
+//
+// The step after the forward path (page "[Bug] DSV4 unfused CSA indexer loss uses a
+// compressed-only teacher ...": the proposal comment keeps a custom backward that
+// recomputes from saved tensors and returns gradients only for the indexer q, weights
+// and k, the teacher being detached; page "Megatron-LM pull request 8539", item 1: the
+// sparse path's ids are global).  Three kernels:
+//
+//  1. score gradients, one wave per row: with the forward's predictor p = softmax of the
+//     scores over the support and the given teacher t,
+//        g_j = c (p_j R - r_j),  r_j = t_j p_j / (p_j + 1e-10),  R = sum_j r_j,
+//     written densely into G[t, 0..max_seqlen_k) (0 off the support; the sparse mode
+//     zero-fills G first and then scatters).  Normalisers and g in fp64, like the
+//     forward's KL.
+//  2. dq / dweights, one workgroup per 16-token block: for every 64-key tile below the
+//     block's causal limit and every indexer head h, D^T = K Q_h^T (keys x tokens) is
+//     recomputed on MFMA, E = G o [D > 0], and U_h^T += K^T E on MFMA; at the end
+//     dq = ws * U and dweights = s_idx * sum_j G max(D, 0).
+//  3. dk, one workgroup per 64-key tile of a segment (wave = 16 keys): for every 16-token
+//     block with a token that sees the tile, D = Q_h K^T, E'' = G * ws o [D > 0], and
+//     dK^T += Q_h^T E'' on MFMA, summed over heads and blocks in a fixed order.
+//
+// The gradient factors E are fp32; they enter the bf16 MFMAs as a hi/lo pair
+// (hi = bf16(E), lo = bf16(E - hi)), so every product carries ~16 significant bits of E
+// and the bf16 inputs exactly, with fp32 accumulation.  Transposed operands (K^T, Q_h^T)
+// come from LDS through the transposing 64-bit read.  No atomics: every output element
+// is written once, in a fixed summation order.
+#include <algorithm>
+
+#include "common.h"
+#include "../launch.h"
+
+namespace csa {
+
+constexpr float BWD_EPS = 1e-10f;   // the KL's epsilon
+constexpr int BWD_TOK = 16;         // tokens per block
+
+// bf16 hi/lo split of four fp32 values, as two 16x16x16 MFMA operands
+__device__ __forceinline__ void split_bf16x4(const float (&x)[4], uint2 &hi, uint2 &lo) {
+  hi = uint2{pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3])};
+  const float r0 = x[0] - bf16_lo(hi.x), r1 = x[1] - bf16_hi(hi.x);
+  const float r2 = x[2] - bf16_lo(hi.y), r3 = x[3] - bf16_hi(hi.y);
+  lo = uint2{pack2_bf16(r0, r1), pack2_bf16(r2, r3)};
+}
+
+// ---------------------------------------------------------------- 1. score gradients
+__global__ __launch_bounds__(256) void zero_rows_kernel(float *__restrict__ g, int64_t ld, int rows,
+                                                        int cols) {
+  const int64_t n = (int64_t)rows * cols;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / cols, c = e - r * cols;
+    g[r * ld + c] = 0.f;
+  }
+}
+
+// SPL support slots per lane: sparse -> k_eff slots (slot j <-> ids[t, j]); dense ->
+// columns j < max_seqlen_k
+template <int SPL>
+__global__ __launch_bounds__(256) void grad_scores_kernel(
+    LayoutDev L, int T, int sparse, const float *__restrict__ scores, int64_t ld,
+    const int32_t *__restrict__ ids, int k_eff, const float *__restrict__ teacher, int64_t ldt,
+    float gscale, float *__restrict__ grad, int64_t ldg, int max_sk) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + w;
+  if (t >= T) return;
+  const RowGeo geo = row_geo(L, t);
+  float *gr = grad + (int64_t)t * ldg;
+  const int nslot = sparse ? k_eff : max_sk;
+  int col[SPL];
+  float s[SPL], te[SPL];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    const int j = v * 64 + lane;
+    bool valid;
+    if (sparse) {
+      const int id = j < k_eff ? ids[(int64_t)t * k_eff + j] : -1;
+      valid = id >= 0;
+      col[v] = id - geo.k_base;
+    } else {
+      valid = j < geo.n_valid;
+      col[v] = j;
+    }
+    if (!valid) col[v] = -1;
+    s[v] = valid ? scores[(int64_t)t * ld + col[v]] : -__builtin_inff();
+    te[v] = valid ? teacher[(int64_t)t * ldt + j] : 0.f;
+    mx = fmaxf(mx, s[v]);
+  }
+  if (geo.n_valid == 0) {
+    if (!sparse)
+      for (int j = lane; j < max_sk; j += 64) gr[j] = 0.f;
+    return;
+  }
+  mx = wave_max_dpp(mx);
+  float e[SPL];
+  double es = 0.0;
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    e[v] = col[v] >= 0 ? fast_exp2((s[v] - mx) * LOG2E) : 0.f;
+    es += (double)e[v];
+  }
+  es = wave_sum_f64_dpp(es);
+  const double inv_es = 1.0 / es;
+  double rs = 0.0;
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    const double pv = (double)e[v] * inv_es;
+    rs += (double)te[v] * pv / (pv + (double)BWD_EPS);
+  }
+  rs = wave_sum_f64_dpp(rs);
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    const int j = v * 64 + lane;
+    const double pv = (double)e[v] * inv_es;
+    const double rv = (double)te[v] * pv / (pv + (double)BWD_EPS);
+    const float g = (float)((double)gscale * (pv * rs - rv));
+    if (sparse) {
+      if (col[v] >= 0) gr[col[v]] = g;
+    } else if (j < nslot) {
+      gr[j] = col[v] >= 0 ? g : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- shared LDS staging
+// q_idx rows t0 .. t0+15 (RB bytes each) -> LDS, 16-byte chunk q of row r at slot
+// r*CPR + (q ^ r) (one instruction moves 1 KiB of one row; rows past the end of the
+// buffer read as zeros).  Waves w = first, first + step, ... of the workgroup share it.
+template <int RB>
+__device__ __forceinline__ void dma_q_block(const uint16_t *q_idx, int row0, int total_q, char *dst,
+                                            int w, int nw, int lane) {
+  constexpr int CPR = RB / 16, PPR = RB / 1024;
+  const int rows_left = min(BWD_TOK, total_q - row0);
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(q_idx + (int64_t)row0 * (RB / 2), (uint32_t)(max(rows_left, 0) * RB));
+  for (int m = w; m < BWD_TOK * PPR; m += nw) {
+    const int r = m / PPR, q0 = (m - r * PPR) * 64;
+    dma16(rq, dst + (size_t)(r * CPR + q0) * 16, (uint32_t)(r * RB + (((q0 + lane) ^ r) << 4)));
+  }
+}
+
+// ---------------------------------------------------------------- 2. dq / dweights
+// HPW heads per wave per pass; 4 waves; passes = HI / (4 * HPW).
+template <int DI, int HI, int HPW>
+__global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
+    const float *__restrict__ weights, float idx_scale, const float *__restrict__ grad, int64_t ldg,
+    int max_sk, int total_q, int nqb, float *__restrict__ dq, float *__restrict__ dw) {
+  constexpr int RB = HI * DI * 2, CPR = RB / 16;
+  constexpr int NCD = DI / 32;         // MFMA 16x16x32 K-chunks per dot product
+  constexpr int NDT = DI / 16;         // 16-dim output tiles
+  constexpr int ROWB = DI * 2;         // bytes per key row
+  constexpr int PIECES = DI / 8, RPI = 64 / PIECES, NI = 64 / RPI;   // key-tile DMA shape
+  constexpr int KT = 64 * ROWB;        // one 64-key tile
+  constexpr int PASSES = HI / (4 * HPW);
+  static_assert(HI % (4 * HPW) == 0, "heads per pass");
+  __shared__ __attribute__((aligned(16))) u32x4 qs[BWD_TOK * CPR];
+  __shared__ __attribute__((aligned(16))) char kt_lds[2][KT];
+
+  const int seg = blockIdx.x % L.num_seqs;
+  const int qb = nqb - 1 - (int)(blockIdx.x / L.num_seqs);   // heaviest blocks first
+  const int q_start = __ldg(L.cu_q + seg);
+  const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
+  const int t0 = qb * BWD_TOK;
+  if (t0 >= q_len) return;
+  const int k_base = __ldg(L.cu_k + seg);
+  const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
+  const int off = seg_offset(L, seg, q_len, s_k);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nv_last = n_valid_of(min(t0 + BWD_TOK, q_len) - 1, off, L.ratio, s_k);
+  const int nlive = (nv_last + 63) / 64;
+  const int t = t0 + r16;              // this lane's token (C / B operand column)
+  const bool t_ok = t < q_len;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_idx + (int64_t)k_base * DI, (uint32_t)(max(s_k, 0) * ROWB));
+
+  dma_q_block<RB>(q_idx, q_start + t0, total_q, reinterpret_cast<char *>(qs), w, 4, lane);
+  // key tile kt -> buffer b: NI instructions of RPI rows, dealt over the 4 waves
+  const int kgg = lane / PIECES, kpp = lane % PIECES;
+  auto dma_k = [&](int kt, int b) {
+    for (int i = w; i < NI; i += 4) {
+      const int R = i * RPI + kgg, j = kt * 64 + R;
+      const uint32_t o = j < s_k ? (uint32_t)j * ROWB + 16 * (kpp ^ row_swz<DI>(R)) : BUF_OOB;
+      dma16(rk, kt_lds[b] + i * 1024, o);
+    }
+  };
+  const char *qrow = reinterpret_cast<const char *>(qs) + r16 * RB;
+  auto a_frag = [&](int h, int c) -> u32x4 {   // Q_h^T operand: token r16, piece 4c+g
+    const int q = h * (DI / 8) + 4 * c + g;
+    return *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
+  };
+
+  for (int pass = 0; pass < PASSES; ++pass) {
+    f32x4 u[HPW][NDT];
+    float dwa[HPW];
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) {
+      dwa[k] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) u[k][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (nlive > 0) dma_k(0, 0);
+    for (int kt = 0; kt < nlive; ++kt) {
+      wait_vmcnt<0>();
+      __syncthreads();   // tile kt (and, first time, the q block) visible to every wave
+      if (kt + 1 < nlive) dma_k(kt + 1, (kt + 1) & 1);
+      const char *kb = kt_lds[kt & 1];
+      const int j0 = kt * 64;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        // G[t, j0 + 16m + 4g + i]: this lane's E^T entries (0 past the row or segment)
+        float gv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 16 * m + 4 * g + i;
+          gv[i] = (t_ok && j < max_sk) ? grad[(int64_t)(q_start + t) * ldg + j] : 0.f;
+        }
+        // K row operand (rows 16m + r16) for D^T = K Q_h^T
+        u32x4 ka[NCD];
+        const int R = 16 * m + r16;
+#pragma unroll
+        for (int c = 0; c < NCD; ++c)
+          ka[c] = *reinterpret_cast<const u32x4 *>(kb + R * ROWB + 16 * ((4 * c + g) ^ row_swz<DI>(R)));
+        // K^T operand (dims x keys 16m + 4g .. +3) by the transposing read, per dim tile
+        uint2 kt_op[NDT];
+        {
+          const int rr = 16 * m + 4 * g + (r16 >> 2);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const int piece = 2 * dt + ((r16 & 3) >> 1);
+            kt_op[dt] = lds_read_tr16(kb + rr * ROWB + 16 * (piece ^ row_swz<DI>(rr)) + 8 * (r16 & 1));
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < HPW; ++k) {
+          const int h = pass * 4 * HPW + k * 4 + w;
+          f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NCD; ++c) d = mfma16x16x32(ka[c], a_frag(h, c), d);
+          float e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            e[i] = d[i] > 0.f ? gv[i] : 0.f;
+            dwa[k] = fmaf(gv[i], fmaxf(d[i], 0.f), dwa[k]);
+          }
+          uint2 ehi, elo;
+          split_bf16x4(e, ehi, elo);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            u[k][dt] = mfma16x16x16(kt_op[dt], ehi, u[k][dt]);
+            u[k][dt] = mfma16x16x16(kt_op[dt], elo, u[k][dt]);
+          }
+        }
+      }
+      __syncthreads();   // every wave is done with tile kt before it is overwritten
+    }
+    // outputs: lane (token r16, group g) holds dims 16dt + 4g + i of U_h^T
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) {
+      const int h = pass * 4 * HPW + k * 4 + w;
+      float s = dwa[k];
+      s += __shfl_xor(s, 16, 64);
+      s += __shfl_xor(s, 32, 64);
+      if (t_ok) {
+        const int64_t row = (int64_t)(q_start + t) * HI + h;
+        const float ws = weights[row] * idx_scale;
+        float *dst = dq + row * DI + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<f32x4 *>(dst + 16 * dt) = u[k][dt] * ws;
+        if (g == 0) dw[row] = s * idx_scale;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 3. dk
+template <int DI, int HI>
+__global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
+    const float *__restrict__ weights, float idx_scale, const float *__restrict__ grad, int64_t ldg,
+    int max_sk, int total_q, int nkt, float *__restrict__ dk) {
+  constexpr int RB = HI * DI * 2, CPR = RB / 16;
+  constexpr int NCD = DI / 32, NDT = DI / 16;
+  __shared__ __attribute__((aligned(16))) u32x4 qs[2][BWD_TOK * CPR];
+  __shared__ __attribute__((aligned(16))) float wsl[2][HI * BWD_TOK];   // [h][token]
+
+  const int seg = blockIdx.x % L.num_seqs;
+  const int kt = (int)(blockIdx.x / L.num_seqs);   // low tiles see the most tokens: first
+  const int k_base = __ldg(L.cu_k + seg);
+  const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
+  const int j0 = kt * 64;
+  if (j0 >= s_k) return;
+  const int q_start = __ldg(L.cu_q + seg);
+  const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
+  const int off = seg_offset(L, seg, q_len, s_k);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = j0 + 16 * w + r16;     // this lane's key (B operand / C column)
+  const bool j_ok = j < s_k;
+  // key operand of D = Q_h K^T: key row j, piece 4c+g (kept for every token block)
+  u32x4 kb[NCD];
+  {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(k_idx + (int64_t)(k_base + min(j, s_k - 1)) * DI) + g;
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) kb[c] = p[4 * c];
+  }
+  // first 16-token block with a token that sees key j0 (n_valid is nondecreasing in t)
+  const int nqb = (q_len + BWD_TOK - 1) / BWD_TOK;
+  int b_lo = nqb;
+  for (int b = 0; b < nqb; ++b)
+    if (n_valid_of(min(b * BWD_TOK + BWD_TOK, q_len) - 1, off, L.ratio, s_k) > j0) { b_lo = b; break; }
+
+  auto stage = [&](int b, int buf) {   // q rows and fp32(w * s_idx) of block b
+    dma_q_block<RB>(q_idx, q_start + b * BWD_TOK, total_q, reinterpret_cast<char *>(qs[buf]), w, 4, lane);
+    for (int e = tid; e < HI * BWD_TOK; e += 256) {
+      const int tt = e / HI, h = e - tt * HI;
+      const int t = b * BWD_TOK + tt;
+      wsl[buf][h * BWD_TOK + tt] = t < q_len ? weights[(int64_t)(q_start + t) * HI + h] * idx_scale : 0.f;
+    }
+  };
+  // a key may collect terms from every row of its segment: each token block's partial
+  // sum (MFMA, fp32) is added to the total with Kahan compensation
+  f32x4 acc[NDT], cmp[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = cmp[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (b_lo < nqb) stage(b_lo, 0);
+  for (int b = b_lo; b < nqb; ++b) {
+    const int buf = (b - b_lo) & 1;
+    wait_vmcnt<0>();
+    __syncthreads();   // block b staged (q rows by DMA, weights by stores)
+    if (b + 1 < nqb) stage(b + 1, buf ^ 1);
+    const int t0 = b * BWD_TOK;
+    // G[t0 + 4g + i, j]: this lane's E'' column entries (0 past the segment)
+    float gv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      gv[i] = (t < q_len && j_ok) ? grad[(int64_t)(q_start + t) * ldg + j] : 0.f;
+    }
+    const char *qb = reinterpret_cast<const char *>(qs[buf]);
+    const char *qrow = qb + r16 * RB;
+    const float *wsb = wsl[buf];
+    f32x4 part[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) part[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < HI; ++h) {
+      // D = Q_h K^T: A = Q_h rows (token r16, piece 4c+g), B = key operand
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) {
+        const int q = h * (DI / 8) + 4 * c + g;
+        const u32x4 qa = *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
+        d = mfma16x16x32(qa, kb[c], d);
+      }
+      // lane (key r16, group g) holds D[token 4g + i][key]
+      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsb + h * BWD_TOK + 4 * g);
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = d[i] > 0.f ? gv[i] * wv[i] : 0.f;
+      uint2 ehi, elo;
+      split_bf16x4(e, ehi, elo);
+      // Q_h^T operand (dims 16dt + r16 x tokens 4g .. +3) by the transposing read:
+      // lane supplies row 4g + r16/4, dims 16dt + 4(r16%4) .. +3 of head h
+      const int rr = 4 * g + (r16 >> 2);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int col = h * DI + 16 * dt + 4 * (r16 & 3);    // bf16 column in the row
+        const int q = col >> 3;                               // 16-byte chunk
+        const uint2 qt = lds_read_tr16(qb + rr * RB + ((q ^ rr) << 4) + 8 * ((col >> 2) & 1));
+        part[dt] = mfma16x16x16(qt, ehi, part[dt]);
+        part[dt] = mfma16x16x16(qt, elo, part[dt]);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const f32x4 y = part[dt] - cmp[dt];
+      const f32x4 tot = acc[dt] + y;
+      cmp[dt] = (tot - acc[dt]) - y;
+      acc[dt] = tot;
+    }
+    __syncthreads();   // every wave is done with buffer buf before it is restaged
+  }
+  // lane (key r16, group g) holds dims 16dt + 4g + i of dK^T[:, key]
+  if (j_ok) {
+    float *dst = dk + (int64_t)(k_base + j) * DI + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = acc[dt];
+  }
+}
+
+// ---------------------------------------------------------------- launch
+template <int DI, int HI, int HPW>
+static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+                               const float *weights, float idx_scale, const float *grad, int64_t ldg,
+                               float *dq, float *dw, float *dk, hipStream_t st) {
+  const int nqb = (LL.max_seqlen_q + BWD_TOK - 1) / BWD_TOK;
+  const int nkt = (LL.max_seqlen_k + 63) / 64;
+  if (LL.total_q > 0) {
+    hipLaunchKernelGGL((idx_bwd_dq_kernel<DI, HI, HPW>), dim3((unsigned)(LL.num_seqs * nqb)), dim3(256), 0, st,
+                       LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
+                       weights, idx_scale, grad, ldg, LL.max_seqlen_k, LL.total_q, nqb, dq, dw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((idx_bwd_dk_kernel<DI, HI>), dim3((unsigned)(LL.num_seqs * nkt)), dim3(256), 0, st,
+                     LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
+                     weights, idx_scale, grad, ldg, LL.max_seqlen_k, LL.total_q, nkt, dk);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const void *q_idx,
+                                  const void *k_idx, const float *weights, int Hi, int Di,
+                                  float idx_scale, const float *scores, int64_t ld_scores,
+                                  const int32_t *ids, int k_eff, const float *teacher,
+                                  int64_t ld_teacher, float grad_scale, float *grad, int64_t ld_grad,
+                                  float *dq, float *dw, float *dk, hipStream_t st) {
+  if (LL.total_q > 0) {
+    if (sparse) {
+      const int64_t n = (int64_t)LL.total_q * LL.max_seqlen_k;
+      const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
+      hipLaunchKernelGGL(zero_rows_kernel, dim3(blocks), dim3(256), 0, st, grad, ld_grad, LL.total_q,
+                         LL.max_seqlen_k);
+    }
+    const int nslot = sparse ? k_eff : LL.max_seqlen_k;
+    const dim3 grid((unsigned)((LL.total_q + 3) / 4));
+#define CSA_GS_CASE(S)                                                                              \
+    if (nslot <= 64 * S) {                                                                          \
+      hipLaunchKernelGGL(grad_scores_kernel<S>, grid, dim3(256), 0, st, LL.dev, LL.total_q,         \
+                         sparse ? 1 : 0, scores, ld_scores, ids, k_eff, teacher, ld_teacher,        \
+                         grad_scale, grad, ld_grad, LL.max_seqlen_k);                               \
+    } else
+    CSA_GS_CASE(1) CSA_GS_CASE(2) CSA_GS_CASE(4) CSA_GS_CASE(8) CSA_GS_CASE(16) CSA_GS_CASE(32)
+    CSA_GS_CASE(64) { return hipErrorInvalidValue; }
+#undef CSA_GS_CASE
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+#define CSA_BWD_ARGS LL, q_idx, k_idx, weights, idx_scale, grad, ld_grad, dq, dw, dk, st
+  if (Di == 64) {
+    switch (Hi) {
+      case 4: return launch_bwd_t<64, 4, 1>(CSA_BWD_ARGS);
+      case 8: return launch_bwd_t<64, 8, 2>(CSA_BWD_ARGS);
+      case 16: return launch_bwd_t<64, 16, 4>(CSA_BWD_ARGS);
+      case 32: return launch_bwd_t<64, 32, 4>(CSA_BWD_ARGS);
+    }
+  } else if (Di == 128) {
+    switch (Hi) {
+      case 4: return launch_bwd_t<128, 4, 1>(CSA_BWD_ARGS);
+      case 8: return launch_bwd_t<128, 8, 2>(CSA_BWD_ARGS);
+      case 16: return launch_bwd_t<128, 16, 2>(CSA_BWD_ARGS);
+    }
+  }
+#undef CSA_BWD_ARGS
+  return hipErrorInvalidValue;
+}
+
+bool indexer_bwd_supported(bool bf16, int Hi, int Di, int k_eff, bool sparse, int max_seqlen_k) {
+  if (!bf16) return false;
+  if ((sparse ? k_eff : max_seqlen_k) > 64 * 64) return false;   // score-gradient slots per row
+  if (Di == 64) return Hi == 4 || Hi == 8 || Hi == 16 || Hi == 32;
+  if (Di == 128) return Hi == 4 || Hi == 8 || Hi == 16;
+  return false;
+}
+
+}  // namespace csa

@@ -306,14 +306,6 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
 // logit exceeds it by 2^8) and a per-lane partial sum; the compressed logits stay in
 // registers so that cmass = sum_h exp(c - lse) is formed once lse is final.
 // ============================================================================
-// 16-byte piece p of tile row R is stored at piece position p ^ row_swz<D>(R).  With 64
-// LDS banks of 4 bytes (256 bytes per bank row), this keeps conflict-free: the K-operand
-// reads (16 lanes = rows 0..15, one piece each), the transposing V reads (32 lanes =
-// 8 rows x 2 pieces x 2 halves) and the O staging writes.
-template <int D> __device__ __forceinline__ int row_swz(int r) {
-  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
-  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-}
 
 template <int D, int KC>
 __global__ __launch_bounds__(256) void sparse_attn_dma_kernel(

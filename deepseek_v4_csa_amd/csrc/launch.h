@@ -29,10 +29,18 @@ hipError_t launch_teacher_kl(const LaunchLayout &L, bool sparse, const float *sc
                              float scale, bool per_token, float *teacher, int64_t ld_teacher,
                              float *kl_row, float *loss, hipStream_t st);
 
+hipError_t launch_indexer_loss_bwd(const LaunchLayout &L, bool sparse, const void *q_idx,
+                                  const void *k_idx, const float *weights, int Hi, int Di,
+                                  float idx_scale, const float *scores, int64_t ld_scores,
+                                  const int32_t *ids, int k_eff, const float *teacher,
+                                  int64_t ld_teacher, float grad_scale, float *grad, int64_t ld_grad,
+                                  float *dq, float *dw, float *dk, hipStream_t st);
+
 // shape support tables (host side, used by validation before any launch)
 bool indexer_supported(bool bf16, int Hi, int Di);
 bool topk_supported(int max_seqlen_k, int k_eff);
 bool attn_supported(bool bf16, int H, int D, int k_eff);
 bool dense_teacher_supported(bool bf16, int H, int D, int max_seqlen_k);
+bool indexer_bwd_supported(bool bf16, int Hi, int Di, int k_eff, bool sparse, int max_seqlen_k);
 
 }  // namespace csa

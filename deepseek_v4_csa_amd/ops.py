@@ -35,7 +35,7 @@ class _CLayout(ctypes.Structure):
 
 
 EXPORTS = ("csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
-           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl")
+           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd")
 
 
 def lib_path() -> str:
@@ -66,6 +66,9 @@ def load():
     lib.csa_indexer_teacher_kl.restype = ctypes.c_int
     lib.csa_indexer_teacher_kl.argtypes = [LP, I32, P, I64, P, I32, P, P, P, P, ctypes.c_int, I32,
                                            I32, F32, I32, P, I64, P, P, P]
+    lib.csa_indexer_loss_bwd.restype = ctypes.c_int
+    lib.csa_indexer_loss_bwd.argtypes = [LP, I32, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, P, I32,
+                                         P, I64, F32, I32, P, I64, P, P, P, P]
     _lib = lib
     return lib
 
@@ -193,6 +196,28 @@ def csa_indexer_teacher_kl(layout: Layout, sparse_loss: bool, scores, ids, cmass
         1 if per_token else 0, _ptr(teacher) if teacher is not None else None,
         teacher.stride(0) if teacher is not None else 0, _ptr(kl_row), _ptr(loss), _stream()))
     return teacher, kl_row, loss
+
+
+def csa_indexer_loss_bwd(layout: Layout, sparse_loss: bool, q_idx, k_idx, weights, idx_scale: float,
+                         scores, ids, teacher, grad_loss: float = 1.0, per_token: bool = False,
+                         grad_scores=None, dq_idx=None, dweights=None, dk_idx=None):
+    """Indexer-loss gradients (fp32) for q_idx, weights and k_idx; the teacher and the
+    selection (ids) of the forward are held fixed."""
+    T, Hi, Di = q_idx.shape
+    dev = q_idx.device
+    k_eff_ = ids.shape[1] if ids is not None else 0
+    if grad_scores is None:
+        grad_scores = torch.empty((T, layout.max_seqlen_k), dtype=torch.float32, device=dev)
+    dq_idx = torch.empty((T, Hi, Di), dtype=torch.float32, device=dev) if dq_idx is None else dq_idx
+    dweights = torch.empty((T, Hi), dtype=torch.float32, device=dev) if dweights is None else dweights
+    dk_idx = torch.empty(tuple(k_idx.shape), dtype=torch.float32, device=dev) if dk_idx is None else dk_idx
+    _check(load().csa_indexer_loss_bwd(
+        ctypes.byref(layout.c()), 1 if sparse_loss else 0, _ptr(q_idx), _ptr(k_idx), _ptr(weights),
+        _dtype(q_idx), Hi, Di, float(idx_scale), _ptr(scores), scores.stride(0),
+        _ptr(ids) if ids is not None else None, k_eff_, _ptr(teacher), teacher.stride(0),
+        float(grad_loss), 1 if per_token else 0, _ptr(grad_scores), grad_scores.stride(0),
+        _ptr(dq_idx), _ptr(dweights), _ptr(dk_idx), _stream()))
+    return dq_idx, dweights, dk_idx
 
 
 def layout_of_inputs(inp) -> Layout:

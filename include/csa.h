@@ -9,6 +9,7 @@
  *                          compressed probabilities (cmass) the teacher needs
  *   csa_indexer_teacher_kl paper-equivalent teacher, KL(teacher || indexer softmax)
  *                          and the loss reduction
+ * and, after it, csa_indexer_loss_bwd (the loss gradients for the indexer inputs).
  *
  * Sources cited below by tag:
  *  [I5776]  page "[Bug] DSV4 unfused CSA indexer loss uses a compressed-only teacher
@@ -179,6 +180,41 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss,
                                     csa_dtype_t dt, int32_t H, int32_t D, float softmax_scale,
                                     int32_t per_token_loss, float *teacher, int64_t ld_teacher,
                                     float *kl_row, float *loss, void *stream);
+
+/*
+ * csa_indexer_loss_bwd -- gradients of the indexer loss for the indexer q, weights and k.
+ * The step after the forward path ([I5776] proposal comment and review comment: the loss
+ * keeps a custom backward that recomputes what it needs from saved tensors and returns
+ * gradients only for the indexer q, weights and k; every teacher-side input is detached;
+ * [PR8539] item 1: the sparse path's ids are global).  The teacher (from
+ * csa_indexer_teacher_kl's `teacher` output) and the selection are inputs held fixed.
+ * With the support C_t, predictor p = softmax(scores[t, C_t]) and teacher t_j of the
+ * forward, and c = grad_loss / total_q (or grad_loss if per_token_loss != 0):
+ *   r_j = t_j p_j / (p_j + 1e-10),  g_tj = c * (p_j * sum_{j' in C} r_j' - r_j)  (j in C),
+ *   g_tj = 0 elsewhere  -- the derivative of the KL of csa_indexer_teacher_kl;
+ *   with d_thj = q_idx[t,h,:] . k_idx[cu_k[s]+j,:], a = [d > 0], ws = fp32(w[t,h]*idx_scale):
+ *   dq_idx[t,h,:]      = ws * sum_j g_tj a_thj k_idx[cu_k[s]+j,:]
+ *   dweights[t,h]      = idx_scale * sum_j g_tj max(d_thj, 0)
+ *   dk_idx[cu_k[s]+j,:] = sum_{t in s} sum_h g_tj ws a_thj q_idx[t,h,:]
+ * Arguments:
+ *   q_idx [T, Hi, Di], k_idx [T_k, Di] (dtype dt);  weights [T, Hi] fp32;
+ *   scores [T, ld_scores] fp32 (the forward's);  sparse: ids [T, k_eff] int32 and
+ *   teacher [T, ld_teacher >= k_eff] (slot-aligned with ids); dense: ids may be NULL and
+ *   teacher [T, ld_teacher >= max_seqlen_k] (column j for j < n_valid);
+ *   grad_scores: workspace [T, ld_grad >= max_seqlen_k] fp32, overwritten with g;
+ *   dq_idx [T, Hi, Di], dweights [T, Hi], dk_idx [T_k, Di]: fp32, overwritten (every
+ *   element, including rows and keys that get no gradient).  Deterministic: no atomics.
+ * Supported: dt = CSA_BF16; Di = 64 with Hi in {4, 8, 16, 32}, or Di = 128 with Hi in
+ * {4, 8, 16}; sparse k_eff <= 4096, dense max_seqlen_k <= 4096.
+ */
+csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss,
+                                  const void *q_idx, const void *k_idx, const float *weights,
+                                  csa_dtype_t dt, int32_t Hi, int32_t Di, float idx_scale,
+                                  const float *scores, int64_t ld_scores, const int32_t *ids,
+                                  int32_t k_eff, const float *teacher, int64_t ld_teacher,
+                                  float grad_loss, int32_t per_token_loss, float *grad_scores,
+                                  int64_t ld_grad, float *dq_idx, float *dweights, float *dk_idx,
+                                  void *stream);
 
 #ifdef __cplusplus
 }

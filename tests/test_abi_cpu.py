@@ -27,7 +27,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) == {"csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
-                          "csa_sparse_attn_fwd", "csa_indexer_teacher_kl"}
+                          "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -74,6 +74,21 @@ def test_argument_misuse_is_rejected(lib):
     assert lib.csa_indexer_teacher_kl(B(L), 0, FAKE, 16, None, 0, None, FAKE, FAKE, FAKE, 0, 4, 64,
                                       0.1, 0, None, 0, FAKE, FAKE, None) == 2    # dense fp32
     assert "dense" in lib.csa_last_error().decode()
+    bwd = lib.csa_indexer_loss_bwd
+    args = [B(L), 1, FAKE, FAKE, FAKE, 1, 16, 64, 0.1, FAKE, 16, FAKE, 4, FAKE, 4, 1.0, 0, FAKE, 16,
+            FAKE, FAKE, FAKE, None]
+    a = list(args); a[11] = None
+    assert bwd(*a) == 1                                                            # sparse without ids
+    a = list(args); a[14] = 3
+    assert bwd(*a) == 1                                                            # ld_teacher < k_eff
+    a = list(args); a[18] = 8
+    assert bwd(*a) == 1                                                            # ld_grad < max_seqlen_k
+    a = list(args); a[7] = 96
+    assert bwd(*a) == 2                                                            # Di = 96
+    a = list(args); a[5] = 0
+    assert bwd(*a) == 2                                                            # fp32
+    a = list(args); a[19] = None
+    assert bwd(*a) == 1                                                            # null dq
 
 
 def test_k_eff(lib):
