@@ -58,11 +58,14 @@ class Layout:
     ratio: int >= 1         compression ratio
     off  : int array [B] or None  per-segment causal offsets; None means the
                              bottom-right default of ``default_offsets``.
+    cu_q_real : int array [B+1] or None  real (unpadded) query boundaries of a batch
+                             whose segments carry trailing padding rows; None: no padding.
     """
     cu_q: np.ndarray
     cu_k: np.ndarray
     ratio: int
     off: np.ndarray | None = None
+    cu_q_real: np.ndarray | None = None
 
     @property
     def num_seqs(self) -> int:
@@ -115,6 +118,7 @@ class RowGeom:
     n_valid: int    # visible compressed keys
     k_base: int     # cu_k[s]  (global id of local key 0)
     q_start: int    # cu_q[s]
+    padding: bool = False   # row past its segment's real length (left out of the loss)
 
 
 def segment_of_row(cu_q, t: int) -> int:
@@ -135,6 +139,11 @@ def row_geometry(L: Layout, t: int) -> RowGeom:
     mask bottom-right; i = r + 1 + off[s].
     READING: a non-positive numerator means no visible key (clamp at 0), and a row never
     sees past its own segment's keys (clamp at S_k(s)).
+
+    Padding ([I5776, dsa_kernels.py fused-path excerpt, step 4b]): when CUDA-graph padding
+    makes cu_q cover every physical row, the unpadded boundaries give each segment's real
+    length, and a row whose position in its segment is at or past that length is padding
+    (every row of a trailing dummy segment of real length 0 is).
     """
     s = segment_of_row(L.cu_q, t)
     r = t - int(L.cu_q[s])
@@ -142,7 +151,11 @@ def row_geometry(L: Layout, t: int) -> RowGeom:
     s_k = int(L.cu_k[s + 1] - L.cu_k[s])
     n = i // L.ratio if i > 0 else 0
     n = max(0, min(n, s_k))
-    return RowGeom(seg=s, local=r, pos=i, n_valid=n, k_base=int(L.cu_k[s]), q_start=int(L.cu_q[s]))
+    padding = False
+    if L.cu_q_real is not None:
+        padding = r >= int(L.cu_q_real[s + 1] - L.cu_q_real[s])
+    return RowGeom(seg=s, local=r, pos=i, n_valid=n, k_base=int(L.cu_k[s]), q_start=int(L.cu_q[s]),
+                   padding=padding)
 
 
 def k_eff_of(L: Layout, topk: int) -> int:
@@ -411,9 +424,10 @@ def kl_row(teacher, pred) -> float:
 def reduce_loss(kl_rows, total_q: int, per_token: bool) -> float:
     """Loss reduction.  READING (the dsa.py excerpt is cut off before the reduction):
     per-row KL sum, then the mean over all physical query rows -- rows with nothing
-    visible contribute 0 but stay in the divisor, as the review comment in [I5776]
-    describes for padded THD (divisor = physical total_q).  With per-token loss the
-    per-row values are summed."""
+    visible and padding rows contribute 0 but stay in the divisor, as the review comment
+    in [I5776] describes for padded THD (real segment losses weighted by their real
+    lengths, divided by the physical total_q).  With per-token loss the per-row values
+    are summed."""
     s = float(np.sum(np.asarray(kl_rows, dtype=np.float64)))
     return s if per_token else s / float(total_q)
 
@@ -468,9 +482,12 @@ def run_row(P: Problem, t: int, ids_override=None, scores_override=None) -> RowR
     ids = topk_row(scores, g.n_valid, k_eff, g.k_base) if ids_override is None else np.asarray(ids_override, dtype=np.int64)
     win = window_rows(t, g.q_start, P.window)
     attn = attention_row(P.q[t], P.kv, P.ckv, P.sink, ids, win, P.scale)
-    if g.n_valid == 0:
+    if g.n_valid == 0 or g.padding:
         # no visible compressed key: the row's loss terms are zeroed
-        # ([I5776, dsa.py excerpt]: fully masked rows are zeroed before and after the softmax)
+        # ([I5776, dsa.py excerpt]: fully masked rows are zeroed before and after the softmax).
+        # A padding row keeps its scores, ids and attention output (the fused path masks
+        # clones of them for the loss only) and contributes nothing to the loss
+        # ([I5776, fused-path excerpt, steps 4b and 5]).
         n = k_eff if P.sparse_loss else 0
         return RowResult(t, g, scores, ids, attn, np.zeros(n), np.zeros(n), 0.0)
     if P.sparse_loss:
@@ -543,7 +560,7 @@ def indexer_grads_row(q_idx_t, w_t, k_idx_seg, idx_scale, cols, g_cols, exact_ws
 def loss_support(P: Problem, r: RowResult):
     """The support C of row r as local columns, with the teacher and predictor on it."""
     g = r.geom
-    if g.n_valid == 0:
+    if g.n_valid == 0 or g.padding:
         return np.zeros(0, dtype=np.int64), np.zeros(0), np.zeros(0)
     if P.sparse_loss:
         valid = r.ids >= 0
