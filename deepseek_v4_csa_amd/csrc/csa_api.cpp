@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 
 #include "launch.h"
@@ -55,6 +56,7 @@ csa_status_t check_layout(const csa_layout_t *L, const char *fn, csa::LaunchLayo
   out->dev.cu_q = L->cu_seqlens_q;
   out->dev.cu_k = L->cu_seqlens_k;
   out->dev.off = L->q_causal_offsets;
+  out->dev.cu_q_real = L->cu_seqlens_q_unpadded;
   out->dev.num_seqs = L->num_seqs;
   out->dev.ratio = L->compress_ratio;
   out->num_seqs = L->num_seqs;
@@ -224,6 +226,56 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, co
                                                   ld_teacher, gscale, grad_scores, ld_grad, dq_idx,
                                                   dweights, dk_idx, static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+csa_status_t csa_cp_plan(int32_t num_docs, const int32_t *doc_len, int32_t ratio, int32_t cp_size,
+                         int32_t cp_rank, int32_t *num_segs, int32_t *cu_q, int32_t *cu_k,
+                         int32_t *off, int32_t *q_src, int32_t *k_src) {
+  const char *fn = "csa_cp_plan";
+  if (!doc_len || !num_segs || !cu_q || !cu_k || !off || !q_src || !k_src)
+    return fail(CSA_ERR_INVALID, "%s: NULL argument", fn);
+  if (num_docs < 1 || ratio < 1 || cp_size < 1)
+    return fail(CSA_ERR_INVALID, "%s: num_docs=%d ratio=%d cp_size=%d must be >= 1", fn, num_docs,
+                ratio, cp_size);
+  if (cp_rank < 0 || cp_rank >= cp_size)
+    return fail(CSA_ERR_INVALID, "%s: cp_rank=%d outside [0, %d)", fn, cp_rank, cp_size);
+  const int64_t nchunk = 2 * (int64_t)cp_size;
+  int64_t tq = 0, tk = 0, bq = 0, bk = 0;
+  for (int32_t d = 0; d < num_docs; ++d) {
+    if (doc_len[d] < 1 || doc_len[d] % nchunk != 0)
+      return fail(CSA_ERR_INVALID, "%s: doc_len[%d]=%d is not a positive multiple of 2*cp_size=%lld",
+                  fn, d, doc_len[d], (long long)nchunk);
+    const int64_t c = doc_len[d] / nchunk;
+    tq += 2 * c;
+    tk += (((int64_t)cp_rank + 1) * c) / ratio + ((nchunk - cp_rank) * c) / ratio;
+    bq += doc_len[d];
+    bk += doc_len[d] / ratio;
+  }
+  if (tq > INT32_MAX || tk > INT32_MAX || bq > INT32_MAX || bk > INT32_MAX)
+    return fail(CSA_ERR_INVALID, "%s: totals exceed int32", fn);
+  int32_t s = 0, row = 0, key = 0;
+  cu_q[0] = cu_k[0] = 0;
+  int64_t doc_row = 0, doc_key = 0;
+  for (int32_t d = 0; d < num_docs; ++d) {
+    const int32_t c = (int32_t)(doc_len[d] / nchunk);
+    const int32_t held[2] = {cp_rank, (int32_t)(nchunk - 1 - cp_rank)};
+    for (int32_t h = 0; h < 2; ++h) {
+      const int32_t start = held[h] * c;
+      const int32_t nkeys = (start + c) / ratio;
+      off[s] = start;
+      q_src[s] = (int32_t)(doc_row + start);
+      k_src[s] = (int32_t)doc_key;
+      row += c;
+      key += nkeys;
+      cu_q[s + 1] = row;
+      cu_k[s + 1] = key;
+      ++s;
+    }
+    doc_row += doc_len[d];
+    doc_key += doc_len[d] / ratio;
+  }
+  *num_segs = s;
+  return ok();
 }
 
 }  // extern "C"

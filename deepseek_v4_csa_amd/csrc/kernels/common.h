@@ -127,6 +127,7 @@ struct LayoutDev {
   const int32_t *cu_q;
   const int32_t *cu_k;
   const int32_t *off;  // may be null: bottom-right default
+  const int32_t *cu_q_real;  // may be null: no padding rows
   int32_t num_seqs;
   int32_t ratio;
 };
@@ -162,6 +163,16 @@ __device__ __forceinline__ RowGeo row_geo(const LayoutDev &L, int t) {
   int off = L.off ? __ldg(L.off + g.seg) : g.s_k * L.ratio - g.q_len;
   g.n_valid = n_valid_of(t - g.q_start, off, L.ratio, g.s_k);
   return g;
+}
+
+// A row adds nothing to the loss when it sees no compressed key or is a padding row (its
+// position in the segment at or past the segment's real length).  Padding rows are still
+// scored, selected and attended like any row.
+__device__ __forceinline__ bool loss_row_empty(const LayoutDev &L, const RowGeo &g, int t) {
+  if (g.n_valid == 0) return true;
+  if (!L.cu_q_real) return false;
+  const int real = __ldg(L.cu_q_real + g.seg + 1) - __ldg(L.cu_q_real + g.seg);
+  return t - g.q_start >= real;
 }
 
 __device__ __forceinline__ int seg_offset(const LayoutDev &L, int s, int q_len, int s_k) {

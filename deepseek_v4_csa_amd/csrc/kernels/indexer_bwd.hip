@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void grad_scores_kernel(
     te[v] = valid ? teacher[(int64_t)t * ldt + j] : 0.f;
     mx = fmaxf(mx, s[v]);
   }
-  if (geo.n_valid == 0) {
+  if (loss_row_empty(L, geo, t)) {
     if (!sparse)
       for (int j = lane; j < max_sk; j += 64) gr[j] = 0.f;
     return;

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
   const float *cm = cmass + (int64_t)t * k_eff;
   const float *sr = scores + (int64_t)t * ld;
   float *te = teacher ? teacher + (int64_t)t * ldt : nullptr;
-  if (geo.n_valid == 0) {
+  if (loss_row_empty(L, geo, t)) {
     if (te)
       for (int j = lane; j < k_eff; j += 64) te[j] = 0.f;
     if (lane == 0) kl_row[t] = 0.f;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   const bool h_ok = h < H;
   const RowGeo geo = row_geo(L, t);
   const int n = geo.n_valid;
-  if (n == 0) {
+  if (loss_row_empty(L, geo, t)) {
     if (teacher)
       for (int j = tid; j < ldt; j += NT) teacher[(int64_t)t * ldt + j] = 0.f;
     if (tid == 0) kl_row[t] = 0.f;

@@ -120,6 +120,7 @@ class Inputs:
     scale: float
     family: str = "gauss"
     extra: dict = field(default_factory=dict)
+    cu_q_real: torch.Tensor | None = None   # int32 [B+1] real boundaries of a padded batch
 
 
 def _randn(gen, shape, device, std, dtype):
@@ -208,3 +209,36 @@ def uniform_rows(total: int, n: int, seed: int = 11) -> list:
     g.manual_seed(seed)
     perm = torch.randperm(total, generator=g)[: min(n, total)]
     return sorted(perm.tolist())
+
+
+def pad_inputs(inp: Inputs, n_pad: int, dummy: bool = False, seed: int = 4242) -> Inputs:
+    """The same batch padded to a static shape with n_pad padding rows: appended to the
+    last segment (dummy=False) or as a trailing dummy segment of real length 0.  The real
+    rows and keys are the input's own; padding rows (and the compressed keys the padded
+    segment gains) are fresh draws from the same distributions.  cu_q_real keeps the
+    real boundaries."""
+    wl = inp.wl
+    segs = list(wl.seg_lens)
+    if dummy:
+        segs.append(int(n_pad))
+    else:
+        segs[-1] += int(n_pad)
+    pw = scaled_down(wl, segs, name=f"{wl.name}-pad{n_pad}{'-dummy' if dummy else ''}")
+    dev = inp.q.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    dt = wl.torch_dtype
+    sd = 1.0 / math.sqrt(wl.D)
+    extra_k = pw.total_k - wl.total_k
+    q = torch.cat([inp.q, _randn(gen, (n_pad, wl.H, wl.D), dev, sd, dt)])
+    kv = torch.cat([inp.kv, _randn(gen, (n_pad, wl.D), dev, sd * wl.kv_scale, dt)])
+    ckv = torch.cat([inp.ckv, _randn(gen, (extra_k, wl.D), dev, sd, dt)])
+    q_idx = torch.cat([inp.q_idx, _randn(gen, (n_pad, wl.Hi, wl.Di), dev, sd, dt)])
+    k_idx = torch.cat([inp.k_idx, _randn(gen, (extra_k, wl.Di), dev, sd, dt)])
+    weights = torch.cat([inp.weights, torch.rand((n_pad, wl.Hi), generator=gen, device=dev,
+                                                 dtype=torch.float32)])
+    cu_q, cu_k, off = layout_tensors(pw, dev)
+    real = inp.cu_q.tolist() + ([inp.cu_q[-1].item()] if dummy else [])
+    cu_real = torch.tensor(real, dtype=torch.int32, device=dev)
+    return Inputs(pw, cu_q, cu_k, off, q, kv, ckv, q_idx, k_idx, weights, inp.sink,
+                  inp.idx_scale, inp.scale, inp.family, cu_q_real=cu_real)

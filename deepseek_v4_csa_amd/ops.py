@@ -31,11 +31,12 @@ class _CLayout(ctypes.Structure):
         ("cu_seqlens_q", ctypes.c_void_p),
         ("cu_seqlens_k", ctypes.c_void_p),
         ("q_causal_offsets", ctypes.c_void_p),
+        ("cu_seqlens_q_unpadded", ctypes.c_void_p),
     ]
 
 
 EXPORTS = ("csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
-           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd")
+           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd", "csa_cp_plan")
 
 
 def lib_path() -> str:
@@ -69,6 +70,8 @@ def load():
     lib.csa_indexer_loss_bwd.restype = ctypes.c_int
     lib.csa_indexer_loss_bwd.argtypes = [LP, I32, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, P, I32,
                                          P, I64, F32, I32, P, I64, P, P, P, P]
+    lib.csa_cp_plan.restype = ctypes.c_int
+    lib.csa_cp_plan.argtypes = [I32, P, I32, I32, I32, P, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -103,7 +106,7 @@ def _stream():
 
 @dataclass
 class Layout:
-    """Packed layout: device int32 cu_seqlens (and offsets) plus host sizes."""
+    """Packed layout: device int32 cu_seqlens (offsets, unpadded cu_seqlens) plus host sizes."""
     cu_q: torch.Tensor
     cu_k: torch.Tensor
     ratio: int
@@ -112,6 +115,7 @@ class Layout:
     max_seqlen_q: int
     max_seqlen_k: int
     offsets: torch.Tensor | None = None
+    cu_q_real: torch.Tensor | None = None
 
     @property
     def num_seqs(self) -> int:
@@ -131,7 +135,8 @@ class Layout:
     def c(self) -> _CLayout:
         return _CLayout(self.num_seqs, int(self.total_q), int(self.total_k), int(self.max_seqlen_q),
                         int(self.max_seqlen_k), int(self.ratio), _ptr(self.cu_q), _ptr(self.cu_k),
-                        _ptr(self.offsets) if self.offsets is not None else None)
+                        _ptr(self.offsets) if self.offsets is not None else None,
+                        _ptr(self.cu_q_real) if self.cu_q_real is not None else None)
 
 
 def k_eff(layout: Layout, topk: int) -> int:
@@ -220,11 +225,27 @@ def csa_indexer_loss_bwd(layout: Layout, sparse_loss: bool, q_idx, k_idx, weight
     return dq_idx, dweights, dk_idx
 
 
+def csa_cp_plan(doc_lens, ratio: int, cp_size: int, cp_rank: int) -> dict:
+    """Host-only: the packed layout of one rank's CP share (lists of Python ints:
+    cu_q, cu_k, off, q_src, k_src)."""
+    lib = load()
+    n = len(doc_lens)
+    arr = lambda m: (ctypes.c_int32 * m)()
+    dl = (ctypes.c_int32 * n)(*[int(x) for x in doc_lens])
+    ns = ctypes.c_int32(0)
+    cu_q, cu_k, off, q_src, k_src = arr(2 * n + 1), arr(2 * n + 1), arr(2 * n), arr(2 * n), arr(2 * n)
+    _check(lib.csa_cp_plan(n, dl, int(ratio), int(cp_size), int(cp_rank), ctypes.byref(ns), cu_q,
+                           cu_k, off, q_src, k_src))
+    m = ns.value
+    return dict(cu_q=list(cu_q[:m + 1]), cu_k=list(cu_k[:m + 1]), off=list(off[:m]),
+                q_src=list(q_src[:m]), k_src=list(k_src[:m]))
+
+
 def layout_of_inputs(inp) -> Layout:
     """Layout of a deepseek_v4_csa_amd.inputs.Inputs (device tensors already built)."""
     wl = inp.wl
     return Layout(inp.cu_q, inp.cu_k, wl.ratio, wl.total_q, wl.total_k, wl.max_seqlen_q,
-                  wl.max_seqlen_k, inp.offsets)
+                  wl.max_seqlen_k, inp.offsets, inp.cu_q_real)
 
 
 def forward(inp, want_teacher=False):

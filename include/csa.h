@@ -76,6 +76,17 @@ typedef struct {
                                       bottom-right default S_k(s)*ratio - seg_len_q(s)
                                       ([PR8539], item 2).  A query chunk scored against
                                       its key prefix passes off = chunk start. */
+  const int32_t *cu_seqlens_q_unpadded; /* device [B+1] or NULL (no padding).  Real segment
+                                      boundaries of a batch padded to a static shape: row t
+                                      of segment s is a padding row iff
+                                      t - cu_q[s] >= cu_unp[s+1] - cu_unp[s] (a trailing
+                                      dummy segment has real length 0).  The forward calls
+                                      compute padding rows like any other row; the loss
+                                      leaves them out (teacher 0, kl_row 0, no gradient)
+                                      while the mean-mode divisor stays the physical
+                                      total_q ([I5776] fused-path excerpt, step 4b; review
+                                      comment on the padded-THD divisor).  Precondition:
+                                      0 <= real length <= physical length per segment. */
 } csa_layout_t;
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -215,6 +226,35 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss,
                                   float grad_loss, int32_t per_token_loss, float *grad_scores,
                                   int64_t ld_grad, float *dq_idx, float *dweights, float *dk_idx,
                                   void *stream);
+
+/*
+ * csa_cp_plan -- host-only layout of one rank's share of context-parallel (CP) scoring.
+ * ([PR8539], item 2 and its test plan: the CP scorers score each query chunk against its
+ * document's key prefix, cropped at the chunk end, and pass the chunk's absolute causal
+ * offset explicitly, so every row sees exactly its absolute causal keys whatever the
+ * default alignment.)
+ * Each of num_docs documents (doc_len[d] query rows, packed back to back; doc_len[d] /
+ * ratio compressed keys, packed back to back) is cut into 2*cp_size chunks of
+ * doc_len[d] / (2*cp_size) rows; rank cp_rank holds chunks cp_rank and
+ * 2*cp_size-1-cp_rank of every document (the zig-zag split that evens out causal work).
+ * Each held chunk is one segment of the share's packed layout, documents in order, the
+ * lower chunk first:
+ *   cu_q[s+1]-cu_q[s] = chunk rows;  off[s] = chunk start within the document;
+ *   cu_k[s+1]-cu_k[s] = floor((off[s] + chunk rows) / ratio), the key prefix the chunk's
+ *   last row sees;
+ *   q_src[s] = batch row of the chunk's first row (share rows cu_q[s].. hold batch rows
+ *   q_src[s]..);  k_src[s] = batch key row of the document's first key (share key rows
+ *   cu_k[s].. hold batch key rows k_src[s]..).
+ * A share id g of segment s is batch key k_src[s] + (g - cu_k[s]).
+ * Outputs are HOST arrays owned by the caller, sized for 2*num_docs segments (cu_q and
+ * cu_k 2*num_docs+1); *num_segs = 2*num_docs.  Nothing touches the GPU.
+ * Errors (CSA_ERR_INVALID, nothing written): a NULL pointer, num_docs < 1, ratio < 1,
+ * cp_size < 1, cp_rank outside [0, cp_size), a doc_len < 1 or not divisible by
+ * 2*cp_size, totals beyond int32.
+ */
+csa_status_t csa_cp_plan(int32_t num_docs, const int32_t *doc_len, int32_t ratio, int32_t cp_size,
+                         int32_t cp_rank, int32_t *num_segs, int32_t *cu_q, int32_t *cu_k,
+                         int32_t *off, int32_t *q_src, int32_t *k_src);
 
 #ifdef __cplusplus
 }

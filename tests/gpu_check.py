@@ -114,46 +114,57 @@ def check_rows(inp, res, rows, exact_scores=False, check_scores=True, dense=None
 def recall_all_rows(inp, res, chunk=4096):
     """Top-k recall of every row against torch.topk in fp32 on the GPU over the row's
     causally visible keys: the fraction of the selected keys whose score is at least
-    the reference K_t-th largest.  Returns (mean, min)."""
+    the reference K_t-th largest.  Every row must also hold exactly K_t valid ids.
+    Returns (mean, min)."""
+    return recall_rows(inp, res["scores"], res["ids"], None, strict=True, chunk=chunk)
+
+
+def recall_rows(inp, scores, ids, rows=None, strict=False, chunk=4096):
+    """Recall of `ids` ([len(rows), k] global ids of the batch `inp`) for the batch rows
+    `rows` (all rows if None) against torch.topk of the batch `scores` over each row's
+    causally visible keys.  strict: also require exactly K_t valid ids per row."""
     wl = inp.wl
-    sc = res["scores"]
-    ids = res["ids"]
+    sc = scores
+    dev = sc.device
     T = wl.total_q
     cu_q = inp.cu_q.cpu().tolist()
     cu_k = inp.cu_k.cpu().tolist()
     seg = torch.zeros(T, dtype=torch.long)
     for s in range(len(cu_q) - 1):
         seg[cu_q[s]:cu_q[s + 1]] = s
-    seg = seg.to(sc.device)
-    cu_q_t = torch.tensor(cu_q, device=sc.device)
-    cu_k_t = torch.tensor(cu_k, device=sc.device)
-    off = inp.offsets.to(sc.device).long()
-    local = torch.arange(T, device=sc.device) - cu_q_t[seg]
+    seg = seg.to(dev)
+    cu_q_t = torch.tensor(cu_q, device=dev)
+    cu_k_t = torch.tensor(cu_k, device=dev)
+    off = inp.offsets.to(dev).long()
+    local = torch.arange(T, device=dev) - cu_q_t[seg]
     pos = local + 1 + off[seg]
     s_k = (cu_k_t[1:] - cu_k_t[:-1])[seg]
     n_valid = torch.clamp(torch.div(pos, wl.ratio, rounding_mode="floor"), min=0)
     n_valid = torch.minimum(n_valid, s_k)
-    k_eff = ids.shape[1]
+    row_idx = torch.arange(T, device=dev) if rows is None else torch.tensor(list(rows), device=dev)
+    k_eff = min(wl.topk, wl.max_seqlen_k)
     recalls = []
-    for r0 in range(0, T, chunk):
-        r1 = min(T, r0 + chunk)
-        x = sc[r0:r1, :wl.max_seqlen_k].clone()
-        cols = torch.arange(wl.max_seqlen_k, device=sc.device)[None, :]
-        x = torch.where(cols < n_valid[r0:r1, None], x, torch.full_like(x, -float("inf")))
-        kt = torch.clamp(n_valid[r0:r1], max=k_eff)
+    for r0 in range(0, row_idx.numel(), chunk):
+        r1 = min(row_idx.numel(), r0 + chunk)
+        ri = row_idx[r0:r1]
+        x = sc.index_select(0, ri)[:, :wl.max_seqlen_k].clone()
+        cols = torch.arange(wl.max_seqlen_k, device=dev)[None, :]
+        nv = n_valid[ri]
+        x = torch.where(cols < nv[:, None], x, torch.full_like(x, -float("inf")))
+        kt = torch.clamp(nv, max=k_eff)
         vals = torch.topk(x, k_eff, dim=1).values                      # [rows, k_eff]
         kth = vals.gather(1, torch.clamp(kt - 1, min=0)[:, None]).squeeze(1)
         gid = ids[r0:r1].long()
-        base = cu_k_t[seg[r0:r1]][:, None]
+        base = cu_k_t[seg[ri]][:, None]
         loc = torch.where(gid >= 0, gid - base, torch.zeros_like(gid))
         picked = x.gather(1, loc)
         ok = (gid >= 0) & (picked >= kth[:, None])
         cnt = ok.sum(1).float()
         has = kt > 0
         rec = torch.where(has, cnt / torch.clamp(kt.float(), min=1), torch.ones_like(cnt))
-        # a row must also hold exactly K_t valid ids
-        nvalid_ids = (gid >= 0).sum(1)
-        assert torch.equal(nvalid_ids, kt), "a row holds a wrong number of valid ids"
+        if strict:
+            nvalid_ids = (gid >= 0).sum(1)
+            assert torch.equal(nvalid_ids, kt), "a row holds a wrong number of valid ids"
         recalls.append(rec)
     rec = torch.cat(recalls)
     return float(rec.mean()), float(rec.min())

@@ -34,7 +34,9 @@ def layout_of(inp, with_offsets=True) -> oracle.Layout:
     return oracle.Layout(cu_q=inp.cu_q.cpu().numpy().astype(np.int64),
                          cu_k=inp.cu_k.cpu().numpy().astype(np.int64),
                          ratio=inp.wl.ratio,
-                         off=inp.offsets.cpu().numpy().astype(np.int64) if with_offsets else None)
+                         off=inp.offsets.cpu().numpy().astype(np.int64) if with_offsets else None,
+                         cu_q_real=(inp.cu_q_real.cpu().numpy().astype(np.int64)
+                                    if inp.cu_q_real is not None else None))
 
 
 def problem_of(inp, rows=None) -> oracle.Problem:

@@ -27,7 +27,10 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) == {"csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
-                          "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd"}
+                          "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd",
+                          "csa_cp_plan"}
+    from deepseek_v4_csa_amd import ops
+    assert set(ops.EXPORTS) == set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -97,3 +100,62 @@ def test_k_eff(lib):
     assert lib.csa_k_eff(ctypes.byref(L), 4) == 4
     assert lib.csa_k_eff(ctypes.byref(L), 400) == 16
     assert lib.csa_k_eff(ctypes.byref(L), -1) == -1
+
+
+def test_ctypes_layout_matches_the_header(tmp_path):
+    """csa_layout_t as the C compiler lays it out (gcc on the header) equals the binding's
+    ctypes mirror, field by field."""
+    import shutil
+    import subprocess
+    from deepseek_v4_csa_amd import ops
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    fields = [f for f, _ in ops._CLayout._fields_]
+    src = tmp_path / "lay.c"
+    body = "".join(f'  printf("%zu ", offsetof(csa_layout_t, {f}));\n' for f in fields)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "csa.h"\nint main(void) {\n'
+                   + body + '  printf("%zu\\n", sizeof(csa_layout_t));\n  return 0;\n}\n')
+    exe = tmp_path / "lay"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = [getattr(ops._CLayout, f).offset for f in fields] + [ctypes.sizeof(ops._CLayout)]
+    assert got == want
+
+
+CP_CASES = [((4096,), 4, 1, 0), ((4096,), 4, 2, 0), ((4096,), 4, 2, 1), ((1024, 2048), 4, 2, 0),
+            ((1024, 2048), 4, 2, 1), ((96, 48, 240), 3, 4, 3), ((40,), 16, 2, 1)]
+
+
+@pytest.mark.parametrize("docs,ratio,cp,rank", CP_CASES)
+def test_cp_plan_matches_the_zigzag_rule(lib, docs, ratio, cp, rank):
+    from deepseek_v4_csa_amd import ops
+    from tests import cp_rule
+    plan = ops.csa_cp_plan(docs, ratio, cp, rank)
+    want = cp_rule.share(docs, ratio, cp, rank)
+    assert len(plan["off"]) == len(want) == 2 * len(docs)
+    for s, (d, a, c, nk, r0, k0) in enumerate(want):
+        assert plan["cu_q"][s + 1] - plan["cu_q"][s] == c
+        assert plan["cu_k"][s + 1] - plan["cu_k"][s] == nk
+        assert (plan["off"][s], plan["q_src"][s], plan["k_src"][s]) == (a, r0, k0)
+    assert plan["cu_q"][0] == plan["cu_k"][0] == 0
+
+
+def test_cp_plan_ranks_cover_every_row_once(lib):
+    from deepseek_v4_csa_amd import ops
+    docs, cp = (64, 128, 32), 4
+    seen = []
+    for r in range(cp):
+        p = ops.csa_cp_plan(docs, 4, cp, r)
+        for s in range(len(p["off"])):
+            seen += range(p["q_src"][s], p["q_src"][s] + p["cu_q"][s + 1] - p["cu_q"][s])
+    assert sorted(seen) == list(range(sum(docs)))
+
+
+@pytest.mark.parametrize("args", [((0,), 4, 1, 0), ((4096,), 0, 1, 0), ((4096,), 4, 0, 0),
+                                  ((4096,), 4, 2, 2), ((4096,), 4, 2, -1), ((100,), 4, 3, 0)])
+def test_cp_plan_rejects_misuse(lib, args):
+    from deepseek_v4_csa_amd import ops
+    with pytest.raises(RuntimeError, match="csa_cp_plan"):
+        ops.csa_cp_plan(*args)
