@@ -195,7 +195,8 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, co
                                   const int32_t *ids, int32_t k_eff, const float *teacher,
                                   int64_t ld_teacher, float grad_loss, int32_t per_token_loss,
                                   float *grad_scores, int64_t ld_grad, float *dq_idx, float *dweights,
-                                  float *dk_idx, void *stream) {
+                                  float *dk_idx, void *workspace, int64_t workspace_bytes,
+                                  void *stream) {
   const char *fn = "csa_indexer_loss_bwd";
   csa::LaunchLayout LL;
   csa_status_t st = check_layout(L, fn, &LL);
@@ -220,12 +221,29 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, co
   if (!csa::indexer_bwd_supported(dt == CSA_BF16, Hi, Di, k_eff, sparse_loss != 0, L->max_seqlen_k))
     return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d Hi=%d Di=%d k_eff=%d", fn, (int)dt, Hi,
                 Di, k_eff);
+  const int64_t need = csa::indexer_bwd_workspace_bytes(L->num_seqs, L->total_k, L->max_seqlen_q,
+                                                        L->max_seqlen_k, Di);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(CSA_ERR_INVALID, "%s: workspace of %lld bytes given, %lld needed", fn,
+                (long long)(workspace ? workspace_bytes : 0), (long long)need);
   const float gscale = per_token_loss ? grad_loss : (L->total_q > 0 ? grad_loss / (float)L->total_q : 0.f);
   return hip_status(csa::launch_indexer_loss_bwd(LL, sparse_loss != 0, q_idx, k_idx, weights, Hi, Di,
                                                   idx_scale, scores, ld_scores, ids, k_eff, teacher,
                                                   ld_teacher, gscale, grad_scores, ld_grad, dq_idx,
-                                                  dweights, dk_idx, static_cast<hipStream_t>(stream)),
+                                                  dweights, dk_idx, workspace,
+                                                  static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int64_t csa_indexer_loss_bwd_workspace(const csa_layout_t *L, int32_t Hi, int32_t Di) {
+  csa::LaunchLayout LL;
+  if (check_layout(L, "csa_indexer_loss_bwd_workspace", &LL) != CSA_OK) return -1;
+  if (!csa::indexer_bwd_supported(true, Hi, Di, 1, true, 1)) {
+    fail(CSA_ERR_UNSUPPORTED, "csa_indexer_loss_bwd_workspace: no kernel for Hi=%d Di=%d", Hi, Di);
+    return -1;
+  }
+  ok();
+  return csa::indexer_bwd_workspace_bytes(L->num_seqs, L->total_k, L->max_seqlen_q, L->max_seqlen_k, Di);
 }
 
 csa_status_t csa_cp_plan(int32_t num_docs, const int32_t *doc_len, int32_t ratio, int32_t cp_size,

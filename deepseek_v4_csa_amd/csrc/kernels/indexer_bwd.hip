@@ -16,9 +16,12 @@
 //     block's causal limit and every indexer head h, D^T = K Q_h^T (keys x tokens) is
 //     recomputed on MFMA, E = G o [D > 0], and U_h^T += K^T E on MFMA; at the end
 //     dq = ws * U and dweights = s_idx * sum_j G max(D, 0).
-//  3. dk, one workgroup per 64-key tile of a segment (wave = 16 keys): for every 16-token
-//     block with a token that sees the tile, D = Q_h K^T, E'' = G * ws o [D > 0], and
-//     dK^T += Q_h^T E'' on MFMA, summed over heads and blocks in a fixed order.
+//  3. dk, one workgroup per (64-key tile of a segment, chunk of 16-token blocks) (wave =
+//     16 keys): for every block of the chunk with a token that sees the tile,
+//     D = Q_h K^T, E'' = G * ws o [D > 0], and dK^T += Q_h^T E'' on MFMA, summed over
+//     heads and blocks in a fixed order.  With more than one chunk per tile each chunk
+//     writes a partial to the caller's workspace and a fourth kernel adds the partials
+//     of every key in chunk order (in fp64).
 //
 // The gradient factors E are fp32; they enter the bf16 MFMAs as a hi/lo pair
 // (hi = bf16(E), lo = bf16(E - hi)), so every product carries ~16 significant bits of E
@@ -276,18 +279,31 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- 3. dk
+// First 16-token block of a segment holding a token that sees key j0: n_valid(t) > j0
+// exactly when the token's position i = t + 1 + off reaches (j0 + 1) * ratio.  The number
+// of blocks if no token does.
+__device__ __forceinline__ int first_block_seeing(int j0, int off, int ratio, int q_len) {
+  const long long tmin = (long long)(j0 + 1) * ratio - 1 - off;
+  if (tmin >= q_len) return (q_len + BWD_TOK - 1) / BWD_TOK;
+  return tmin <= 0 ? 0 : (int)(tmin / BWD_TOK);
+}
+
+// grid: num_seqs x nkt x nsplit (segment fastest); the workgroup of split s covers the
+// blocks [s*ch, (s+1)*ch) that see its tile and writes its sum to out + s*split_stride
+// (split_stride 0 with one split: out is dk itself).
 template <int DI, int HI>
 __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
     LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const float *__restrict__ weights, float idx_scale, const float *__restrict__ grad, int64_t ldg,
-    int max_sk, int total_q, int nkt, float *__restrict__ dk) {
+    int total_q, int nkt, int ch, int64_t split_stride, float *__restrict__ out) {
   constexpr int RB = HI * DI * 2, CPR = RB / 16;
   constexpr int NCD = DI / 32, NDT = DI / 16;
   __shared__ __attribute__((aligned(16))) u32x4 qs[2][BWD_TOK * CPR];
   __shared__ __attribute__((aligned(16))) float wsl[2][HI * BWD_TOK];   // [h][token]
 
   const int seg = blockIdx.x % L.num_seqs;
-  const int kt = (int)(blockIdx.x / L.num_seqs);   // low tiles see the most tokens: first
+  const int rest = (int)(blockIdx.x / L.num_seqs);
+  const int kt = rest % nkt, split = rest / nkt;
   const int k_base = __ldg(L.cu_k + seg);
   const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
   const int j0 = kt * 64;
@@ -306,11 +322,17 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
 #pragma unroll
     for (int c = 0; c < NCD; ++c) kb[c] = p[4 * c];
   }
-  // first 16-token block with a token that sees key j0 (n_valid is nondecreasing in t)
-  const int nqb = (q_len + BWD_TOK - 1) / BWD_TOK;
-  int b_lo = nqb;
-  for (int b = 0; b < nqb; ++b)
-    if (n_valid_of(min(b * BWD_TOK + BWD_TOK, q_len) - 1, off, L.ratio, s_k) > j0) { b_lo = b; break; }
+  // this workgroup's blocks: those of its chunk from the first block that sees key j0
+  const int b_lo = max(first_block_seeing(j0, off, L.ratio, q_len), split * ch);
+  const int b_hi = min((q_len + BWD_TOK - 1) / BWD_TOK, (split + 1) * ch);
+  if (b_lo >= b_hi) {
+    if (split_stride == 0 && j_ok) {   // a single chunk writes dk itself: zeros here
+      float *dst = out + (int64_t)(k_base + j) * DI + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
 
   auto stage = [&](int b, int buf) {   // q rows and fp32(w * s_idx) of block b
     dma_q_block<RB>(q_idx, q_start + b * BWD_TOK, total_q, reinterpret_cast<char *>(qs[buf]), w, 4, lane);
@@ -325,12 +347,12 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
   f32x4 acc[NDT], cmp[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = cmp[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (b_lo < nqb) stage(b_lo, 0);
-  for (int b = b_lo; b < nqb; ++b) {
+  stage(b_lo, 0);
+  for (int b = b_lo; b < b_hi; ++b) {
     const int buf = (b - b_lo) & 1;
     wait_vmcnt<0>();
     __syncthreads();   // block b staged (q rows by DMA, weights by stores)
-    if (b + 1 < nqb) stage(b + 1, buf ^ 1);
+    if (b + 1 < b_hi) stage(b + 1, buf ^ 1);
     const int t0 = b * BWD_TOK;
     // G[t0 + 4g + i, j]: this lane's E'' column entries (0 past the segment)
     float gv[4];
@@ -384,19 +406,74 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
   }
   // lane (key r16, group g) holds dims 16dt + 4g + i of dK^T[:, key]
   if (j_ok) {
-    float *dst = dk + (int64_t)(k_base + j) * DI + 4 * g;
+    float *dst = out + split * split_stride + (int64_t)(k_base + j) * DI + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = acc[dt];
   }
 }
 
+// dk[key] = sum over the chunks that wrote a partial for the key's tile, in chunk order,
+// in fp64 (one thread per 4 dims of a key; keys that no token sees get 0).
+template <int DI>
+__global__ __launch_bounds__(256) void idx_bwd_dk_reduce_kernel(LayoutDev L, int total_k, int ch,
+                                                                const float *__restrict__ part,
+                                                                int64_t split_stride,
+                                                                float *__restrict__ dk) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)total_k * (DI / 4)) return;
+  const int key = (int)(e / (DI / 4)), d4 = (int)(e - (int64_t)key * (DI / 4));
+  const int seg = segment_of(L.cu_k, L.num_seqs, key);
+  const int k_base = __ldg(L.cu_k + seg);
+  const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
+  const int q_start = __ldg(L.cu_q + seg);
+  const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
+  const int off = seg_offset(L, seg, q_len, s_k);
+  const int j0 = ((key - k_base) / 64) * 64;
+  const int b_lo = first_block_seeing(j0, off, L.ratio, q_len);
+  const int nqb = (q_len + BWD_TOK - 1) / BWD_TOK;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  if (b_lo < nqb) {
+    const int s_hi = (nqb - 1) / ch;
+    for (int s = b_lo / ch; s <= s_hi; ++s) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(part + s * split_stride + (int64_t)key * DI + 4 * d4);
+      a0 += v[0];
+      a1 += v[1];
+      a2 += v[2];
+      a3 += v[3];
+    }
+  }
+  *reinterpret_cast<f32x4 *>(dk + (int64_t)key * DI + 4 * d4) =
+      f32x4{(float)a0, (float)a1, (float)a2, (float)a3};
+}
+
 // ---------------------------------------------------------------- launch
+// Chunks of token blocks per key tile: enough workgroups to fill the chip (about 1024),
+// at least 4 blocks per chunk.
+void indexer_bwd_dk_split(int num_seqs, int max_seqlen_q, int max_seqlen_k, int *ch, int *ns) {
+  const int nqb = (max_seqlen_q + BWD_TOK - 1) / BWD_TOK;
+  const int nkt = (max_seqlen_k + 63) / 64;
+  const long long tiles = (long long)num_seqs * nkt;
+  long long want = (1024 + tiles - 1) / tiles;
+  want = std::max(1LL, std::min(want, (long long)(nqb + 3) / 4));
+  const int c = (int)((nqb + want - 1) / want);
+  *ch = std::max(c, 1);
+  *ns = (nqb + *ch - 1) / *ch;
+}
+
+int64_t indexer_bwd_workspace_bytes(int num_seqs, int total_k, int max_seqlen_q, int max_seqlen_k, int Di) {
+  int ch, ns;
+  indexer_bwd_dk_split(num_seqs, max_seqlen_q, max_seqlen_k, &ch, &ns);
+  return ns > 1 ? (int64_t)ns * total_k * Di * (int64_t)sizeof(float) : 0;
+}
+
 template <int DI, int HI, int HPW>
 static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
                                const float *weights, float idx_scale, const float *grad, int64_t ldg,
-                               float *dq, float *dw, float *dk, hipStream_t st) {
+                               float *dq, float *dw, float *dk, float *ws, hipStream_t st) {
   const int nqb = (LL.max_seqlen_q + BWD_TOK - 1) / BWD_TOK;
   const int nkt = (LL.max_seqlen_k + 63) / 64;
+  int ch, ns;
+  indexer_bwd_dk_split(LL.num_seqs, LL.max_seqlen_q, LL.max_seqlen_k, &ch, &ns);
   if (LL.total_q > 0) {
     hipLaunchKernelGGL((idx_bwd_dq_kernel<DI, HI, HPW>), dim3((unsigned)(LL.num_seqs * nqb)), dim3(256), 0, st,
                        LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
@@ -404,9 +481,16 @@ static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((idx_bwd_dk_kernel<DI, HI>), dim3((unsigned)(LL.num_seqs * nkt)), dim3(256), 0, st,
-                     LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
-                     weights, idx_scale, grad, ldg, LL.max_seqlen_k, LL.total_q, nkt, dk);
+  const int64_t stride = ns > 1 ? (int64_t)LL.total_k * DI : 0;
+  float *out = ns > 1 ? ws : dk;
+  hipLaunchKernelGGL((idx_bwd_dk_kernel<DI, HI>), dim3((unsigned)((int64_t)LL.num_seqs * nkt * ns)), dim3(256),
+                     0, st, LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
+                     weights, idx_scale, grad, ldg, LL.total_q, nkt, ch, stride, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  const int64_t nthr = (int64_t)LL.total_k * (DI / 4);
+  hipLaunchKernelGGL(idx_bwd_dk_reduce_kernel<DI>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st, LL.dev,
+                     LL.total_k, ch, ws, stride, dk);
   return hipGetLastError();
 }
 
@@ -415,7 +499,7 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const vo
                                   float idx_scale, const float *scores, int64_t ld_scores,
                                   const int32_t *ids, int k_eff, const float *teacher,
                                   int64_t ld_teacher, float grad_scale, float *grad, int64_t ld_grad,
-                                  float *dq, float *dw, float *dk, hipStream_t st) {
+                                  float *dq, float *dw, float *dk, void *workspace, hipStream_t st) {
   if (LL.total_q > 0) {
     if (sparse) {
       const int64_t n = (int64_t)LL.total_q * LL.max_seqlen_k;
@@ -437,7 +521,8 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#define CSA_BWD_ARGS LL, q_idx, k_idx, weights, idx_scale, grad, ld_grad, dq, dw, dk, st
+#define CSA_BWD_ARGS LL, q_idx, k_idx, weights, idx_scale, grad, ld_grad, dq, dw, dk, \
+                     static_cast<float *>(workspace), st
   if (Di == 64) {
     switch (Hi) {
       case 4: return launch_bwd_t<64, 4, 1>(CSA_BWD_ARGS);

@@ -34,7 +34,9 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &L, bool sparse, const voi
                                   float idx_scale, const float *scores, int64_t ld_scores,
                                   const int32_t *ids, int k_eff, const float *teacher,
                                   int64_t ld_teacher, float grad_scale, float *grad, int64_t ld_grad,
-                                  float *dq, float *dw, float *dk, hipStream_t st);
+                                  float *dq, float *dw, float *dk, void *workspace, hipStream_t st);
+// device workspace of the indexer-loss backward (dk partials per token-block chunk; 0: none)
+int64_t indexer_bwd_workspace_bytes(int num_seqs, int total_k, int max_seqlen_q, int max_seqlen_k, int Di);
 
 // shape support tables (host side, used by validation before any launch)
 bool indexer_supported(bool bf16, int Hi, int Di);

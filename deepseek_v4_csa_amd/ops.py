@@ -36,7 +36,8 @@ class _CLayout(ctypes.Structure):
 
 
 EXPORTS = ("csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
-           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd", "csa_cp_plan")
+           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd", "csa_indexer_loss_bwd_workspace",
+           "csa_cp_plan")
 
 
 def lib_path() -> str:
@@ -69,7 +70,9 @@ def load():
                                            I32, F32, I32, P, I64, P, P, P]
     lib.csa_indexer_loss_bwd.restype = ctypes.c_int
     lib.csa_indexer_loss_bwd.argtypes = [LP, I32, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, P, I32,
-                                         P, I64, F32, I32, P, I64, P, P, P, P]
+                                         P, I64, F32, I32, P, I64, P, P, P, P, I64, P]
+    lib.csa_indexer_loss_bwd_workspace.restype = I64
+    lib.csa_indexer_loss_bwd_workspace.argtypes = [LP, I32, I32]
     lib.csa_cp_plan.restype = ctypes.c_int
     lib.csa_cp_plan.argtypes = [I32, P, I32, I32, I32, P, P, P, P, P, P]
     _lib = lib
@@ -205,9 +208,10 @@ def csa_indexer_teacher_kl(layout: Layout, sparse_loss: bool, scores, ids, cmass
 
 def csa_indexer_loss_bwd(layout: Layout, sparse_loss: bool, q_idx, k_idx, weights, idx_scale: float,
                          scores, ids, teacher, grad_loss: float = 1.0, per_token: bool = False,
-                         grad_scores=None, dq_idx=None, dweights=None, dk_idx=None):
+                         grad_scores=None, dq_idx=None, dweights=None, dk_idx=None, workspace=None):
     """Indexer-loss gradients (fp32) for q_idx, weights and k_idx; the teacher and the
-    selection (ids) of the forward are held fixed."""
+    selection (ids) of the forward are held fixed.  workspace: a uint8 device tensor of at
+    least csa_indexer_loss_bwd_workspace bytes (allocated here if None)."""
     T, Hi, Di = q_idx.shape
     dev = q_idx.device
     k_eff_ = ids.shape[1] if ids is not None else 0
@@ -216,13 +220,24 @@ def csa_indexer_loss_bwd(layout: Layout, sparse_loss: bool, q_idx, k_idx, weight
     dq_idx = torch.empty((T, Hi, Di), dtype=torch.float32, device=dev) if dq_idx is None else dq_idx
     dweights = torch.empty((T, Hi), dtype=torch.float32, device=dev) if dweights is None else dweights
     dk_idx = torch.empty(tuple(k_idx.shape), dtype=torch.float32, device=dev) if dk_idx is None else dk_idx
+    if workspace is None:
+        n = csa_indexer_loss_bwd_workspace(layout, Hi, Di)
+        workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
     _check(load().csa_indexer_loss_bwd(
         ctypes.byref(layout.c()), 1 if sparse_loss else 0, _ptr(q_idx), _ptr(k_idx), _ptr(weights),
         _dtype(q_idx), Hi, Di, float(idx_scale), _ptr(scores), scores.stride(0),
         _ptr(ids) if ids is not None else None, k_eff_, _ptr(teacher), teacher.stride(0),
         float(grad_loss), 1 if per_token else 0, _ptr(grad_scores), grad_scores.stride(0),
-        _ptr(dq_idx), _ptr(dweights), _ptr(dk_idx), _stream()))
+        _ptr(dq_idx), _ptr(dweights), _ptr(dk_idx), _ptr(workspace), workspace.numel(), _stream()))
     return dq_idx, dweights, dk_idx
+
+
+def csa_indexer_loss_bwd_workspace(layout: Layout, Hi: int, Di: int) -> int:
+    """Bytes of device workspace csa_indexer_loss_bwd needs (host-only query)."""
+    n = int(load().csa_indexer_loss_bwd_workspace(ctypes.byref(layout.c()), int(Hi), int(Di)))
+    if n < 0:
+        raise RuntimeError(f"libcsa: {load().csa_last_error().decode()}")
+    return n
 
 
 def csa_cp_plan(doc_lens, ratio: int, cp_size: int, cp_rank: int) -> dict:

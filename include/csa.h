@@ -215,6 +215,10 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss,
  *   grad_scores: workspace [T, ld_grad >= max_seqlen_k] fp32, overwritten with g;
  *   dq_idx [T, Hi, Di], dweights [T, Hi], dk_idx [T_k, Di]: fp32, overwritten (every
  *   element, including rows and keys that get no gradient).  Deterministic: no atomics.
+ *   workspace: device scratch of workspace_bytes >= csa_indexer_loss_bwd_workspace(L,
+ *   Hi, Di) bytes (may be NULL when that is 0), caller-owned, contents undefined after
+ *   the call; it holds per-chunk partial sums of dk_idx, which a last kernel adds in a
+ *   fixed order.  A smaller workspace is CSA_ERR_INVALID.
  * Supported: dt = CSA_BF16; Di = 64 with Hi in {4, 8, 16, 32}, or Di = 128 with Hi in
  * {4, 8, 16}; sparse k_eff <= 4096, dense max_seqlen_k <= 4096.
  */
@@ -225,7 +229,12 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss,
                                   int32_t k_eff, const float *teacher, int64_t ld_teacher,
                                   float grad_loss, int32_t per_token_loss, float *grad_scores,
                                   int64_t ld_grad, float *dq_idx, float *dweights, float *dk_idx,
-                                  void *stream);
+                                  void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace csa_indexer_loss_bwd needs for this layout and indexer
+ * shape (0: none); -1 for an invalid layout or an unsupported shape (message in
+ * csa_last_error).  Host-only: reads nothing on the device. */
+int64_t csa_indexer_loss_bwd_workspace(const csa_layout_t *L, int32_t Hi, int32_t Di);
 
 /*
  * csa_cp_plan -- host-only layout of one rank's share of context-parallel (CP) scoring.

@@ -12,7 +12,7 @@ HEADER = os.path.join(ROOT, "include", "csa.h")
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:csa_status_t|const char \*|int32_t)\s*(csa_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:csa_status_t|const char \*|int32_t|int64_t)\s*(csa_\w+)\s*\(", src, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) == {"csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
                           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd",
-                          "csa_cp_plan"}
+                          "csa_indexer_loss_bwd_workspace", "csa_cp_plan"}
     from deepseek_v4_csa_amd import ops
     assert set(ops.EXPORTS) == set(names)
     for n in names:
@@ -79,7 +79,7 @@ def test_argument_misuse_is_rejected(lib):
     assert "dense" in lib.csa_last_error().decode()
     bwd = lib.csa_indexer_loss_bwd
     args = [B(L), 1, FAKE, FAKE, FAKE, 1, 16, 64, 0.1, FAKE, 16, FAKE, 4, FAKE, 4, 1.0, 0, FAKE, 16,
-            FAKE, FAKE, FAKE, None]
+            FAKE, FAKE, FAKE, FAKE, 0, None]
     a = list(args); a[11] = None
     assert bwd(*a) == 1                                                            # sparse without ids
     a = list(args); a[14] = 3
@@ -92,6 +92,23 @@ def test_argument_misuse_is_rejected(lib):
     assert bwd(*a) == 2                                                            # fp32
     a = list(args); a[19] = None
     assert bwd(*a) == 1                                                            # null dq
+    # a long segment splits dk over token chunks: the workspace must hold the partials
+    Lb = _layout(ops, total_q=4096, max_seqlen_q=4096, total_k=1024, max_seqlen_k=1024)
+    need = lib.csa_indexer_loss_bwd_workspace(B(Lb), 16, 64)
+    assert need == 64 * 1024 * 64 * 4
+    a = list(args); a[0] = B(Lb); a[10] = a[18] = 1024; a[23] = need - 1
+    assert bwd(*a) == 1                                                            # workspace too small
+    assert "workspace" in lib.csa_last_error().decode()
+    a[22] = None; a[23] = need
+    assert bwd(*a) == 1                                                            # workspace NULL
+
+
+def test_backward_workspace_query(lib):
+    from deepseek_v4_csa_amd import ops
+    B = ctypes.byref
+    assert lib.csa_indexer_loss_bwd_workspace(B(_layout(ops)), 16, 64) == 0        # one chunk
+    assert lib.csa_indexer_loss_bwd_workspace(B(_layout(ops)), 16, 96) == -1       # no kernel
+    assert lib.csa_indexer_loss_bwd_workspace(B(_layout(ops, total_k=0)), 16, 64) == -1
 
 
 def test_k_eff(lib):
