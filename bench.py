@@ -1,13 +1,22 @@
 """Throughput of the CSA forward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bshd-b2-s4096]
+                    [--row path|backward|cp-share]
 
 One step = the four calls of the path (indexer scores, top-k, window+top-k sparse
 attention with sink and teacher masses, teacher + KL + loss) over one batch of seeded
 synthetic inputs already resident in HBM.  Prints one JSON line: query tokens/s over K
 timed steps, the roofline of the dominant kernel (HIP events on the launch stream,
-around every launch inside the timed region) and the CPU oracle timed on a bounded
-row sample of the same workload (cpu_baseline).
+around the attention launch inside the timed region) and the CPU oracle timed on a
+bounded row sample of the same workload (cpu_baseline).
+
+The steps after the path are measured the same way, one JSON line each:
+  --row backward   one step = csa_indexer_loss_bwd (score gradients, dq_idx/dweights,
+                   dk_idx) after one forward, on the same workload;
+  --row cp-share   one step = csa_indexer_score + csa_topk on one rank's share of
+                   context-parallel scoring (csa_cp_plan): the 65,536-token sequence at
+                   CP = 8, rank 0 (chunks 0 and 15, 8,192 rows, key prefixes cropped at
+                   the chunk ends).
 """
 from __future__ import annotations
 
@@ -34,6 +43,9 @@ def parse():
     ap.add_argument("--workload", default="bshd-b2-s4096")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row", default="path", choices=("path", "backward", "cp-share"))
+    ap.add_argument("--cp", type=int, default=8, help="cp-share: CP size")
+    ap.add_argument("--rank", type=int, default=0, help="cp-share: rank")
     return ap.parse_args()
 
 
@@ -120,16 +132,244 @@ def cpu_baseline(inp, seconds):
                       f"per row in NumPy float64, {el:.1f} s"}
 
 
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _oracle_problem(inp, rows=None):
+    """oracle.Problem over host copies of the inputs (only `rows` of the per-row tensors
+    when given, as a dict-backed row map)."""
+    import numpy as np
+    import torch
+    import oracle
+    wl = inp.wl
+    h = lambda x: x.detach().to("cpu", torch.float64).numpy()
+
+    class Rows:
+        def __init__(self, full):
+            idx = torch.tensor(sorted(rows), device=full.device)
+            self.pos = {r: i for i, r in enumerate(sorted(rows))}
+            self.v = h(full.index_select(0, idx))
+
+        def __getitem__(self, t):
+            return self.v[self.pos[int(t)]]
+
+    pr = (lambda x: h(x)) if rows is None else Rows
+    L = oracle.Layout(cu_q=inp.cu_q.cpu().numpy(), cu_k=inp.cu_k.cpu().numpy(), ratio=wl.ratio,
+                      off=inp.offsets.cpu().numpy())
+    return oracle.Problem(layout=L, q=pr(inp.q), kv=h(inp.kv), ckv=h(inp.ckv), q_idx=pr(inp.q_idx),
+                          k_idx=h(inp.k_idx), weights=pr(inp.weights), sink=h(inp.sink), topk=wl.topk,
+                          window=wl.window, scale=inp.scale, idx_scale=inp.idx_scale,
+                          sparse_loss=wl.sparse_loss)
+
+
+def _line(metric, value, args, ms, dtype, config, roof, cpu, extra):
+    d = {"metric": metric, "value": value, "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+         "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": config,
+         "roofline": roof, "cpu_baseline": cpu}
+    d.update(extra)
+    print(json.dumps(d))
+
+
+def _roof(kernel, flop, nbytes, sec, mfma_peak):
+    """The binding resource is the one with the larger ideal time."""
+    t_mfma = flop / (mfma_peak * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        r = {"kernel": kernel, "bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS,
+             "unit": "GB/s"}
+    else:
+        r = {"kernel": kernel, "bound": "mfma", "achieved": flop / sec / 1e12, "peak": mfma_peak,
+             "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = None
+    r["algorithmic"] = {"flop": flop, "bytes": nbytes}
+    return r
+
+
+def bench_backward(args):
+    """Indexer-loss backward (the step after the path) on the workload."""
+    import numpy as np
+    import torch
+    from deepseek_v4_csa_amd import inputs as I
+    from deepseek_v4_csa_amd import ops
+    wl = next(w for w in I.WORKLOADS if w.name == args.workload)
+    dev = torch.device("cuda:0")
+    inp = I.make_inputs(wl, device="cuda")
+    res = ops.forward(inp, want_teacher=True)
+    L = ops.layout_of_inputs(inp)
+    T = wl.total_q
+    g = torch.empty((T, wl.max_seqlen_k), dtype=torch.float32, device=dev)
+    dq = torch.empty(tuple(inp.q_idx.shape), dtype=torch.float32, device=dev)
+    dw = torch.empty(tuple(inp.weights.shape), dtype=torch.float32, device=dev)
+    dk = torch.empty(tuple(inp.k_idx.shape), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(ops.csa_indexer_loss_bwd_workspace(L, wl.Hi, wl.Di), 1),), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: ops.csa_indexer_loss_bwd(L, wl.sparse_loss, inp.q_idx, inp.k_idx, inp.weights,
+                                            inp.idx_scale, res["scores"], res["ids"], res["teacher"],
+                                            grad_scores=g, dq_idx=dq, dweights=dw, dk_idx=dk, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        call()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    nv, kt, _ = geometry(wl)
+    S = int(kt.sum()) if wl.sparse_loss else int(nv.sum())      # support pairs
+    P = int(nv.sum())
+    flop = 6 * wl.Hi * wl.Di * S          # d recomputed once, dq and dk contractions
+    nbytes = (2 * T * wl.Hi * wl.Di + 2 * wl.total_k * wl.Di + 4 * T * wl.Hi
+              + (12 * T * wl.k_eff if wl.sparse_loss else 8 * P)
+              + 4 * T * wl.Hi * wl.Di + 4 * T * wl.Hi + 4 * wl.total_k * wl.Di)
+    roof = _roof("csa_indexer_loss_bwd (score gradients, dq/dweights, dk, dk reduce)", flop, nbytes,
+                 call_ms * 1e-3, BF16_MFMA_PEAK_TFLOPS)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = I.uniform_rows(T, 4096, seed=13)
+        P_ = _oracle_problem(inp, rows)
+        Lo = P_.layout
+        t1 = time.perf_counter()
+        done = 0
+        for t in rows:
+            r = oracle.run_row(P_, int(t))
+            cols, tch, prd = oracle.loss_support(P_, r)
+            if cols.size:
+                gs = oracle.kl_grad_scores(tch, prd) / T
+                ge = r.geom
+                oracle.indexer_grads_row(P_.q_idx[t], P_.weights[t],
+                                         P_.k_idx[ge.k_base:int(Lo.cu_k[ge.seg + 1])], P_.idx_scale, cols, gs)
+            done += 1
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        e1 = time.perf_counter() - t1
+        cpu = {"value": done / e1, "unit": "query tokens/s", "cores": int(_threads()), "kind": "oracle",
+               "sample": f"{done} uniformly drawn rows of {T} ({wl.name}): each row's forward (for the "
+                         f"teacher) and its indexer gradients in NumPy float64, {e1:.1f} s"}
+    _line("query tokens/s through the indexer-loss backward (dq_idx, dweights, dk_idx)", T * args.steps / el,
+          args, el / args.steps * 1e3, "bf16", {**wl.describe(), "row": "indexer-loss backward",
+                                                 "support_pairs": S, "parallelism": "none (1 GPU)"},
+          roof, cpu, {"call_us": call_ms * 1e3})
+
+
+def bench_cp_share(args):
+    """One rank's share of CP scoring (indexer + top-k) of the 65,536-token sequence."""
+    import numpy as np
+    import torch
+    from deepseek_v4_csa_amd import inputs as I
+    from deepseek_v4_csa_amd import ops
+    base = I.WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    plan = ops.csa_cp_plan(list(base.seg_lens), base.ratio, args.cp, args.rank)
+    nseg = len(plan["off"])
+    seg_q = [plan["cu_q"][s + 1] - plan["cu_q"][s] for s in range(nseg)]
+    seg_k = [plan["cu_k"][s + 1] - plan["cu_k"][s] for s in range(nseg)]
+    # the rank's own rows and the sequence's keys, drawn like the workload's indexer inputs
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(I.SEED_BASE + 300 + args.rank)
+    sd = 1.0 / np.sqrt(base.D)
+    Ts = sum(seg_q)
+    q_idx = (torch.randn((Ts, base.Hi, base.Di), generator=gen, device=dev) * sd).to(torch.bfloat16)
+    weights = torch.rand((Ts, base.Hi), generator=gen, device=dev)
+    k_all = (torch.randn((base.total_k, base.Di), generator=gen, device=dev) * sd).to(torch.bfloat16)
+    kidx = torch.cat([torch.arange(plan["k_src"][s], plan["k_src"][s] + seg_k[s], device=dev)
+                      for s in range(nseg)])
+    k_idx = k_all.index_select(0, kidx).contiguous()
+    L = ops.Layout.from_lengths(seg_q, seg_k, base.ratio, offsets=plan["off"])
+    k_eff = ops.k_eff(L, base.topk)
+    scores = torch.empty((Ts, L.max_seqlen_k), dtype=torch.float32, device=dev)
+    ids = torch.empty((Ts, k_eff), dtype=torch.int32, device=dev)
+    idx_scale = 1.0 / np.sqrt(base.Di)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        ops.csa_indexer_score(L, q_idx, k_idx, weights, idx_scale, scores=scores)
+        if ev: ev[1].record()
+        ops.csa_topk(L, scores, base.topk, ids=ids)
+        if ev: ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    idx_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    topk_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    # causal pairs of the share: row at absolute position i sees floor(i / ratio) keys
+    P = 0
+    for s in range(nseg):
+        i = np.arange(plan["off"][s] + 1, plan["off"][s] + seg_q[s] + 1)
+        P += int(np.minimum(i // base.ratio, seg_k[s]).sum())
+    flop = 2 * base.Hi * base.Di * P
+    roof = _roof("indexer_score", flop, 2 * Ts * base.Hi * base.Di + 2 * sum(seg_k) * base.Di + 4 * P,
+                 idx_ms * 1e-3, BF16_MFMA_PEAK_TFLOPS)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        qh = q_idx.to("cpu", torch.float64).numpy()
+        wh = weights.cpu().numpy()
+        kh = k_idx.to("cpu", torch.float64).numpy()
+        cu_k = plan["cu_k"]
+        rng = np.random.default_rng(17)
+        order = rng.permutation(Ts)
+        t1 = time.perf_counter()
+        done = 0
+        starts = np.asarray(plan["cu_q"])
+        for t in order:
+            s = int(np.searchsorted(starts, t, side="right") - 1)
+            nvv = min((plan["off"][s] + (t - starts[s]) + 1) // base.ratio, seg_k[s])
+            sc = oracle.indexer_scores_row(qh[t], wh[t], kh[cu_k[s]:cu_k[s + 1]], idx_scale, nvv)
+            oracle.topk_row(sc, nvv, k_eff, cu_k[s])
+            done += 1
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        e1 = time.perf_counter() - t1
+        cpu = {"value": done / e1, "unit": "query tokens/s", "cores": int(_threads()), "kind": "oracle",
+               "sample": f"{done} uniformly drawn rows of the {Ts}-row share: indexer scores and top-k "
+                         f"per row in NumPy float64, {e1:.1f} s"}
+    _line("query tokens/s of one rank's CP scoring share (indexer + top-k)", Ts * args.steps / el, args,
+          el / args.steps * 1e3, "bf16",
+          {"workload": f"{base.name}-cp{args.cp}-rank{args.rank}", "sequence": base.seg_lens[0],
+           "cp_size": args.cp, "rank": args.rank, "share_rows": Ts, "segments": seg_q,
+           "key_prefixes": seg_k, "offsets": plan["off"], "indexer_heads": base.Hi,
+           "indexer_dim": base.Di, "topk": base.topk, "compress_ratio": base.ratio,
+           "parallelism": "one rank's share on 1 GPU"},
+          roof, cpu, {"kernels": {"indexer_score": {"us": idx_ms * 1e3,
+                                                    "tflops": flop / (idx_ms * 1e-3) / 1e12},
+                                  "topk": {"us": topk_ms * 1e3,
+                                           "gbs": (4 * P + 4 * Ts * k_eff) / (topk_ms * 1e-3) / 1e9}}})
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
-    from deepseek_v4_csa_amd import inputs as I
     from deepseek_v4_csa_amd import ops
-
     ops.load()
+    torch.cuda.set_device(0)
+    if args.row == "backward":
+        return bench_backward(args)
+    if args.row == "cp-share":
+        return bench_cp_share(args)
+    from deepseek_v4_csa_amd import inputs as I
+
     wl = next(w for w in I.WORKLOADS if w.name == args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
