@@ -9,9 +9,10 @@
 //  1. score gradients, one wave per row: with the forward's predictor p = softmax of the
 //     scores over the support and the given teacher t,
 //        g_j = c (p_j R - r_j),  r_j = t_j p_j / (p_j + 1e-10),  R = sum_j r_j,
-//     written densely into G[t, 0..max_seqlen_k) (0 off the support; the sparse mode
-//     zero-fills G first and then scatters).  Normalisers and g in fp64, like the
-//     forward's KL.
+//     written densely into G[t, 0..W) (0 off the support), W = the 64-key tiles that the
+//     row's 16-token block reaches -- every column the next two kernels read (the sparse
+//     mode writes the zeros, waits for them, then scatters).  Normalisers and g in fp64,
+//     like the forward's KL.
 //  2. dq / dweights, one workgroup per 16-token block: for every 64-key tile below the
 //     block's causal limit and every indexer head h, D^T = K Q_h^T (keys x tokens) is
 //     recomputed on MFMA, E = G o [D > 0], and U_h^T += K^T E on MFMA; at the end
@@ -47,15 +48,6 @@ __device__ __forceinline__ void split_bf16x4(const float (&x)[4], uint2 &hi, uin
 }
 
 // ---------------------------------------------------------------- 1. score gradients
-__global__ __launch_bounds__(256) void zero_rows_kernel(float *__restrict__ g, int64_t ld, int rows,
-                                                        int cols) {
-  const int64_t n = (int64_t)rows * cols;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-    const int64_t r = e / cols, c = e - r * cols;
-    g[r * ld + c] = 0.f;
-  }
-}
-
 // SPL support slots per lane: sparse -> k_eff slots (slot j <-> ids[t, j]); dense ->
 // columns j < max_seqlen_k
 template <int SPL>
@@ -70,6 +62,16 @@ __global__ __launch_bounds__(256) void grad_scores_kernel(
   const RowGeo geo = row_geo(L, t);
   float *gr = grad + (int64_t)t * ldg;
   const int nslot = sparse ? k_eff : max_sk;
+  // columns read later: the 64-key tiles below the causal limit of the row's 16-token
+  // block (its last token sees the most keys)
+  const int last = min(((t - geo.q_start) / BWD_TOK) * BWD_TOK + BWD_TOK, geo.q_len) - 1;
+  const int off = seg_offset(L, geo.seg, geo.q_len, geo.s_k);
+  const int wcols = min(max_sk, (n_valid_of(last, off, L.ratio, geo.s_k) + 63) & ~63);
+  auto zero_cols = [&]() {   // G[t, 0..wcols) = 0: 16-byte stores where the row allows
+    const int wv = (reinterpret_cast<uintptr_t>(gr) & 15) == 0 ? (wcols & ~3) : 0;
+    for (int j = 4 * lane; j < wv; j += 256) *reinterpret_cast<f32x4 *>(gr + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = wv + lane; j < wcols; j += 64) gr[j] = 0.f;
+  };
   int col[SPL];
   float s[SPL], te[SPL];
   float mx = -__builtin_inff();
@@ -91,8 +93,7 @@ __global__ __launch_bounds__(256) void grad_scores_kernel(
     mx = fmaxf(mx, s[v]);
   }
   if (loss_row_empty(L, geo, t)) {
-    if (!sparse)
-      for (int j = lane; j < max_sk; j += 64) gr[j] = 0.f;
+    zero_cols();
     return;
   }
   mx = wave_max_dpp(mx);
@@ -112,16 +113,24 @@ __global__ __launch_bounds__(256) void grad_scores_kernel(
     rs += (double)te[v] * pv / (pv + (double)BWD_EPS);
   }
   rs = wave_sum_f64_dpp(rs);
+  float gval[SPL];
 #pragma unroll
   for (int v = 0; v < SPL; ++v) {
-    const int j = v * 64 + lane;
     const double pv = (double)e[v] * inv_es;
     const double rv = (double)te[v] * pv / (pv + (double)BWD_EPS);
-    const float g = (float)((double)gscale * (pv * rs - rv));
-    if (sparse) {
-      if (col[v] >= 0) gr[col[v]] = g;
-    } else if (j < nslot) {
-      gr[j] = col[v] >= 0 ? g : 0.f;
+    gval[v] = (float)((double)gscale * (pv * rs - rv));
+  }
+  if (sparse) {
+    zero_cols();
+    wait_vmcnt<0>();   // the zeros have landed before any lane scatters over them
+#pragma unroll
+    for (int v = 0; v < SPL; ++v)
+      if (col[v] >= 0) gr[col[v]] = gval[v];
+  } else {
+#pragma unroll
+    for (int v = 0; v < SPL; ++v) {
+      const int j = v * 64 + lane;
+      if (j < nslot && j < wcols) gr[j] = col[v] >= 0 ? gval[v] : 0.f;
     }
   }
 }
@@ -203,22 +212,33 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) u[k][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (nlive > 0) dma_k(0, 0);
+    // G[t, j0 + 16m + 4g + i]: this lane's E^T entries of tile kt (0 past the row or
+    // segment), loaded one tile ahead
+    float gcur[4][4], gnext[4][4];
+    auto load_g = [&](int kt, float (&dst)[4][4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = kt * 64 + 16 * m + 4 * g + i;
+          dst[m][i] = (t_ok && j < max_sk) ? grad[(int64_t)(q_start + t) * ldg + j] : 0.f;
+        }
+    };
+    if (nlive > 0) {
+      dma_k(0, 0);
+      load_g(0, gcur);
+    }
     for (int kt = 0; kt < nlive; ++kt) {
       wait_vmcnt<0>();
       __syncthreads();   // tile kt (and, first time, the q block) visible to every wave
-      if (kt + 1 < nlive) dma_k(kt + 1, (kt + 1) & 1);
+      if (kt + 1 < nlive) {
+        dma_k(kt + 1, (kt + 1) & 1);
+        load_g(kt + 1, gnext);
+      }
       const char *kb = kt_lds[kt & 1];
-      const int j0 = kt * 64;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        // G[t, j0 + 16m + 4g + i]: this lane's E^T entries (0 past the row or segment)
-        float gv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 16 * m + 4 * g + i;
-          gv[i] = (t_ok && j < max_sk) ? grad[(int64_t)(q_start + t) * ldg + j] : 0.f;
-        }
+        const float *gv = gcur[m];
         // K row operand (rows 16m + r16) for D^T = K Q_h^T
         u32x4 ka[NCD];
         const int R = 16 * m + r16;
@@ -256,6 +276,10 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
           }
         }
       }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gcur[m][i] = gnext[m][i];
       __syncthreads();   // every wave is done with tile kt before it is overwritten
     }
     // outputs: lane (token r16, group g) holds dims 16dt + 4g + i of U_h^T
@@ -334,12 +358,32 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
     return;
   }
 
-  auto stage = [&](int b, int buf) {   // q rows and fp32(w * s_idx) of block b
-    dma_q_block<RB>(q_idx, q_start + b * BWD_TOK, total_q, reinterpret_cast<char *>(qs[buf]), w, 4, lane);
-    for (int e = tid; e < HI * BWD_TOK; e += 256) {
-      const int tt = e / HI, h = e - tt * HI;
+  // per block b: q rows by DMA into qs[buf]; fp32(w * s_idx) through registers into
+  // wsl[buf] (loaded one block ahead, stored after the block's compute); this lane's
+  // G[t0 + 4g + i, j] (0 past the segment), loaded one block ahead
+  constexpr int WPT = (HI * BWD_TOK + 255) / 256;
+  float wreg[WPT];
+  auto load_w = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int e = tid + 256 * k, tt = e / HI, h = e - tt * HI;
       const int t = b * BWD_TOK + tt;
-      wsl[buf][h * BWD_TOK + tt] = t < q_len ? weights[(int64_t)(q_start + t) * HI + h] * idx_scale : 0.f;
+      wreg[k] = (e < HI * BWD_TOK && t < q_len) ? weights[(int64_t)(q_start + t) * HI + h] : 0.f;
+    }
+  };
+  auto store_w = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int e = tid + 256 * k, tt = e / HI, h = e - tt * HI;
+      if (e < HI * BWD_TOK) wsl[buf][h * BWD_TOK + tt] = wreg[k] * idx_scale;
+    }
+  };
+  float gcur[4], gnext[4];
+  auto load_g = [&](int b, float (&dst)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = b * BWD_TOK + 4 * g + i;
+      dst[i] = (t < q_len && j_ok) ? grad[(int64_t)(q_start + t) * ldg + j] : 0.f;
     }
   };
   // a key may collect terms from every row of its segment: each token block's partial
@@ -347,20 +391,22 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
   f32x4 acc[NDT], cmp[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = cmp[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stage(b_lo, 0);
+  dma_q_block<RB>(q_idx, q_start + b_lo * BWD_TOK, total_q, reinterpret_cast<char *>(qs[0]), w, 4, lane);
+  load_w(b_lo);
+  load_g(b_lo, gcur);
+  store_w(0);
   for (int b = b_lo; b < b_hi; ++b) {
     const int buf = (b - b_lo) & 1;
+    const bool more = b + 1 < b_hi;
     wait_vmcnt<0>();
     __syncthreads();   // block b staged (q rows by DMA, weights by stores)
-    if (b + 1 < b_hi) stage(b + 1, buf ^ 1);
-    const int t0 = b * BWD_TOK;
-    // G[t0 + 4g + i, j]: this lane's E'' column entries (0 past the segment)
-    float gv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * g + i;
-      gv[i] = (t < q_len && j_ok) ? grad[(int64_t)(q_start + t) * ldg + j] : 0.f;
+    if (more) {
+      dma_q_block<RB>(q_idx, q_start + (b + 1) * BWD_TOK, total_q, reinterpret_cast<char *>(qs[buf ^ 1]), w, 4,
+                      lane);
+      load_w(b + 1);
+      load_g(b + 1, gnext);
     }
+    const float *gv = gcur;
     const char *qb = reinterpret_cast<const char *>(qs[buf]);
     const char *qrow = qb + r16 * RB;
     const float *wsb = wsl[buf];
@@ -401,6 +447,11 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
       const f32x4 tot = acc[dt] + y;
       cmp[dt] = (tot - acc[dt]) - y;
       acc[dt] = tot;
+    }
+    if (more) {
+      store_w(buf ^ 1);   // its last readers (block b - 1) passed the barrier above
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gcur[i] = gnext[i];
     }
     __syncthreads();   // every wave is done with buffer buf before it is restaged
   }
@@ -501,12 +552,6 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const vo
                                   int64_t ld_teacher, float grad_scale, float *grad, int64_t ld_grad,
                                   float *dq, float *dw, float *dk, void *workspace, hipStream_t st) {
   if (LL.total_q > 0) {
-    if (sparse) {
-      const int64_t n = (int64_t)LL.total_q * LL.max_seqlen_k;
-      const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
-      hipLaunchKernelGGL(zero_rows_kernel, dim3(blocks), dim3(256), 0, st, grad, ld_grad, LL.total_q,
-                         LL.max_seqlen_k);
-    }
     const int nslot = sparse ? k_eff : LL.max_seqlen_k;
     const dim3 grid((unsigned)((LL.total_q + 3) / 4));
 #define CSA_GS_CASE(S)                                                                              \
