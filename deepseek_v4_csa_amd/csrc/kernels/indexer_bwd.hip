@@ -9,7 +9,7 @@
 //  1. score gradients, one wave per row: with the forward's predictor p = softmax of the
 //     scores over the support and the given teacher t,
 //        g_j = c (p_j R - r_j),  r_j = t_j p_j / (p_j + 1e-10),  R = sum_j r_j,
-//     written densely into G[t, 0..W) (0 off the support), W = the 64-key tiles that the
+//     written densely into G[t, 0..W) (0 off the support), W = the key tiles that the
 //     row's 16-token block reaches -- every column the next two kernels read (the sparse
 //     mode writes the zeros, waits for them, then scatters).  Normalisers and g in fp64,
 //     like the forward's KL.
@@ -17,11 +17,11 @@
 //     block's causal limit and every indexer head h, D^T = K Q_h^T (keys x tokens) is
 //     recomputed on MFMA, E = G o [D > 0], and U_h^T += K^T E on MFMA; at the end
 //     dq = ws * U and dweights = s_idx * sum_j G max(D, 0).
-//  3. dk, one workgroup per (64-key tile of a segment, chunk of 16-token blocks) (wave =
-//     16 keys): for every block of the chunk with a token that sees the tile,
+//  3. dk, one workgroup per (128-key tile of a segment, chunk of 16-token blocks) (wave =
+//     2 x 16 keys): for every block of the chunk with a token that sees the tile,
 //     D = Q_h K^T, E'' = G * ws o [D > 0], and dK^T += Q_h^T E'' on MFMA, summed over
 //     heads and blocks in a fixed order.  With more than one chunk per tile each chunk
-//     writes a partial to the caller's workspace and a fourth kernel adds the partials
+//     writes its partial to the caller's workspace and a fourth kernel adds the partials
 //     of every key in chunk order (in fp64).
 //
 // The gradient factors E are fp32; they enter the bf16 MFMAs as a hi/lo pair
@@ -38,6 +38,8 @@ namespace csa {
 
 constexpr float BWD_EPS = 1e-10f;   // the KL's epsilon
 constexpr int BWD_TOK = 16;         // tokens per block
+constexpr int DK_TILE = 128;        // keys per dk workgroup (4 waves x 32)
+static_assert(DK_TILE % 64 == 0, "G is zeroed in DK_TILE steps, which must cover the 64-key dq tiles");
 
 // bf16 hi/lo split of four fp32 values, as two 16x16x16 MFMA operands
 __device__ __forceinline__ void split_bf16x4(const float (&x)[4], uint2 &hi, uint2 &lo) {
@@ -62,11 +64,13 @@ __global__ __launch_bounds__(256) void grad_scores_kernel(
   const RowGeo geo = row_geo(L, t);
   float *gr = grad + (int64_t)t * ldg;
   const int nslot = sparse ? k_eff : max_sk;
-  // columns read later: the 64-key tiles below the causal limit of the row's 16-token
-  // block (its last token sees the most keys)
+  // columns read later: the key tiles (64 keys in the dq kernel, DK_TILE in the dk
+  // kernel) below the causal limit of the row's 16-token block (its last token sees the
+  // most keys); every one of them must hold g or 0
   const int last = min(((t - geo.q_start) / BWD_TOK) * BWD_TOK + BWD_TOK, geo.q_len) - 1;
   const int off = seg_offset(L, geo.seg, geo.q_len, geo.s_k);
-  const int wcols = min(max_sk, (n_valid_of(last, off, L.ratio, geo.s_k) + 63) & ~63);
+  const int nvl = n_valid_of(last, off, L.ratio, geo.s_k);
+  const int wcols = min(max_sk, (nvl + DK_TILE - 1) / DK_TILE * DK_TILE);
   auto zero_cols = [&]() {   // G[t, 0..wcols) = 0: 16-byte stores where the row allows
     const int wv = (reinterpret_cast<uintptr_t>(gr) & 15) == 0 ? (wcols & ~3) : 0;
     for (int j = 4 * lane; j < wv; j += 256) *reinterpret_cast<f32x4 *>(gr + j) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -136,20 +140,37 @@ __global__ __launch_bounds__(256) void grad_scores_kernel(
 }
 
 // ---------------------------------------------------------------- shared LDS staging
-// q_idx rows t0 .. t0+15 (RB bytes each) -> LDS, 16-byte chunk q of row r at slot
-// r*CPR + (q ^ r) (one instruction moves 1 KiB of one row; rows past the end of the
-// buffer read as zeros).  Waves w = first, first + step, ... of the workgroup share it.
+// Bytes [col0, col0 + PB) of the rows row0 .. row0+15 of a tensor with RB-byte rows ->
+// LDS (PB bytes per row), 16-byte chunk q of row r at slot r*(PB/16) + (q ^ r) (rows past
+// the end of the buffer read as zeros).  One instruction moves 1 KiB: a part of one row
+// (PB >= 1 KiB) or whole rows (PB < 1 KiB).  Waves w, w + nw, ... of the workgroup share it.
+template <int RB, int PB>
+__device__ __forceinline__ void dma_rows(const uint16_t *base, int row0, int total_rows, int col0, char *dst,
+                                         int w, int nw, int lane) {
+  constexpr int CPP = PB / 16;
+  static_assert(CPP >= BWD_TOK && (PB % 512) == 0, "the XOR swizzle needs 16-chunk rows");
+  const int rows_left = min(BWD_TOK, total_rows - row0);
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(base + (int64_t)row0 * (RB / 2), (uint32_t)(max(rows_left, 0) * RB));
+  if constexpr (PB >= 1024) {
+    constexpr int IPR = PB / 1024;
+    for (int m = w; m < BWD_TOK * IPR; m += nw) {
+      const int r = m / IPR, q0 = (m - r * IPR) * 64;
+      dma16(rq, dst + (size_t)(r * CPP + q0) * 16, (uint32_t)(r * RB + col0 + (((q0 + lane) ^ r) << 4)));
+    }
+  } else {
+    constexpr int RPI = 1024 / PB;
+    for (int m = w; m < BWD_TOK / RPI; m += nw) {
+      const int r = m * RPI + lane / CPP, c = lane % CPP;
+      dma16(rq, dst + (size_t)m * 1024, (uint32_t)(r * RB + col0 + ((c ^ r) << 4)));
+    }
+  }
+}
+
 template <int RB>
 __device__ __forceinline__ void dma_q_block(const uint16_t *q_idx, int row0, int total_q, char *dst,
                                             int w, int nw, int lane) {
-  constexpr int CPR = RB / 16, PPR = RB / 1024;
-  const int rows_left = min(BWD_TOK, total_q - row0);
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc(q_idx + (int64_t)row0 * (RB / 2), (uint32_t)(max(rows_left, 0) * RB));
-  for (int m = w; m < BWD_TOK * PPR; m += nw) {
-    const int r = m / PPR, q0 = (m - r * PPR) * 64;
-    dma16(rq, dst + (size_t)(r * CPR + q0) * 16, (uint32_t)(r * RB + (((q0 + lane) ^ r) << 4)));
-  }
+  dma_rows<RB, RB>(q_idx, row0, total_q, 0, dst, w, nw, lane);
 }
 
 // ---------------------------------------------------------------- 2. dq / dweights
@@ -312,17 +333,21 @@ __device__ __forceinline__ int first_block_seeing(int j0, int off, int ratio, in
   return tmin <= 0 ? 0 : (int)(tmin / BWD_TOK);
 }
 
-// grid: num_seqs x nkt x nsplit (segment fastest); the workgroup of split s covers the
-// blocks [s*ch, (s+1)*ch) that see its tile and writes its sum to out + s*split_stride
-// (split_stride 0 with one split: out is dk itself).
+// grid: num_seqs x nkt x nsplit (segment fastest); a workgroup owns a DK_TILE-key tile
+// (wave = two 16-key sub-tiles, so every LDS operand read feeds both) and the blocks
+// [s*ch, (s+1)*ch) of split s that see it, and writes its sum to out + s*split_stride
+// (split_stride 0 with one split: out is dk itself).  Each block is taken in NG steps of
+// HG heads, so only 16 rows x HG heads of q (16 KiB) sit in each LDS buffer.
 template <int DI, int HI>
-__global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DI == 64 ? 4 : 2))) void idx_bwd_dk_kernel(
     LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const float *__restrict__ weights, float idx_scale, const float *__restrict__ grad, int64_t ldg,
     int total_q, int nkt, int ch, int64_t split_stride, float *__restrict__ out) {
-  constexpr int RB = HI * DI * 2, CPR = RB / 16;
+  constexpr int RB = HI * DI * 2;
+  constexpr int HG = HI < 512 / DI ? HI : 512 / DI;   // heads per step
+  constexpr int NG = HI / HG, PB = HG * DI * 2;       // steps per block, bytes per staged row
   constexpr int NCD = DI / 32, NDT = DI / 16;
-  __shared__ __attribute__((aligned(16))) u32x4 qs[2][BWD_TOK * CPR];
+  __shared__ __attribute__((aligned(16))) u32x4 qs[2][BWD_TOK * PB / 16];
   __shared__ __attribute__((aligned(16))) float wsl[2][HI * BWD_TOK];   // [h][token]
 
   const int seg = blockIdx.x % L.num_seqs;
@@ -330,37 +355,51 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
   const int kt = rest % nkt, split = rest / nkt;
   const int k_base = __ldg(L.cu_k + seg);
   const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
-  const int j0 = kt * 64;
+  const int j0 = kt * DK_TILE;
   if (j0 >= s_k) return;
   const int q_start = __ldg(L.cu_q + seg);
   const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
   const int off = seg_offset(L, seg, q_len, s_k);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = j0 + 16 * w + r16;     // this lane's key (B operand / C column)
-  const bool j_ok = j < s_k;
-  // key operand of D = Q_h K^T: key row j, piece 4c+g (kept for every token block)
-  u32x4 kb[NCD];
-  {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(k_idx + (int64_t)(k_base + min(j, s_k - 1)) * DI) + g;
+  int jj[2];
+  bool jok[2];
+  u32x4 kb[2][NCD];   // key operand of D = Q_h K^T: key row jj[u], piece 4c+g
 #pragma unroll
-    for (int c = 0; c < NCD; ++c) kb[c] = p[4 * c];
+  for (int u = 0; u < 2; ++u) {
+    jj[u] = j0 + 32 * w + 16 * u + r16;
+    jok[u] = jj[u] < s_k;
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(k_idx + (int64_t)(k_base + min(jj[u], s_k - 1)) * DI) + g;
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) kb[u][c] = p[4 * c];
   }
   // this workgroup's blocks: those of its chunk from the first block that sees key j0
   const int b_lo = max(first_block_seeing(j0, off, L.ratio, q_len), split * ch);
   const int b_hi = min((q_len + BWD_TOK - 1) / BWD_TOK, (split + 1) * ch);
-  if (b_lo >= b_hi) {
-    if (split_stride == 0 && j_ok) {   // a single chunk writes dk itself: zeros here
-      float *dst = out + (int64_t)(k_base + j) * DI + 4 * g;
+  f32x4 acc[2][NDT];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto store_out = [&]() __attribute__((always_inline)) {
+    // lane (key r16 of sub-tile u, group g) holds dims 16dt + 4g + i of dK^T[:, key]
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (jok[u]) {
+        float *dst = out + split * split_stride + (int64_t)(k_base + jj[u]) * DI + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = acc[u][dt];
+      }
+  };
+  if (b_lo >= b_hi) {
+    if (split_stride == 0) store_out();   // a single chunk writes dk itself: zeros here
     return;
   }
 
-  // per block b: q rows by DMA into qs[buf]; fp32(w * s_idx) through registers into
-  // wsl[buf] (loaded one block ahead, stored after the block's compute); this lane's
-  // G[t0 + 4g + i, j] (0 past the segment), loaded one block ahead
+  // per block b: fp32(w * s_idx) through registers into wsl[(b - b_lo) & 1] (loaded at
+  // the block before's first step, stored after its last), this lane's G[t0 + 4g + i, jj]
+  // (0 past the segment) likewise one block ahead; per step: the step's q rows by DMA
+  // into qs[step & 1], issued one step ahead
   constexpr int WPT = (HI * BWD_TOK + 255) / 256;
   float wreg[WPT];
   auto load_w = [&](int b) __attribute__((always_inline)) {
@@ -378,89 +417,86 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_kernel(
       if (e < HI * BWD_TOK) wsl[buf][h * BWD_TOK + tt] = wreg[k] * idx_scale;
     }
   };
-  float gcur[4], gnext[4];
-  auto load_g = [&](int b, float (&dst)[4]) __attribute__((always_inline)) {
+  float gcur[2][4], gnext[2][4];
+  auto load_g = [&](int b, float (&dst)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = b * BWD_TOK + 4 * g + i;
-      dst[i] = (t < q_len && j_ok) ? grad[(int64_t)(q_start + t) * ldg + j] : 0.f;
-    }
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = b * BWD_TOK + 4 * g + i;
+        dst[u][i] = (t < q_len && jok[u]) ? grad[(int64_t)(q_start + t) * ldg + jj[u]] : 0.f;
+      }
   };
-  // a key may collect terms from every row of its segment: each token block's partial
-  // sum (MFMA, fp32) is added to the total with Kahan compensation
-  f32x4 acc[NDT], cmp[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[dt] = cmp[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  dma_q_block<RB>(q_idx, q_start + b_lo * BWD_TOK, total_q, reinterpret_cast<char *>(qs[0]), w, 4, lane);
+  auto stage_q = [&](int st, int buf) __attribute__((always_inline)) {
+    const int b = b_lo + st / NG, hg = st - (st / NG) * NG;
+    dma_rows<RB, PB>(q_idx, q_start + b * BWD_TOK, total_q, hg * PB, reinterpret_cast<char *>(qs[buf]), w, 4,
+                     lane);
+  };
+  stage_q(0, 0);
   load_w(b_lo);
   load_g(b_lo, gcur);
   store_w(0);
-  for (int b = b_lo; b < b_hi; ++b) {
-    const int buf = (b - b_lo) & 1;
+  const int nsteps = (b_hi - b_lo) * NG;
+  const int rr = 4 * g + (r16 >> 2);   // row this lane addresses in the transposing read
+  for (int st = 0; st < nsteps; ++st) {
+    const int bi = st / NG, hg = st - bi * NG;
+    const int b = b_lo + bi;
     const bool more = b + 1 < b_hi;
     wait_vmcnt<0>();
-    __syncthreads();   // block b staged (q rows by DMA, weights by stores)
-    if (more) {
-      dma_q_block<RB>(q_idx, q_start + (b + 1) * BWD_TOK, total_q, reinterpret_cast<char *>(qs[buf ^ 1]), w, 4,
-                      lane);
+    __syncthreads();   // step st staged (q rows by DMA; at a block's first step its weights)
+    if (st + 1 < nsteps) stage_q(st + 1, (st + 1) & 1);
+    if (hg == 0 && more) {
       load_w(b + 1);
       load_g(b + 1, gnext);
     }
-    const float *gv = gcur;
-    const char *qb = reinterpret_cast<const char *>(qs[buf]);
-    const char *qrow = qb + r16 * RB;
-    const float *wsb = wsl[buf];
-    f32x4 part[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) part[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int h = 0; h < HI; ++h) {
-      // D = Q_h K^T: A = Q_h rows (token r16, piece 4c+g), B = key operand
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    const char *qb = reinterpret_cast<const char *>(qs[st & 1]);
+    const char *qrow = qb + r16 * PB;
+    const float *wsb = wsl[bi & 1] + hg * HG * BWD_TOK;
+#pragma unroll 2
+    for (int hh = 0; hh < HG; ++hh) {
+      // D = Q_h K^T per sub-tile: A = Q_h rows (token r16, piece 4c+g), B = key operand
+      f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int c = 0; c < NCD; ++c) {
-        const int q = h * (DI / 8) + 4 * c + g;
+        const int q = hh * (DI / 8) + 4 * c + g;
         const u32x4 qa = *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
-        d = mfma16x16x32(qa, kb[c], d);
+        d[0] = mfma16x16x32(qa, kb[0][c], d[0]);
+        d[1] = mfma16x16x32(qa, kb[1][c], d[1]);
       }
-      // lane (key r16, group g) holds D[token 4g + i][key]
-      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsb + h * BWD_TOK + 4 * g);
-      float e[4];
+      // lane (key r16, group g) holds D[token 4g + i][key] of each sub-tile
+      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsb + hh * BWD_TOK + 4 * g);
+      uint2 ehi[2], elo[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = d[i] > 0.f ? gv[i] * wv[i] : 0.f;
-      uint2 ehi, elo;
-      split_bf16x4(e, ehi, elo);
+      for (int u = 0; u < 2; ++u) {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = d[u][i] > 0.f ? gcur[u][i] * wv[i] : 0.f;
+        split_bf16x4(e, ehi[u], elo[u]);
+      }
       // Q_h^T operand (dims 16dt + r16 x tokens 4g .. +3) by the transposing read:
       // lane supplies row 4g + r16/4, dims 16dt + 4(r16%4) .. +3 of head h
-      const int rr = 4 * g + (r16 >> 2);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const int col = h * DI + 16 * dt + 4 * (r16 & 3);    // bf16 column in the row
+        const int col = hh * DI + 16 * dt + 4 * (r16 & 3);   // bf16 column in the staged row
         const int q = col >> 3;                               // 16-byte chunk
-        const uint2 qt = lds_read_tr16(qb + rr * RB + ((q ^ rr) << 4) + 8 * ((col >> 2) & 1));
-        part[dt] = mfma16x16x16(qt, ehi, part[dt]);
-        part[dt] = mfma16x16x16(qt, elo, part[dt]);
+        const uint2 qt = lds_read_tr16(qb + rr * PB + ((q ^ rr) << 4) + 8 * ((col >> 2) & 1));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          acc[u][dt] = mfma16x16x16(qt, ehi[u], acc[u][dt]);
+          acc[u][dt] = mfma16x16x16(qt, elo[u], acc[u][dt]);
+        }
       }
     }
+    if (hg == NG - 1 && more) {
+      store_w((bi + 1) & 1);   // its last readers (block b - 1) passed the barriers of block b
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const f32x4 y = part[dt] - cmp[dt];
-      const f32x4 tot = acc[dt] + y;
-      cmp[dt] = (tot - acc[dt]) - y;
-      acc[dt] = tot;
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gcur[u][i] = gnext[u][i];
     }
-    if (more) {
-      store_w(buf ^ 1);   // its last readers (block b - 1) passed the barrier above
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gcur[i] = gnext[i];
-    }
-    __syncthreads();   // every wave is done with buffer buf before it is restaged
+    __syncthreads();   // every wave is done with qs[st & 1] before it is restaged
   }
-  // lane (key r16, group g) holds dims 16dt + 4g + i of dK^T[:, key]
-  if (j_ok) {
-    float *dst = out + split * split_stride + (int64_t)(k_base + j) * DI + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = acc[dt];
-  }
+  store_out();
 }
 
 // dk[key] = sum over the chunks that wrote a partial for the key's tile, in chunk order,
@@ -479,7 +515,7 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_reduce_kernel(LayoutDev L, int
   const int q_start = __ldg(L.cu_q + seg);
   const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
   const int off = seg_offset(L, seg, q_len, s_k);
-  const int j0 = ((key - k_base) / 64) * 64;
+  const int j0 = ((key - k_base) / DK_TILE) * DK_TILE;
   const int b_lo = first_block_seeing(j0, off, L.ratio, q_len);
   const int nqb = (q_len + BWD_TOK - 1) / BWD_TOK;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
@@ -502,7 +538,7 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_reduce_kernel(LayoutDev L, int
 // at least 4 blocks per chunk.
 void indexer_bwd_dk_split(int num_seqs, int max_seqlen_q, int max_seqlen_k, int *ch, int *ns) {
   const int nqb = (max_seqlen_q + BWD_TOK - 1) / BWD_TOK;
-  const int nkt = (max_seqlen_k + 63) / 64;
+  const int nkt = (max_seqlen_k + DK_TILE - 1) / DK_TILE;
   const long long tiles = (long long)num_seqs * nkt;
   long long want = (1024 + tiles - 1) / tiles;
   want = std::max(1LL, std::min(want, (long long)(nqb + 3) / 4));
@@ -522,7 +558,7 @@ static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const 
                                const float *weights, float idx_scale, const float *grad, int64_t ldg,
                                float *dq, float *dw, float *dk, float *ws, hipStream_t st) {
   const int nqb = (LL.max_seqlen_q + BWD_TOK - 1) / BWD_TOK;
-  const int nkt = (LL.max_seqlen_k + 63) / 64;
+  const int nkt = (LL.max_seqlen_k + DK_TILE - 1) / DK_TILE;
   int ch, ns;
   indexer_bwd_dk_split(LL.num_seqs, LL.max_seqlen_q, LL.max_seqlen_k, &ch, &ns);
   if (LL.total_q > 0) {

@@ -6,6 +6,9 @@ is run on exactly those (ids/scores overridden, teacher replaced by the GPU's) a
 comparison isolates the backward.  Small workloads: every element of dq_idx, dweights
 and dk_idx.  Full-size: seeded row samples for dq/dweights and a few keys for dk_idx.
 
+Both workspaces (score gradients, dk partials) are handed in filled with NaN, so a read
+of an element the kernels did not write first fails the comparison.
+
 Tolerance (derived): the gradient factors enter the bf16 MFMAs as a hi/lo pair, 2^-17
 relative each; products accumulate in fp32 over at most a few thousand terms per MFMA
 chain (dk adds its per-token-block partials with compensated summation), so every
@@ -34,14 +37,26 @@ def _ops():
     return ops
 
 
+def nan_workspaces(ops, L, inp):
+    """The score-gradient and dk-partial workspaces filled with NaN: any element the
+    kernels read without writing first poisons the result."""
+    wl = inp.wl
+    g = torch.full((wl.total_q, L.max_seqlen_k), float("nan"), dtype=torch.float32, device="cuda")
+    n = max(ops.csa_indexer_loss_bwd_workspace(L, wl.Hi, wl.Di), 4)
+    ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
+    return g, ws
+
+
 def _gpu(inp, grad_loss=1.0, per_token=False, res=None):
     ops = _ops()
     if res is None:
         res = ops.forward(inp, want_teacher=True)
     L = ops.layout_of_inputs(inp)
+    g, ws = nan_workspaces(ops, L, inp)
     dq, dw, dk = ops.csa_indexer_loss_bwd(L, inp.wl.sparse_loss, inp.q_idx, inp.k_idx, inp.weights,
                                           inp.idx_scale, res["scores"], res["ids"], res["teacher"],
-                                          grad_loss=grad_loss, per_token=per_token)
+                                          grad_loss=grad_loss, per_token=per_token, grad_scores=g,
+                                          workspace=ws)
     torch.cuda.synchronize()
     return res, dq, dw, dk
 
@@ -85,6 +100,21 @@ def test_small_workloads_every_element(gpu_ok, name):
     _close(f"{name} dq", B.host(dq), rdq)
     _close(f"{name} dw", B.host(dw), rdw)
     _close(f"{name} dk", B.host(dk), rdk)
+
+
+@pytest.mark.parametrize("Hi,Di", [(4, 64), (8, 64), (32, 64), (4, 128), (8, 128), (16, 128)])
+def test_every_supported_indexer_shape(gpu_ok, Hi, Di):
+    """Each (Hi, Di) the backward supports, every element, on a ragged two-segment batch
+    (q rows of 4 x 64 bf16 are 512 bytes: the staging path for rows under 1 KiB)."""
+    wl = I.scaled_down(I.WORKLOADS[1], (272, 200), topk=24, Hi=Hi, Di=Di, name=f"bshd-hi{Hi}-di{Di}")
+    inp = I.make_inputs(wl, device="cuda", seed=Hi * 1000 + Di)
+    res, dq, dw, dk = _gpu(inp)
+    P = B.problem_of(inp)
+    rows = _oracle_rows(P, res, range(wl.total_q))
+    rdq, rdw, rdk = oracle.indexer_loss_backward(P, rows)
+    _close(f"Hi={Hi} Di={Di} dq", B.host(dq), rdq)
+    _close(f"Hi={Hi} Di={Di} dw", B.host(dw), rdw)
+    _close(f"Hi={Hi} Di={Di} dk", B.host(dk), rdk)
 
 
 def test_per_token_loss_and_upstream_gradient(gpu_ok):

@@ -16,7 +16,7 @@ import oracle
 from deepseek_v4_csa_amd import inputs as I
 from tests import gpu_check as C
 from tests import oracle_bridge as B
-from tests.test_gpu_backward import _close, _oracle_rows
+from tests.test_gpu_backward import _close, _oracle_rows, nan_workspaces
 
 pytestmark = pytest.mark.gpu
 
@@ -89,8 +89,10 @@ def test_padded_small_backward_every_element(gpu_ok, name):
     pad = I.pad_inputs(I.make_inputs(wl, device="cuda"), n_pad, dummy=dummy)
     res = _fwd(pad)
     L = ops.layout_of_inputs(pad)
+    g, ws = nan_workspaces(ops, L, pad)
     dq, dw, dk = ops.csa_indexer_loss_bwd(L, pad.wl.sparse_loss, pad.q_idx, pad.k_idx, pad.weights,
-                                          pad.idx_scale, res["scores"], res["ids"], res["teacher"])
+                                          pad.idx_scale, res["scores"], res["ids"], res["teacher"],
+                                          grad_scores=g, workspace=ws)
     torch.cuda.synchronize()
     P = B.problem_of(pad)
     rows = _oracle_rows(P, res, range(pad.wl.total_q))
