@@ -500,15 +500,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DI == 64 ? 
 }
 
 // dk[key] = sum over the chunks that wrote a partial for the key's tile, in chunk order,
-// in fp64 (one thread per 4 dims of a key; keys that no token sees get 0).
+// in fp64 (one thread per element of a key row, so each load instruction reads 1 KiB of
+// consecutive partial rows; eight chunks in flight; keys that no token sees get 0).
 template <int DI>
 __global__ __launch_bounds__(256) void idx_bwd_dk_reduce_kernel(LayoutDev L, int total_k, int ch,
                                                                 const float *__restrict__ part,
                                                                 int64_t split_stride,
                                                                 float *__restrict__ dk) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)total_k * (DI / 4)) return;
-  const int key = (int)(e / (DI / 4)), d4 = (int)(e - (int64_t)key * (DI / 4));
+  if (e >= (int64_t)total_k * DI) return;
+  const int key = (int)(e / DI);
   const int seg = segment_of(L.cu_k, L.num_seqs, key);
   const int k_base = __ldg(L.cu_k + seg);
   const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
@@ -518,19 +519,21 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_reduce_kernel(LayoutDev L, int
   const int j0 = ((key - k_base) / DK_TILE) * DK_TILE;
   const int b_lo = first_block_seeing(j0, off, L.ratio, q_len);
   const int nqb = (q_len + BWD_TOK - 1) / BWD_TOK;
-  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  double a = 0.0;
   if (b_lo < nqb) {
-    const int s_hi = (nqb - 1) / ch;
-    for (int s = b_lo / ch; s <= s_hi; ++s) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(part + s * split_stride + (int64_t)key * DI + 4 * d4);
-      a0 += v[0];
-      a1 += v[1];
-      a2 += v[2];
-      a3 += v[3];
+    const int s_end = (nqb - 1) / ch + 1;
+    int s = b_lo / ch;
+    const float *p = part + e;
+    for (; s + 8 <= s_end; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(s + u) * split_stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a += (double)v[u];
     }
+    for (; s < s_end; ++s) a += (double)p[(int64_t)s * split_stride];
   }
-  *reinterpret_cast<f32x4 *>(dk + (int64_t)key * DI + 4 * d4) =
-      f32x4{(float)a0, (float)a1, (float)a2, (float)a3};
+  dk[e] = (float)a;
 }
 
 // ---------------------------------------------------------------- launch
@@ -575,7 +578,7 @@ static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const 
                      weights, idx_scale, grad, ldg, LL.total_q, nkt, ch, stride, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  const int64_t nthr = (int64_t)LL.total_k * (DI / 4);
+  const int64_t nthr = (int64_t)LL.total_k * DI;
   hipLaunchKernelGGL(idx_bwd_dk_reduce_kernel<DI>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st, LL.dev,
                      LL.total_k, ch, ws, stride, dk);
   return hipGetLastError();
