@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--row", default="path", choices=("path", "backward", "cp-share"))
+    ap.add_argument("--unfused", action="store_true",
+                    help="path: score and top-k as two calls (the score matrix stored) even where "
+                         "the fused call applies")
     ap.add_argument("--cp", type=int, default=8, help="cp-share: CP size")
     ap.add_argument("--rank", type=int, default=0, help="cp-share: rank")
     return ap.parse_args()
@@ -386,14 +389,31 @@ def main():
     kl_row = torch.empty((T,), dtype=torch.float32, device=dev)
     loss = torch.empty((1,), dtype=torch.float32, device=dev)
 
-    names = ("indexer_score", "topk", "sparse_attn", "teacher_kl")
+    # the fused score + top-k call where it applies (sparse loss, supported shape): the
+    # score matrix is never stored and the teacher/KL reads the selected scores
+    fused = wl.sparse_loss and not args.unfused
+    sel = None
+    if fused:
+        sel = torch.empty((T, k_eff), dtype=torch.float32, device=dev)
+        try:
+            ops.csa_indexer_topk(L, inp.q_idx, inp.k_idx, inp.weights, inp.idx_scale, wl.topk, ids=ids,
+                                 sel_scores=sel)
+        except RuntimeError:
+            fused, sel = False, None
+    if fused:
+        scores = None
+    names = ("indexer_topk", "sparse_attn", "teacher_kl") if fused else \
+        ("indexer_score", "topk", "sparse_attn", "teacher_kl")
     # every ctypes argument is marshalled once, so the host enqueues far ahead of the GPU
     P = ops.Prepared(L, inp, scores, ids, out, lse, lse_nc, cmass, kl_row, loss,
-                     wl.sparse_loss, wl.topk, wl.window)
+                     wl.sparse_loss, wl.topk, wl.window, sel=sel)
 
     def step(ev=None):
-        P.csa_indexer_score()
-        P.csa_topk()
+        if fused:
+            P.csa_indexer_topk()
+        else:
+            P.csa_indexer_score()
+            P.csa_topk()
         if ev: ev[0].record()
         P.csa_sparse_attn_fwd()
         if ev: ev[1].record()
@@ -415,8 +435,9 @@ def main():
 
     # per-call breakdown from a separate, untimed pass with events between all calls
     nb = min(args.steps, 50)
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nb)]
-    calls = (P.csa_indexer_score, P.csa_topk, P.csa_sparse_attn_fwd, P.csa_indexer_teacher_kl)
+    calls = ((P.csa_indexer_topk,) if fused else (P.csa_indexer_score, P.csa_topk)) + \
+        (P.csa_sparse_attn_fwd, P.csa_indexer_teacher_kl)
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(nb)]
     for ev in bev:
         ev[0].record()
         for i, f in enumerate(calls):
@@ -432,17 +453,25 @@ def main():
             "traffic": traffic_of(wl.name, "sparse_attn")}
     roof["frac"] = roof["achieved"] / roof["peak"]
     idx_peak = FP32_MFMA_PEAK_TFLOPS if wl.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
-    kernels = {
-        "indexer_score": {"us": per_kernel_ms["indexer_score"] * 1e3,
-                          "tflops": wm["indexer_flop"] / (per_kernel_ms["indexer_score"] * 1e-3) / 1e12,
-                          "frac_mfma_peak": wm["indexer_flop"] / (per_kernel_ms["indexer_score"] * 1e-3) / 1e12 / idx_peak},
-        "topk": {"us": per_kernel_ms["topk"] * 1e3,
-                 "gbs": wm["topk_bytes"] / (per_kernel_ms["topk"] * 1e-3) / 1e9},
+    kernels = {}
+    if fused:
+        kernels["indexer_topk"] = {
+            "us": per_kernel_ms["indexer_topk"] * 1e3,
+            "tflops": wm["indexer_flop"] / (per_kernel_ms["indexer_topk"] * 1e-3) / 1e12,
+            "frac_mfma_peak": wm["indexer_flop"] / (per_kernel_ms["indexer_topk"] * 1e-3) / 1e12 / idx_peak}
+    else:
+        kernels["indexer_score"] = {
+            "us": per_kernel_ms["indexer_score"] * 1e3,
+            "tflops": wm["indexer_flop"] / (per_kernel_ms["indexer_score"] * 1e-3) / 1e12,
+            "frac_mfma_peak": wm["indexer_flop"] / (per_kernel_ms["indexer_score"] * 1e-3) / 1e12 / idx_peak}
+        kernels["topk"] = {"us": per_kernel_ms["topk"] * 1e3,
+                           "gbs": wm["topk_bytes"] / (per_kernel_ms["topk"] * 1e-3) / 1e9}
+    kernels.update({
         "sparse_attn": {"us": att_ms * 1e3, "gbs_gather_model": roof["achieved"],
                         "tflops": wm["attn_flop"] / (att_ms * 1e-3) / 1e12},
         "teacher_kl": {"us": per_kernel_ms["teacher_kl"] * 1e3,
                        "gbs": wm["teacher_bytes"] / (per_kernel_ms["teacher_kl"] * 1e-3) / 1e9},
-    }
+    })
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds)
@@ -452,7 +481,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if wl.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {**wl.describe(), "parallelism": "none (1 GPU)"},
+        "config": {**wl.describe(), "parallelism": "none (1 GPU)",
+                   "score_path": "fused score + top-k (no score matrix)" if fused else "score and top-k calls"},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
         "loss": float(loss[0]),
     }

@@ -124,6 +124,29 @@ csa_status_t csa_topk(const csa_layout_t *L, const float *scores, int64_t ld_sco
   return hip_status(csa::launch_topk(LL, scores, ld_scores, k_eff, ids, static_cast<hipStream_t>(stream)), fn);
 }
 
+csa_status_t csa_indexer_topk(const csa_layout_t *L, const void *q_idx, const void *k_idx,
+                              const float *weights, csa_dtype_t dt, int32_t Hi, int32_t Di,
+                              float idx_scale, int32_t topk, int32_t *ids, float *sel_scores,
+                              float *row_lse, void *stream) {
+  const char *fn = "csa_indexer_topk";
+  csa::LaunchLayout LL;
+  csa_status_t st = check_layout(L, fn, &LL);
+  if (st != CSA_OK) return st;
+  if (!q_idx || !k_idx || !weights || !ids || !sel_scores)
+    return fail(CSA_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+  if (Hi < 1 || Di < 1) return fail(CSA_ERR_INVALID, "%s: Hi=%d, Di=%d must be >= 1", fn, Hi, Di);
+  if (topk < 1) return fail(CSA_ERR_INVALID, "%s: topk=%d < 1", fn, topk);
+  if (!csa::indexer_topk_supported(dt == CSA_BF16, Hi, Di, L->max_seqlen_k))
+    return fail(CSA_ERR_UNSUPPORTED,
+                "%s: no fused kernel for dtype=%d Hi=%d Di=%d max_seqlen_k=%d (bf16 (Hi, Di) in {(8,64), "
+                "(16,64), (4,128), (8,128)} with the score rows of two 16-token blocks in 160 KiB of LDS)",
+                fn, (int)dt, Hi, Di, L->max_seqlen_k);
+  return hip_status(csa::launch_indexer_topk(LL, q_idx, k_idx, weights, Hi, Di, idx_scale, k_eff_of(L, topk),
+                                             ids, sel_scores, row_lse, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 csa_status_t csa_sparse_attn_fwd(const csa_layout_t *L, const void *q, const void *kv,
                                  const void *ckv, const float *sink, const int32_t *ids,
                                  int32_t k_eff, int32_t window, csa_dtype_t dt, int32_t H,
@@ -151,7 +174,8 @@ csa_status_t csa_sparse_attn_fwd(const csa_layout_t *L, const void *q, const voi
 }
 
 csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, const float *scores,
-                                    int64_t ld_scores, const int32_t *ids, int32_t k_eff,
+                                    int64_t ld_scores, int32_t scores_selected, const int32_t *ids,
+                                    int32_t k_eff,
                                     const float *cmass, const void *q, const void *ckv,
                                     const float *lse_nc, csa_dtype_t dt, int32_t H, int32_t D,
                                     float softmax_scale, int32_t per_token_loss, float *teacher,
@@ -161,9 +185,11 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, 
   csa_status_t st = check_layout(L, fn, &LL);
   if (st != CSA_OK) return st;
   if (!scores || !kl_row || !loss) return fail(CSA_ERR_INVALID, "%s: scores/kl_row/loss is NULL", fn);
-  if (ld_scores < L->max_seqlen_k)
-    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld < max_seqlen_k=%d", fn, (long long)ld_scores,
-                L->max_seqlen_k);
+  if (scores_selected && !sparse_loss)
+    return fail(CSA_ERR_INVALID, "%s: selected scores need the sparse loss", fn);
+  const int need_ld = scores_selected ? k_eff : L->max_seqlen_k;
+  if (ld_scores < need_ld)
+    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld < %d", fn, (long long)ld_scores, need_ld);
   if (sparse_loss) {
     if (k_eff < 1 || k_eff > L->max_seqlen_k)
       return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [1, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
@@ -182,7 +208,8 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, 
       return fail(CSA_ERR_UNSUPPORTED, "%s: no dense kernel for dtype=%d H=%d D=%d max_seqlen_k=%d", fn,
                   (int)dt, H, D, L->max_seqlen_k);
   }
-  return hip_status(csa::launch_teacher_kl(LL, sparse_loss != 0, scores, ld_scores, ids, k_eff, cmass, q,
+  return hip_status(csa::launch_teacher_kl(LL, sparse_loss != 0, scores, ld_scores, scores_selected != 0,
+                                           ids, k_eff, cmass, q,
                                            ckv, lse_nc, dt == CSA_BF16, H, D, softmax_scale,
                                            per_token_loss != 0, teacher, ld_teacher, kl_row, loss,
                                            static_cast<hipStream_t>(stream)),
@@ -192,7 +219,8 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, 
 csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, const void *q_idx,
                                   const void *k_idx, const float *weights, csa_dtype_t dt, int32_t Hi,
                                   int32_t Di, float idx_scale, const float *scores, int64_t ld_scores,
-                                  const int32_t *ids, int32_t k_eff, const float *teacher,
+                                  int32_t scores_selected, const int32_t *ids, int32_t k_eff,
+                                  const float *teacher,
                                   int64_t ld_teacher, float grad_loss, int32_t per_token_loss,
                                   float *grad_scores, int64_t ld_grad, float *dq_idx, float *dweights,
                                   float *dk_idx, void *workspace, int64_t workspace_bytes,
@@ -205,9 +233,11 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, co
     return fail(CSA_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
   if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
   if (Hi < 1 || Di < 1) return fail(CSA_ERR_INVALID, "%s: Hi=%d, Di=%d must be >= 1", fn, Hi, Di);
-  if (ld_scores < L->max_seqlen_k || ld_grad < L->max_seqlen_k)
-    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld / ld_grad=%lld < max_seqlen_k=%d", fn,
-                (long long)ld_scores, (long long)ld_grad, L->max_seqlen_k);
+  if (scores_selected && !sparse_loss)
+    return fail(CSA_ERR_INVALID, "%s: selected scores need the sparse loss", fn);
+  if (ld_scores < (scores_selected ? k_eff : L->max_seqlen_k) || ld_grad < L->max_seqlen_k)
+    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld / ld_grad=%lld too small (max_seqlen_k=%d, k_eff=%d)",
+                fn, (long long)ld_scores, (long long)ld_grad, L->max_seqlen_k, k_eff);
   if (sparse_loss) {
     if (k_eff < 1 || k_eff > L->max_seqlen_k)
       return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [1, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
@@ -228,7 +258,8 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, co
                 (long long)(workspace ? workspace_bytes : 0), (long long)need);
   const float gscale = per_token_loss ? grad_loss : (L->total_q > 0 ? grad_loss / (float)L->total_q : 0.f);
   return hip_status(csa::launch_indexer_loss_bwd(LL, sparse_loss != 0, q_idx, k_idx, weights, Hi, Di,
-                                                  idx_scale, scores, ld_scores, ids, k_eff, teacher,
+                                                  idx_scale, scores, ld_scores, scores_selected != 0, ids,
+                                                  k_eff, teacher,
                                                   ld_teacher, gscale, grad_scores, ld_grad, dq_idx,
                                                   dweights, dk_idx, workspace,
                                                   static_cast<hipStream_t>(stream)),

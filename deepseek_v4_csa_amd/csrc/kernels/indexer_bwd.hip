@@ -54,7 +54,7 @@ __device__ __forceinline__ void split_bf16x4(const float (&x)[4], uint2 &hi, uin
 // columns j < max_seqlen_k
 template <int SPL>
 __global__ __launch_bounds__(256) void grad_scores_kernel(
-    LayoutDev L, int T, int sparse, const float *__restrict__ scores, int64_t ld,
+    LayoutDev L, int T, int sparse, const float *__restrict__ scores, int64_t ld, int selected,
     const int32_t *__restrict__ ids, int k_eff, const float *__restrict__ teacher, int64_t ldt,
     float gscale, float *__restrict__ grad, int64_t ldg, int max_sk) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256) void grad_scores_kernel(
       col[v] = j;
     }
     if (!valid) col[v] = -1;
-    s[v] = valid ? scores[(int64_t)t * ld + col[v]] : -__builtin_inff();
+    // sparse + selected: the score of slot j sits at column j of the selected-score row
+    s[v] = valid ? scores[(int64_t)t * ld + (selected ? j : col[v])] : -__builtin_inff();
     te[v] = valid ? teacher[(int64_t)t * ldt + j] : 0.f;
     mx = fmaxf(mx, s[v]);
   }
@@ -587,7 +588,7 @@ static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const 
 hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const void *q_idx,
                                   const void *k_idx, const float *weights, int Hi, int Di,
                                   float idx_scale, const float *scores, int64_t ld_scores,
-                                  const int32_t *ids, int k_eff, const float *teacher,
+                                  bool selected, const int32_t *ids, int k_eff, const float *teacher,
                                   int64_t ld_teacher, float grad_scale, float *grad, int64_t ld_grad,
                                   float *dq, float *dw, float *dk, void *workspace, hipStream_t st) {
   if (LL.total_q > 0) {
@@ -596,7 +597,8 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const vo
 #define CSA_GS_CASE(S)                                                                              \
     if (nslot <= 64 * S) {                                                                          \
       hipLaunchKernelGGL(grad_scores_kernel<S>, grid, dim3(256), 0, st, LL.dev, LL.total_q,         \
-                         sparse ? 1 : 0, scores, ld_scores, ids, k_eff, teacher, ld_teacher,        \
+                         sparse ? 1 : 0, scores, ld_scores, selected ? 1 : 0, ids, k_eff, teacher,  \
+                         ld_teacher,                                                                \
                          grad_scale, grad, ld_grad, LL.max_seqlen_k);                               \
     } else
     CSA_GS_CASE(1) CSA_GS_CASE(2) CSA_GS_CASE(4) CSA_GS_CASE(8) CSA_GS_CASE(16) CSA_GS_CASE(32)

@@ -15,6 +15,7 @@
 // accumulator.  The per-head [token, head, key] product never leaves registers.
 // Tiles entirely above the causal limit are only filled with -inf.
 #include "common.h"
+#include "wave_select.h"
 #include "../launch.h"
 
 namespace csa {
@@ -182,17 +183,27 @@ __global__ __launch_bounds__(IDX_THREADS) void indexer_score_kernel(
 constexpr int IXL_TOK = 16;
 constexpr int IXL_WAVES = 8;
 
+// Outputs of the fused score + top-k variant (FUSED = true): the score tiles go to an LDS
+// row area instead of HBM and each row is then selected there by one wave.
+struct TopkOut {
+  int32_t *ids;    // [T, k_eff] global ids, ascending, -1 tail
+  float *sel;      // [T, k_eff] score of each selected key, -inf at -1 slots
+  float *lse;      // [T] log-sum-exp of the row's visible scores (-inf if none), or null
+  int k_eff;
+  int cap;         // score area capacity in 64-key tiles per 16 rows
+};
+
 // max(x, 0) in one integer max on the bit pattern: a float with the sign bit set is a
 // negative int32 (-> +0), a non-negative float keeps its bits
 __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
-template <int DI, int HI>
+template <int DI, int HI, bool FUSED, int VPL>
 __global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
     LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const float *__restrict__ weights, float idx_scale, float *__restrict__ scores, int64_t ld,
-    int max_sk, int total_q) {
+    int max_sk, int total_q, TopkOut to) {
   constexpr int RB = HI * DI * 2;   // bytes of one token's q_idx row
   constexpr int CPR = RB / 16;      // 16-byte chunks per row
   constexpr int PPR = RB / 1024;    // 1 KiB pieces per row
@@ -203,6 +214,10 @@ __global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
   static_assert(CH == 8 || CH == 16, "Di of 64 or 128");
   __shared__ __attribute__((aligned(16))) u32x4 qs[2][IXL_TOK * CPR];
   __shared__ __attribute__((aligned(16))) float ws[2][HI * IXL_TOK];
+  // FUSED: score rows of the blocks of the current phase (row stride = live tiles * 64 + 4
+  // floats, so the four token groups of a tile store hit different banks), then one
+  // 256-word histogram per wave for the selection
+  extern __shared__ __attribute__((aligned(16))) float score_lds[];
 
   const int seg = blockIdx.x % L.num_seqs;
   const int pair = blockIdx.x / L.num_seqs;
@@ -250,7 +265,7 @@ __global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
   };
   const f32x4 zero4[4] = {};
   // tiles above the causal limit: (block, tile) pairs dealt round-robin over the waves
-  {
+  if constexpr (!FUSED) {
     const int nf0 = ntiles - nl0, nf = nf0 + (nblk > 1 ? ntiles - nl1 : 0);
     for (int v = w; v < nf; v += IXL_WAVES) {
       if (v < nf0) store_tile(tb0, (nl0 + v) * 64, zero4, true);
@@ -258,6 +273,22 @@ __global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
     }
   }
   const int nlive = nl0 + nl1;
+  if constexpr (FUSED) {
+    if (nlive == 0) {   // no row of either block sees a key: -1 ids, -inf scores and lse
+      for (int bk = 0; bk < nblk; ++bk) {
+        const int t0 = bk ? tb1 : tb0;
+        for (int e = tid; e < IXL_TOK * to.k_eff; e += NTHR) {
+          const int r = e / to.k_eff, c = e - r * to.k_eff;
+          if (t0 + r < q_len) {
+            to.ids[(int64_t)(q_start + t0 + r) * to.k_eff + c] = -1;
+            to.sel[(int64_t)(q_start + t0 + r) * to.k_eff + c] = -__builtin_inff();
+          }
+        }
+        if (to.lse && tid < IXL_TOK && t0 + tid < q_len) to.lse[q_start + t0 + tid] = -__builtin_inff();
+      }
+      return;
+    }
+  }
   if (nlive == 0) return;  // uniform: no barrier is skipped by part of the workgroup
 
   // q_idx rows of both blocks -> LDS (rows past the end of the buffer read as zeros)
@@ -330,14 +361,29 @@ __global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
     }
   }
 
-  for (int u = w; u < nlive; u += IXL_WAVES) {
+  // FUSED: both blocks' rows in one phase when they fit the score area, else block 0 then
+  // block 1 (each phase: its tiles, a barrier, the selection of its rows, a barrier)
+  const bool one_phase = !FUSED || nl0 + nl1 <= to.cap;
+  const int nphase = one_phase ? 1 : 2;
+  const int str0 = nl0 * 64 + 4, str1 = nl1 * 64 + 4;   // row strides of the score area
+  auto row_ptr = [&](int bk, int r) -> float * {
+    return score_lds + (bk ? (one_phase ? IXL_TOK * str0 : 0) + r * str1 : r * str0);
+  };
+  for (int ph = 0; ph < nphase; ++ph) {
+  const int u_lo = one_phase ? 0 : (ph ? nl0 : 0), u_hi = one_phase ? nlive : (ph ? nlive : nl0);
+  if (ph > 0 && u_lo + w < u_hi) {   // phase 2: its first key tile (phase 1 stopped short)
+    int bk, tile;
+    tile_of(u_lo + w, bk, tile);
+    load_k(tile, kbn);
+  }
+  for (int u = u_lo + w; u < u_hi; u += IXL_WAVES) {
     int bk, tile;
     tile_of(u, bk, tile);
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int c = 0; c < NCD; ++c) kb[n][c] = kbn[n][c];
-    if (u + IXL_WAVES < nlive) {
+    if (u + IXL_WAVES < u_hi) {
       int bk2, tile2;
       tile_of(u + IXL_WAVES, bk2, tile2);
       load_k(tile2, kbn);
@@ -404,7 +450,63 @@ __global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    store_tile(bk ? tb1 : tb0, tile * 64, acc, false);
+    if constexpr (FUSED) {
+      // lane (token 4g+i, key tile*64 + 16n + r16) -> the block's LDS score row
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float *dst = row_ptr(bk, 4 * g + i) + tile * 64 + r16;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) dst[16 * n] = acc[n][i];
+      }
+    } else {
+      store_tile(bk ? tb1 : tb0, tile * 64, acc, false);
+    }
+  }
+  if constexpr (FUSED) {
+    __syncthreads();   // every score tile of the phase is in LDS
+    // rows of the phase, one wave per row: top-k, selected scores, log-sum-exp
+    const int b_lo = one_phase ? 0 : ph, b_hi = one_phase ? nblk : ph + 1;
+    uint32_t *hist = reinterpret_cast<uint32_t *>(
+        score_lds + IXL_TOK * (one_phase ? str0 + (nblk > 1 ? str1 : 0) : max(str0, str1))) + 256 * w;
+    for (int rr = w; rr < (b_hi - b_lo) * IXL_TOK; rr += IXL_WAVES) {
+      const int bk = b_lo + rr / IXL_TOK, r = rr % IXL_TOK;
+      const int t = (bk ? tb1 : tb0) + r;
+      if (t >= q_len) continue;
+      const int n = n_valid_of(t, off, L.ratio, s_k);
+      const float *row = row_ptr(bk, r);
+      float val[VPL];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int j = v * 64 + lane;
+        val[v] = j < n ? row[j] : -__builtin_inff();
+      }
+      const int64_t o = (int64_t)(q_start + t) * to.k_eff;
+      if (to.lse) {
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) m = fmaxf(m, val[v]);
+        m = wave_max_dpp(m);
+        double sum = 0.0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (v * 64 + lane < n) sum += (double)__expf(val[v] - m);
+        sum = wave_sum_f64_dpp(sum);
+        if (lane == 0) to.lse[q_start + t] = n > 0 ? m + (float)log(sum) : -__builtin_inff();
+      }
+      if (n <= to.k_eff) {   // every visible key is selected
+        for (int c = lane; c < to.k_eff; c += 64) {
+          to.ids[o + c] = c < n ? k_base + c : -1;
+          to.sel[o + c] = c < n ? row[c] : -__builtin_inff();
+        }
+      } else {
+        wave_select<VPL>(val, n, to.k_eff, hist, [&](int pos, int j, int v) {
+          to.ids[o + pos] = k_base + j;
+          to.sel[o + pos] = val[v];
+        });
+      }
+    }
+    __syncthreads();   // the score area is free for the next phase
+  }
   }
 }
 
@@ -415,10 +517,79 @@ static hipError_t launch_lds(const LaunchLayout &LL, const void *q_idx, const vo
   const int npair = ((LL.max_seqlen_q + IXL_TOK - 1) / IXL_TOK + 1) / 2;
   const int64_t grid = (int64_t)LL.num_seqs * npair;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((indexer_score_lds_kernel<DI, HI>), dim3((unsigned)grid), dim3(64 * IXL_WAVES), 0, st,
-                     LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
-                     weights, idx_scale, scores, ld, LL.max_seqlen_k, LL.total_q);
+  hipLaunchKernelGGL((indexer_score_lds_kernel<DI, HI, false, 1>), dim3((unsigned)grid), dim3(64 * IXL_WAVES),
+                     0, st, LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
+                     weights, idx_scale, scores, ld, LL.max_seqlen_k, LL.total_q, TopkOut{});
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fused score + top-k
+// Static LDS of the paired-block kernel (q rows of both blocks + fp32(w * s_idx)).
+template <int DI, int HI> constexpr int lds_static_bytes() {
+  return 2 * IXL_TOK * HI * DI * 2 + 2 * HI * IXL_TOK * 4;
+}
+constexpr int LDS_PER_CU = 160 * 1024;
+
+// Score area: one phase holds the rows of both blocks when their live tiles fit `cap`
+// tiles; a single block always fits (cap >= tiles of a row).  cap = one row's tiles + 1
+// covers the usual pairing (a heavy and a light block of one causal segment).
+static int fused_cap(int max_sk) { return (max_sk + 63) / 64 + 1; }
+static int fused_dyn_bytes(int max_sk) {
+  const int cap = fused_cap(max_sk);
+  return (IXL_TOK * (cap * 64 + 8) + 256 * IXL_WAVES) * 4;
+}
+
+template <int DI, int HI, int VPL>
+static hipError_t launch_fused_t(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+                                 const float *weights, float idx_scale, const TopkOut &to, hipStream_t st) {
+  const int npair = ((LL.max_seqlen_q + IXL_TOK - 1) / IXL_TOK + 1) / 2;
+  const int64_t grid = (int64_t)LL.num_seqs * npair;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int dyn = fused_dyn_bytes(LL.max_seqlen_k);
+  auto kern = indexer_score_lds_kernel<DI, HI, true, VPL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * IXL_WAVES), dyn, st, LL.dev,
+                     static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx), weights,
+                     idx_scale, nullptr, (int64_t)0, LL.max_seqlen_k, LL.total_q, to);
+  return hipGetLastError();
+}
+
+template <int DI, int HI>
+static hipError_t launch_fused_v(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+                                 const float *weights, float idx_scale, const TopkOut &to, hipStream_t st) {
+  const int vpl = (LL.max_seqlen_k + 63) / 64;
+  if (vpl <= 4) return launch_fused_t<DI, HI, 4>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (vpl <= 8) return launch_fused_t<DI, HI, 8>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (vpl <= 16) return launch_fused_t<DI, HI, 16>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (vpl <= 32) return launch_fused_t<DI, HI, 32>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  return hipErrorInvalidValue;
+}
+
+bool indexer_topk_supported(bool bf16, int Hi, int Di, int max_seqlen_k) {
+  // rows up to 2048 keys (Di = 64) or 512 keys (Di = 128: longer rows would spill the
+  // selection's registers)
+  if (!bf16 || max_seqlen_k > (Di == 128 ? 8 : 32) * 64) return false;
+  int stat;
+  if (Di == 64 && Hi == 8) stat = lds_static_bytes<64, 8>();
+  else if (Di == 64 && Hi == 16) stat = lds_static_bytes<64, 16>();
+  else if (Di == 128 && Hi == 4) stat = lds_static_bytes<128, 4>();
+  else if (Di == 128 && Hi == 8) stat = lds_static_bytes<128, 8>();
+  else return false;
+  return stat + fused_dyn_bytes(max_seqlen_k) <= LDS_PER_CU;
+}
+
+hipError_t launch_indexer_topk(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+                               const float *weights, int Hi, int Di, float idx_scale, int k_eff,
+                               int32_t *ids, float *sel, float *lse, hipStream_t st) {
+  if (LL.total_q == 0) return hipSuccess;
+  const TopkOut to{ids, sel, lse, k_eff, fused_cap(LL.max_seqlen_k)};
+  if (Di == 64 && Hi == 8) return launch_fused_v<64, 8>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (Di == 64 && Hi == 16) return launch_fused_v<64, 16>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (Di == 128 && Hi == 4) return launch_fused_v<128, 4>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (Di == 128 && Hi == 8) return launch_fused_v<128, 8>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  return hipErrorInvalidValue;
 }
 
 template <typename IN, int DI>

@@ -52,9 +52,9 @@ __device__ __forceinline__ float log1p_kl(float x) {
 // relative error.  log(t+eps) - log(p+eps) is taken as one log of the ratio.
 template <int SPL>
 __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
-    LayoutDev L, int T, const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ ids,
-    int k_eff, const float *__restrict__ cmass, float *__restrict__ teacher, int64_t ldt,
-    float *__restrict__ kl_row) {
+    LayoutDev L, int T, const float *__restrict__ scores, int64_t ld, int selected,
+    const int32_t *__restrict__ ids, int k_eff, const float *__restrict__ cmass, float *__restrict__ teacher,
+    int64_t ldt, float *__restrict__ kl_row) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + w;
@@ -81,7 +81,9 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
   float mx = -__builtin_inff();
 #pragma unroll
   for (int v = 0; v < SPL; ++v) {
-    sc[v] = id[v] >= 0 ? sr[id[v] - geo.k_base] : -__builtin_inff();
+    // the score of slot j: gathered from the full row, or read in place (selected scores)
+    const int col = selected ? v * 64 + lane : id[v] - geo.k_base;
+    sc[v] = id[v] >= 0 ? sr[col] : -__builtin_inff();
     mx = fmaxf(mx, sc[v]);
   }
   double ms = 0.0;
@@ -332,7 +334,7 @@ static hipError_t launch_dense(const LaunchLayout &LL, const float *scores, int6
 }
 
 hipError_t launch_teacher_kl(const LaunchLayout &LL, bool sparse, const float *scores, int64_t ld,
-                             const int32_t *ids, int k_eff, const float *cmass, const void *q,
+                             bool selected, const int32_t *ids, int k_eff, const float *cmass, const void *q,
                              const void *ckv, const float *lse_nc, bool bf16, int H, int D,
                              float scale, bool per_token, float *teacher, int64_t ld_teacher,
                              float *kl_row, float *loss, hipStream_t st) {
@@ -344,7 +346,8 @@ hipError_t launch_teacher_kl(const LaunchLayout &LL, bool sparse, const float *s
 #define CSA_TKS_CASE(V)                                                                              \
       if (spl <= V) {                                                                                \
         hipLaunchKernelGGL(teacher_kl_sparse_kernel<V>, grid, dim3(256), 0, st, LL.dev, LL.total_q,  \
-                           scores, ld, ids, k_eff, cmass, teacher, ld_teacher, kl_row);              \
+                           scores, ld, selected ? 1 : 0, ids, k_eff, cmass, teacher, ld_teacher,     \
+                           kl_row);                                                                  \
         e = hipGetLastError();                                                                       \
       } else
       CSA_TKS_CASE(1) CSA_TKS_CASE(2) CSA_TKS_CASE(4) CSA_TKS_CASE(8) CSA_TKS_CASE(16)

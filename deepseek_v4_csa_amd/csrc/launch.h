@@ -24,7 +24,7 @@ hipError_t launch_sparse_attn(const LaunchLayout &L, const void *q, const void *
                               float *lse, float *lse_nc, float *cmass, hipStream_t st);
 
 hipError_t launch_teacher_kl(const LaunchLayout &L, bool sparse, const float *scores, int64_t ld,
-                             const int32_t *ids, int k_eff, const float *cmass, const void *q,
+                             bool selected, const int32_t *ids, int k_eff, const float *cmass, const void *q,
                              const void *ckv, const float *lse_nc, bool bf16, int H, int D,
                              float scale, bool per_token, float *teacher, int64_t ld_teacher,
                              float *kl_row, float *loss, hipStream_t st);
@@ -32,14 +32,19 @@ hipError_t launch_teacher_kl(const LaunchLayout &L, bool sparse, const float *sc
 hipError_t launch_indexer_loss_bwd(const LaunchLayout &L, bool sparse, const void *q_idx,
                                   const void *k_idx, const float *weights, int Hi, int Di,
                                   float idx_scale, const float *scores, int64_t ld_scores,
-                                  const int32_t *ids, int k_eff, const float *teacher,
+                                  bool selected, const int32_t *ids, int k_eff, const float *teacher,
                                   int64_t ld_teacher, float grad_scale, float *grad, int64_t ld_grad,
                                   float *dq, float *dw, float *dk, void *workspace, hipStream_t st);
 // device workspace of the indexer-loss backward (dk partials per token-block chunk; 0: none)
 int64_t indexer_bwd_workspace_bytes(int num_seqs, int total_k, int max_seqlen_q, int max_seqlen_k, int Di);
 
+hipError_t launch_indexer_topk(const LaunchLayout &L, const void *q_idx, const void *k_idx,
+                               const float *weights, int Hi, int Di, float idx_scale, int k_eff,
+                               int32_t *ids, float *sel, float *lse, hipStream_t st);
+
 // shape support tables (host side, used by validation before any launch)
 bool indexer_supported(bool bf16, int Hi, int Di);
+bool indexer_topk_supported(bool bf16, int Hi, int Di, int max_seqlen_k);
 bool topk_supported(int max_seqlen_k, int k_eff);
 bool attn_supported(bool bf16, int H, int D, int k_eff);
 bool dense_teacher_supported(bool bf16, int H, int D, int max_seqlen_k);

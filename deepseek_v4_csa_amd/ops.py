@@ -37,7 +37,7 @@ class _CLayout(ctypes.Structure):
 
 EXPORTS = ("csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
            "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd", "csa_indexer_loss_bwd_workspace",
-           "csa_cp_plan")
+           "csa_cp_plan", "csa_indexer_topk")
 
 
 def lib_path() -> str:
@@ -66,13 +66,15 @@ def load():
     lib.csa_sparse_attn_fwd.argtypes = [LP, P, P, P, P, P, I32, I32, ctypes.c_int, I32, I32, F32,
                                         P, P, P, P, P]
     lib.csa_indexer_teacher_kl.restype = ctypes.c_int
-    lib.csa_indexer_teacher_kl.argtypes = [LP, I32, P, I64, P, I32, P, P, P, P, ctypes.c_int, I32,
+    lib.csa_indexer_teacher_kl.argtypes = [LP, I32, P, I64, I32, P, I32, P, P, P, P, ctypes.c_int, I32,
                                            I32, F32, I32, P, I64, P, P, P]
     lib.csa_indexer_loss_bwd.restype = ctypes.c_int
-    lib.csa_indexer_loss_bwd.argtypes = [LP, I32, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, P, I32,
-                                         P, I64, F32, I32, P, I64, P, P, P, P, I64, P]
+    lib.csa_indexer_loss_bwd.argtypes = [LP, I32, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, I32, P,
+                                         I32, P, I64, F32, I32, P, I64, P, P, P, P, I64, P]
     lib.csa_indexer_loss_bwd_workspace.restype = I64
     lib.csa_indexer_loss_bwd_workspace.argtypes = [LP, I32, I32]
+    lib.csa_indexer_topk.restype = ctypes.c_int
+    lib.csa_indexer_topk.argtypes = [LP, P, P, P, ctypes.c_int, I32, I32, F32, I32, P, P, P, P]
     lib.csa_cp_plan.restype = ctypes.c_int
     lib.csa_cp_plan.argtypes = [I32, P, I32, I32, I32, P, P, P, P, P, P]
     _lib = lib
@@ -182,9 +184,27 @@ def csa_sparse_attn_fwd(layout: Layout, q, kv, ckv, sink, ids, window: int, soft
     return out, lse, lse_nc, cmass
 
 
+def csa_indexer_topk(layout: Layout, q_idx, k_idx, weights, idx_scale: float, topk: int, ids=None,
+                     sel_scores=None, row_lse=None, want_lse: bool = False):
+    """Fused scores + top-k: (ids, sel_scores, row_lse or None); the score matrix is never
+    stored."""
+    T, Hi, Di = q_idx.shape
+    dev = q_idx.device
+    k = k_eff(layout, topk)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    sel_scores = torch.empty((T, k), dtype=torch.float32, device=dev) if sel_scores is None else sel_scores
+    if want_lse and row_lse is None:
+        row_lse = torch.empty((T,), dtype=torch.float32, device=dev)
+    _check(load().csa_indexer_topk(ctypes.byref(layout.c()), _ptr(q_idx), _ptr(k_idx), _ptr(weights),
+                                   _dtype(q_idx), Hi, Di, float(idx_scale), int(topk), _ptr(ids),
+                                   _ptr(sel_scores), _ptr(row_lse) if row_lse is not None else None,
+                                   _stream()))
+    return ids, sel_scores, row_lse
+
+
 def csa_indexer_teacher_kl(layout: Layout, sparse_loss: bool, scores, ids, cmass, q, ckv, lse_nc,
                            softmax_scale: float, per_token: bool = False, want_teacher: bool = False,
-                           teacher=None, kl_row=None, loss=None):
+                           teacher=None, kl_row=None, loss=None, scores_selected: bool = False):
     T = scores.shape[0]
     dev = scores.device
     H = q.shape[1] if q is not None else 1
@@ -198,6 +218,7 @@ def csa_indexer_teacher_kl(layout: Layout, sparse_loss: bool, scores, ids, cmass
     dt = _dtype(q) if q is not None else CSA_BF16
     _check(load().csa_indexer_teacher_kl(
         ctypes.byref(layout.c()), 1 if sparse_loss else 0, _ptr(scores), scores.stride(0),
+        1 if scores_selected else 0,
         _ptr(ids) if ids is not None else None, k_eff_, _ptr(cmass) if cmass is not None else None,
         _ptr(q) if q is not None else None, _ptr(ckv) if ckv is not None else None,
         _ptr(lse_nc) if lse_nc is not None else None, dt, H, D, float(softmax_scale),
@@ -208,7 +229,8 @@ def csa_indexer_teacher_kl(layout: Layout, sparse_loss: bool, scores, ids, cmass
 
 def csa_indexer_loss_bwd(layout: Layout, sparse_loss: bool, q_idx, k_idx, weights, idx_scale: float,
                          scores, ids, teacher, grad_loss: float = 1.0, per_token: bool = False,
-                         grad_scores=None, dq_idx=None, dweights=None, dk_idx=None, workspace=None):
+                         grad_scores=None, dq_idx=None, dweights=None, dk_idx=None, workspace=None,
+                         scores_selected: bool = False):
     """Indexer-loss gradients (fp32) for q_idx, weights and k_idx; the teacher and the
     selection (ids) of the forward are held fixed.  workspace: a uint8 device tensor of at
     least csa_indexer_loss_bwd_workspace bytes (allocated here if None)."""
@@ -225,7 +247,7 @@ def csa_indexer_loss_bwd(layout: Layout, sparse_loss: bool, q_idx, k_idx, weight
         workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
     _check(load().csa_indexer_loss_bwd(
         ctypes.byref(layout.c()), 1 if sparse_loss else 0, _ptr(q_idx), _ptr(k_idx), _ptr(weights),
-        _dtype(q_idx), Hi, Di, float(idx_scale), _ptr(scores), scores.stride(0),
+        _dtype(q_idx), Hi, Di, float(idx_scale), _ptr(scores), scores.stride(0), 1 if scores_selected else 0,
         _ptr(ids) if ids is not None else None, k_eff_, _ptr(teacher), teacher.stride(0),
         float(grad_loss), 1 if per_token else 0, _ptr(grad_scores), grad_scores.stride(0),
         _ptr(dq_idx), _ptr(dweights), _ptr(dk_idx), _ptr(workspace), workspace.numel(), _stream()))
@@ -263,18 +285,28 @@ def layout_of_inputs(inp) -> Layout:
                   wl.max_seqlen_k, inp.offsets, inp.cu_q_real)
 
 
-def forward(inp, want_teacher=False):
-    """The whole path on one Inputs: the four calls on the current stream."""
+def forward(inp, want_teacher=False, fused=False):
+    """The whole path on one Inputs, on the current stream: the four calls, or with
+    fused=True (sparse loss) csa_indexer_topk in place of the score and top-k calls, the
+    teacher/KL then reading the selected scores (no score matrix: scores is None)."""
     wl = inp.wl
     L = layout_of_inputs(inp)
-    scores = csa_indexer_score(L, inp.q_idx, inp.k_idx, inp.weights, inp.idx_scale)
-    ids = csa_topk(L, scores, wl.topk)
+    sel = row_lse = scores = None
+    if fused:
+        if not wl.sparse_loss:
+            raise RuntimeError("the fused score + top-k path serves the sparse loss")
+        ids, sel, row_lse = csa_indexer_topk(L, inp.q_idx, inp.k_idx, inp.weights, inp.idx_scale, wl.topk,
+                                             want_lse=True)
+    else:
+        scores = csa_indexer_score(L, inp.q_idx, inp.k_idx, inp.weights, inp.idx_scale)
+        ids = csa_topk(L, scores, wl.topk)
     out, lse, lse_nc, cmass = csa_sparse_attn_fwd(L, inp.q, inp.kv, inp.ckv, inp.sink, ids, wl.window,
                                                   inp.scale, want_cmass=wl.sparse_loss)
-    teacher, kl_row, loss = csa_indexer_teacher_kl(L, wl.sparse_loss, scores, ids, cmass, inp.q, inp.ckv,
-                                                   lse_nc, inp.scale, want_teacher=want_teacher)
+    teacher, kl_row, loss = csa_indexer_teacher_kl(L, wl.sparse_loss, sel if fused else scores, ids, cmass,
+                                                   inp.q, inp.ckv, lse_nc, inp.scale, want_teacher=want_teacher,
+                                                   scores_selected=fused)
     return dict(scores=scores, ids=ids, out=out, lse=lse, lse_nc=lse_nc, cmass=cmass,
-                teacher=teacher, kl_row=kl_row, loss=loss)
+                teacher=teacher, kl_row=kl_row, loss=loss, sel=sel, row_lse=row_lse)
 
 
 class Prepared:
@@ -287,7 +319,7 @@ class Prepared:
     """
 
     def __init__(self, layout: Layout, inp, scores, ids, out, lse, lse_nc, cmass, kl_row, loss,
-                 sparse_loss: bool, topk: int, window: int, teacher=None):
+                 sparse_loss: bool, topk: int, window: int, teacher=None, sel=None):
         lib = load()
         self._lib = lib
         self._L = layout.c()
@@ -296,16 +328,21 @@ class Prepared:
         T, Hi, Di = inp.q_idx.shape
         _, H, D = inp.q.shape
         k_eff_ = ids.shape[1]
-        self._keep = (inp, scores, ids, out, lse, lse_nc, cmass, kl_row, loss, teacher)
-        self.args_score = (Lp, _ptr(inp.q_idx), _ptr(inp.k_idx), _ptr(inp.weights), _dtype(inp.q_idx),
-                           Hi, Di, ctypes.c_float(inp.idx_scale), _ptr(scores),
-                           ctypes.c_int64(scores.stride(0)), st)
-        self.args_topk = (Lp, _ptr(scores), ctypes.c_int64(scores.stride(0)), int(topk), _ptr(ids), st)
+        self._keep = (inp, scores, ids, out, lse, lse_nc, cmass, kl_row, loss, teacher, sel)
+        if scores is not None:
+            self.args_score = (Lp, _ptr(inp.q_idx), _ptr(inp.k_idx), _ptr(inp.weights), _dtype(inp.q_idx),
+                               Hi, Di, ctypes.c_float(inp.idx_scale), _ptr(scores),
+                               ctypes.c_int64(scores.stride(0)), st)
+            self.args_topk = (Lp, _ptr(scores), ctypes.c_int64(scores.stride(0)), int(topk), _ptr(ids), st)
+        if sel is not None:   # fused score + top-k; the teacher/KL reads the selected scores
+            self.args_fused = (Lp, _ptr(inp.q_idx), _ptr(inp.k_idx), _ptr(inp.weights), _dtype(inp.q_idx),
+                               Hi, Di, ctypes.c_float(inp.idx_scale), int(topk), _ptr(ids), _ptr(sel), None, st)
+        tkl_scores = sel if sel is not None else scores
         self.args_attn = (Lp, _ptr(inp.q), _ptr(inp.kv), _ptr(inp.ckv), _ptr(inp.sink), _ptr(ids), k_eff_,
                           int(window), _dtype(inp.q), H, D, ctypes.c_float(inp.scale), _ptr(out), _ptr(lse),
                           _ptr(lse_nc), _ptr(cmass) if cmass is not None else None, st)
-        self.args_tkl = (Lp, 1 if sparse_loss else 0, _ptr(scores), ctypes.c_int64(scores.stride(0)),
-                         _ptr(ids), k_eff_, _ptr(cmass) if cmass is not None else None, _ptr(inp.q),
+        self.args_tkl = (Lp, 1 if sparse_loss else 0, _ptr(tkl_scores), ctypes.c_int64(tkl_scores.stride(0)),
+                         1 if sel is not None else 0, _ptr(ids), k_eff_, _ptr(cmass) if cmass is not None else None, _ptr(inp.q),
                          _ptr(inp.ckv), _ptr(lse_nc), _dtype(inp.q), H, D, ctypes.c_float(inp.scale), 0,
                          _ptr(teacher) if teacher is not None else None,
                          ctypes.c_int64(teacher.stride(0) if teacher is not None else 0),
@@ -316,6 +353,9 @@ class Prepared:
 
     def csa_topk(self):
         _check(self._lib.csa_topk(*self.args_topk))
+
+    def csa_indexer_topk(self):
+        _check(self._lib.csa_indexer_topk(*self.args_fused))
 
     def csa_sparse_attn_fwd(self):
         _check(self._lib.csa_sparse_attn_fwd(*self.args_attn))

@@ -128,6 +128,29 @@ csa_status_t csa_topk(const csa_layout_t *L, const float *scores, int64_t ld_sco
                       int32_t topk, int32_t *ids, void *stream);
 
 /*
+ * csa_indexer_topk -- csa_indexer_score and csa_topk in one pass that never stores the
+ * [T, max_seqlen_k] score matrix (the per-indexer-head and per-row score tensors are the
+ * memory cost the pages point at: [I5776] review comment on the unfused path).  Each
+ * 16-token block's score rows are built in on-chip memory and selected there.
+ *   ids [T, k_eff] int32: exactly csa_topk's ids of csa_indexer_score's scores (same
+ *       arithmetic, same lowest-index tie rule), k_eff = min(topk, max_seqlen_k);
+ *   sel_scores [T, k_eff] fp32: scores[t, ids[t,j] - cu_k[s]] at every valid slot, -inf
+ *       at -1 slots -- what the sparse-loss predictor reads (pass it to
+ *       csa_indexer_teacher_kl / csa_indexer_loss_bwd with scores_selected = 1);
+ *   row_lse [T] fp32 or NULL: log sum_{j < n_valid(t)} exp(scores[t, j]) (-inf when
+ *       n_valid(t) = 0), the dense-mode predictor's normaliser.
+ * Inputs as csa_indexer_score.  Supported: dt = CSA_BF16 with (Hi, Di) in {(8, 64),
+ * (16, 64), (4, 128), (8, 128)}, max_seqlen_k <= 2048 (512 for Di = 128), and the q rows
+ * of two 16-token blocks plus 16 score rows of 64 * (ceil(max_seqlen_k / 64) + 1) floats
+ * within the 160 KiB of LDS of a compute unit (for (16, 64): max_seqlen_k <= 1024);
+ * other shapes return CSA_ERR_UNSUPPORTED (use the two calls).
+ */
+csa_status_t csa_indexer_topk(const csa_layout_t *L, const void *q_idx, const void *k_idx,
+                              const float *weights, csa_dtype_t dt, int32_t Hi, int32_t Di,
+                              float idx_scale, int32_t topk, int32_t *ids, float *sel_scores,
+                              float *row_lse, void *stream);
+
+/*
  * csa_sparse_attn_fwd -- sliding-window + top-k compressed attention with a sink.
  * For query row t of segment s and head h ([I5776] "Paper reference", Z_h equation;
  * csa.py sparse-attention excerpt: window ids concatenated with the top-k ids, the
@@ -169,6 +192,8 @@ csa_status_t csa_sparse_attn_fwd(const csa_layout_t *L, const void *q, const voi
  *   q[t,h,:] . ckv[cu_k[s]+j,:] recomputed here for every j < n_valid(t).
  * Predictor p = softmax of scores[t, .] over C (sparse: the scores at the local columns
  * ids - cu_k[s]; dense: columns 0..n_valid(t)-1) ([I5776], dsa_kernels.py excerpt).
+ * scores_selected != 0 (sparse mode only): `scores` is [T, ld_scores >= k_eff], slot j
+ * holding the score of ids[t, j] (sel_scores of csa_indexer_topk).
  *   kl_row[t] = sum_{j in C} teacher_j * (log(teacher_j + 1e-10) - log(p_j + 1e-10))
  *   ([I5776], dsa.py excerpt; review comment "KL numerical contract"); 0 if n_valid(t)=0.
  *   loss[0] = sum_t kl_row[t] / total_q  (every physical row is in the divisor), or the
@@ -186,7 +211,7 @@ csa_status_t csa_sparse_attn_fwd(const csa_layout_t *L, const void *q, const voi
  */
 csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss,
                                     const float *scores, int64_t ld_scores,
-                                    const int32_t *ids, int32_t k_eff, const float *cmass,
+                                    int32_t scores_selected, const int32_t *ids, int32_t k_eff, const float *cmass,
                                     const void *q, const void *ckv, const float *lse_nc,
                                     csa_dtype_t dt, int32_t H, int32_t D, float softmax_scale,
                                     int32_t per_token_loss, float *teacher, int64_t ld_teacher,
@@ -209,7 +234,9 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss,
  *   dk_idx[cu_k[s]+j,:] = sum_{t in s} sum_h g_tj ws a_thj q_idx[t,h,:]
  * Arguments:
  *   q_idx [T, Hi, Di], k_idx [T_k, Di] (dtype dt);  weights [T, Hi] fp32;
- *   scores [T, ld_scores] fp32 (the forward's);  sparse: ids [T, k_eff] int32 and
+ *   scores [T, ld_scores] fp32 (the forward's; sparse mode with scores_selected != 0:
+ *   [T, ld_scores >= k_eff] slot-aligned with ids, as csa_indexer_topk writes them);
+ *   sparse: ids [T, k_eff] int32 and
  *   teacher [T, ld_teacher >= k_eff] (slot-aligned with ids); dense: ids may be NULL and
  *   teacher [T, ld_teacher >= max_seqlen_k] (column j for j < n_valid);
  *   grad_scores: workspace [T, ld_grad >= max_seqlen_k] fp32, overwritten with g;
@@ -225,7 +252,8 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss,
 csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss,
                                   const void *q_idx, const void *k_idx, const float *weights,
                                   csa_dtype_t dt, int32_t Hi, int32_t Di, float idx_scale,
-                                  const float *scores, int64_t ld_scores, const int32_t *ids,
+                                  const float *scores, int64_t ld_scores, int32_t scores_selected,
+                                  const int32_t *ids,
                                   int32_t k_eff, const float *teacher, int64_t ld_teacher,
                                   float grad_loss, int32_t per_token_loss, float *grad_scores,
                                   int64_t ld_grad, float *dq_idx, float *dweights, float *dk_idx,

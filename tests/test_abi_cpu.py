@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) == {"csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
                           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd",
-                          "csa_indexer_loss_bwd_workspace", "csa_cp_plan"}
+                          "csa_indexer_loss_bwd_workspace", "csa_cp_plan", "csa_indexer_topk"}
     from deepseek_v4_csa_amd import ops
     assert set(ops.EXPORTS) == set(names)
     for n in names:
@@ -72,35 +72,53 @@ def test_argument_misuse_is_rejected(lib):
                                    FAKE, FAKE, FAKE, None, None) == 2            # D = 96
     assert lib.csa_sparse_attn_fwd(B(L), FAKE, FAKE, FAKE, FAKE, FAKE, 32, 8, 1, 4, 64, 0.1,
                                    FAKE, FAKE, FAKE, None, None) == 1            # k_eff > max_seqlen_k
-    assert lib.csa_indexer_teacher_kl(B(L), 1, FAKE, 16, None, 4, FAKE, None, None, None, 1, 4, 64,
+    assert lib.csa_indexer_teacher_kl(B(L), 1, FAKE, 16, 0, None, 4, FAKE, None, None, None, 1, 4, 64,
                                       0.1, 0, None, 0, FAKE, FAKE, None) == 1    # sparse without ids
-    assert lib.csa_indexer_teacher_kl(B(L), 0, FAKE, 16, None, 0, None, FAKE, FAKE, FAKE, 0, 4, 64,
+    assert lib.csa_indexer_teacher_kl(B(L), 0, FAKE, 16, 1, None, 0, None, FAKE, FAKE, FAKE, 1, 4, 64,
+                                      0.1, 0, None, 0, FAKE, FAKE, None) == 1    # dense + selected
+    assert "selected" in lib.csa_last_error().decode()
+    assert lib.csa_indexer_teacher_kl(B(L), 1, FAKE, 3, 1, FAKE, 4, FAKE, None, None, None, 1, 4, 64,
+                                      0.1, 0, None, 0, FAKE, FAKE, None) == 1    # selected ld < k_eff
+    assert lib.csa_indexer_teacher_kl(B(L), 0, FAKE, 16, 0, None, 0, None, FAKE, FAKE, FAKE, 0, 4, 64,
                                       0.1, 0, None, 0, FAKE, FAKE, None) == 2    # dense fp32
     assert "dense" in lib.csa_last_error().decode()
     bwd = lib.csa_indexer_loss_bwd
-    args = [B(L), 1, FAKE, FAKE, FAKE, 1, 16, 64, 0.1, FAKE, 16, FAKE, 4, FAKE, 4, 1.0, 0, FAKE, 16,
+    args = [B(L), 1, FAKE, FAKE, FAKE, 1, 16, 64, 0.1, FAKE, 16, 0, FAKE, 4, FAKE, 4, 1.0, 0, FAKE, 16,
             FAKE, FAKE, FAKE, FAKE, 0, None]
-    a = list(args); a[11] = None
+    a = list(args); a[12] = None
     assert bwd(*a) == 1                                                            # sparse without ids
-    a = list(args); a[14] = 3
+    a = list(args); a[15] = 3
     assert bwd(*a) == 1                                                            # ld_teacher < k_eff
-    a = list(args); a[18] = 8
+    a = list(args); a[19] = 8
     assert bwd(*a) == 1                                                            # ld_grad < max_seqlen_k
     a = list(args); a[7] = 96
     assert bwd(*a) == 2                                                            # Di = 96
     a = list(args); a[5] = 0
     assert bwd(*a) == 2                                                            # fp32
-    a = list(args); a[19] = None
+    a = list(args); a[20] = None
     assert bwd(*a) == 1                                                            # null dq
+    a = list(args); a[1] = 0; a[11] = 1
+    assert bwd(*a) == 1                                                            # dense + selected
+    a = list(args); a[10] = 3; a[11] = 1
+    assert bwd(*a) == 1                                                            # selected ld < k_eff
     # a long segment splits dk over token chunks: the workspace must hold the partials
     Lb = _layout(ops, total_q=4096, max_seqlen_q=4096, total_k=1024, max_seqlen_k=1024)
     need = lib.csa_indexer_loss_bwd_workspace(B(Lb), 16, 64)
     assert need == 64 * 1024 * 64 * 4
-    a = list(args); a[0] = B(Lb); a[10] = a[18] = 1024; a[23] = need - 1
+    a = list(args); a[0] = B(Lb); a[10] = a[19] = 1024; a[24] = need - 1
     assert bwd(*a) == 1                                                            # workspace too small
     assert "workspace" in lib.csa_last_error().decode()
-    a[22] = None; a[23] = need
+    a[23] = None; a[24] = need
     assert bwd(*a) == 1                                                            # workspace NULL
+    # fused score + top-k
+    fz = lib.csa_indexer_topk
+    assert fz(B(L), FAKE, FAKE, FAKE, 1, 16, 64, 0.1, 0, FAKE, FAKE, None, None) == 1   # topk < 1
+    assert fz(B(L), FAKE, FAKE, FAKE, 1, 16, 64, 0.1, 4, FAKE, None, None, None) == 1   # null sel
+    assert fz(B(L), FAKE, FAKE, FAKE, 1, 32, 64, 0.1, 4, FAKE, FAKE, None, None) == 2   # Hi = 32
+    assert fz(B(L), FAKE, FAKE, FAKE, 0, 16, 64, 0.1, 4, FAKE, FAKE, None, None) == 2   # fp32
+    Lw = _layout(ops, total_q=8192, max_seqlen_q=8192, total_k=2048, max_seqlen_k=2048)
+    assert fz(B(Lw), FAKE, FAKE, FAKE, 1, 16, 64, 0.1, 4, FAKE, FAKE, None, None) == 2  # rows too long
+    assert "fused" in lib.csa_last_error().decode()
 
 
 def test_backward_workspace_query(lib):
