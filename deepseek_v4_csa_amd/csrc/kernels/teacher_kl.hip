@@ -59,17 +59,12 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + w;
   if (t >= T) return;
-  const RowGeo geo = row_geo(L, t);
   const int32_t *idr = ids + (int64_t)t * k_eff;
   const float *cm = cmass + (int64_t)t * k_eff;
   const float *sr = scores + (int64_t)t * ld;
   float *te = teacher ? teacher + (int64_t)t * ldt : nullptr;
-  if (loss_row_empty(L, geo, t)) {
-    if (te)
-      for (int j = lane; j < k_eff; j += 64) te[j] = 0.f;
-    if (lane == 0) kl_row[t] = 0.f;
-    return;
-  }
+  // every load that needs only the row index goes out first (ids, cmass and, in place,
+  // the selected scores); the segment search and the score gather follow
   int id[SPL];
   float c[SPL], sc[SPL];
 #pragma unroll
@@ -77,13 +72,21 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
     const int j = v * 64 + lane;
     id[v] = j < k_eff ? idr[j] : -1;
     c[v] = j < k_eff ? cm[j] : 0.f;
+    sc[v] = (selected && j < k_eff) ? sr[j] : 0.f;
+  }
+  const RowGeo geo = row_geo(L, t);
+  if (loss_row_empty(L, geo, t)) {
+    if (te)
+      for (int j = lane; j < k_eff; j += 64) te[j] = 0.f;
+    if (lane == 0) kl_row[t] = 0.f;
+    return;
   }
   float mx = -__builtin_inff();
 #pragma unroll
   for (int v = 0; v < SPL; ++v) {
-    // the score of slot j: gathered from the full row, or read in place (selected scores)
-    const int col = selected ? v * 64 + lane : id[v] - geo.k_base;
-    sc[v] = id[v] >= 0 ? sr[col] : -__builtin_inff();
+    // the score of slot j: read in place (selected scores) or gathered from the full row
+    if (!selected) sc[v] = id[v] >= 0 ? sr[id[v] - geo.k_base] : 0.f;
+    sc[v] = id[v] >= 0 ? sc[v] : -__builtin_inff();
     mx = fmaxf(mx, sc[v]);
   }
   double ms = 0.0;
@@ -293,7 +296,16 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float *__restri
                                                            int per_token, float *__restrict__ loss) {
   __shared__ double part[16];
   double s = 0.0;
-  for (int i = threadIdx.x; i < T; i += 1024) s += (double)kl_row[i];
+  // eight loads in flight per thread, then added in index order (a fixed order per T)
+  int i = threadIdx.x;
+  for (; i + 7 * 1024 < T; i += 8 * 1024) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = kl_row[i + u * 1024];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += (double)v[u];
+  }
+  for (; i < T; i += 1024) s += (double)kl_row[i];
   s = wave_sum_f64_dpp(s);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
