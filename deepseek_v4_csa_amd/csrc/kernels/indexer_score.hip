@@ -592,6 +592,144 @@ hipError_t launch_indexer_topk(const LaunchLayout &LL, const void *q_idx, const 
   return hipErrorInvalidValue;
 }
 
+// ============================================================================
+// Head-grouped variant for long q_idx rows (bf16, Hi * Di * 2 above what the paired-block
+// kernel stages).  One workgroup (8 waves) = 64 tokens x 128 keys; wave w = 16 tokens
+// (w % 4) x 64 keys (w / 4), its key fragments in registers for the whole head loop.  The
+// q rows are staged in LDS one head group at a time (HG heads = 512 bytes of each token
+// row, 32 KiB per group, double-buffered, buffer->LDS loads of 1 KiB = two rows each),
+// chunk q of token row r at slot q ^ (r % 16) so the 16 lanes of an A-operand read hit 16
+// bank groups; fp32(w * s_idx) of every head is staged once.  Per head: Di/32 x 4
+// MFMAs, then the ReLU x weight accumulate.  Each staged byte of q feeds 128 keys.
+// ============================================================================
+constexpr int HGK_TOK = 64;
+constexpr int HGK_KEYS = 128;
+constexpr int HGK_WAVES = 8;
+
+template <int DI>
+__global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(4))) void indexer_score_hg_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
+    const float *__restrict__ weights, int Hi, float idx_scale, float *__restrict__ scores, int64_t ld,
+    int max_sk, int total_q, int nqb) {
+  constexpr int HG = 256 / DI;        // heads per staged group
+  constexpr int PB = HG * DI * 2;     // bytes of a token row per group (512)
+  constexpr int CPP = PB / 16;        // 16-byte chunks per staged row
+  constexpr int NCD = DI / 32;
+  constexpr int NTHR = 64 * HGK_WAVES;
+  static_assert(PB == 512 && CPP >= 16, "512-byte staged rows");
+  __shared__ __attribute__((aligned(16))) u32x4 qs[2][HGK_TOK * CPP];
+  extern __shared__ __attribute__((aligned(16))) float wsl[];   // [Hi][HGK_TOK]
+
+  const int seg = blockIdx.x / nqb;
+  const int qb = blockIdx.x - seg * nqb;
+  const int q_start = __ldg(L.cu_q + seg);
+  const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
+  const int t0 = qb * HGK_TOK;
+  if (t0 >= q_len) return;
+  const int k_base = __ldg(L.cu_k + seg);
+  const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
+  const int off = seg_offset(L, seg, q_len, s_k);
+  const int j0 = blockIdx.y * HGK_KEYS;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tw = w & 3, jw = j0 + 64 * (w >> 2);
+  const int nv_last = n_valid_of(min(t0 + HGK_TOK, q_len) - 1, off, L.ratio, s_k);
+
+  if (j0 >= nv_last) {   // the whole tile is above the causal limit
+    for (int e = tid; e < HGK_TOK * HGK_KEYS; e += NTHR) {
+      const int tt = e / HGK_KEYS, j = j0 + (e - tt * HGK_KEYS);
+      if (t0 + tt < q_len && j < max_sk) scores[(int64_t)(q_start + t0 + tt) * ld + j] = -__builtin_inff();
+    }
+    return;
+  }
+  const int64_t RB = (int64_t)Hi * DI * 2;   // bytes of one token's q_idx row
+  const int rows_left = min(HGK_TOK, total_q - (q_start + t0));
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(q_idx + (int64_t)(q_start + t0) * Hi * DI, (uint32_t)(rows_left * RB));
+  auto stage = [&](int grp, int buf) {   // 64 rows x 512 bytes: 32 instructions, 4 per wave
+#pragma unroll
+    for (int k = 0; k < 32 / HGK_WAVES; ++k) {
+      const int m = k * HGK_WAVES + w;
+      const int r = 2 * m + (lane >> 5), c = lane & 31;
+      dma16(rq, reinterpret_cast<char *>(qs[buf]) + (size_t)m * 1024,
+            (uint32_t)(r * RB + grp * PB + ((c ^ (r & 15)) << 4)));
+    }
+  };
+  stage(0, 0);
+  // key fragments (B operand: lane column r16 = key, piece 4c+g); keys past the segment
+  // are clamped to its last key (their scores are masked)
+  u32x4 kb[4][NCD];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int j = min(jw + 16 * n + r16, s_k - 1);
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(k_idx + (int64_t)(k_base + j) * DI) + g;
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) kb[n][c] = kp[4 * c];
+  }
+  for (int e = tid; e < Hi * HGK_TOK; e += NTHR) {
+    const int tt = e / Hi, h = e - tt * Hi;
+    const int t = t0 + tt;
+    wsl[h * HGK_TOK + tt] = t < q_len ? weights[(int64_t)(q_start + t) * Hi + h] * idx_scale : 0.f;
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ngrp = Hi / HG;
+  const int rrow = (tw * 16 + r16) * PB;
+  for (int grp = 0; grp < ngrp; ++grp) {
+    wait_vmcnt<0>();
+    __syncthreads();   // group grp staged (and, first time, the weights)
+    if (grp + 1 < ngrp) stage(grp + 1, (grp + 1) & 1);   // its buffer was last read at grp - 1
+    const char *qb = reinterpret_cast<const char *>(qs[grp & 1]) + rrow;
+#pragma unroll
+    for (int hl = 0; hl < HG; ++hl) {
+      u32x4 qa[NCD];
+#pragma unroll
+      for (int c = 0; c < NCD; ++c)
+        qa[c] = *reinterpret_cast<const u32x4 *>(qb + (((hl * (DI / 8) + 4 * c + g) ^ r16) << 4));
+      f32x4 d[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) d[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NCD; ++c)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) d[n] = mfma16x16x32(qa[c], kb[n][c], d[n]);
+      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsl + (grp * HG + hl) * HGK_TOK + tw * 16 + 4 * g);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[n][i] = fmaf(wv[i], relu_bits(d[n][i]), acc[n][i]);
+    }
+  }
+  // lane (token tw*16 + 4g + i, key jw + 16n + r16)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + tw * 16 + 4 * g + i;
+    if (t >= q_len) continue;
+    const int nv = n_valid_of(t, off, L.ratio, s_k);
+    float *dst = scores + (int64_t)(q_start + t) * ld;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int j = jw + 16 * n + r16;
+      if (j < max_sk) dst[j] = j < nv ? acc[n][i] : -__builtin_inff();
+    }
+  }
+}
+
+template <int DI>
+static hipError_t launch_hg(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+                            const float *weights, int Hi, float idx_scale, float *scores, int64_t ld,
+                            hipStream_t st) {
+  const int nqb = (LL.max_seqlen_q + HGK_TOK - 1) / HGK_TOK;
+  const int nkb = (LL.max_seqlen_k + HGK_KEYS - 1) / HGK_KEYS;
+  dim3 grid((unsigned)(LL.num_seqs * nqb), (unsigned)nkb);
+  const size_t lds = (size_t)Hi * HGK_TOK * sizeof(float);
+  hipLaunchKernelGGL((indexer_score_hg_kernel<DI>), grid, dim3(64 * HGK_WAVES), lds, st, LL.dev,
+                     static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx), weights, Hi,
+                     idx_scale, scores, ld, LL.max_seqlen_k, LL.total_q, nqb);
+  return hipGetLastError();
+}
+
 template <typename IN, int DI>
 static hipError_t launch_t(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
                            const float *weights, int Hi, float idx_scale, float *scores,
@@ -615,6 +753,11 @@ hipError_t launch_indexer_score(const LaunchLayout &LL, const void *q_idx, const
     if (Di == 64 && Hi == 32) return launch_lds<64, 32>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
     if (Di == 128 && Hi == 4) return launch_lds<128, 4>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
     if (Di == 128 && Hi == 8) return launch_lds<128, 8>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
+    // long rows: head groups staged in LDS (64 tokens x 512 bytes per group)
+    if (Di == 64 && Hi >= 64 && Hi % 4 == 0)
+      return launch_hg<64>(LL, q_idx, k_idx, weights, Hi, idx_scale, scores, ld, st);
+    if (Di == 128 && Hi >= 16 && Hi % 2 == 0)
+      return launch_hg<128>(LL, q_idx, k_idx, weights, Hi, idx_scale, scores, ld, st);
   }
   if (bf16) {
     switch (Di) {
