@@ -933,7 +933,9 @@ static hipError_t launch_dma(const LaunchLayout &LL, const void *q, const void *
   if (hgc == 1 && window > 0) {
     // persistent: two workgroups of 4 waves per CU, each wave walking a strided list of rows
     int dev = 0, ncu = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+      ncu = 256;   // the query failed: assume the MI355X's count
     const int64_t need = (LL.total_q + 3) / 4;
     dim3 pgrid((unsigned)std::min<int64_t>(need, 2 * (int64_t)ncu));
 #define CSA_PIPE_CASE(K)                                                                             \

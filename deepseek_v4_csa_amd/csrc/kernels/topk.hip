@@ -22,33 +22,45 @@ namespace csa {
 constexpr int TK_THREADS = 256;
 constexpr int TK_WAVES = TK_THREADS / 64;
 
-// exclusive prefix count of `flag` over the block in thread order; returns the rank
-// and writes the block total.  Uses two LDS slots per wave and two barriers.
-__device__ __forceinline__ int block_rank(bool flag, int *wsum, int &total) {
+// Exclusive prefix sums over the block (thread order) of two counts at once, with
+// their totals; two barriers.  wsum: 2 * TK_WAVES words of LDS.
+__device__ __forceinline__ void block_scan2(int a, int b, int *wsum, int &pa, int &pb, int &ta, int &tb) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint64_t m = __ballot(flag);
-  const int in_wave = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-  if (lane == 0) wsum[w] = __popcll(m);
+  int ia = a, ib = b;   // inclusive scans within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ya = __shfl_up(ia, o, 64), yb = __shfl_up(ib, o, 64);
+    if (lane >= o) { ia += ya; ib += yb; }
+  }
+  if (lane == 63) { wsum[w] = ia; wsum[TK_WAVES + w] = ib; }
   __syncthreads();
-  int before = 0;
-  total = 0;
+  int ba = 0, bb = 0;
+  ta = tb = 0;
 #pragma unroll
   for (int i = 0; i < TK_WAVES; ++i) {
-    const int c = wsum[i];
-    before += i < w ? c : 0;
-    total += c;
+    const int ca = wsum[i], cb = wsum[TK_WAVES + i];
+    ba += i < w ? ca : 0;
+    bb += i < w ? cb : 0;
+    ta += ca;
+    tb += cb;
   }
   __syncthreads();
-  return before + in_wave;
+  pa = ba + ia - a;
+  pb = bb + ib - b;
 }
 
+// One workgroup per row (rows above 4096 keys); thread i owns the VPT consecutive keys
+// j = i*VPT + v, so index order is thread order then v.  The radix passes stop as soon as
+// the threshold bin is taken whole; the compaction is one block scan of the per-thread
+// counts of keys above the threshold and of ties, then every thread writes its own
+// picks in index order.
 template <int VPT>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const float *__restrict__ scores,
                                                           int64_t ld, int k_eff, int32_t *__restrict__ ids) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t red[2 * TK_WAVES];
-  __shared__ int wsum[TK_WAVES];
-  __shared__ uint32_t sel_digit, sel_above;
+  __shared__ int wsum[2 * TK_WAVES];
+  __shared__ uint32_t sel_digit, sel_above, sel_cnt;
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -59,14 +71,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     for (int j = tid; j < k_eff; j += TK_THREADS) out[j] = j < n ? g.k_base + j : -1;
     return;
   }
-  const float *row = scores + (int64_t)t * ld;
+  const float *row = scores + (int64_t)t * ld + (int64_t)tid * VPT;
+  const int j0 = tid * VPT;
 
   uint32_t key[VPT];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const int j = v * TK_THREADS + tid;
-    key[v] = j < n ? ordered_key(row[j]) : 0u;
+    const int j = j0 + v;
+    key[v] = j < n ? ordered_key(row[v]) : 0u;
     if (j < n) { kmin = min(kmin, key[v]); kmax = max(kmax, key[v]); }
   }
 #pragma unroll
@@ -86,6 +99,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   uint32_t thr = 0;       // known high bits of the threshold (relative key)
   int need = k_eff;       // elements still to take among those matching `thr`
   int cur = range ? 32 - __builtin_clz(range) : 0;   // bits above `cur` are all equal
+  bool whole = false;     // the last threshold bin was taken whole
   while (cur > 0) {
     const int width = cur < 8 ? cur : 8;
     const int sh = cur - width;
@@ -93,8 +107,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-      const int j = v * TK_THREADS + tid;
-      const bool in_play = j < n && (cur >= 32 || (key[v] >> cur) == thr);
+      const bool in_play = j0 + v < n && (cur >= 32 || (key[v] >> cur) == thr);
       if (in_play) atomicAdd(&hist[(key[v] >> sh) & ((1u << width) - 1u)], 1u);
     }
     __syncthreads();
@@ -116,32 +129,42 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
         else { above += c1; d = 0; }
         sel_digit = 4 * lane + d;
         sel_above = above;
+        sel_cnt = d == 3 ? c3 : d == 2 ? c2 : d == 1 ? c1 : c0;
       }
     }
     __syncthreads();
     thr = (thr << width) | sel_digit;
     need -= (int)sel_above;
     cur = sh;
+    const bool done = (uint32_t)need == sel_cnt;
     __syncthreads();
+    if (done) { whole = true; break; }
   }
 
-  // compaction in index order: key > thr, or key == thr among the first `need` ties
-  int base = 0, tie_base = 0;
+  // compaction in index order: keys whose prefix (bits >= cur) is above thr -- or equal to
+  // it when the bin was taken whole -- and the first `need` ties otherwise
+  int ngt = 0, neq = 0;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    if (v * TK_THREADS >= n) break;  // block-uniform
-    const int j = v * TK_THREADS + tid;
-    const bool valid = j < n;
-    const bool gt = valid && key[v] > thr;
-    const bool eq = valid && key[v] == thr;
-    int eq_total;
-    const int eq_rank = block_rank(eq, wsum, eq_total);
-    const bool sel = gt || (eq && tie_base + eq_rank < need);
-    int sel_total;
-    const int pos = block_rank(sel, wsum, sel_total);
-    if (sel && base + pos < k_eff) out[base + pos] = g.k_base + j;
-    base += sel_total;
-    tie_base += eq_total;
+    const bool valid = j0 + v < n;
+    const uint32_t kp = key[v] >> cur;
+    ngt += (valid && (kp > thr || (whole && kp == thr))) ? 1 : 0;
+    neq += (valid && !whole && kp == thr) ? 1 : 0;
+  }
+  int gt_before, eq_before, gt_total, eq_total;
+  block_scan2(ngt, neq, wsum, gt_before, eq_before, gt_total, eq_total);
+  int pos = gt_before + min(eq_before, need);
+  int eq_rank = eq_before;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const bool valid = j0 + v < n;
+    const uint32_t kp = key[v] >> cur;
+    const bool gt = valid && (kp > thr || (whole && kp == thr));
+    const bool eq = valid && !whole && kp == thr;
+    const bool sel = gt || (eq && eq_rank < need);
+    if (sel && pos < k_eff) out[pos] = g.k_base + j0 + v;
+    pos += sel ? 1 : 0;
+    eq_rank += eq ? 1 : 0;
   }
 }
 
