@@ -49,6 +49,15 @@ __device__ __forceinline__ void split_bf16x4(const float (&x)[4], uint2 &hi, uin
   lo = uint2{pack2_bf16(r0, r1), pack2_bf16(r2, r3)};
 }
 
+// the same for eight values, as the K = 32 MFMA operands
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
+  uint2 h0, l0, h1, l1;
+  split_bf16x4({x[0], x[1], x[2], x[3]}, h0, l0);
+  split_bf16x4({x[4], x[5], x[6], x[7]}, h1, l1);
+  hi = u32x4{h0.x, h0.y, h1.x, h1.y};
+  lo = u32x4{l0.x, l0.y, l1.x, l1.y};
+}
+
 // ---------------------------------------------------------------- 1. score gradients
 // SPL support slots per lane: sparse -> k_eff slots (slot j <-> ids[t, j]); dense ->
 // columns j < max_seqlen_k
@@ -259,42 +268,53 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
       }
       const char *kb = kt_lds[kt & 1];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float *gv = gcur[m];
-        // K row operand (rows 16m + r16) for D^T = K Q_h^T
-        u32x4 ka[NCD];
-        const int R = 16 * m + r16;
+      for (int mp = 0; mp < 2; ++mp) {   // 32 keys: sub-tiles m = 2mp, 2mp + 1
+        // K row operands (rows 16m + r16) for D^T = K Q_h^T
+        u32x4 ka[2][NCD];
 #pragma unroll
-        for (int c = 0; c < NCD; ++c)
-          ka[c] = *reinterpret_cast<const u32x4 *>(kb + R * ROWB + 16 * ((4 * c + g) ^ row_swz<DI>(R)));
-        // K^T operand (dims x keys 16m + 4g .. +3) by the transposing read, per dim tile
-        uint2 kt_op[NDT];
-        {
-          const int rr = 16 * m + 4 * g + (r16 >> 2);
+        for (int s = 0; s < 2; ++s) {
+          const int R = 16 * (2 * mp + s) + r16;
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const int piece = 2 * dt + ((r16 & 3) >> 1);
-            kt_op[dt] = lds_read_tr16(kb + rr * ROWB + 16 * (piece ^ row_swz<DI>(rr)) + 8 * (r16 & 1));
+          for (int c = 0; c < NCD; ++c)
+            ka[s][c] = *reinterpret_cast<const u32x4 *>(kb + R * ROWB + 16 * ((4 * c + g) ^ row_swz<DI>(R)));
+        }
+        // K^T operand of U^T += K^T E over 32 keys: MFMA k index 8g+e <-> key
+        // 16m + 4g + e (e < 4, m = 2mp) or 16(m+1) + 4g + e-4 (e >= 4), two transposing
+        // reads per dim tile
+        u32x4 kt_op[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int piece = 2 * dt + ((r16 & 3) >> 1);
+          uint2 h2[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int rr = 16 * (2 * mp + s) + 4 * g + (r16 >> 2);
+            h2[s] = lds_read_tr16(kb + rr * ROWB + 16 * (piece ^ row_swz<DI>(rr)) + 8 * (r16 & 1));
           }
+          kt_op[dt] = u32x4{h2[0].x, h2[0].y, h2[1].x, h2[1].y};
         }
 #pragma unroll
         for (int k = 0; k < HPW; ++k) {
           const int h = pass * 4 * HPW + k * 4 + w;
-          f32x4 d = {0.f, 0.f, 0.f, 0.f};
+          float e[8];
 #pragma unroll
-          for (int c = 0; c < NCD; ++c) d = mfma16x16x32(ka[c], a_frag(h, c), d);
-          float e[4];
+          for (int s = 0; s < 2; ++s) {
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            e[i] = d[i] > 0.f ? gv[i] : 0.f;
-            dwa[k] = fmaf(gv[i], fmaxf(d[i], 0.f), dwa[k]);
+            for (int c = 0; c < NCD; ++c) d = mfma16x16x32(ka[s][c], a_frag(h, c), d);
+            const float *gv = gcur[2 * mp + s];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              e[4 * s + i] = d[i] > 0.f ? gv[i] : 0.f;
+              dwa[k] = fmaf(gv[i], fmaxf(d[i], 0.f), dwa[k]);
+            }
           }
-          uint2 ehi, elo;
-          split_bf16x4(e, ehi, elo);
+          u32x4 ehi, elo;
+          split_bf16x8(e, ehi, elo);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            u[k][dt] = mfma16x16x16(kt_op[dt], ehi, u[k][dt]);
-            u[k][dt] = mfma16x16x16(kt_op[dt], elo, u[k][dt]);
+            u[k][dt] = mfma16x16x32(kt_op[dt], ehi, u[k][dt]);
+            u[k][dt] = mfma16x16x32(kt_op[dt], elo, u[k][dt]);
           }
         }
       }
