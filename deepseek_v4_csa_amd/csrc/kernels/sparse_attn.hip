@@ -147,8 +147,11 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
     float *__restrict__ cmass) {
   using C = AttnCfg<IN, D>;
   constexpr int NT = 64 * HG;
-  __shared__ __attribute__((aligned(16))) char rows[ATT_CHUNK * C::RS];
-  __shared__ int row_ok[ATT_CHUNK];
+  constexpr int PPT = (ATT_CHUNK * C::PIECES + NT - 1) / NT;   // 16-byte pieces per thread
+  // dynamic LDS: two row buffers, then the query's ids
+  extern __shared__ __attribute__((aligned(16))) char att_dyn[];
+  int *ids_lds = reinterpret_cast<int *>(att_dyn + 2 * ATT_CHUNK * C::RS);
+  __shared__ int row_ok[2][ATT_CHUNK];
   __shared__ float cm_part[HG][ATT_CHUNK];
 
   const int t = blockIdx.x;
@@ -161,30 +164,50 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
   const int32_t *idrow = ids + (int64_t)t * k_eff;
   const int nwc = (nw + ATT_CHUNK - 1) / ATT_CHUNK;
   const int ncc = (k_eff + ATT_CHUNK - 1) / ATT_CHUNK;
+  for (int i = tid; i < k_eff; i += NT) ids_lds[i] = idrow[i];
 
   QFrag<IN, D> qf;
   qf.load(q + ((int64_t)t * H + (h_ok ? h : 0)) * D, g, h_ok);
 
-  // stage chunk `ci` (window chunks first, then compressed) into LDS
-  auto stage = [&](int ci) {
+  // chunk `ci` (window chunks first, then compressed) is staged through registers into LDS
+  // buffer ci & 1 while chunk ci - 1 is consumed from the other one, so each chunk costs one
+  // barrier; the loads are issued after the compute (issuing them before it costs occupancy
+  // for no gain on these shapes)
+  u32x4 stg[PPT];
+  bool stg_ok[PPT];
+  auto load_regs = [&](int ci) __attribute__((always_inline)) {
     const bool win = ci < nwc;
     const int s0 = (win ? ci : ci - nwc) * ATT_CHUNK;
-    for (int p = tid; p < ATT_CHUNK * C::PIECES; p += NT) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int p = tid + k * NT;
       const int r = p / C::PIECES, pc = p - r * C::PIECES;
       const int slot = s0 + r;
       const IN *src = nullptr;
-      if (win) {
-        if (slot < nw) src = kv + (int64_t)(w_lo + slot) * D;
-      } else if (slot < k_eff) {
-        const int id = idrow[slot];
-        if (id >= 0) src = ckv + (int64_t)id * D;
+      if (p < ATT_CHUNK * C::PIECES) {
+        if (win) {
+          if (slot < nw) src = kv + (int64_t)(w_lo + slot) * D;
+        } else if (slot < k_eff) {
+          const int id = ids_lds[slot];
+          if (id >= 0) src = ckv + (int64_t)id * D;
+        }
       }
-      u32x4 val = {0, 0, 0, 0};
-      if (src) val = reinterpret_cast<const u32x4 *>(src)[pc];
-      *reinterpret_cast<u32x4 *>(rows + r * C::RS + pc * 16) = val;
-      if (pc == 0) row_ok[r] = src != nullptr;
+      stg[k] = src ? reinterpret_cast<const u32x4 *>(src)[pc] : u32x4{0, 0, 0, 0};
+      stg_ok[k] = src != nullptr;
     }
   };
+  auto store_regs = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int p = tid + k * NT;
+      if (p < ATT_CHUNK * C::PIECES) {
+        const int r = p / C::PIECES, pc = p - r * C::PIECES;
+        *reinterpret_cast<u32x4 *>((att_dyn + buf * (ATT_CHUNK * C::RS)) + r * C::RS + pc * 16) = stg[k];
+        if (pc == 0) row_ok[buf][r] = stg_ok[k];
+      }
+    }
+  };
+  __syncthreads();   // ids in LDS
 
   // ---------------------------------------------------------------- pass 1: max / sum
   const float a2 = sink[h_ok ? h : 0] * LOG2E;
@@ -192,17 +215,22 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
   float l = (g == 0 && h_ok && a2 > -__builtin_inff()) ? 1.f : 0.f;
   float m_nc = m, l_nc = l;
   const int nch = nwc + ncc;
+  if (nch > 0) {
+    load_regs(0);
+    store_regs(0);
+  }
   for (int ci = 0; ci < nch; ++ci) {
     if (ci == nwc) { m_nc = m; l_nc = l; }
-    stage(ci);
-    __syncthreads();
+    __syncthreads();   // chunk ci in row buffer ci & 1; that buffer's previous readers are done
+    const char *rows = att_dyn + (ci & 1) * (ATT_CHUNK * C::RS);
+    const int *rok = row_ok[ci & 1];
     float s[8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const f32x4 st = s_tile<D>(rows, 16 * tau, qf, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = row_ok[16 * tau + 4 * g + i] && h_ok;
+        const bool ok = rok[16 * tau + 4 * g + i] && h_ok;
         s[4 * tau + i] = ok ? st[i] * scale_log2 : -__builtin_inff();
       }
     }
@@ -217,7 +245,10 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
       l = acc;
       m = mn;
     }
-    __syncthreads();
+    if (ci + 1 < nch) {
+      load_regs(ci + 1);
+      store_regs((ci + 1) & 1);
+    }
   }
   if (ncc == 0) { m_nc = m; l_nc = l; }
   // combine the 4 lane groups of each head
@@ -233,16 +264,22 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
 #pragma unroll
   for (int i = 0; i < C::NDT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool any = lse2 > -__builtin_inff();
+  __syncthreads();   // pass 1 is done with both buffers
+  if (nch > 0) {
+    load_regs(0);
+    store_regs(0);
+  }
   for (int ci = 0; ci < nch; ++ci) {
-    stage(ci);
-    __syncthreads();
+    __syncthreads();   // chunk ci in row buffer ci & 1; that buffer's previous readers are done
+    const char *rows = att_dyn + (ci & 1) * (ATT_CHUNK * C::RS);
+    const int *rok = row_ok[ci & 1];
     f32x4 p[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const f32x4 st = s_tile<D>(rows, 16 * tau, qf, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = row_ok[16 * tau + 4 * g + i] && h_ok && any;
+        const bool ok = rok[16 * tau + 4 * g + i] && h_ok && any;
         p[tau][i] = ok ? exp2f(st[i] * scale_log2 - lse2) : 0.f;
       }
     }
@@ -266,7 +303,10 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
         }
       }
     }
-    __syncthreads();
+    if (ci + 1 < nch) {
+      load_regs(ci + 1);
+      store_regs((ci + 1) & 1);
+    }
   }
 
   // ---------------------------------------------------------------- outputs
@@ -979,9 +1019,16 @@ static hipError_t launch_d(const LaunchLayout &LL, const void *q, const void *kv
   const float sl2 = scale * LOG2E;
   dim3 grid((unsigned)LL.total_q);
   const int hg = (H + 15) / 16;
+  const size_t dyn = 2 * (size_t)ATT_CHUNK * AttnCfg<IN, D>::RS + (size_t)k_eff * sizeof(int);
 #define CSA_ATT_CASE(G)                                                                           \
   if (hg <= G) {                                                                                  \
-    hipLaunchKernelGGL((sparse_attn_kernel<IN, D, G>), grid, dim3(64 * G), 0, st, LL.dev,         \
+    if (dyn > 65536) {                                                                            \
+      const hipError_t ea = hipFuncSetAttribute(                                                  \
+          reinterpret_cast<const void *>(sparse_attn_kernel<IN, D, G>),                          \
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);                                  \
+      if (ea != hipSuccess) return ea;                                                            \
+    }                                                                                             \
+    hipLaunchKernelGGL((sparse_attn_kernel<IN, D, G>), grid, dim3(64 * G), dyn, st, LL.dev,       \
                        static_cast<const IN *>(q), static_cast<const IN *>(kv),                   \
                        static_cast<const IN *>(ckv), sink, ids, k_eff, window, H, sl2,            \
                        static_cast<IN *>(out), lse, lse_nc, cmass);                               \
