@@ -251,10 +251,14 @@ namespace csa {
 // stored at piece position p ^ row_swz<D>(R).  With 64 LDS banks of 4 bytes (256 bytes
 // per bank row), this keeps conflict-free the row-operand reads (16 lanes = rows 0..15,
 // one piece each), the transposing reads (32 lanes = 8 rows x 2 pieces x 2 halves) and
-// the row-staging writes.
+// the row-staging writes.  Rows of 256*k bytes (D = 128, 256, 512) take all 16 values;
+// rows of 128 or 384 bytes (D = 64, 192), where consecutive rows already start half a
+// bank row apart, take the 8 values < 8, which also keeps p ^ swz inside a row of 24
+// pieces.  The pattern repeats every 16 rows.
 template <int D> __device__ __forceinline__ int row_swz(int r) {
-  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
-  else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  static_assert(D == 64 || D == 128 || D == 192 || D == 256 || D == 512, "row size");
+  if constexpr (D == 64 || D == 192) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  else return 2 * (r & 7) + ((r >> 3) & 1);
 }
 
 // ---------------------------------------------------------------- LDS DMA
@@ -265,9 +269,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, (int)voff, 0, 0, 0);
 }
-// s_waitcnt with only vmcnt constrained (expcnt 7 and lgkmcnt 15 = no wait); N <= 15
+// s_waitcnt with only vmcnt constrained (expcnt 7 and lgkmcnt 15 = no wait); the 6-bit
+// count is split over bits 3:0 and 15:14 of the immediate
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 15, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 }  // namespace csa

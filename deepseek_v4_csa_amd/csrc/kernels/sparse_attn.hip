@@ -330,6 +330,265 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
 }
 
 // ============================================================================
+// Workgroup variant (bf16; any H up to 16*HG; D = 64, 128, 192, 256 or 512; k_eff <= 4096).
+//
+// One workgroup per query row, wave w owning heads [16w, 16w+16), the same two passes as
+// the kernel above (exact per-head max and sum first, then P, O and cmass with lse
+// already final).  The gathered rows are staged 32 at a time into two LDS tiles by
+// direct buffer->LDS loads: the waves split the D/16 load instructions of a tile between
+// them, and the next tile's loads are issued right after the step's barrier, so they
+// stream in while the current tile is consumed.  Rows are stored with the XOR swizzle
+// of row_swz<D> (position = piece ^ swz(R)), so both operand reads are conflict-free:
+//   S^T = K Q^T     K operand: 16-byte LDS reads, piece 4c+g of row r16 for K-chunk c
+//   O^T += V^T P^T  V^T operand: transposing LDS reads of 4 rows x 16 features
+// Per-key sums over heads (cmass) are reduced across waves through LDS one step later,
+// behind the next barrier.
+// ============================================================================
+template <int D, int HG>
+__global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
+    const uint16_t *__restrict__ ckv, const float *__restrict__ sink,
+    const int32_t *__restrict__ ids, int k_eff, int window, int H, int total_q, int total_k,
+    float sl2, uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ lse_nc,
+    float *__restrict__ cmass) {
+  constexpr int NC = D / 32;          // MFMA K-chunks per row
+  constexpr int ROWB = D * 2;         // bytes per KV row
+  constexpr int PIECES = D / 8;       // 16-byte pieces per row
+  constexpr int NI = PIECES / 2;      // load instructions per 32-row tile (64 pieces each)
+  constexpr int NIW = (NI + HG - 1) / HG;   // of them issued by one wave
+  constexpr int TILE = 32 * ROWB;
+  constexpr int NT = 64 * HG;
+  constexpr int BDT = D >= 512 ? D / 128 : D / 32;   // d-tiles per batch of V^T reads
+  constexpr float NINF = -__builtin_inff();
+  extern __shared__ __attribute__((aligned(16))) char wg_dyn[];   // 2 tiles, then the ids
+  int *ids_l = reinterpret_cast<int *>(wg_dyn + 2 * TILE);
+  __shared__ float cm_part[2][HG][32];
+
+  const int t = blockIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int h = 16 * w + r16;
+  const bool h_ok = h < H;
+  const RowGeo geo = row_geo(L, t);
+  const int w_lo = max(geo.q_start, t - window + 1);
+  const int nw = window > 0 ? t - w_lo + 1 : 0;
+  const int nwc = (nw + 31) >> 5, ncc = (k_eff + 31) >> 5, nch = nwc + ncc;
+  // the row's ids, padded with -1 to whole 32-row chunks
+  for (int i = tid; i < ncc * 32; i += NT) ids_l[i] = i < k_eff ? ids[(int64_t)t * k_eff + i] : -1;
+  // Q^T operand, MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
+  u32x4 qf[NC];
+  {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok ? h : 0)) * D) + g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = h_ok ? p[4 * c] : u32x4{0, 0, 0, 0};
+  }
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)total_q * ROWB);
+  const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * ROWB);
+  // this wave's loads: instruction i = w + k*HG writes tile bytes [1024 i, 1024 i + 1024),
+  // lane l the 16 bytes of piece slot pc of row R (64 i + l = R * PIECES + pc), which
+  // hold the row's logical piece pc ^ swz(R)
+  // (re-derived at every use from an opaque copy of the lane index, so that they are
+  // not kept live across the steps)
+  auto dslot = [&](int k, int ln, int &R, int &off) __attribute__((always_inline)) {
+    const int P = 64 * (w + k * HG) + ln;
+    R = P / PIECES;
+    off = 16 * ((P - R * PIECES) ^ row_swz<D>(R));
+  };
+  // K operand: row r16 (+16), piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3))
+  const int ksw = row_swz<D>(r16);
+  const int kbase = r16 * ROWB + 16 * (g ^ (ksw & 3)), kx = ksw >> 2;
+  // V^T operand: rows rho (+16), piece (2dt + hb) ^ swz = 2 (dt ^ (swz >> 1)) + (hb ^ (swz & 1))
+  const int rho = 4 * g + (r16 >> 2);
+  const int vsw = row_swz<D>(rho);
+  const int vbase = rho * ROWB + 16 * (((r16 & 3) >> 1) ^ (vsw & 1)) + 8 * (r16 & 1), vx = vsw >> 1;
+
+  // rows of chunk ci (window chunks first, then compressed) into tile `buf`
+  auto issue = [&](int ci, char *buf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (ci < nwc) {
+#pragma unroll
+      for (int k = 0; k < NIW; ++k) {
+        const int i = w + k * HG;
+        if (NI % HG == 0 || i < NI) {
+          int R, doff;
+          dslot(k, ln, R, doff);
+          const int slot = 32 * ci + R;
+          const uint32_t off = slot < nw ? (uint32_t)(w_lo + slot) * ROWB + doff : BUF_OOB;
+          dma16(rkv, buf + i * 1024, off);
+        }
+      }
+    } else {
+      const int *il = ids_l + 32 * (ci - nwc);
+#pragma unroll
+      for (int k = 0; k < NIW; ++k) {
+        const int i = w + k * HG;
+        if (NI % HG == 0 || i < NI) {
+          int R, doff;
+          dslot(k, ln, R, doff);
+          const int id = il[R];
+          const uint32_t off = id >= 0 ? (uint32_t)id * ROWB + doff : BUF_OOB;
+          dma16(rck, buf + i * 1024, off);
+        }
+      }
+    }
+  };
+  // valid rows of chunk ci as bits
+  auto row_mask = [&](int ci) -> uint32_t {
+    if (ci < nwc) {
+      const int n = nw - 32 * ci;
+      return n >= 32 ? 0xffffffffu : (1u << n) - 1u;
+    }
+    return (uint32_t)__ballot(ids_l[32 * (ci - nwc) + (lane & 31)] >= 0);
+  };
+  // S^T for the 32 rows of a tile, this lane's 8 logits (rows 4g+i and 16+4g+i, head r16),
+  // scaled to log2 units, -inf where masked
+  auto logits = [&](const char *base, uint32_t bm, float (&sv)[8]) {
+    int kxs = kx;
+    asm volatile("" : "+v"(kxs));
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const char *kp = base + kbase + 64 * (c ^ kxs);
+      const u32x4 k0 = *reinterpret_cast<const u32x4 *>(kp);
+      const u32x4 k1 = *reinterpret_cast<const u32x4 *>(kp + 16 * ROWB);
+      acc0 = mfma16x16x32(k0, qf[c], acc0);
+      acc1 = mfma16x16x32(k1, qf[c], acc1);
+    }
+    const uint32_t m0 = h_ok ? (bm >> (4 * g)) : 0u, m1 = h_ok ? (bm >> (16 + 4 * g)) : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = ((m0 >> i) & 1) ? acc0[i] * sl2 : NINF;
+      sv[4 + i] = ((m1 >> i) & 1) ? acc1[i] * sl2 : NINF;
+    }
+  };
+
+  __syncthreads();   // ids in LDS
+  // Steps: pass 1 over the chunks, then pass 2; step n reads tile n & 1 and, right after
+  // its barrier (its own loads have landed, so after the barrier every wave's have, and
+  // every wave has finished reading tile n - 1), requests the rows of step n + 1 into the
+  // other tile, where they stream in while tile n is consumed.  (A third tile, requests
+  // two steps ahead, measured slower on these shapes.)
+  const int ns = 2 * nch;
+  auto chunk_of = [&](int n) { return n < nch ? n : n - nch; };
+  auto tile = [&](int n) { return wg_dyn + (n & 1) * TILE; };
+  auto top = [&](int n) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (n + 1 < ns) issue(chunk_of(n + 1), tile(n + 1));
+  };
+  if (ns > 0) issue(0, tile(0));
+
+  // ---------------------------------------------------------------- pass 1: max / sum
+  const float a2 = h_ok ? sink[h] * LOG2E : NINF;
+  float m = (g == 0) ? a2 : NINF;
+  float l = (g == 0 && a2 > NINF) ? 1.f : 0.f;
+  float m_nc = m, l_nc = l;
+  for (int ci = 0; ci < nch; ++ci) {
+    const int n = ci;
+    top(n);
+    if (ci == nwc) { m_nc = m; l_nc = l; }
+    float sv[8];
+    logits(tile(n), row_mask(ci), sv);
+    float cm = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
+    const float mn = fmaxf(m, cm);
+    if (mn > NINF) {
+      float acc = l * fast_exp2(m - mn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += fast_exp2(sv[e] - mn);
+      l = acc;
+      m = mn;
+    }
+  }
+  if (ncc == 0) { m_nc = m; l_nc = l; }
+  const float M = across_groups_max(m);
+  const float Ls = across_groups_sum(M > NINF ? l * fast_exp2(m - M) : 0.f);
+  const float Mnc = across_groups_max(m_nc);
+  const float Lnc = across_groups_sum(Mnc > NINF ? l_nc * fast_exp2(m_nc - Mnc) : 0.f);
+  const float lse2 = Ls > 0.f ? M + __log2f(Ls) : NINF;
+  const float lse2_nc = Lnc > 0.f ? Mnc + __log2f(Lnc) : NINF;
+  const float nl = lse2 > NINF ? -lse2 : NINF;   // exp2(-inf) = 0: no probability at all
+
+  // ---------------------------------------------------------------- pass 2: P, O, cmass
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float *crow = cmass ? cmass + (int64_t)t * k_eff : nullptr;
+  // sums over the waves of the compressed chunk staged at the previous step
+  auto flush = [&](int cprev, int pbuf) {
+    if (crow && cprev >= nwc && tid < 32) {
+      const int slot = 32 * (cprev - nwc) + tid;
+      if (slot < k_eff) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < HG; ++ww) sum += cm_part[pbuf][ww][tid];
+        crow[slot] = sum;
+      }
+    }
+  };
+  for (int ci = 0; ci < nch; ++ci) {
+    const int n = nch + ci;
+    top(n);
+    if (ci > 0) flush(ci - 1, (n - 1) & 1);
+    const char *base = tile(n);
+    float sv[8];
+    logits(base, row_mask(ci), sv);
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(sv[e] + nl);
+    const u32x4 pb = {pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]),
+                      pack2_bf16(p[6], p[7])};
+    int vxs = vx;
+    asm volatile("" : "+v"(vxs));
+    // V^T operands in batches of BDT d-tiles (fewer registers in flight)
+#pragma unroll
+    for (int hf = 0; hf < D / 16 / BDT; ++hf) {
+      uint2 xv[2 * BDT];
+#pragma unroll
+      for (int k = 0; k < BDT; ++k) {
+        const int dt = hf * BDT + k;
+        const uint32_t va = lds_addr_of(base + vbase + 32 * (dt ^ vxs));
+        xv[2 * k] = lds_read_tr16_nowait_off<0>(va);
+        xv[2 * k + 1] = lds_read_tr16_nowait_off<16 * ROWB>(va);
+      }
+      lds_tr16_wait(xv);
+#pragma unroll
+      for (int k = 0; k < BDT; ++k) {
+        const int dt = hf * BDT + k;
+        const u32x4 a = {xv[2 * k].x, xv[2 * k].y, xv[2 * k + 1].x, xv[2 * k + 1].y};
+        o[dt] = mfma16x16x32(a, pb, o[dt]);
+      }
+    }
+    if (crow && ci >= nwc) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float sh = group16_sum(p[e]);
+        if (r16 == 0) cm_part[n & 1][w][(e < 4 ? 4 * g + e : 16 + 4 * g + e - 4)] = sh;
+      }
+    }
+  }
+  if (nch > 0) {
+    __syncthreads();
+    flush(nch - 1, (ns - 1) & 1);
+  }
+
+  // ---------------------------------------------------------------- outputs
+  if (h_ok) {
+    uint16_t *orow = out + ((int64_t)t * H + h) * D + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<uint2 *>(orow + 16 * dt) =
+          uint2{pack2_bf16(o[dt][0], o[dt][1]), pack2_bf16(o[dt][2], o[dt][3])};
+    if (g == 0) {
+      lse[(int64_t)t * H + h] = lse2 * LN2;
+      lse_nc[(int64_t)t * H + h] = lse2_nc * LN2;
+    }
+  }
+}
+
+// ============================================================================
 // Gather-optimised variant (bf16; 16 heads per wave; k_eff <= 32*KC, KC <= 8).
 //
 // One wave per (query row, group of 16 heads), independent waves (no barriers).
@@ -1042,6 +1301,37 @@ static hipError_t launch_d(const LaunchLayout &LL, const void *q, const void *kv
   return hipErrorInvalidValue;
 }
 
+template <int D>
+static hipError_t launch_wg(const LaunchLayout &LL, const void *q, const void *kv, const void *ckv,
+                            const float *sink, const int32_t *ids, int k_eff, int window, int H,
+                            float scale, void *out, float *lse, float *lse_nc, float *cmass,
+                            hipStream_t st) {
+  const float sl2 = scale * LOG2E;
+  const int hg = (H + 15) / 16;
+  const int ncc = (k_eff + 31) / 32;
+  const size_t dyn = 2 * (size_t)32 * D * 2 + (size_t)ncc * 32 * sizeof(int);
+#define CSA_WG_CASE(G)                                                                                \
+  if (hg <= G) {                                                                                      \
+    auto kern = sparse_attn_wg_kernel<D, G>;                                                          \
+    if (dyn > 65536) {                                                                                \
+      const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),                 \
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn); \
+      if (ea != hipSuccess) return ea;                                                                \
+    }                                                                                                 \
+    hipLaunchKernelGGL(kern, dim3((unsigned)LL.total_q), dim3(64 * G), dyn, st, LL.dev,               \
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),           \
+                       static_cast<const uint16_t *>(ckv), sink, ids, k_eff, window, H, LL.total_q,   \
+                       LL.total_k, sl2, static_cast<uint16_t *>(out), lse, lse_nc, cmass);            \
+    return hipGetLastError();                                                                         \
+  }
+  CSA_WG_CASE(1)
+  CSA_WG_CASE(2)
+  CSA_WG_CASE(4)
+  CSA_WG_CASE(8)
+#undef CSA_WG_CASE
+  return hipErrorInvalidValue;
+}
+
 bool attn_supported(bool bf16, int H, int D, int k_eff) {
   if (H < 1 || H > 128 || k_eff < 0 || k_eff > 4096) return false;
   if (bf16) return D == 64 || D == 128 || D == 192 || D == 256 || D == 512;
@@ -1061,6 +1351,16 @@ hipError_t launch_sparse_attn(const LaunchLayout &LL, const void *q, const void 
     switch (D) {
       case 64: return launch_dma<64>(CSA_ARGS);
       case 128: return launch_dma<128>(CSA_ARGS);
+    }
+  }
+  // workgroup variant: rows staged by direct buffer->LDS loads (32-bit buffer offsets)
+  if (bf16 && (int64_t)LL.total_q * D * 2 < (1ll << 31) && (int64_t)LL.total_k * D * 2 < (1ll << 31)) {
+    switch (D) {
+      case 64: return launch_wg<64>(CSA_ARGS);
+      case 128: return launch_wg<128>(CSA_ARGS);
+      case 192: return launch_wg<192>(CSA_ARGS);
+      case 256: return launch_wg<256>(CSA_ARGS);
+      case 512: return launch_wg<512>(CSA_ARGS);
     }
   }
   if (bf16) {
