@@ -620,8 +620,18 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(16))) u32x4 qs[2][HGK_TOK * CPP];
   extern __shared__ __attribute__((aligned(16))) float wsl[];   // [Hi][HGK_TOK]
 
-  const int seg = blockIdx.x / nqb;
-  const int qb = blockIdx.x - seg * nqb;
+  // Workgroup id -> tile, XCD-aware: workgroups are dealt to the 8 XCDs round-robin by id,
+  // so id = 8 * slot + xcd; token block b goes to XCD b % 8, and an XCD's consecutive slots
+  // walk all key tiles of one of its token blocks before the next.  The 64 q rows of a
+  // block (Hi * Di * 2 bytes each) are then fetched from HBM about once and re-read from
+  // that XCD's L2 by the block's key tiles, instead of once per key tile.
+  const int nkb = (max_sk + HGK_KEYS - 1) / HGK_KEYS;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int lq = slot / nkb, kt = slot - lq * nkb;
+  const int b = lq * 8 + xcd;
+  if (b >= L.num_seqs * nqb) return;
+  const int seg = b / nqb;
+  const int qb = b - seg * nqb;
   const int q_start = __ldg(L.cu_q + seg);
   const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
   const int t0 = qb * HGK_TOK;
@@ -629,7 +639,7 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int k_base = __ldg(L.cu_k + seg);
   const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
   const int off = seg_offset(L, seg, q_len, s_k);
-  const int j0 = blockIdx.y * HGK_KEYS;
+  const int j0 = kt * HGK_KEYS;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tw = w & 3, jw = j0 + 64 * (w >> 2);
@@ -722,7 +732,9 @@ static hipError_t launch_hg(const LaunchLayout &LL, const void *q_idx, const voi
                             hipStream_t st) {
   const int nqb = (LL.max_seqlen_q + HGK_TOK - 1) / HGK_TOK;
   const int nkb = (LL.max_seqlen_k + HGK_KEYS - 1) / HGK_KEYS;
-  dim3 grid((unsigned)(LL.num_seqs * nqb), (unsigned)nkb);
+  const int64_t nblk = ((int64_t)LL.num_seqs * nqb + 7) / 8 * 8;   // token blocks, padded to the 8 XCDs
+  if (nblk * nkb > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)(nblk * nkb));
   const size_t lds = (size_t)Hi * HGK_TOK * sizeof(float);
   hipLaunchKernelGGL((indexer_score_hg_kernel<DI>), grid, dim3(64 * HGK_WAVES), lds, st, LL.dev,
                      static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx), weights, Hi,
