@@ -127,28 +127,35 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
 }
 
 // ---------------------------------------------------------------- dense
-constexpr int DN_CHUNK = 32;
-
-template <int D> struct DenseCfg {
-  static constexpr int RS = D * 2 + 16;
-  static constexpr int PIECES = D * 2 / 16;
-};
-
+// One workgroup per row, wave w owning heads 16w..16w+15.  The row's visible keys are the
+// first n rows of its segment's ckv, contiguous: they are staged 32 at a time into two LDS
+// tiles by buffer->LDS loads that the waves split between them (D/16 instructions of
+// 1 KiB per tile), each 16-byte piece p of tile row R at position p ^ row_swz<D>(R), and
+// the next tile is requested right after each step's barrier.  The buffer resource spans
+// exactly the n visible rows, so the loads past them read zeros.  Two passes over the
+// tiles: the exact l_h, then the head-summed probabilities m_j (summed within a wave on
+// DPP, across waves through LDS one step later, behind the next barrier).
 template <int D, int HG>
 __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
     LayoutDev L, const float *__restrict__ scores, int64_t ld, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ ckv, const float *__restrict__ lse_nc, int H, float scale_log2,
     float *__restrict__ teacher, int64_t ldt, float *__restrict__ kl_row) {
-  using C = DenseCfg<D>;
+  constexpr int NC = D / 32;          // MFMA K-chunks per row
+  constexpr int ROWB = D * 2;
+  constexpr int PIECES = D / 8;
+  constexpr int NI = PIECES / 2;      // load instructions per 32-row tile
+  constexpr int NIW = (NI + HG - 1) / HG;
+  constexpr int TILE = 32 * ROWB;
   constexpr int NT = 64 * HG;
+  constexpr float NINF = -__builtin_inff();
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char *rows = smem;                                                   // [DN_CHUNK][RS]
-  float *mj = reinterpret_cast<float *>(smem + DN_CHUNK * C::RS);      // [n_valid]
-  __shared__ float part[HG][DN_CHUNK];
+  float *mj = reinterpret_cast<float *>(smem + 2 * TILE);      // [n_valid]
+  __shared__ float part[2][HG][32];
   __shared__ float red[2 * 16];
 
   const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, hl = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, hl = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = 16 * w + hl;
   const bool h_ok = h < H;
   const RowGeo geo = row_geo(L, t);
@@ -159,99 +166,117 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
     if (tid == 0) kl_row[t] = 0.f;
     return;
   }
-  // q^T fragment (16 heads of this wave)
-  u32x4 qf[D / 32];
+  // Q^T operand, MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
+  u32x4 qf[NC];
   {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok ? h : 0)) * D + g * (D / 4));
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok ? h : 0)) * D) + g;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) qf[c] = h_ok ? p[c] : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NC; ++c) qf[c] = h_ok ? p[4 * c] : u32x4{0, 0, 0, 0};
   }
-  const uint16_t *kseg = ckv + (int64_t)geo.k_base * D;
-  const int nch = (n + DN_CHUNK - 1) / DN_CHUNK;
-  auto stage = [&](int ci) {
-    for (int p = tid; p < DN_CHUNK * C::PIECES; p += NT) {
-      const int r = p / C::PIECES, pc = p - r * C::PIECES;
-      const int j = ci * DN_CHUNK + r;
-      u32x4 v = {0, 0, 0, 0};
-      if (j < n) v = reinterpret_cast<const u32x4 *>(kseg + (int64_t)j * D)[pc];
-      *reinterpret_cast<u32x4 *>(rows + r * C::RS + pc * 16) = v;
-    }
-  };
-  auto s_tile = [&](int row0) {
-    const char *base = rows + (row0 + hl) * C::RS + g * (D / 4) * 2;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(ckv + (int64_t)geo.k_base * D, (uint32_t)n * ROWB);
+  const int nch = (n + 31) / 32;
+  // this wave's loads of chunk ci: instruction i = w + k*HG, lane l -> piece slot 64 i + l
+  auto issue = [&](int ci, char *buf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) acc = mfma16x16x32(*reinterpret_cast<const u32x4 *>(base + 16 * c), qf[c], acc);
-    return acc;
-  };
-
-  // pass 1: l_h = log2(2^{u_h} + sum_j 2^{c_hj})   (base-2 logits)
-  const float u2 = h_ok ? lse_nc[(int64_t)t * H + h] * LOG2E : -__builtin_inff();
-  float m = g == 0 ? u2 : -__builtin_inff();
-  float l = (g == 0 && u2 > -__builtin_inff()) ? 1.f : 0.f;
-  for (int ci = 0; ci < nch; ++ci) {
-    stage(ci);
-    __syncthreads();
-    float s[8];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const f32x4 st = s_tile(16 * tau);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = ci * DN_CHUNK + 16 * tau + 4 * g + i;
-        s[4 * tau + i] = (j < n && h_ok) ? st[i] * scale_log2 : -__builtin_inff();
+    for (int k = 0; k < NIW; ++k) {
+      const int i = w + k * HG;
+      if (NI % HG == 0 || i < NI) {
+        const int P = 64 * i + ln;
+        const int R = P / PIECES, pc = P - R * PIECES;
+        dma16(rk, buf + i * 1024, (uint32_t)(32 * ci + R) * ROWB + 16 * (pc ^ row_swz<D>(R)));
       }
     }
+  };
+  // K operand: row r16 (+16), piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3))
+  const int ksw = row_swz<D>(hl);
+  const int kbase = hl * ROWB + 16 * (g ^ (ksw & 3)), kx = ksw >> 2;
+  // this lane's 8 logits of chunk ci in log2 units (rows 4g+i and 16+4g+i, head h)
+  auto logits = [&](const char *base, int ci, float (&sv)[8]) {
+    int kxs = kx;
+    asm volatile("" : "+v"(kxs));
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const char *kp = base + kbase + 64 * (c ^ kxs);
+      acc0 = mfma16x16x32(*reinterpret_cast<const u32x4 *>(kp), qf[c], acc0);
+      acc1 = mfma16x16x32(*reinterpret_cast<const u32x4 *>(kp + 16 * ROWB), qf[c], acc1);
+    }
+    const int j0 = 32 * ci + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = (j0 + i < n && h_ok) ? acc0[i] * scale_log2 : NINF;
+      sv[4 + i] = (j0 + 16 + i < n && h_ok) ? acc1[i] * scale_log2 : NINF;
+    }
+  };
+  const int ns = 2 * nch;   // steps: pass 1 over the chunks, then pass 2
+  auto tile = [&](int s) { return smem + (s & 1) * TILE; };
+  auto top = [&](int s) {
+    wait_vmcnt<0>();
+    __syncthreads();   // step s's tile landed for every wave; tile s-1 is no longer read
+    if (s + 1 < ns) issue(s + 1 < nch ? s + 1 : s + 1 - nch, tile(s + 1));
+  };
+  if (ns > 0) issue(0, tile(0));
+
+  // pass 1: l_h = log2(2^{u_h} + sum_j 2^{c_hj})   (base-2 logits)
+  const float u2 = h_ok ? lse_nc[(int64_t)t * H + h] * LOG2E : NINF;
+  float m = g == 0 ? u2 : NINF;
+  float l = (g == 0 && u2 > NINF) ? 1.f : 0.f;
+  for (int ci = 0; ci < nch; ++ci) {
+    top(ci);
+    float s[8];
+    logits(tile(ci), ci, s);
     float cmx = s[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) cmx = fmaxf(cmx, s[e]);
     const float mn = fmaxf(m, cmx);
-    if (mn > -__builtin_inff()) {
-      float acc = l * exp2f(m - mn);
+    if (mn > NINF) {
+      float acc = l * fast_exp2(m - mn);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += exp2f(s[e] - mn);
+      for (int e = 0; e < 8; ++e) acc += fast_exp2(s[e] - mn);
       l = acc;
       m = mn;
     }
-    __syncthreads();
   }
   const float M = across_groups_max(m);
-  const float Ls = across_groups_sum(M > -__builtin_inff() ? l * exp2f(m - M) : 0.f);
-  const float ell2 = Ls > 0.f ? M + __log2f(Ls) : -__builtin_inff();
-  const bool any = ell2 > -__builtin_inff();
+  const float Ls = across_groups_sum(M > NINF ? l * fast_exp2(m - M) : 0.f);
+  const float ell2 = Ls > 0.f ? M + __log2f(Ls) : NINF;
+  const float nl = ell2 > NINF ? -ell2 : NINF;   // exp2(-inf) = 0: no mass at all
 
   // pass 2: m_j = sum_h 2^{c_hj - l_h}
-  for (int ci = 0; ci < nch; ++ci) {
-    stage(ci);
-    __syncthreads();
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const f32x4 st = s_tile(16 * tau);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = ci * DN_CHUNK + 16 * tau + 4 * g + i;
-        const float p = (j < n && h_ok && any) ? exp2f(st[i] * scale_log2 - ell2) : 0.f;
-        const float sh = group16_sum(p);
-        if (hl == 0) part[w][16 * tau + 4 * g + i] = sh;
-      }
-    }
-    __syncthreads();
-    if (tid < DN_CHUNK) {
-      const int j = ci * DN_CHUNK + tid;
+  auto flush = [&](int cprev) {
+    if (tid < 32) {
+      const int j = 32 * cprev + tid;
       if (j < n) {
         float sum = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < HG; ++ww) sum += part[ww][tid];
+        for (int ww = 0; ww < HG; ++ww) sum += part[(nch + cprev) & 1][ww][tid];
         mj[j] = sum;
       }
     }
-    __syncthreads();
+  };
+  for (int ci = 0; ci < nch; ++ci) {
+    const int st = nch + ci;
+    top(st);
+    if (ci > 0) flush(ci - 1);
+    float s[8];
+    logits(tile(st), ci, s);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sh = group16_sum(fast_exp2(s[e] + nl));
+      if (hl == 0) part[st & 1][w][e < 4 ? 4 * g + e : 16 + 4 * g + e - 4] = sh;
+    }
   }
+  __syncthreads();
+  if (nch > 0) flush(nch - 1);
+  __syncthreads();   // m_j complete
 
-  // predictor over j < n, teacher normalisation, KL (finished in fp64, see above)
+  // predictor over j < n, teacher normalisation, KL: exponentials and log1p in fp32, the
+  // sums, normalisers and t - p in fp64 (as in the sparse kernel above)
   const float *sr = scores + (int64_t)t * ld;
   __shared__ double dred[2 * 16];
-  float mx = -__builtin_inff();
+  float mx = NINF;
   double msum = 0.0;
   for (int j = tid; j < n; j += NT) { mx = fmaxf(mx, sr[j]); msum += (double)mj[j]; }
   mx = wave_max(mx);
@@ -262,19 +287,20 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   for (int ww = 1; ww < HG; ++ww) { mx = fmaxf(mx, red[ww]); msum += dred[ww]; }
   __syncthreads();
   double es = 0.0;
-  for (int j = tid; j < n; j += NT) es += exp((double)sr[j] - (double)mx);
+  for (int j = tid; j < n; j += NT) es += (double)fast_exp2((sr[j] - mx) * LOG2E);
   es = wave_sum_f64(es);
   if (lane == 0) dred[16 + w] = es;
   __syncthreads();
   es = 0.0;
   for (int ww = 0; ww < HG; ++ww) es += dred[16 + ww];
-  const double lse_i = (double)mx + log(es);
+  const double inv_es = 1.0 / es;
   const double inv_m = 1.0 / fmax(msum, (double)EPS);
   double kl = 0.0;
   for (int j = tid; j < n; j += NT) {
     const double tj = (double)mj[j] * inv_m;
-    const double pj = exp((double)sr[j] - lse_i);
-    kl += tj * (log(tj + (double)EPS) - log(pj + (double)EPS));
+    const double pj = (double)fast_exp2((sr[j] - mx) * LOG2E) * inv_es;
+    const float x = (float)(tj - pj) / ((float)pj + EPS);
+    kl += tj * (double)log1p_kl(x);
     if (teacher) teacher[(int64_t)t * ldt + j] = (float)tj;
   }
   if (teacher)
@@ -285,9 +311,9 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   if (lane == 0) kred[w] = kl;
   __syncthreads();
   if (tid == 0) {
-    double s = 0.0;
-    for (int ww = 0; ww < HG; ++ww) s += kred[ww];
-    kl_row[t] = (float)s;
+    double sacc = 0.0;
+    for (int ww = 0; ww < HG; ++ww) sacc += kred[ww];
+    kl_row[t] = (float)sacc;
   }
 }
 
@@ -319,8 +345,8 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float *__restri
 bool dense_teacher_supported(bool bf16, int H, int D, int max_seqlen_k) {
   if (!bf16 || H < 1 || H > 128 || max_seqlen_k > 8192) return false;
   if (!(D == 64 || D == 128 || D == 192 || D == 256 || D == 512)) return false;
-  // dynamic LDS: one staged key chunk plus the row's head-summed masses
-  return (size_t)DN_CHUNK * (D * 2 + 16) + (size_t)max_seqlen_k * sizeof(float) <= 65536;
+  // dynamic LDS: two staged key tiles plus the row's head-summed masses (static: < 4 KiB)
+  return (size_t)2 * 32 * D * 2 + (size_t)max_seqlen_k * sizeof(float) <= 156 * 1024;
 }
 
 template <int D>
@@ -328,10 +354,16 @@ static hipError_t launch_dense(const LaunchLayout &LL, const float *scores, int6
                                const void *ckv, const float *lse_nc, int H, float scale,
                                float *teacher, int64_t ldt, float *kl_row, hipStream_t st) {
   const int hg = (H + 15) / 16;
-  const size_t lds = DN_CHUNK * DenseCfg<D>::RS + (size_t)LL.max_seqlen_k * sizeof(float);
+  const size_t lds = (size_t)2 * 32 * D * 2 + (size_t)LL.max_seqlen_k * sizeof(float);
   const float sl2 = scale * LOG2E;
 #define CSA_DN_CASE(G)                                                                              \
   if (hg <= G) {                                                                                    \
+    if (lds > 65536) {                                                                              \
+      const hipError_t ea = hipFuncSetAttribute(                                                    \
+          reinterpret_cast<const void *>(teacher_kl_dense_kernel<D, G>),                            \
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                                    \
+      if (ea != hipSuccess) return ea;                                                              \
+    }                                                                                               \
     hipLaunchKernelGGL((teacher_kl_dense_kernel<D, G>), dim3((unsigned)LL.total_q), dim3(64 * G), \
                        lds, st, LL.dev, scores, ld, static_cast<const uint16_t *>(q),               \
                        static_cast<const uint16_t *>(ckv), lse_nc, H, sl2, teacher, ldt, kl_row);   \
