@@ -49,17 +49,20 @@ __device__ __forceinline__ void block_scan2(int a, int b, int *wsum, int &pa, in
   pb = bb + ib - b;
 }
 
-// One workgroup per row (rows above 4096 keys); thread i owns the VPT consecutive keys
-// j = i*VPT + v, so index order is thread order then v.  The radix passes stop as soon as
-// the threshold bin is taken whole; the compaction is one block scan of the per-thread
-// counts of keys above the threshold and of ties, then every thread writes its own
-// picks in index order.
+// One workgroup per row (rows above 4096 keys).  Key j = v*256 + tid sits in key[v] of
+// thread tid, so every load instruction reads 1 KiB of the row contiguously, and index
+// order is v, then wave, then lane.  The radix passes stop as soon as the threshold bin is
+// taken whole.  Compaction: each wave counts, per v, its keys above the threshold and its
+// ties (ballot popcounts), one block scan over the (v, wave) counts in index order gives
+// every group its offsets, and each lane places its picks with mbcnt ranks.
 template <int VPT>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const float *__restrict__ scores,
                                                           int64_t ld, int k_eff, int32_t *__restrict__ ids) {
+  static_assert(VPT * TK_WAVES <= TK_THREADS, "one scan entry per (v, wave)");
   __shared__ uint32_t hist[256];
   __shared__ uint32_t red[2 * TK_WAVES];
   __shared__ int wsum[2 * TK_WAVES];
+  __shared__ int cnt[2][VPT * TK_WAVES];
   __shared__ uint32_t sel_digit, sel_above, sel_cnt;
 
   const int t = blockIdx.x;
@@ -71,15 +74,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     for (int j = tid; j < k_eff; j += TK_THREADS) out[j] = j < n ? g.k_base + j : -1;
     return;
   }
-  const float *row = scores + (int64_t)t * ld + (int64_t)tid * VPT;
-  const int j0 = tid * VPT;
+  const float *row = scores + (int64_t)t * ld;
 
   uint32_t key[VPT];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const int j = j0 + v;
-    key[v] = j < n ? ordered_key(row[v]) : 0u;
+    const int j = v * TK_THREADS + tid;
+    key[v] = j < n ? ordered_key(row[j]) : 0u;
     if (j < n) { kmin = min(kmin, key[v]); kmax = max(kmax, key[v]); }
   }
 #pragma unroll
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-      const bool in_play = j0 + v < n && (cur >= 32 || (key[v] >> cur) == thr);
+      const bool in_play = v * TK_THREADS + tid < n && (cur >= 32 || (key[v] >> cur) == thr);
       if (in_play) atomicAdd(&hist[(key[v] >> sh) & ((1u << width) - 1u)], 1u);
     }
     __syncthreads();
@@ -143,28 +145,43 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
 
   // compaction in index order: keys whose prefix (bits >= cur) is above thr -- or equal to
   // it when the bin was taken whole -- and the first `need` ties otherwise
-  int ngt = 0, neq = 0;
+  // (the ballots are taken twice rather than kept: 2 * VPT 64-bit masks would not fit the
+  // scalar registers)
+  auto ballots = [&](int v, uint64_t &bg, uint64_t &be) __attribute__((always_inline)) {
+    const bool valid = v * TK_THREADS + tid < n;
+    const uint32_t kp = key[v] >> cur;
+    bg = __ballot(valid && (kp > thr || (whole && kp == thr)));
+    be = __ballot(valid && !whole && kp == thr);
+  };
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const bool valid = j0 + v < n;
-    const uint32_t kp = key[v] >> cur;
-    ngt += (valid && (kp > thr || (whole && kp == thr))) ? 1 : 0;
-    neq += (valid && !whole && kp == thr) ? 1 : 0;
+    uint64_t bg, be;
+    ballots(v, bg, be);
+    if (lane == 0) {
+      cnt[0][v * TK_WAVES + w] = __popcll(bg);
+      cnt[1][v * TK_WAVES + w] = __popcll(be);
+    }
   }
-  int gt_before, eq_before, gt_total, eq_total;
-  block_scan2(ngt, neq, wsum, gt_before, eq_before, gt_total, eq_total);
-  int pos = gt_before + min(eq_before, need);
-  int eq_rank = eq_before;
+  __syncthreads();
+  {
+    const int a = tid < VPT * TK_WAVES ? cnt[0][tid] : 0, b2 = tid < VPT * TK_WAVES ? cnt[1][tid] : 0;
+    int pa, pb, ta, tb;
+    block_scan2(a, b2, wsum, pa, pb, ta, tb);
+    if (tid < VPT * TK_WAVES) { cnt[0][tid] = pa; cnt[1][tid] = pb; }
+  }
+  __syncthreads();
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const bool valid = j0 + v < n;
-    const uint32_t kp = key[v] >> cur;
-    const bool gt = valid && (kp > thr || (whole && kp == thr));
-    const bool eq = valid && !whole && kp == thr;
-    const bool sel = gt || (eq && eq_rank < need);
-    if (sel && pos < k_eff) out[pos] = g.k_base + j0 + v;
-    pos += sel ? 1 : 0;
-    eq_rank += eq ? 1 : 0;
+    uint64_t bg, be;
+    ballots(v, bg, be);
+    const int gt_before = cnt[0][v * TK_WAVES + w] +
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0));
+    const int eq_before = cnt[1][v * TK_WAVES + w] +
+        __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0));
+    const bool gt = (bg >> lane) & 1, eq = (be >> lane) & 1;
+    const bool sel = gt || (eq && eq_before < need);
+    const int pos = gt_before + min(eq_before, need);
+    if (sel && pos < k_eff) out[pos] = g.k_base + v * TK_THREADS + tid;
   }
 }
 
