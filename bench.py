@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="path: score and top-k as two calls (the score matrix stored) even where "
                          "the fused call applies")
+    ap.add_argument("--unfused-attn", action="store_true",
+                    help="path: attention and teacher/KL as two calls (csa_sparse_attn_fwd, "
+                         "csa_indexer_teacher_kl) instead of csa_sparse_attn_kl_fwd")
     ap.add_argument("--cp", type=int, default=8, help="cp-share: CP size")
     ap.add_argument("--rank", type=int, default=0, help="cp-share: rank")
     return ap.parse_args()
@@ -402,11 +405,16 @@ def main():
             fused, sel = False, None
     if fused:
         scores = None
-    names = ("indexer_topk", "sparse_attn", "teacher_kl") if fused else \
-        ("indexer_score", "topk", "sparse_attn", "teacher_kl")
+    # sparse loss: attention, teacher and KL in one call (the loss reduced by its own call)
+    attn_kl = wl.sparse_loss and not args.unfused_attn
+    att_name = "sparse_attn_kl" if attn_kl else "sparse_attn"
+    names = (("indexer_topk",) if fused else ("indexer_score", "topk")) + \
+        ((att_name, "loss_reduce") if attn_kl else (att_name, "teacher_kl"))
     # every ctypes argument is marshalled once, so the host enqueues far ahead of the GPU
     P = ops.Prepared(L, inp, scores, ids, out, lse, lse_nc, cmass, kl_row, loss,
                      wl.sparse_loss, wl.topk, wl.window, sel=sel)
+    att_call = P.csa_sparse_attn_kl_fwd if attn_kl else P.csa_sparse_attn_fwd
+    tail_call = P.csa_loss_reduce if attn_kl else P.csa_indexer_teacher_kl
 
     def step(ev=None):
         if fused:
@@ -415,9 +423,9 @@ def main():
             P.csa_indexer_score()
             P.csa_topk()
         if ev: ev[0].record()
-        P.csa_sparse_attn_fwd()
+        att_call()
         if ev: ev[1].record()
-        P.csa_indexer_teacher_kl()
+        tail_call()
 
     for _ in range(args.warmup):
         step()
@@ -435,8 +443,7 @@ def main():
 
     # per-call breakdown from a separate, untimed pass with events between all calls
     nb = min(args.steps, 50)
-    calls = ((P.csa_indexer_topk,) if fused else (P.csa_indexer_score, P.csa_topk)) + \
-        (P.csa_sparse_attn_fwd, P.csa_indexer_teacher_kl)
+    calls = ((P.csa_indexer_topk,) if fused else (P.csa_indexer_score, P.csa_topk)) + (att_call, tail_call)
     bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(nb)]
     for ev in bev:
         ev[0].record()
@@ -448,9 +455,12 @@ def main():
     value = T * args.steps / elapsed
     wm = work_model(wl)
 
-    roof = {"kernel": "sparse_attn", "bound": "hbm",
-            "achieved": wm["attn_bytes"] / (att_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "traffic": traffic_of(wl.name, "sparse_attn")}
+    # the attention's algorithmic bytes; with the teacher/KL finished in its epilogue also
+    # the selected scores it reads and kl_row (ids and cmass are already in attn_bytes)
+    att_bytes = wm["attn_bytes"] + ((4 * T * k_eff + 4 * T) if attn_kl else 0)
+    roof = {"kernel": att_name, "bound": "hbm",
+            "achieved": att_bytes / (att_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "traffic": traffic_of(wl.name, att_name)}
     roof["frac"] = roof["achieved"] / roof["peak"]
     idx_peak = FP32_MFMA_PEAK_TFLOPS if wl.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
     kernels = {}
@@ -466,12 +476,13 @@ def main():
             "frac_mfma_peak": wm["indexer_flop"] / (per_kernel_ms["indexer_score"] * 1e-3) / 1e12 / idx_peak}
         kernels["topk"] = {"us": per_kernel_ms["topk"] * 1e3,
                            "gbs": wm["topk_bytes"] / (per_kernel_ms["topk"] * 1e-3) / 1e9}
-    kernels.update({
-        "sparse_attn": {"us": att_ms * 1e3, "gbs_gather_model": roof["achieved"],
-                        "tflops": wm["attn_flop"] / (att_ms * 1e-3) / 1e12},
-        "teacher_kl": {"us": per_kernel_ms["teacher_kl"] * 1e3,
-                       "gbs": wm["teacher_bytes"] / (per_kernel_ms["teacher_kl"] * 1e-3) / 1e9},
-    })
+    kernels[att_name] = {"us": att_ms * 1e3, "gbs_gather_model": roof["achieved"],
+                         "tflops": wm["attn_flop"] / (att_ms * 1e-3) / 1e12}
+    if attn_kl:
+        kernels["loss_reduce"] = {"us": per_kernel_ms["loss_reduce"] * 1e3}
+    else:
+        kernels["teacher_kl"] = {"us": per_kernel_ms["teacher_kl"] * 1e3,
+                                 "gbs": wm["teacher_bytes"] / (per_kernel_ms["teacher_kl"] * 1e-3) / 1e9}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds)
@@ -482,7 +493,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if wl.dtype == "f32" else "bf16",
         "data": "synthetic",
         "config": {**wl.describe(), "parallelism": "none (1 GPU)",
-                   "score_path": "fused score + top-k (no score matrix)" if fused else "score and top-k calls"},
+                   "score_path": "fused score + top-k (no score matrix)" if fused else "score and top-k calls",
+                   "attention_path": "attention + teacher/KL in one call" if attn_kl
+                   else "attention and teacher/KL calls"},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
         "loss": float(loss[0]),
     }

@@ -216,6 +216,67 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, 
                     fn);
 }
 
+csa_status_t csa_sparse_attn_kl_fwd(const csa_layout_t *L, const void *q, const void *kv, const void *ckv,
+                                    const float *sink, const int32_t *ids, int32_t k_eff, int32_t window,
+                                    csa_dtype_t dt, int32_t H, int32_t D, float softmax_scale,
+                                    const float *scores, int64_t ld_scores, int32_t scores_selected,
+                                    int32_t per_token_loss, void *out, float *lse, float *lse_nc,
+                                    float *cmass, float *teacher, int64_t ld_teacher, float *kl_row,
+                                    float *loss, void *stream) {
+  const char *fn = "csa_sparse_attn_kl_fwd";
+  csa::LaunchLayout LL;
+  csa_status_t st = check_layout(L, fn, &LL);
+  if (st != CSA_OK) return st;
+  if (!q || !kv || !ckv || !sink || !ids || !out || !lse || !lse_nc || !cmass || !scores || !kl_row)
+    return fail(CSA_ERR_INVALID, "%s: a required tensor pointer is NULL", fn);
+  if (k_eff < 1 || k_eff > L->max_seqlen_k)
+    return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [1, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
+  if (window < 0) return fail(CSA_ERR_INVALID, "%s: window=%d < 0", fn, window);
+  if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+  if (H < 1 || D < 1) return fail(CSA_ERR_INVALID, "%s: H=%d, D=%d must be >= 1", fn, H, D);
+  const int need_ld = scores_selected ? k_eff : L->max_seqlen_k;
+  if (ld_scores < need_ld)
+    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld < %d", fn, (long long)ld_scores, need_ld);
+  if (teacher && ld_teacher < k_eff)
+    return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < k_eff=%d", fn, (long long)ld_teacher, k_eff);
+  if (!csa::attn_supported(dt == CSA_BF16, H, D, k_eff))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d H=%d D=%d k_eff=%d", fn, (int)dt, H, D, k_eff);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (scores_selected && csa::attn_kl_fused_supported(LL, dt == CSA_BF16, H, D, k_eff, window)) {
+    // one attention launch that also finishes the teacher and the KL, then the loss
+    if (L->total_q > 0) {
+      const csa::KlArgs kla{scores, ld_scores, teacher, ld_teacher, kl_row};
+      st = hip_status(csa::launch_sparse_attn_kl(LL, q, kv, ckv, sink, ids, k_eff, window, H, D, softmax_scale,
+                                                 out, lse, lse_nc, cmass, kla, hs),
+                      fn);
+      if (st != CSA_OK) return st;
+    }
+    if (!loss) return ok();
+    return hip_status(csa::launch_loss_reduce(kl_row, L->total_q, per_token_loss != 0, loss, hs), fn);
+  }
+  if (L->total_q > 0) {
+    st = hip_status(csa::launch_sparse_attn(LL, q, kv, ckv, sink, ids, k_eff, window, dt == CSA_BF16, H, D,
+                                            softmax_scale, out, lse, lse_nc, cmass, hs),
+                    fn);
+    if (st != CSA_OK) return st;
+  }
+  return hip_status(csa::launch_teacher_kl(LL, true, scores, ld_scores, scores_selected != 0, ids, k_eff, cmass,
+                                           nullptr, nullptr, nullptr, dt == CSA_BF16, H, D, softmax_scale,
+                                           per_token_loss != 0, teacher, ld_teacher, kl_row, loss, hs),
+                    fn);
+}
+
+csa_status_t csa_loss_reduce(const float *kl_row, int32_t total_q, int32_t per_token_loss, float *loss,
+                             void *stream) {
+  const char *fn = "csa_loss_reduce";
+  if (!loss) return fail(CSA_ERR_INVALID, "%s: loss is NULL", fn);
+  if (total_q < 0) return fail(CSA_ERR_INVALID, "%s: total_q=%d < 0", fn, total_q);
+  if (total_q > 0 && !kl_row) return fail(CSA_ERR_INVALID, "%s: kl_row is NULL", fn);
+  return hip_status(csa::launch_loss_reduce(kl_row, total_q, per_token_loss != 0, loss,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, const void *q_idx,
                                   const void *k_idx, const float *weights, csa_dtype_t dt, int32_t Hi,
                                   int32_t Di, float idx_scale, const float *scores, int64_t ld_scores,

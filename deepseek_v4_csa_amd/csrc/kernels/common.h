@@ -134,11 +134,18 @@ struct LayoutDev {
 
 // segment s with cu_q[s] <= t < cu_q[s+1] (binary search; cu_q is non-decreasing,
 // empty segments are skipped because the search finds the last s with cu_q[s] <= t)
+// A load through the constant address space: the layout arrays are never written while a
+// kernel runs, so at a wave-uniform address this is a scalar load (counted by lgkmcnt),
+// and waiting for it does not wait for the wave's vector-memory traffic in flight.
+__device__ __forceinline__ int32_t ldc(const int32_t *p) {
+  return *(const __attribute__((address_space(4))) int32_t *)(p);
+}
+
 __device__ __forceinline__ int segment_of(const int32_t *cu_q, int nseq, int t) {
   int lo = 0, hi = nseq - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if (__ldg(cu_q + mid) <= t) lo = mid; else hi = mid - 1;
+    if (ldc(cu_q + mid) <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -156,11 +163,11 @@ __device__ __forceinline__ int n_valid_of(int local, int off, int ratio, int s_k
 __device__ __forceinline__ RowGeo row_geo(const LayoutDev &L, int t) {
   RowGeo g;
   g.seg = segment_of(L.cu_q, L.num_seqs, t);
-  g.q_start = __ldg(L.cu_q + g.seg);
-  g.q_len = __ldg(L.cu_q + g.seg + 1) - g.q_start;
-  g.k_base = __ldg(L.cu_k + g.seg);
-  g.s_k = __ldg(L.cu_k + g.seg + 1) - g.k_base;
-  int off = L.off ? __ldg(L.off + g.seg) : g.s_k * L.ratio - g.q_len;
+  g.q_start = ldc(L.cu_q + g.seg);
+  g.q_len = ldc(L.cu_q + g.seg + 1) - g.q_start;
+  g.k_base = ldc(L.cu_k + g.seg);
+  g.s_k = ldc(L.cu_k + g.seg + 1) - g.k_base;
+  int off = L.off ? ldc(L.off + g.seg) : g.s_k * L.ratio - g.q_len;
   g.n_valid = n_valid_of(t - g.q_start, off, L.ratio, g.s_k);
   return g;
 }
@@ -171,12 +178,12 @@ __device__ __forceinline__ RowGeo row_geo(const LayoutDev &L, int t) {
 __device__ __forceinline__ bool loss_row_empty(const LayoutDev &L, const RowGeo &g, int t) {
   if (g.n_valid == 0) return true;
   if (!L.cu_q_real) return false;
-  const int real = __ldg(L.cu_q_real + g.seg + 1) - __ldg(L.cu_q_real + g.seg);
+  const int real = ldc(L.cu_q_real + g.seg + 1) - ldc(L.cu_q_real + g.seg);
   return t - g.q_start >= real;
 }
 
 __device__ __forceinline__ int seg_offset(const LayoutDev &L, int s, int q_len, int s_k) {
-  return L.off ? __ldg(L.off + s) : s_k * L.ratio - q_len;
+  return L.off ? ldc(L.off + s) : s_k * L.ratio - q_len;
 }
 
 }  // namespace csa
@@ -268,6 +275,10 @@ template <int D> __device__ __forceinline__ int row_swz(int r) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, (int)voff, 0, 0, 0);
+}
+// the 4-byte form: lane l writes lds_base + 4 l
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 4, (int)voff, 0, 0, 0);
 }
 // s_waitcnt with only vmcnt constrained (expcnt 7 and lgkmcnt 15 = no wait); the 6-bit
 // count is split over bits 3:0 and 15:14 of the immediate

@@ -27,6 +27,7 @@
 #include <utility>
 
 #include "common.h"
+#include "sparse_kl.h"
 #include "../launch.h"
 
 namespace csa {
@@ -892,13 +893,13 @@ template <int N, class F> __device__ __forceinline__ void static_for(F &f) {
 // Compressed probabilities are kept in fp32 (rescaled with O when the running max is
 // raised), so at the end cmass[j] = sum_h p_hj / L_h needs no second exponential.
 // ============================================================================
-template <int D, int KC>
+template <int D, int KC, bool KL>
 __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
     LayoutDev L, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const uint16_t *__restrict__ ckv, const float *__restrict__ sink,
     const int32_t *__restrict__ ids, int k_eff, int window, int H, int total_q, int total_k,
     float sl2, uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ lse_nc,
-    float *__restrict__ cmass) {
+    float *__restrict__ cmass, KlArgs kla) {
   constexpr int NC = D / 32;          // MFMA K-chunks per row
   constexpr int ROWB = D * 2;         // bytes per KV row
   constexpr int PIECES = D / 8;       // 16-byte pieces per row
@@ -909,8 +910,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
   constexpr int IPL = (IDS + 63) / 64;  // id slots per lane
   constexpr float NINF = -__builtin_inff();
   constexpr float RESCALE = 8.f;
+  constexpr int NSC = (IDS + 63) / 64;  // 4-byte loads of a row's selected scores (KL)
   static_assert(NI <= 15, "vmcnt");
-  __shared__ __attribute__((aligned(16))) char lds_all[4][2 * TILE + 2 * IDS * 4];
+  // per wave: two tiles, two id buffers and (KL) the selected scores of the current query
+  __shared__ __attribute__((aligned(16))) char lds_all[4][2 * TILE + 2 * IDS * 4 + (KL ? 4 * 64 * NSC : 0)];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const int nwaves = gridDim.x * 4;
@@ -918,6 +921,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
   if (t >= total_q) return;           // no block-level barrier below
   char *tiles = lds_all[w];
   int *ids_lds = reinterpret_cast<int *>(tiles + 2 * TILE);   // [2][IDS]
+  float *sc_lds = reinterpret_cast<float *>(tiles + 2 * TILE + 2 * IDS * 4);   // [64 NSC] (KL)
   const int h = r16;
   const bool h_ok = h < H;
   const bool group_full = H >= 16;
@@ -939,32 +943,30 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
 #pragma unroll
   for (int i = 0; i < 2 * TILE / 1024; ++i) reinterpret_cast<u32x4 *>(tiles)[i * 64 + lane] = u32x4{0, 0, 0, 0};
 
-  struct Geo { int w_lo, nw, nwc; };
+  // a query's geometry is found one query ahead, so its loads have landed long before use
+  // (kl_empty: the row is left out of the loss; KL only)
+  struct Geo { int w_lo, nw, nwc; bool kl_empty; };
   auto geo_of = [&](int tq) {
     const RowGeo rg = row_geo(L, tq);
     Geo o;
     o.w_lo = max(rg.q_start, tq - window + 1);
     o.nw = tq - o.w_lo + 1;
     o.nwc = (o.nw + 31) >> 5;
+    o.kl_empty = KL ? loss_row_empty(L, rg, tq) : false;
     return o;
   };
-  auto load_ids = [&](int tq, int (&r)[IPL]) {
+  // The ids of query tq go straight into id buffer b by 4-byte buffer->LDS loads (no
+  // registers, so no wait for them beyond the step waits).  LDS order [step]
+  // [row-in-instruction][instruction], so a lane's ids of one step are contiguous: position
+  // p holds slot (p & ~31) + ((p & 31) % NI) * RPI + (p & 31) / NI.  Lanes whose slot is
+  // at or past k_eff are masked off, so those positions keep the -1 written at the start.
+  auto dma_ids = [&](int tq, int b) {
+    const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids + (int64_t)tq * k_eff, (uint32_t)k_eff * 4);
 #pragma unroll
     for (int i = 0; i < IPL; ++i) {
-      const int sl = i * 64 + lane;
-      r[i] = sl < k_eff ? ids[(int64_t)tq * k_eff + sl] : -1;
-    }
-  };
-  // LDS order [step][row-in-instruction][instruction]: a lane's ids of one step are contiguous
-  auto store_ids = [&](int buf, const int (&r)[IPL]) {
-    int *dst = ids_lds + buf * IDS;
-#pragma unroll
-    for (int i = 0; i < IPL; ++i) {
-      const int sl = i * 64 + lane;
-      if (sl < IDS) {
-        const int rs = sl & 31;
-        dst[(sl & ~31) + (rs % RPI) * NI + rs / RPI] = r[i];
-      }
+      const int p = 64 * i + lane, pl = p & 31;
+      const int sl = (p & ~31) + (pl % NI) * RPI + pl / NI;
+      if (p < IDS && sl < k_eff) dma4(rid, ids_lds + b * IDS + 64 * i, (uint32_t)sl * 4);
     }
   };
   // MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
@@ -1004,19 +1006,22 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
     }
   };
 
+  // the sink logit of this lane's head (the same for every query)
+  const float a2 = h_ok ? sink[h] * LOG2E : NINF;
   // ---- stream start: the first query's ids and q, then its first two tiles
   u32x4 qf[NC];
   int buf = 0;
-  {
-    int r[IPL];
-    load_ids(t, r);
-    load_q(t, qf);
-    store_ids(0, r);
-  }
+#pragma unroll
+  for (int i = 0; i < 2 * IPL; ++i)
+    if (64 * i + lane < 2 * IDS) ids_lds[64 * i + lane] = -1;
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // the -1 fill is in LDS before any id load lands
+  dma_ids(t, 0);
+  load_q(t, qf);
+  wait_vmcnt<0>();                      // the first query's ids are in LDS
   Geo G = geo_of(t);
   int tn = t + nwaves;
   bool has_next = tn < total_q;
-  Geo Gn = {0, 0, 0};
+  Geo Gn = {0, 0, 0, false};
   if (has_next) Gn = geo_of(tn);
   __builtin_amdgcn_s_waitcnt(0xC07F);   // zeroing and id stores have executed
   dma_step(true, G, 0, 0, tiles);
@@ -1026,12 +1031,39 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
   }
   int n = 0;  // stream step index: step n reads tile n & 1
 
+  // KL: each lane holds, for every other step c = 2i + half, the slot 32c + jl (e = r16 & 7
+  // of its lane group's head sums), so the 64 lanes share a row's slots evenly
+  constexpr int NO = (KC + 1) / 2;
+  const int half = r16 >> 3;
+  const int jl = 16 * ((r16 >> 2) & 1) + 4 * g + (r16 & 3);   // slot within a step
+  const int jo = (jl % RPI) * NI + jl / RPI;                    // its place in ids_lds
+  int kp_t = -1;          // the query whose teacher and KL are pending (-1: none)
+  bool kp_empty = false;  // its row is left out of the loss
+  bool kp_ok[NO];         // slot in the support (a valid id)
+  float kp_own[NO], kp_sc[NO];   // head-summed mass and selected score of the slot
+  auto kl_finish = [&]() __attribute__((always_inline)) {
+    float *te = kla.teacher ? kla.teacher + (int64_t)kp_t * kla.ldt : nullptr;
+    float tj[NO];
+    double kl = 0.0;
+    if (kp_empty) {
+#pragma unroll
+      for (int i = 0; i < NO; ++i) tj[i] = 0.f;
+    } else {
+      kl = sparse_kl_wave(kp_ok, kp_own, kp_sc, tj);
+    }
+    if (te) {
+#pragma unroll
+      for (int i = 0; i < NO; ++i) {
+        const int c = 2 * i + half, j = 32 * c + jl;
+        if (c < ncc && j < k_eff) te[j] = tj[i];
+      }
+    }
+    if (lane == 0) kla.kl_row[kp_t] = (float)kl;
+  };
+
   for (;;) {
     const int nsteps = G.nwc + ncc;
-    int idn[IPL];
-    bool ids_done = !has_next;
 
-    const float a2 = h_ok ? sink[h] * LOG2E : NINF;
     float m = a2;                                        // shared by the 4 lane groups of a head
     float l = (g == 0 && a2 > NINF) ? 1.f : 0.f;         // per-lane partial sum
     f32x4 o[D / 16];
@@ -1044,17 +1076,25 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
       for (int e = 0; e < 8; ++e) pk[c][e] = 0.f;
 
     // Top of step s: its tile has landed (at most the NI loads of step n+1 outstanding)
-    // and every LDS access of step n-1 has returned; the next query's ids are fetched at
-    // s = 0 and written to the other buffer at s = 1 (they are first needed by a request
-    // issued at s >= 1: the next query's first step is a window step).
+    // and every LDS access of step n-1 has returned.  At s = 0 the next query's ids are
+    // requested into the other id buffer (issued before the request of step 2, they have
+    // landed by the top of step 1; they are first read by a request issued at s >= 1: the
+    // next query's first step is a window step).
     auto top = [&](int s) __attribute__((always_inline)) {
       wait_vmcnt<NI>();
       __builtin_amdgcn_s_waitcnt(0xC07F);
-      if (s == 0 && has_next) load_ids(tn, idn);
-      if (s == 1 && !ids_done) {
-        store_ids(buf ^ 1, idn);
-        ids_done = true;
+      // KL: this query's selected scores into LDS; issued before the request of step 2,
+      // they have landed by the top of step 1 (there are always at least two steps)
+      if constexpr (KL) {
+        if (s == 0) {
+          const __amdgpu_buffer_rsrc_t rsc = make_rsrc(kla.scores + (int64_t)t * kla.ld, (uint32_t)k_eff * 4);
+#pragma unroll
+          for (int i = 0; i < NSC; ++i) dma4(rsc, sc_lds + 64 * i, (uint32_t)(64 * i + lane) * 4);
+        }
       }
+      // the next query's ids and q rows: issued ahead of this query's row requests, so
+      // that waiting for them never waits for a tile still in flight
+      if (s == 0 && has_next) dma_ids(tn, buf ^ 1);
     };
     // the rows of stream step n+2 into the tile step n has just finished reading
     auto request = [&](int s) __attribute__((always_inline)) {
@@ -1146,7 +1186,16 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
       request(s);   // the tile is free: its LDS reads have all returned
     };
 
-    for (int s = 0; s < G.nwc; ++s, ++n) {
+    top(0);
+    // the previous query's teacher and KL: their chain of wave reductions runs while the
+    // rows of step 1 are in flight, and their stores go out before the request of step 2
+    // (a store issued after it would make the wait at the top of step 1 wait for it)
+    if constexpr (KL) {
+      if (kp_t >= 0) kl_finish();
+    }
+    step(std::integral_constant<int, -1>{}, 0, G.nw >= 32 ? 0xffffffffu : (1u << G.nw) - 1u);
+    ++n;
+    for (int s = 1; s < G.nwc; ++s, ++n) {
       top(s);
       const int nwin = G.nw - 32 * s;
       step(std::integral_constant<int, -1>{}, s, nwin >= 32 ? 0xffffffffu : (1u << nwin) - 1u);
@@ -1166,7 +1215,6 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
       }
     };
     static_for<KC>(comp_step);
-    if (!ids_done) store_ids(buf ^ 1, idn);   // (only if this query had a single step)
     // the next query's q rows stream in during this query's epilogue
     if (has_next) load_q(tn, qf);
 
@@ -1188,26 +1236,53 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
         *reinterpret_cast<uint2 *>(orow + 16 * dt) =
             uint2{pack2_bf16(o[dt][0] * inv, o[dt][1] * inv), pack2_bf16(o[dt][2] * inv, o[dt][3] * inv)};
     }
-    if (cmass != nullptr) {
-      float *crow = cmass + (int64_t)t * k_eff;
+    // head sums of the compressed probabilities: after the group sum every lane of group
+    // g holds sums[e] of slot 32c + 16 (e >> 2) + 4g + (e & 3).  For the KL each lane
+    // keeps one of them for every other step: e = r16 & 7 of the steps c = 2i + (r16 >> 3)
+    // in own[i], so the 64 lanes share the row's slots evenly.
+    float own[NO];
+#pragma unroll
+    for (int i = 0; i < NO; ++i) own[i] = 0.f;
+    if (cmass != nullptr || KL) {
+      float *crow = cmass ? cmass + (int64_t)t * k_eff : nullptr;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        if (c >= ncc) break;
-        float sums[8];
+        if (c < ncc) {
+          float sums[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sums[e] = group16_sum(pk[c][e] * inv);
-        // lane r16 = tau of group g writes slots 32c + 16*tau + 4g + (0..3)
-        const int slot0 = 32 * c + 16 * r16 + 4 * g;
-        if (r16 < 2) {
-          const f32x4 v = r16 ? f32x4{sums[4], sums[5], sums[6], sums[7]} : f32x4{sums[0], sums[1], sums[2], sums[3]};
-          if (slot0 + 4 <= k_eff) {
-            *reinterpret_cast<f32x4 *>(crow + slot0) = v;
-          } else {
+          for (int e = 0; e < 8; ++e) sums[e] = group16_sum(pk[c][e] * inv);
+          if constexpr (KL) {
+            float v = sums[0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (slot0 + i < k_eff) crow[slot0 + i] = v[i];
+            for (int e = 1; e < 8; ++e) v = (r16 & 7) == e ? sums[e] : v;
+            if (half == (c & 1)) own[c >> 1] = v;
+          }
+          // lane r16 = tau of group g writes slots 32c + 16*tau + 4g + (0..3)
+          const int slot0 = 32 * c + 16 * r16 + 4 * g;
+          if (crow && r16 < 2) {
+            const f32x4 v = r16 ? f32x4{sums[4], sums[5], sums[6], sums[7]} : f32x4{sums[0], sums[1], sums[2], sums[3]};
+            if (slot0 + 4 <= k_eff) {
+              *reinterpret_cast<f32x4 *>(crow + slot0) = v;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (slot0 + i < k_eff) crow[slot0 + i] = v[i];
+            }
           }
         }
+      }
+    }
+    if constexpr (KL) {
+      // what the row's teacher and KL need, taken before its id and score buffers are
+      // reused; the arithmetic is finished during the next query's first step
+      kp_t = t;
+      kp_empty = G.kl_empty;
+#pragma unroll
+      for (int i = 0; i < NO; ++i) {
+        const int c = 2 * i + half, j = 32 * c + jl;
+        kp_ok[i] = c < ncc && j < k_eff && ids_lds[buf * IDS + 32 * c + jo] >= 0;
+        kp_sc[i] = kp_ok[i] ? sc_lds[j] : 0.f;
+        kp_own[i] = own[i];
       }
     }
     if (!has_next) break;
@@ -1218,14 +1293,17 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
     has_next = tn < total_q;
     if (has_next) Gn = geo_of(tn);
   }
+  if constexpr (KL) kl_finish();   // the last query's
   wait_vmcnt<0>();   // the stream's trailing out-of-range requests
 }
 
+// kla != nullptr: the pipelined kernel also finishes the sparse teacher and KL (only
+// called so when pipe_kl_supported holds)
 template <int D>
 static hipError_t launch_dma(const LaunchLayout &LL, const void *q, const void *kv, const void *ckv,
                              const float *sink, const int32_t *ids, int k_eff, int window, int H,
                              float scale, void *out, float *lse, float *lse_nc, float *cmass,
-                             hipStream_t st) {
+                             hipStream_t st, const KlArgs *kla = nullptr) {
   const int hgc = (H + 15) / 16;
   const int qpw = 4 / hgc;
   const float sl2 = scale * LOG2E;
@@ -1239,11 +1317,18 @@ static hipError_t launch_dma(const LaunchLayout &LL, const void *q, const void *
     dim3 pgrid((unsigned)std::min<int64_t>(need, 2 * (int64_t)ncu));
 #define CSA_PIPE_CASE(K)                                                                             \
     if (k_eff <= 32 * K) {                                                                           \
-      hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, K>), pgrid, dim3(256), 0, st, LL.dev,           \
-                         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),        \
-                         static_cast<const uint16_t *>(ckv), sink, ids, k_eff, window, H,            \
-                         LL.total_q, LL.total_k, sl2, static_cast<uint16_t *>(out), lse, lse_nc,     \
-                         cmass);                                                                     \
+      if (kla != nullptr)                                                                            \
+        hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, K, true>), pgrid, dim3(256), 0, st, LL.dev,   \
+                           static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),      \
+                           static_cast<const uint16_t *>(ckv), sink, ids, k_eff, window, H,          \
+                           LL.total_q, LL.total_k, sl2, static_cast<uint16_t *>(out), lse, lse_nc,   \
+                           cmass, *kla);                                                             \
+      else                                                                                           \
+        hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, K, false>), pgrid, dim3(256), 0, st, LL.dev,  \
+                           static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),      \
+                           static_cast<const uint16_t *>(ckv), sink, ids, k_eff, window, H,          \
+                           LL.total_q, LL.total_k, sl2, static_cast<uint16_t *>(out), lse, lse_nc,   \
+                           cmass, KlArgs{});                                                         \
       return hipGetLastError();                                                                      \
     }
     CSA_PIPE_CASE(1)
@@ -1329,6 +1414,29 @@ static hipError_t launch_wg(const LaunchLayout &LL, const void *q, const void *k
   CSA_WG_CASE(4)
   CSA_WG_CASE(8)
 #undef CSA_WG_CASE
+  return hipErrorInvalidValue;
+}
+
+// shapes of the pipelined kernel (bf16, one wave per query for H <= 16 heads, a window,
+// 1 <= k_eff <= 256, KV within the 2 GiB reach of 32-bit buffer offsets)
+static bool pipe_shape(const LaunchLayout &LL, bool bf16, int H, int D, int k_eff, int window) {
+  return bf16 && H <= 16 && k_eff >= 1 && k_eff <= 256 && window > 0 && (D == 64 || D == 128) &&
+         (int64_t)LL.total_q * D * 2 < (1ll << 31) && (int64_t)LL.total_k * D * 2 < (1ll << 31);
+}
+
+bool attn_kl_fused_supported(const LaunchLayout &LL, bool bf16, int H, int D, int k_eff, int window) {
+  return pipe_shape(LL, bf16, H, D, k_eff, window);
+}
+
+hipError_t launch_sparse_attn_kl(const LaunchLayout &LL, const void *q, const void *kv,
+                                 const void *ckv, const float *sink, const int32_t *ids, int k_eff,
+                                 int window, int H, int D, float scale, void *out, float *lse,
+                                 float *lse_nc, float *cmass, const KlArgs &kla, hipStream_t st) {
+  if (LL.total_q == 0) return hipSuccess;
+  switch (D) {
+    case 64: return launch_dma<64>(LL, q, kv, ckv, sink, ids, k_eff, window, H, scale, out, lse, lse_nc, cmass, st, &kla);
+    case 128: return launch_dma<128>(LL, q, kv, ckv, sink, ids, k_eff, window, H, scale, out, lse, lse_nc, cmass, st, &kla);
+  }
   return hipErrorInvalidValue;
 }
 

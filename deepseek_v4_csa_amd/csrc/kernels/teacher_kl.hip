@@ -18,38 +18,15 @@
 // then the head-summed probabilities).  kl_row is then reduced to the loss by a
 // single-workgroup kernel in a fixed order (deterministic, no atomics).
 #include "common.h"
+#include "sparse_kl.h"
 #include "../launch.h"
 
 namespace csa {
 
-constexpr float EPS = 1e-10f;
-
-// log(1 + x) for x > -1: |x| < 1/2 by the series 2 atanh(u), u = x / (2 + x) (|u| < 1/3,
-// terms through u^15: truncation below 3e-9 relative); otherwise the hardware log of 1 + x,
-// where 1 + x is exact enough (relative error ~1e-7 of the result).
-__device__ __forceinline__ float log1p_kl(float x) {
-  if (fabsf(x) < 0.5f) {
-    const float u = x / (2.f + x);
-    const float u2 = u * u;
-    float p = 1.f / 15.f;
-    p = fmaf(p, u2, 1.f / 13.f);
-    p = fmaf(p, u2, 1.f / 11.f);
-    p = fmaf(p, u2, 1.f / 9.f);
-    p = fmaf(p, u2, 1.f / 7.f);
-    p = fmaf(p, u2, 1.f / 5.f);
-    p = fmaf(p, u2, 1.f / 3.f);
-    p = fmaf(p, u2, 1.f);
-    return 2.f * u * p;
-  }
-  return __log2f(1.f + x) * LN2;
-}
-
 // ---------------------------------------------------------------- sparse
 // One wave per row; slot j = v*64 + lane (v < SPL), so every load is issued up front and
-// coalesced except the score gather (one dependent load per slot).  The KL of two nearly
-// equal distributions is a second-order quantity, so the normalisers and the log-ratios
-// are finished in fp64: an fp32 error in either normaliser shifts the KL by about that
-// relative error.  log(t+eps) - log(p+eps) is taken as one log of the ratio.
+// coalesced except the score gather (one dependent load per slot); the row is finished by
+// sparse_kl_wave.
 template <int SPL>
 __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
     LayoutDev L, int T, const float *__restrict__ scores, int64_t ld, int selected,
@@ -81,48 +58,20 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
     if (lane == 0) kl_row[t] = 0.f;
     return;
   }
-  float mx = -__builtin_inff();
+  bool ok[SPL];
 #pragma unroll
   for (int v = 0; v < SPL; ++v) {
+    ok[v] = id[v] >= 0;
     // the score of slot j: read in place (selected scores) or gathered from the full row
-    if (!selected) sc[v] = id[v] >= 0 ? sr[id[v] - geo.k_base] : 0.f;
-    sc[v] = id[v] >= 0 ? sc[v] : -__builtin_inff();
-    mx = fmaxf(mx, sc[v]);
+    if (!selected) sc[v] = ok[v] ? sr[id[v] - geo.k_base] : 0.f;
   }
-  double ms = 0.0;
+  float tj[SPL];
+  const double kl = sparse_kl_wave(ok, c, sc, tj);
+  if (te) {
 #pragma unroll
-  for (int v = 0; v < SPL; ++v) ms += id[v] >= 0 ? (double)c[v] : 0.0;
-  mx = wave_max_dpp(mx);
-  ms = wave_sum_f64_dpp(ms);
-  // Predictor terms in fp32 (an independent relative error d_j in e_j moves the KL only
-  // through sum_j (t_j - p_j) d_j), the normalisations in fp64.
-  float e[SPL];
-  double es = 0.0;
-#pragma unroll
-  for (int v = 0; v < SPL; ++v) {
-    e[v] = id[v] >= 0 ? fast_exp2((sc[v] - mx) * LOG2E) : 0.f;
-    es += (double)e[v];
+    for (int v = 0; v < SPL; ++v)
+      if (v * 64 + lane < k_eff) te[v * 64 + lane] = tj[v];
   }
-  es = wave_sum_f64_dpp(es);
-  const double inv_es = 1.0 / es;
-  const double inv_m = 1.0 / fmax(ms, (double)EPS);
-  // log(t+eps) - log(p+eps) = log1p(x), x = (t - p) / (p + eps): the difference t - p is
-  // taken in fp64, the rest in fp32, so x and log1p(x) err by ~1e-7 of |x| -- the KL
-  // moves by ~1e-7 * sum_j t_j |x_j|, far below its tolerance.
-  double kl = 0.0;
-#pragma unroll
-  for (int v = 0; v < SPL; ++v) {
-    const int j = v * 64 + lane;
-    double tj = 0.0;
-    if (id[v] >= 0) {
-      tj = (double)c[v] * inv_m;
-      const double pj = (double)e[v] * inv_es;
-      const float x = (float)(tj - pj) / ((float)pj + EPS);
-      kl += tj * (double)log1p_kl(x);
-    }
-    if (te && j < k_eff) te[j] = (float)tj;
-  }
-  kl = wave_sum_f64_dpp(kl);
   if (lane == 0) kl_row[t] = (float)kl;
 }
 
@@ -294,12 +243,12 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   es = 0.0;
   for (int ww = 0; ww < HG; ++ww) es += dred[16 + ww];
   const double inv_es = 1.0 / es;
-  const double inv_m = 1.0 / fmax(msum, (double)EPS);
+  const double inv_m = 1.0 / fmax(msum, (double)KL_EPS);
   double kl = 0.0;
   for (int j = tid; j < n; j += NT) {
     const double tj = (double)mj[j] * inv_m;
     const double pj = (double)fast_exp2((sr[j] - mx) * LOG2E) * inv_es;
-    const float x = (float)(tj - pj) / ((float)pj + EPS);
+    const float x = (float)(tj - pj) / ((float)pj + KL_EPS);
     kl += tj * (double)log1p_kl(x);
     if (teacher) teacher[(int64_t)t * ldt + j] = (float)tj;
   }
@@ -410,8 +359,12 @@ hipError_t launch_teacher_kl(const LaunchLayout &LL, bool sparse, const float *s
     }
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, st, kl_row, LL.total_q,
-                     per_token ? 1 : 0, loss);
+  if (loss == nullptr) return hipSuccess;   // the caller reduces kl_row itself
+  return launch_loss_reduce(kl_row, LL.total_q, per_token, loss, st);
+}
+
+hipError_t launch_loss_reduce(const float *kl_row, int T, bool per_token, float *loss, hipStream_t st) {
+  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, st, kl_row, T, per_token ? 1 : 0, loss);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include "kernels/common.h"
+#include "kernels/sparse_kl.h"
 
 namespace csa {
 
@@ -23,11 +24,20 @@ hipError_t launch_sparse_attn(const LaunchLayout &L, const void *q, const void *
                               int window, bool bf16, int H, int D, float scale, void *out,
                               float *lse, float *lse_nc, float *cmass, hipStream_t st);
 
+// attention whose epilogue also finishes the sparse teacher and KL (kl_row, teacher)
+// from the selected scores; only for shapes where attn_kl_fused_supported holds
+hipError_t launch_sparse_attn_kl(const LaunchLayout &L, const void *q, const void *kv,
+                                 const void *ckv, const float *sink, const int32_t *ids, int k_eff,
+                                 int window, int H, int D, float scale, void *out, float *lse,
+                                 float *lse_nc, float *cmass, const KlArgs &kla, hipStream_t st);
+// loss[0] = sum_t kl_row[t] (/ T unless per_token), one workgroup, fixed order
+hipError_t launch_loss_reduce(const float *kl_row, int T, bool per_token, float *loss, hipStream_t st);
+
 hipError_t launch_teacher_kl(const LaunchLayout &L, bool sparse, const float *scores, int64_t ld,
                              bool selected, const int32_t *ids, int k_eff, const float *cmass, const void *q,
                              const void *ckv, const float *lse_nc, bool bf16, int H, int D,
                              float scale, bool per_token, float *teacher, int64_t ld_teacher,
-                             float *kl_row, float *loss, hipStream_t st);
+                             float *kl_row, float *loss /* NULL: kl_row only */, hipStream_t st);
 
 hipError_t launch_indexer_loss_bwd(const LaunchLayout &L, bool sparse, const void *q_idx,
                                   const void *k_idx, const float *weights, int Hi, int Di,
@@ -47,6 +57,7 @@ bool indexer_supported(bool bf16, int Hi, int Di);
 bool indexer_topk_supported(bool bf16, int Hi, int Di, int max_seqlen_k);
 bool topk_supported(int max_seqlen_k, int k_eff);
 bool attn_supported(bool bf16, int H, int D, int k_eff);
+bool attn_kl_fused_supported(const LaunchLayout &L, bool bf16, int H, int D, int k_eff, int window);
 bool dense_teacher_supported(bool bf16, int H, int D, int max_seqlen_k);
 bool indexer_bwd_supported(bool bf16, int Hi, int Di, int k_eff, bool sparse, int max_seqlen_k);
 

@@ -37,7 +37,7 @@ class _CLayout(ctypes.Structure):
 
 EXPORTS = ("csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
            "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd", "csa_indexer_loss_bwd_workspace",
-           "csa_cp_plan", "csa_indexer_topk")
+           "csa_cp_plan", "csa_indexer_topk", "csa_sparse_attn_kl_fwd", "csa_loss_reduce")
 
 
 def lib_path() -> str:
@@ -75,6 +75,11 @@ def load():
     lib.csa_indexer_loss_bwd_workspace.argtypes = [LP, I32, I32]
     lib.csa_indexer_topk.restype = ctypes.c_int
     lib.csa_indexer_topk.argtypes = [LP, P, P, P, ctypes.c_int, I32, I32, F32, I32, P, P, P, P]
+    lib.csa_sparse_attn_kl_fwd.restype = ctypes.c_int
+    lib.csa_sparse_attn_kl_fwd.argtypes = [LP, P, P, P, P, P, I32, I32, ctypes.c_int, I32, I32, F32, P, I64, I32,
+                                           I32, P, P, P, P, P, I64, P, P, P]
+    lib.csa_loss_reduce.restype = ctypes.c_int
+    lib.csa_loss_reduce.argtypes = [P, I32, I32, P, P]
     lib.csa_cp_plan.restype = ctypes.c_int
     lib.csa_cp_plan.argtypes = [I32, P, I32, I32, I32, P, P, P, P, P, P]
     _lib = lib
@@ -184,6 +189,45 @@ def csa_sparse_attn_fwd(layout: Layout, q, kv, ckv, sink, ids, window: int, soft
     return out, lse, lse_nc, cmass
 
 
+def csa_sparse_attn_kl_fwd(layout: Layout, q, kv, ckv, sink, ids, window: int, softmax_scale: float, scores,
+                           scores_selected: bool, per_token: bool = False, want_teacher: bool = False,
+                           out=None, lse=None, lse_nc=None, cmass=None, teacher=None, kl_row=None, loss=None,
+                           reduce: bool = True):
+    """Attention + sparse-loss teacher + KL + loss in one call:
+    (out, lse, lse_nc, cmass, teacher or None, kl_row, loss); reduce=False leaves the loss
+    to csa_loss_reduce (loss is then None)."""
+    T, H, D = q.shape
+    k_eff_ = ids.shape[1]
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((T, H), **f32) if lse is None else lse
+    lse_nc = torch.empty((T, H), **f32) if lse_nc is None else lse_nc
+    cmass = torch.empty((T, k_eff_), **f32) if cmass is None else cmass
+    if want_teacher and teacher is None:
+        teacher = torch.empty((T, k_eff_), **f32)
+    kl_row = torch.empty((T,), **f32) if kl_row is None else kl_row
+    if reduce and loss is None:
+        loss = torch.empty((1,), **f32)
+    if not reduce:
+        loss = None
+    _check(load().csa_sparse_attn_kl_fwd(
+        ctypes.byref(layout.c()), _ptr(q), _ptr(kv), _ptr(ckv), _ptr(sink), _ptr(ids), k_eff_, int(window),
+        _dtype(q), H, D, float(softmax_scale), _ptr(scores), scores.stride(0), 1 if scores_selected else 0,
+        1 if per_token else 0, _ptr(out), _ptr(lse), _ptr(lse_nc), _ptr(cmass),
+        _ptr(teacher) if teacher is not None else None, teacher.stride(0) if teacher is not None else 0,
+        _ptr(kl_row), _ptr(loss) if loss is not None else None, _stream()))
+    return out, lse, lse_nc, cmass, teacher, kl_row, loss
+
+
+def csa_loss_reduce(kl_row, per_token: bool = False, loss=None):
+    """loss = sum(kl_row) / len(kl_row) (or the sum), reduced on the GPU in a fixed order."""
+    loss = torch.empty((1,), dtype=torch.float32, device=kl_row.device) if loss is None else loss
+    _check(load().csa_loss_reduce(_ptr(kl_row), int(kl_row.shape[0]), 1 if per_token else 0, _ptr(loss),
+                                  _stream()))
+    return loss
+
+
 def csa_indexer_topk(layout: Layout, q_idx, k_idx, weights, idx_scale: float, topk: int, ids=None,
                      sel_scores=None, row_lse=None, want_lse: bool = False):
     """Fused scores + top-k: (ids, sel_scores, row_lse or None); the score matrix is never
@@ -285,10 +329,12 @@ def layout_of_inputs(inp) -> Layout:
                   wl.max_seqlen_k, inp.offsets, inp.cu_q_real)
 
 
-def forward(inp, want_teacher=False, fused=False):
+def forward(inp, want_teacher=False, fused=False, attn_kl=False):
     """The whole path on one Inputs, on the current stream: the four calls, or with
     fused=True (sparse loss) csa_indexer_topk in place of the score and top-k calls, the
-    teacher/KL then reading the selected scores (no score matrix: scores is None)."""
+    teacher/KL then reading the selected scores (no score matrix: scores is None), and
+    with attn_kl=True (sparse loss) csa_sparse_attn_kl_fwd in place of the attention and
+    teacher/KL calls."""
     wl = inp.wl
     L = layout_of_inputs(inp)
     sel = row_lse = scores = None
@@ -300,6 +346,14 @@ def forward(inp, want_teacher=False, fused=False):
     else:
         scores = csa_indexer_score(L, inp.q_idx, inp.k_idx, inp.weights, inp.idx_scale)
         ids = csa_topk(L, scores, wl.topk)
+    if attn_kl:
+        if not wl.sparse_loss:
+            raise RuntimeError("the attention + teacher/KL call serves the sparse loss")
+        out, lse, lse_nc, cmass, teacher, kl_row, loss = csa_sparse_attn_kl_fwd(
+            L, inp.q, inp.kv, inp.ckv, inp.sink, ids, wl.window, inp.scale, sel if fused else scores,
+            scores_selected=fused, want_teacher=want_teacher)
+        return dict(scores=scores, ids=ids, out=out, lse=lse, lse_nc=lse_nc, cmass=cmass,
+                    teacher=teacher, kl_row=kl_row, loss=loss, sel=sel, row_lse=row_lse)
     out, lse, lse_nc, cmass = csa_sparse_attn_fwd(L, inp.q, inp.kv, inp.ckv, inp.sink, ids, wl.window,
                                                   inp.scale, want_cmass=wl.sparse_loss)
     teacher, kl_row, loss = csa_indexer_teacher_kl(L, wl.sparse_loss, sel if fused else scores, ids, cmass,
@@ -347,6 +401,22 @@ class Prepared:
                          _ptr(teacher) if teacher is not None else None,
                          ctypes.c_int64(teacher.stride(0) if teacher is not None else 0),
                          _ptr(kl_row), _ptr(loss), st)
+        if sparse_loss and cmass is not None:
+            self.args_attn_kl = (Lp, _ptr(inp.q), _ptr(inp.kv), _ptr(inp.ckv), _ptr(inp.sink), _ptr(ids), k_eff_,
+                                 int(window), _dtype(inp.q), H, D, ctypes.c_float(inp.scale), _ptr(tkl_scores),
+                                 ctypes.c_int64(tkl_scores.stride(0)), 1 if sel is not None else 0, 0,
+                                 _ptr(out), _ptr(lse), _ptr(lse_nc), _ptr(cmass),
+                                 _ptr(teacher) if teacher is not None else None,
+                                 ctypes.c_int64(teacher.stride(0) if teacher is not None else 0),
+                                 _ptr(kl_row), None, st)
+            self.args_loss = (_ptr(kl_row), T, 0, _ptr(loss), st)
+
+    def csa_sparse_attn_kl_fwd(self):
+        """attention + teacher + KL (kl_row only; csa_loss_reduce then gives the loss)"""
+        _check(self._lib.csa_sparse_attn_kl_fwd(*self.args_attn_kl))
+
+    def csa_loss_reduce(self):
+        _check(self._lib.csa_loss_reduce(*self.args_loss))
 
     def csa_indexer_score(self):
         _check(self._lib.csa_indexer_score(*self.args_score))

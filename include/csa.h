@@ -10,6 +10,8 @@
  *   csa_indexer_teacher_kl paper-equivalent teacher, KL(teacher || indexer softmax)
  *                          and the loss reduction
  * and, after it, csa_indexer_loss_bwd (the loss gradients for the indexer inputs).
+ * Two calls merge steps: csa_indexer_topk (scores + top-k without the score matrix) and
+ * csa_sparse_attn_kl_fwd (attention + teacher + KL + loss for the sparse loss).
  *
  * Sources cited below by tag:
  *  [I5776]  page "[Bug] DSV4 unfused CSA indexer loss uses a compressed-only teacher
@@ -216,6 +218,45 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss,
                                     csa_dtype_t dt, int32_t H, int32_t D, float softmax_scale,
                                     int32_t per_token_loss, float *teacher, int64_t ld_teacher,
                                     float *kl_row, float *loss, void *stream);
+
+/*
+ * csa_sparse_attn_kl_fwd -- csa_sparse_attn_fwd followed by csa_indexer_teacher_kl with
+ * the sparse loss, as one call: the attention produces the per-head compressed
+ * probabilities, and the teacher and the KL reduce them in the same pass ([I5776]
+ * "Paper reference", t_j equation: the teacher is the attention's own head-summed
+ * distribution over the compressed set, Z_h keeping the sink and window terms).
+ * Computes exactly what the two calls compute, with the same arguments:
+ *   out, lse, lse_nc, cmass      as csa_sparse_attn_fwd (cmass is required here);
+ *   teacher, kl_row, loss        as csa_indexer_teacher_kl with sparse_loss = 1 (the
+ *                                support is the valid top-k slots of ids[t, :]).
+ * scores [T, ld_scores] fp32: with scores_selected != 0 slot j of row t holds the score
+ * of ids[t, j] (sel_scores of csa_indexer_topk, ld_scores >= k_eff); otherwise the full
+ * score rows of csa_indexer_score (ld_scores >= max_seqlen_k).
+ * With scores_selected != 0 and a shape of the one-wave-per-query attention kernel
+ * (dt = CSA_BF16, H <= 16, D in {64, 128}, window >= 1, k_eff <= 256) the attention
+ * kernel finishes each row's teacher and KL in its epilogue and one more kernel reduces
+ * the loss; every other supported shape runs the attention and teacher kernels in turn.
+ * loss may be NULL: then only kl_row is written and csa_loss_reduce finishes the loss.
+ * Supported: as csa_sparse_attn_fwd, with 1 <= k_eff.
+ */
+csa_status_t csa_sparse_attn_kl_fwd(const csa_layout_t *L, const void *q, const void *kv,
+                                    const void *ckv, const float *sink, const int32_t *ids,
+                                    int32_t k_eff, int32_t window, csa_dtype_t dt, int32_t H,
+                                    int32_t D, float softmax_scale, const float *scores,
+                                    int64_t ld_scores, int32_t scores_selected,
+                                    int32_t per_token_loss, void *out, float *lse, float *lse_nc,
+                                    float *cmass, float *teacher, int64_t ld_teacher,
+                                    float *kl_row, float *loss, void *stream);
+
+/*
+ * csa_loss_reduce -- loss[0] = sum_t kl_row[t] / total_q, or the plain sum if
+ * per_token_loss != 0 (the divisor counts every physical row: [I5776] review comment),
+ * 0 for total_q = 0.  The last step of csa_indexer_teacher_kl as a call of its own, for
+ * csa_sparse_attn_kl_fwd with loss = NULL.  Deterministic: one workgroup adds the rows in
+ * a fixed order in fp64.  kl_row [total_q] fp32 (may be NULL if total_q = 0); loss [1].
+ */
+csa_status_t csa_loss_reduce(const float *kl_row, int32_t total_q, int32_t per_token_loss,
+                             float *loss, void *stream);
 
 /*
  * csa_indexer_loss_bwd -- gradients of the indexer loss for the indexer q, weights and k.

@@ -28,7 +28,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) == {"csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
                           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd",
-                          "csa_indexer_loss_bwd_workspace", "csa_cp_plan", "csa_indexer_topk"}
+                          "csa_indexer_loss_bwd_workspace", "csa_cp_plan", "csa_indexer_topk",
+                          "csa_sparse_attn_kl_fwd", "csa_loss_reduce"}
     from deepseek_v4_csa_amd import ops
     assert set(ops.EXPORTS) == set(names)
     for n in names:
@@ -119,6 +120,30 @@ def test_argument_misuse_is_rejected(lib):
     Lw = _layout(ops, total_q=8192, max_seqlen_q=8192, total_k=2048, max_seqlen_k=2048)
     assert fz(B(Lw), FAKE, FAKE, FAKE, 1, 16, 64, 0.1, 4, FAKE, FAKE, None, None) == 2  # rows too long
     assert "fused" in lib.csa_last_error().decode()
+    # attention + teacher/KL in one call
+    akl = lib.csa_sparse_attn_kl_fwd
+    args = [B(L), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 4, 64, 0.1, FAKE, 4, 1, 0,
+            FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None]
+    a = list(args); a[6] = 0
+    assert akl(*a) == 1                                                            # k_eff = 0
+    a = list(args); a[19] = None
+    assert akl(*a) == 1                                                            # null cmass
+    a = list(args); a[12] = None
+    assert akl(*a) == 1                                                            # null scores
+    a = list(args); a[13] = 3
+    assert akl(*a) == 1                                                            # selected ld < k_eff
+    a = list(args); a[14] = 0
+    assert akl(*a) == 1                                                            # full rows ld < max_seqlen_k
+    a = list(args); a[20] = FAKE; a[21] = 3
+    assert akl(*a) == 1                                                            # ld_teacher < k_eff
+    a = list(args); a[7] = -1
+    assert akl(*a) == 1                                                            # window < 0
+    a = list(args); a[10] = 96
+    assert akl(*a) == 2                                                            # D = 96
+    assert lib.csa_last_error().decode().startswith("csa_sparse_attn_kl_fwd")
+    assert lib.csa_loss_reduce(FAKE, 16, 0, None, None) == 1                      # null loss
+    assert lib.csa_loss_reduce(None, 16, 0, FAKE, None) == 1                      # null kl_row
+    assert lib.csa_loss_reduce(FAKE, -1, 0, FAKE, None) == 1                      # total_q < 0
 
 
 def test_backward_workspace_query(lib):
