@@ -68,6 +68,9 @@ csa_status_t check_layout(const csa_layout_t *L, const char *fn, csa::LaunchLayo
 }
 
 bool dtype_ok(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+// the kernels scale logits after taking maxima of unscaled products, so the scale must be
+// positive (and finite: a softmax temperature)
+bool scale_ok(float s) { return s > 0.f && s <= 3.4e38f; }
 
 int k_eff_of(const csa_layout_t *L, int topk) { return topk < L->max_seqlen_k ? topk : L->max_seqlen_k; }
 
@@ -164,6 +167,7 @@ csa_status_t csa_sparse_attn_fwd(const csa_layout_t *L, const void *q, const voi
   if (window < 0) return fail(CSA_ERR_INVALID, "%s: window=%d < 0", fn, window);
   if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
   if (H < 1 || D < 1) return fail(CSA_ERR_INVALID, "%s: H=%d, D=%d must be >= 1", fn, H, D);
+  if (!scale_ok(softmax_scale)) return fail(CSA_ERR_INVALID, "%s: softmax_scale must be finite and > 0", fn);
   if (!csa::attn_supported(dt == CSA_BF16, H, D, k_eff))
     return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d H=%d D=%d k_eff=%d", fn, (int)dt, H, D, k_eff);
   if (L->total_q == 0) return ok();
@@ -199,6 +203,7 @@ csa_status_t csa_indexer_teacher_kl(const csa_layout_t *L, int32_t sparse_loss, 
       return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < k_eff=%d", fn, (long long)ld_teacher, k_eff);
   } else {
     if (!q || !ckv || !lse_nc) return fail(CSA_ERR_INVALID, "%s: dense loss needs q, ckv and lse_nc", fn);
+    if (!scale_ok(softmax_scale)) return fail(CSA_ERR_INVALID, "%s: softmax_scale must be finite and > 0", fn);
     if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
     if (H < 1 || D < 1) return fail(CSA_ERR_INVALID, "%s: H=%d, D=%d must be >= 1", fn, H, D);
     if (teacher && ld_teacher < L->max_seqlen_k)
@@ -239,6 +244,7 @@ csa_status_t csa_sparse_attn_kl_fwd(const csa_layout_t *L, const void *q, const 
     return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld < %d", fn, (long long)ld_scores, need_ld);
   if (teacher && ld_teacher < k_eff)
     return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < k_eff=%d", fn, (long long)ld_teacher, k_eff);
+  if (!scale_ok(softmax_scale)) return fail(CSA_ERR_INVALID, "%s: softmax_scale must be finite and > 0", fn);
   if (!csa::attn_supported(dt == CSA_BF16, H, D, k_eff))
     return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d H=%d D=%d k_eff=%d", fn, (int)dt, H, D, k_eff);
   const hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -345,8 +345,9 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
 // Per-key sums over heads (cmass) are reduced across waves through LDS one step later,
 // behind the next barrier.
 // ============================================================================
-template <int D, int HG>
-__global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
+// (at least three waves per SIMD where the registers of a shape allow it)
+template <int D, int HG, int NG>
+__global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void sparse_attn_wg_kernel(
     LayoutDev L, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const uint16_t *__restrict__ ckv, const float *__restrict__ sink,
     const int32_t *__restrict__ ids, int k_eff, int window, int H, int total_q, int total_k,
@@ -360,6 +361,7 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
   constexpr int TILE = 32 * ROWB;
   constexpr int NT = 64 * HG;
   constexpr int BDT = D >= 512 ? D / 128 : D / 32;   // d-tiles per batch of V^T reads
+  constexpr int HPW = 16 * NG;        // heads per wave
   constexpr float NINF = -__builtin_inff();
   extern __shared__ __attribute__((aligned(16))) char wg_dyn[];   // 2 tiles, then the ids
   int *ids_l = reinterpret_cast<int *>(wg_dyn + 2 * TILE);
@@ -368,20 +370,27 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
   const int t = blockIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-  const int h = 16 * w + r16;
-  const bool h_ok = h < H;
+  // head group gi of the wave: heads HPW*w + 16*gi + (0..15), lane r16 holding one of them
+  int hh[NG];
+  bool h_ok[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    hh[gi] = HPW * w + 16 * gi + r16;
+    h_ok[gi] = hh[gi] < H;
+  }
   const RowGeo geo = row_geo(L, t);
   const int w_lo = max(geo.q_start, t - window + 1);
   const int nw = window > 0 ? t - w_lo + 1 : 0;
   const int nwc = (nw + 31) >> 5, ncc = (k_eff + 31) >> 5, nch = nwc + ncc;
   // the row's ids, padded with -1 to whole 32-row chunks
   for (int i = tid; i < ncc * 32; i += NT) ids_l[i] = i < k_eff ? ids[(int64_t)t * k_eff + i] : -1;
-  // Q^T operand, MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
-  u32x4 qf[NC];
-  {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok ? h : 0)) * D) + g;
+  // Q^T operands, MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
+  u32x4 qf[NG][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = h_ok ? p[4 * c] : u32x4{0, 0, 0, 0};
+  for (int gi = 0; gi < NG; ++gi) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok[gi] ? hh[gi] : 0)) * D) + g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[gi][c] = h_ok[gi] ? p[4 * c] : u32x4{0, 0, 0, 0};
   }
   const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)total_q * ROWB);
   const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * ROWB);
@@ -442,25 +451,43 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
     }
     return (uint32_t)__ballot(ids_l[32 * (ci - nwc) + (lane & 31)] >= 0);
   };
-  // S^T for the 32 rows of a tile, this lane's 8 logits (rows 4g+i and 16+4g+i, head r16),
-  // scaled to log2 units, -inf where masked
-  auto logits = [&](const char *base, uint32_t bm, float (&sv)[8]) {
+  // S^T for the 32 rows of a tile: this lane's 8 products q.k per head group (rows 4g+i
+  // and 16+4g+i, head 16 gi + r16 of the wave), unscaled, -inf where masked.  Each K
+  // operand read from LDS feeds the MFMAs of every head group.  The masking is skipped
+  // when every row of the tile is valid and every head of the wave exists.
+  const bool wave_full = HPW * (w + 1) <= H;
+  auto logits = [&](const char *base, uint32_t bm, float (&sv)[NG][8]) {
     int kxs = kx;
     asm volatile("" : "+v"(kxs));
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc0[NG], acc1[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) acc0[gi] = acc1[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const char *kp = base + kbase + 64 * (c ^ kxs);
       const u32x4 k0 = *reinterpret_cast<const u32x4 *>(kp);
       const u32x4 k1 = *reinterpret_cast<const u32x4 *>(kp + 16 * ROWB);
-      acc0 = mfma16x16x32(k0, qf[c], acc0);
-      acc1 = mfma16x16x32(k1, qf[c], acc1);
-    }
-    const uint32_t m0 = h_ok ? (bm >> (4 * g)) : 0u, m1 = h_ok ? (bm >> (16 + 4 * g)) : 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = ((m0 >> i) & 1) ? acc0[i] * sl2 : NINF;
-      sv[4 + i] = ((m1 >> i) & 1) ? acc1[i] * sl2 : NINF;
+      for (int gi = 0; gi < NG; ++gi) {
+        acc0[gi] = mfma16x16x32(k0, qf[gi][c], acc0[gi]);
+        acc1[gi] = mfma16x16x32(k1, qf[gi][c], acc1[gi]);
+      }
+    }
+    if (wave_full && bm == 0xffffffffu) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sv[gi][i] = acc0[gi][i]; sv[gi][4 + i] = acc1[gi][i]; }
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const uint32_t m0 = h_ok[gi] ? (bm >> (4 * g)) : 0u, m1 = h_ok[gi] ? (bm >> (16 + 4 * g)) : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[gi][i] = ((m0 >> i) & 1) ? acc0[gi][i] : NINF;
+          sv[gi][4 + i] = ((m1 >> i) & 1) ? acc1[gi][i] : NINF;
+        }
+      }
     }
   };
 
@@ -481,41 +508,58 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
   if (ns > 0) issue(0, tile(0));
 
   // ---------------------------------------------------------------- pass 1: max / sum
-  const float a2 = h_ok ? sink[h] * LOG2E : NINF;
-  float m = (g == 0) ? a2 : NINF;
-  float l = (g == 0 && a2 > NINF) ? 1.f : 0.f;
-  float m_nc = m, l_nc = l;
+  float m[NG], l[NG], m_nc[NG], l_nc[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float a2 = h_ok[gi] ? sink[hh[gi]] * LOG2E : NINF;
+    m[gi] = (g == 0) ? a2 : NINF;
+    l[gi] = (g == 0 && a2 > NINF) ? 1.f : 0.f;
+    m_nc[gi] = m[gi];
+    l_nc[gi] = l[gi];
+  }
   for (int ci = 0; ci < nch; ++ci) {
     const int n = ci;
     top(n);
-    if (ci == nwc) { m_nc = m; l_nc = l; }
-    float sv[8];
+    if (ci == nwc) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) { m_nc[gi] = m[gi]; l_nc[gi] = l[gi]; }
+    }
+    float sv[NG][8];
     logits(tile(n), row_mask(ci), sv);
-    float cm = sv[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
-    const float mn = fmaxf(m, cm);
-    if (mn > NINF) {
-      float acc = l * fast_exp2(m - mn);
+    for (int gi = 0; gi < NG; ++gi) {
+      float cm = sv[gi][0];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += fast_exp2(sv[e] - mn);
-      l = acc;
-      m = mn;
+      for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[gi][e]);
+      const float mn = fmaxf(m[gi], cm * sl2);   // log2 units (sl2 > 0 keeps the order)
+      if (mn > NINF) {
+        float acc = l[gi] * fast_exp2(m[gi] - mn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += fast_exp2(fmaf(sv[gi][e], sl2, -mn));
+        l[gi] = acc;
+        m[gi] = mn;
+      }
     }
   }
-  if (ncc == 0) { m_nc = m; l_nc = l; }
-  const float M = across_groups_max(m);
-  const float Ls = across_groups_sum(M > NINF ? l * fast_exp2(m - M) : 0.f);
-  const float Mnc = across_groups_max(m_nc);
-  const float Lnc = across_groups_sum(Mnc > NINF ? l_nc * fast_exp2(m_nc - Mnc) : 0.f);
-  const float lse2 = Ls > 0.f ? M + __log2f(Ls) : NINF;
-  const float lse2_nc = Lnc > 0.f ? Mnc + __log2f(Lnc) : NINF;
-  const float nl = lse2 > NINF ? -lse2 : NINF;   // exp2(-inf) = 0: no probability at all
+  float lse2[NG], lse2_nc[NG], nl[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    if (ncc == 0) { m_nc[gi] = m[gi]; l_nc[gi] = l[gi]; }
+    const float M = across_groups_max(m[gi]);
+    const float Ls = across_groups_sum(M > NINF ? l[gi] * fast_exp2(m[gi] - M) : 0.f);
+    const float Mnc = across_groups_max(m_nc[gi]);
+    const float Lnc = across_groups_sum(Mnc > NINF ? l_nc[gi] * fast_exp2(m_nc[gi] - Mnc) : 0.f);
+    lse2[gi] = Ls > 0.f ? M + __log2f(Ls) : NINF;
+    lse2_nc[gi] = Lnc > 0.f ? Mnc + __log2f(Lnc) : NINF;
+    nl[gi] = lse2[gi] > NINF ? -lse2[gi] : NINF;   // exp2(-inf) = 0: no probability at all
+  }
 
   // ---------------------------------------------------------------- pass 2: P, O, cmass
-  f32x4 o[D / 16];
+  f32x4 o[NG][D / 16];
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[gi][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float *crow = cmass ? cmass + (int64_t)t * k_eff : nullptr;
   // sums over the waves of the compressed chunk staged at the previous step
   auto flush = [&](int cprev, int pbuf) {
@@ -534,16 +578,21 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
     top(n);
     if (ci > 0) flush(ci - 1, (n - 1) & 1);
     const char *base = tile(n);
-    float sv[8];
+    float sv[NG][8];
     logits(base, row_mask(ci), sv);
-    float p[8];
+    float p[NG][8];
+    u32x4 pb[NG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(sv[e] + nl);
-    const u32x4 pb = {pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]),
-                      pack2_bf16(p[6], p[7])};
+    for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[gi][e] = fast_exp2(fmaf(sv[gi][e], sl2, nl[gi]));
+      pb[gi] = u32x4{pack2_bf16(p[gi][0], p[gi][1]), pack2_bf16(p[gi][2], p[gi][3]),
+                     pack2_bf16(p[gi][4], p[gi][5]), pack2_bf16(p[gi][6], p[gi][7])};
+    }
     int vxs = vx;
     asm volatile("" : "+v"(vxs));
-    // V^T operands in batches of BDT d-tiles (fewer registers in flight)
+    // V^T operands in batches of BDT d-tiles (fewer registers in flight); each feeds the
+    // MFMAs of every head group
 #pragma unroll
     for (int hf = 0; hf < D / 16 / BDT; ++hf) {
       uint2 xv[2 * BDT];
@@ -559,13 +608,17 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
       for (int k = 0; k < BDT; ++k) {
         const int dt = hf * BDT + k;
         const u32x4 a = {xv[2 * k].x, xv[2 * k].y, xv[2 * k + 1].x, xv[2 * k + 1].y};
-        o[dt] = mfma16x16x32(a, pb, o[dt]);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) o[gi][dt] = mfma16x16x32(a, pb[gi], o[gi][dt]);
       }
     }
     if (crow && ci >= nwc) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float sh = group16_sum(p[e]);
+        float ps = p[0][e];
+#pragma unroll
+        for (int gi = 1; gi < NG; ++gi) ps += p[gi][e];
+        const float sh = group16_sum(ps);
         if (r16 == 0) cm_part[n & 1][w][(e < 4 ? 4 * g + e : 16 + 4 * g + e - 4)] = sh;
       }
     }
@@ -576,15 +629,18 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_wg_kernel(
   }
 
   // ---------------------------------------------------------------- outputs
-  if (h_ok) {
-    uint16_t *orow = out + ((int64_t)t * H + h) * D + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      *reinterpret_cast<uint2 *>(orow + 16 * dt) =
-          uint2{pack2_bf16(o[dt][0], o[dt][1]), pack2_bf16(o[dt][2], o[dt][3])};
-    if (g == 0) {
-      lse[(int64_t)t * H + h] = lse2 * LN2;
-      lse_nc[(int64_t)t * H + h] = lse2_nc * LN2;
+  for (int gi = 0; gi < NG; ++gi) {
+    if (h_ok[gi]) {
+      uint16_t *orow = out + ((int64_t)t * H + hh[gi]) * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<uint2 *>(orow + 16 * dt) =
+            uint2{pack2_bf16(o[gi][dt][0], o[gi][dt][1]), pack2_bf16(o[gi][dt][2], o[gi][dt][3])};
+      if (g == 0) {
+        lse[(int64_t)t * H + hh[gi]] = lse2[gi] * LN2;
+        lse_nc[(int64_t)t * H + hh[gi]] = lse2_nc[gi] * LN2;
+      }
     }
   }
 }
@@ -1386,18 +1442,21 @@ static hipError_t launch_d(const LaunchLayout &LL, const void *q, const void *kv
   return hipErrorInvalidValue;
 }
 
+// NG head groups of 16 per wave: 2 where the registers allow it (D <= 192), so that every
+// K and V operand read from LDS feeds two MFMAs
 template <int D>
 static hipError_t launch_wg(const LaunchLayout &LL, const void *q, const void *kv, const void *ckv,
                             const float *sink, const int32_t *ids, int k_eff, int window, int H,
                             float scale, void *out, float *lse, float *lse_nc, float *cmass,
                             hipStream_t st) {
+  constexpr int NG = D <= 192 ? 2 : 1;
   const float sl2 = scale * LOG2E;
-  const int hg = (H + 15) / 16;
+  const int hg = (H + 16 * NG - 1) / (16 * NG);
   const int ncc = (k_eff + 31) / 32;
   const size_t dyn = 2 * (size_t)32 * D * 2 + (size_t)ncc * 32 * sizeof(int);
 #define CSA_WG_CASE(G)                                                                                \
   if (hg <= G) {                                                                                      \
-    auto kern = sparse_attn_wg_kernel<D, G>;                                                          \
+    auto kern = sparse_attn_wg_kernel<D, G, NG>;                                                      \
     if (dyn > 65536) {                                                                                \
       const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),                 \
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn); \

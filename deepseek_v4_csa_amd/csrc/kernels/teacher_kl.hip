@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
 }
 
 // ---------------------------------------------------------------- dense
-// One workgroup per row, wave w owning heads 16w..16w+15.  The row's visible keys are the
+// One workgroup per row, wave w owning two groups of 16 heads (32w..32w+31), so that each
+// K operand read from LDS feeds the MFMAs of both.  The row's visible keys are the
 // first n rows of its segment's ckv, contiguous: they are staged 32 at a time into two LDS
 // tiles by buffer->LDS loads that the waves split between them (D/16 instructions of
 // 1 KiB per tile), each 16-byte piece p of tile row R at position p ^ row_swz<D>(R), and
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
 // exactly the n visible rows, so the loads past them read zeros.  Two passes over the
 // tiles: the exact l_h, then the head-summed probabilities m_j (summed within a wave on
 // DPP, across waves through LDS one step later, behind the next barrier).
-template <int D, int HG>
+template <int D, int HG, int NG>
 __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
     LayoutDev L, const float *__restrict__ scores, int64_t ld, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ ckv, const float *__restrict__ lse_nc, int H, float scale_log2,
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   constexpr int NIW = (NI + HG - 1) / HG;
   constexpr int TILE = 32 * ROWB;
   constexpr int NT = 64 * HG;
+  constexpr int HPW = 16 * NG;        // heads per wave (NG groups of 16)
   constexpr float NINF = -__builtin_inff();
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float *mj = reinterpret_cast<float *>(smem + 2 * TILE);      // [n_valid]
@@ -105,8 +107,14 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, hl = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = 16 * w + hl;
-  const bool h_ok = h < H;
+  int hh[NG];
+  bool h_ok[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    hh[gi] = HPW * w + 16 * gi + hl;
+    h_ok[gi] = hh[gi] < H;
+  }
+  const bool wave_full = HPW * (w + 1) <= H;
   const RowGeo geo = row_geo(L, t);
   const int n = geo.n_valid;
   if (loss_row_empty(L, geo, t)) {
@@ -115,12 +123,13 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
     if (tid == 0) kl_row[t] = 0.f;
     return;
   }
-  // Q^T operand, MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
-  u32x4 qf[NC];
-  {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok ? h : 0)) * D) + g;
+  // Q^T operands, MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
+  u32x4 qf[NG][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = h_ok ? p[4 * c] : u32x4{0, 0, 0, 0};
+  for (int gi = 0; gi < NG; ++gi) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok[gi] ? hh[gi] : 0)) * D) + g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[gi][c] = h_ok[gi] ? p[4 * c] : u32x4{0, 0, 0, 0};
   }
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(ckv + (int64_t)geo.k_base * D, (uint32_t)n * ROWB);
   const int nch = (n + 31) / 32;
@@ -141,22 +150,40 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   // K operand: row r16 (+16), piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3))
   const int ksw = row_swz<D>(hl);
   const int kbase = hl * ROWB + 16 * (g ^ (ksw & 3)), kx = ksw >> 2;
-  // this lane's 8 logits of chunk ci in log2 units (rows 4g+i and 16+4g+i, head h)
-  auto logits = [&](const char *base, int ci, float (&sv)[8]) {
+  // this lane's 8 products q.k of chunk ci per head group (rows 4g+i and 16+4g+i, head
+  // 16 gi + hl of the wave), unscaled, -inf past n or for a head past H; each K operand
+  // read from LDS feeds the MFMAs of every head group
+  auto logits = [&](const char *base, int ci, float (&sv)[NG][8]) {
     int kxs = kx;
     asm volatile("" : "+v"(kxs));
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc0[NG], acc1[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) acc0[gi] = acc1[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const char *kp = base + kbase + 64 * (c ^ kxs);
-      acc0 = mfma16x16x32(*reinterpret_cast<const u32x4 *>(kp), qf[c], acc0);
-      acc1 = mfma16x16x32(*reinterpret_cast<const u32x4 *>(kp + 16 * ROWB), qf[c], acc1);
+      const u32x4 k0 = *reinterpret_cast<const u32x4 *>(kp);
+      const u32x4 k1 = *reinterpret_cast<const u32x4 *>(kp + 16 * ROWB);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        acc0[gi] = mfma16x16x32(k0, qf[gi][c], acc0[gi]);
+        acc1[gi] = mfma16x16x32(k1, qf[gi][c], acc1[gi]);
+      }
     }
     const int j0 = 32 * ci + 4 * g;
+    if (wave_full && 32 * ci + 32 <= n) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (j0 + i < n && h_ok) ? acc0[i] * scale_log2 : NINF;
-      sv[4 + i] = (j0 + 16 + i < n && h_ok) ? acc1[i] * scale_log2 : NINF;
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sv[gi][i] = acc0[gi][i]; sv[gi][4 + i] = acc1[gi][i]; }
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[gi][i] = (j0 + i < n && h_ok[gi]) ? acc0[gi][i] : NINF;
+          sv[gi][4 + i] = (j0 + 16 + i < n && h_ok[gi]) ? acc1[gi][i] : NINF;
+        }
     }
   };
   const int ns = 2 * nch;   // steps: pass 1 over the chunks, then pass 2
@@ -168,30 +195,42 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   };
   if (ns > 0) issue(0, tile(0));
 
-  // pass 1: l_h = log2(2^{u_h} + sum_j 2^{c_hj})   (base-2 logits)
-  const float u2 = h_ok ? lse_nc[(int64_t)t * H + h] * LOG2E : NINF;
-  float m = g == 0 ? u2 : NINF;
-  float l = (g == 0 && u2 > NINF) ? 1.f : 0.f;
+  // pass 1: l_h = log2(2^{u_h} + sum_j 2^{c_hj})   (base-2 logits; scale_log2 > 0, so the
+  // maximum of the unscaled products is the maximum of the logits)
+  float m[NG], l[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float u2 = h_ok[gi] ? lse_nc[(int64_t)t * H + hh[gi]] * LOG2E : NINF;
+    m[gi] = g == 0 ? u2 : NINF;
+    l[gi] = (g == 0 && u2 > NINF) ? 1.f : 0.f;
+  }
   for (int ci = 0; ci < nch; ++ci) {
     top(ci);
-    float s[8];
+    float s[NG][8];
     logits(tile(ci), ci, s);
-    float cmx = s[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) cmx = fmaxf(cmx, s[e]);
-    const float mn = fmaxf(m, cmx);
-    if (mn > NINF) {
-      float acc = l * fast_exp2(m - mn);
+    for (int gi = 0; gi < NG; ++gi) {
+      float cmx = s[gi][0];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += fast_exp2(s[e] - mn);
-      l = acc;
-      m = mn;
+      for (int e = 1; e < 8; ++e) cmx = fmaxf(cmx, s[gi][e]);
+      const float mn = fmaxf(m[gi], cmx * scale_log2);
+      if (mn > NINF) {
+        float acc = l[gi] * fast_exp2(m[gi] - mn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += fast_exp2(fmaf(s[gi][e], scale_log2, -mn));
+        l[gi] = acc;
+        m[gi] = mn;
+      }
     }
   }
-  const float M = across_groups_max(m);
-  const float Ls = across_groups_sum(M > NINF ? l * fast_exp2(m - M) : 0.f);
-  const float ell2 = Ls > 0.f ? M + __log2f(Ls) : NINF;
-  const float nl = ell2 > NINF ? -ell2 : NINF;   // exp2(-inf) = 0: no mass at all
+  float nl[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float M = across_groups_max(m[gi]);
+    const float Ls = across_groups_sum(M > NINF ? l[gi] * fast_exp2(m[gi] - M) : 0.f);
+    const float ell2 = Ls > 0.f ? M + __log2f(Ls) : NINF;
+    nl[gi] = ell2 > NINF ? -ell2 : NINF;   // exp2(-inf) = 0: no mass at all
+  }
 
   // pass 2: m_j = sum_h 2^{c_hj - l_h}
   auto flush = [&](int cprev) {
@@ -209,11 +248,14 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
     const int st = nch + ci;
     top(st);
     if (ci > 0) flush(ci - 1);
-    float s[8];
+    float s[NG][8];
     logits(tile(st), ci, s);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float sh = group16_sum(fast_exp2(s[e] + nl));
+      float ps = fast_exp2(fmaf(s[0][e], scale_log2, nl[0]));
+#pragma unroll
+      for (int gi = 1; gi < NG; ++gi) ps += fast_exp2(fmaf(s[gi][e], scale_log2, nl[gi]));
+      const float sh = group16_sum(ps);
       if (hl == 0) part[st & 1][w][e < 4 ? 4 * g + e : 16 + 4 * g + e - 4] = sh;
     }
   }
@@ -302,18 +344,21 @@ template <int D>
 static hipError_t launch_dense(const LaunchLayout &LL, const float *scores, int64_t ld, const void *q,
                                const void *ckv, const float *lse_nc, int H, float scale,
                                float *teacher, int64_t ldt, float *kl_row, hipStream_t st) {
-  const int hg = (H + 15) / 16;
+  // two head groups of 16 per wave where the registers allow it: every K operand read
+  // from LDS then feeds two MFMAs
+  constexpr int NG = 2;
+  const int hg = (H + 16 * NG - 1) / (16 * NG);
   const size_t lds = (size_t)2 * 32 * D * 2 + (size_t)LL.max_seqlen_k * sizeof(float);
   const float sl2 = scale * LOG2E;
 #define CSA_DN_CASE(G)                                                                              \
   if (hg <= G) {                                                                                    \
     if (lds > 65536) {                                                                              \
       const hipError_t ea = hipFuncSetAttribute(                                                    \
-          reinterpret_cast<const void *>(teacher_kl_dense_kernel<D, G>),                            \
+          reinterpret_cast<const void *>(teacher_kl_dense_kernel<D, G, NG>),                            \
           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                                    \
       if (ea != hipSuccess) return ea;                                                              \
     }                                                                                               \
-    hipLaunchKernelGGL((teacher_kl_dense_kernel<D, G>), dim3((unsigned)LL.total_q), dim3(64 * G), \
+    hipLaunchKernelGGL((teacher_kl_dense_kernel<D, G, NG>), dim3((unsigned)LL.total_q), dim3(64 * G), \
                        lds, st, LL.dev, scores, ld, static_cast<const uint16_t *>(q),               \
                        static_cast<const uint16_t *>(ckv), lse_nc, H, sl2, teacher, ldt, kl_row);   \
     return hipGetLastError();                                                                       \

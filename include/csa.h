@@ -171,6 +171,7 @@ csa_status_t csa_indexer_topk(const csa_layout_t *L, const void *q_idx, const vo
  *   q [T, H, D], kv [T, D], ckv [T_k, D]: dtype dt;   out [T, H, D]: dtype dt
  *   sink [H] fp32;  ids [T, k_eff] int32;  lse, lse_nc [T, H] fp32;
  *   cmass [T, k_eff] fp32 or NULL (then not computed).
+ * softmax_scale must be finite and > 0 (CSA_ERR_INVALID otherwise).
  * Supported: dt = CSA_BF16 with D in {64, 128, 192, 256, 512}, dt = CSA_F32 with
  * D in {64, 128}; 1 <= H <= 128; 0 <= window; 0 <= k_eff <= 4096.
  * A row with no key at all and sink = -inf gets out = 0, lse = lse_nc = -inf.

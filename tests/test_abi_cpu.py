@@ -73,6 +73,10 @@ def test_argument_misuse_is_rejected(lib):
                                    FAKE, FAKE, FAKE, None, None) == 2            # D = 96
     assert lib.csa_sparse_attn_fwd(B(L), FAKE, FAKE, FAKE, FAKE, FAKE, 32, 8, 1, 4, 64, 0.1,
                                    FAKE, FAKE, FAKE, None, None) == 1            # k_eff > max_seqlen_k
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert lib.csa_sparse_attn_fwd(B(L), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 4, 64, bad,
+                                       FAKE, FAKE, FAKE, None, None) == 1        # softmax_scale
+        assert "softmax_scale" in lib.csa_last_error().decode()
     assert lib.csa_indexer_teacher_kl(B(L), 1, FAKE, 16, 0, None, 4, FAKE, None, None, None, 1, 4, 64,
                                       0.1, 0, None, 0, FAKE, FAKE, None) == 1    # sparse without ids
     assert lib.csa_indexer_teacher_kl(B(L), 0, FAKE, 16, 1, None, 0, None, FAKE, FAKE, FAKE, 1, 4, 64,
@@ -140,6 +144,8 @@ def test_argument_misuse_is_rejected(lib):
     assert akl(*a) == 1                                                            # window < 0
     a = list(args); a[10] = 96
     assert akl(*a) == 2                                                            # D = 96
+    a = list(args); a[11] = -1.0
+    assert akl(*a) == 1                                                            # softmax_scale < 0
     assert lib.csa_last_error().decode().startswith("csa_sparse_attn_kl_fwd")
     assert lib.csa_loss_reduce(FAKE, 16, 0, None, None) == 1                      # null loss
     assert lib.csa_loss_reduce(None, 16, 0, FAKE, None) == 1                      # null kl_row
