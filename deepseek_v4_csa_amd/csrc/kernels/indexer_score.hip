@@ -499,9 +499,12 @@ __global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
           to.sel[o + c] = c < n ? row[c] : -__builtin_inff();
         }
       } else {
+        // the row's two outputs through buffer stores sharing one 32-bit offset
+        const __amdgpu_buffer_rsrc_t rid = make_rsrc(to.ids + o, (uint32_t)to.k_eff * 4);
+        const __amdgpu_buffer_rsrc_t rsel = make_rsrc(to.sel + o, (uint32_t)to.k_eff * 4);
         wave_select<VPL>(val, n, to.k_eff, hist, [&](int pos, int j, int v) {
-          to.ids[o + pos] = k_base + j;
-          to.sel[o + pos] = val[v];
+          __builtin_amdgcn_raw_buffer_store_b32(k_base + j, rid, pos * 4, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[v]), rsel, pos * 4, 0, 0);
         });
       }
     }

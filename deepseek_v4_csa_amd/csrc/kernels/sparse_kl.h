@@ -27,11 +27,12 @@ struct KlArgs {
 };
 
 // log(1 + x) for x > -1: |x| < 1/2 by the series 2 atanh(u), u = x / (2 + x) (|u| < 1/3,
-// terms through u^15: truncation below 3e-9 relative); otherwise the hardware log of 1 + x,
-// where 1 + x is exact enough (relative error ~1e-7 of the result).
+// terms through u^15: truncation below 3e-9 relative; the quotient by the hardware
+// reciprocal, 1 ulp); otherwise the hardware log of 1 + x, where 1 + x is exact enough
+// (relative error ~1e-7 of the result).
 __device__ __forceinline__ float log1p_kl(float x) {
   if (fabsf(x) < 0.5f) {
-    const float u = x / (2.f + x);
+    const float u = x * __builtin_amdgcn_rcpf(2.f + x);
     const float u2 = u * u;
     float p = 1.f / 15.f;
     p = fmaf(p, u2, 1.f / 13.f);

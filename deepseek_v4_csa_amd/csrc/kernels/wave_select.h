@@ -112,14 +112,27 @@ __device__ __forceinline__ void wave_select(const float (&val)[VPL], int n, int 
   // compaction in index order: the prefix (bits >= cur) above thr, or equal to thr --
   // all of them when the bin was taken whole, else the first `need` ties (cur == 0)
   int base = 0, tie_base = 0;
+  if (whole) {   // the usual case: no tie to rank, every prefix >= thr is selected
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      if (v * 64 >= n) break;
+      const int j = v * 64 + lane;
+      const bool sel = j < n && (key[v] >> cur) >= thr;
+      const uint64_t bs = __ballot(sel);
+      const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0));
+      if (sel && pos < k_eff) emit(pos, j, v);
+      base += __popcll(bs);
+    }
+    return;
+  }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     if (v * 64 >= n) break;
     const int j = v * 64 + lane;
     const bool valid = j < n;
     const uint32_t kp = key[v] >> cur;
-    const bool gt = valid && (kp > thr || (whole && kp == thr));
-    const bool eq = valid && !whole && kp == thr;
+    const bool gt = valid && kp > thr;
+    const bool eq = valid && kp == thr;   // ties at the threshold (cur == 0 here)
     const uint64_t be = __ballot(eq);
     const int eq_rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0));
     const bool sel = gt || (eq && tie_base + eq_rank < need);

@@ -31,6 +31,7 @@ FAMILIES = {
     "indexer_score": ("csa::indexer_score", "indexer_score.hip"),
     "topk": ("csa::topk", "topk.hip"),
     "sparse_attn": ("csa::sparse_attn", "sparse_attn.hip"),
+    "sparse_attn_kl": ("csa::sparse_attn_pipe_kernel", "sparse_attn.hip"),
     "teacher_kl": ("csa::teacher_kl", "teacher_kl.hip"),
     "loss_reduce": ("csa::loss_reduce", "teacher_kl.hip"),
 }
@@ -42,6 +43,9 @@ def short(name: str) -> str:
 
 
 def family_of(name: str):
+    # the attention kernel that also finishes the teacher and KL (csa_sparse_attn_kl_fwd)
+    if "csa::sparse_attn_pipe_kernel" in name and ", true>" in name:
+        return "sparse_attn_kl"
     for fam, (prefix, _) in FAMILIES.items():
         if prefix in name:
             return fam
