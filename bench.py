@@ -47,9 +47,10 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="path: score and top-k as two calls (the score matrix stored) even where "
                          "the fused call applies")
-    ap.add_argument("--unfused-attn", action="store_true",
-                    help="path: attention and teacher/KL as two calls (csa_sparse_attn_fwd, "
-                         "csa_indexer_teacher_kl) instead of csa_sparse_attn_kl_fwd")
+    ap.add_argument("--attn-kl", action="store_true",
+                    help="path: attention, teacher and KL as one call (csa_sparse_attn_kl_fwd, then "
+                         "csa_loss_reduce) instead of csa_sparse_attn_fwd + csa_indexer_teacher_kl "
+                         "(measured about 1%% slower on bshd-b2-s4096, so not the default)")
     ap.add_argument("--cp", type=int, default=8, help="cp-share: CP size")
     ap.add_argument("--rank", type=int, default=0, help="cp-share: rank")
     return ap.parse_args()
@@ -405,8 +406,9 @@ def main():
             fused, sel = False, None
     if fused:
         scores = None
-    # sparse loss: attention, teacher and KL in one call (the loss reduced by its own call)
-    attn_kl = wl.sparse_loss and not args.unfused_attn
+    # --attn-kl (sparse loss): attention, teacher and KL in one call, the loss reduced by
+    # its own call
+    attn_kl = wl.sparse_loss and args.attn_kl
     att_name = "sparse_attn_kl" if attn_kl else "sparse_attn"
     names = (("indexer_topk",) if fused else ("indexer_score", "topk")) + \
         ((att_name, "loss_reduce") if attn_kl else (att_name, "teacher_kl"))
