@@ -66,9 +66,12 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 // reductions over the 16 lanes of a lane group (lanes with the same l/16), on DPP:
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  These controls
+// are permutations within a 16-lane row (every lane has a source), so the plain DPP move
+// is used: no old value to set up first.
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+  static_assert(CTRL == 0xB1 || CTRL == 0x4E || CTRL == 0x141 || CTRL == 0x140, "a full in-row permutation");
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 __device__ __forceinline__ float group16_sum(float v) {
   v += dpp<0xB1>(v);
@@ -80,8 +83,9 @@ __device__ __forceinline__ float group16_sum(float v) {
 // full-wave reductions on DPP (16-lane rows) plus four readlanes; the result is uniform
 template <int CTRL> __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+  static_assert(CTRL == 0xB1 || CTRL == 0x4E || CTRL == 0x141 || CTRL == 0x140, "a full in-row permutation");
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 __device__ __forceinline__ double readlane_f64(double v, int l) {
