@@ -109,7 +109,7 @@ csa_status_t csa_indexer_score(const csa_layout_t *L, const void *q_idx, const v
 }
 
 csa_status_t csa_topk(const csa_layout_t *L, const float *scores, int64_t ld_scores, int32_t topk,
-                      int32_t *ids, void *stream) {
+                      int32_t *ids, float *sel_scores, void *stream) {
   const char *fn = "csa_topk";
   csa::LaunchLayout LL;
   csa_status_t st = check_layout(L, fn, &LL);
@@ -124,7 +124,8 @@ csa_status_t csa_topk(const csa_layout_t *L, const float *scores, int64_t ld_sco
     return fail(CSA_ERR_UNSUPPORTED, "%s: max_seqlen_k=%d exceeds the supported 16384", fn,
                 L->max_seqlen_k);
   if (L->total_q == 0) return ok();
-  return hip_status(csa::launch_topk(LL, scores, ld_scores, k_eff, ids, static_cast<hipStream_t>(stream)), fn);
+  return hip_status(csa::launch_topk(LL, scores, ld_scores, k_eff, ids, sel_scores, static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 csa_status_t csa_indexer_topk(const csa_layout_t *L, const void *q_idx, const void *k_idx,

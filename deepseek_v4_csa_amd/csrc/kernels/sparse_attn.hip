@@ -1099,19 +1099,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
   float kp_own[NO], kp_sc[NO];   // head-summed mass and selected score of the slot
   auto kl_finish = [&]() __attribute__((always_inline)) {
     float *te = kla.teacher ? kla.teacher + (int64_t)kp_t * kla.ldt : nullptr;
-    float tj[NO];
     double kl = 0.0;
     if (kp_empty) {
 #pragma unroll
-      for (int i = 0; i < NO; ++i) tj[i] = 0.f;
+      for (int i = 0; i < NO; ++i) kp_own[i] = 0.f;
     } else {
-      kl = sparse_kl_wave(kp_ok, kp_own, kp_sc, tj);
+      kl = sparse_kl_wave(kp_ok, kp_own, kp_sc);   // kp_own now holds the teacher
     }
     if (te) {
 #pragma unroll
       for (int i = 0; i < NO; ++i) {
         const int c = 2 * i + half, j = 32 * c + jl;
-        if (c < ncc && j < k_eff) te[j] = tj[i];
+        if (c < ncc && j < k_eff) te[j] = kp_own[i];
       }
     }
     if (lane == 0) kla.kl_row[kp_t] = (float)kl;

@@ -47,10 +47,46 @@ __device__ __forceinline__ float log1p_kl(float x) {
   return __log2f(1.f + x) * LN2;
 }
 
-// A wave holds the row's support slots, N per lane in any arrangement: ok[v] marks a slot
+// Reductions over the lanes that hold one row: a whole wave (WaveRed), or NW waves of one
+// workgroup (GroupRed: one LDS entry per wave, combined in wave order, so the result is the
+// same in every lane and every run).  With GroupRed every wave of the workgroup must reach
+// every reduction, whatever row it holds.
+struct WaveRed {
+  __device__ __forceinline__ float max(float v) const { return wave_max_dpp(v); }
+  __device__ __forceinline__ double sum(double v) const { return wave_sum_f64_dpp(v); }
+};
+template <int NW> struct GroupRed {
+  float *fb;    // NW floats of LDS for this row
+  double *db;   // NW doubles of LDS for this row
+  int w;        // this wave's index among the row's NW waves
+  __device__ __forceinline__ float max(float v) const {
+    v = wave_max_dpp(v);
+    if ((threadIdx.x & 63) == 0) fb[w] = v;
+    __syncthreads();
+    float r = fb[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) r = fmaxf(r, fb[i]);
+    __syncthreads();
+    return r;
+  }
+  __device__ __forceinline__ double sum(double v) const {
+    v = wave_sum_f64_dpp(v);
+    if ((threadIdx.x & 63) == 0) db[w] = v;
+    __syncthreads();
+    double r = db[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) r += db[i];
+    __syncthreads();
+    return r;
+  }
+};
+
+// The lanes that hold a row hold its support slots, N per lane in any arrangement: ok[v] marks a slot
 // of the support (a valid id), c[v] its head-summed mass m_j, sc[v] its indexer score.
 // Returns the row's KL (the same value in every lane) and leaves the teacher value of each
-// slot in tj[v] (0 off the support).  Every lane of the wave must take part.
+// slot in c[v] (0 off the support); sc[v] is overwritten (the predictor's exponentials
+// take its place: the arrays are reused so that long rows keep few registers).  Every lane
+// of the wave must take part.
 //
 // The KL of two nearly equal distributions is a second-order quantity, so the normalisers
 // and the log-ratios are finished in fp64: an fp32 error in either normaliser would shift
@@ -59,9 +95,9 @@ __device__ __forceinline__ float log1p_kl(float x) {
 // log(t + eps) - log(p + eps) is taken as log1p(x), x = (t - p) / (p + eps), with t - p in
 // fp64 and the rest in fp32 (the quotient by the hardware reciprocal, 1 ulp), so the KL
 // moves by ~1e-7 * sum_j t_j |x_j|.
-template <int N>
-__device__ __forceinline__ double sparse_kl_wave(const bool (&ok)[N], const float (&c)[N],
-                                                 const float (&sc)[N], float (&tj)[N]) {
+template <int N, class Red = WaveRed>
+__device__ __forceinline__ double sparse_kl_wave(const bool (&ok)[N], float (&c)[N], float (&sc)[N],
+                                                 const Red &red = Red()) {
   float mx = -__builtin_inff();
   double ms = 0.0;
 #pragma unroll
@@ -69,16 +105,15 @@ __device__ __forceinline__ double sparse_kl_wave(const bool (&ok)[N], const floa
     mx = fmaxf(mx, ok[v] ? sc[v] : -__builtin_inff());
     ms += ok[v] ? (double)c[v] : 0.0;
   }
-  mx = wave_max_dpp(mx);
-  ms = wave_sum_f64_dpp(ms);
-  float e[N];
+  mx = red.max(mx);
+  ms = red.sum(ms);
   double es = 0.0;
 #pragma unroll
   for (int v = 0; v < N; ++v) {
-    e[v] = ok[v] ? fast_exp2((sc[v] - mx) * LOG2E) : 0.f;
-    es += (double)e[v];
+    sc[v] = ok[v] ? fast_exp2((sc[v] - mx) * LOG2E) : 0.f;   // e_j from here on
+    es += (double)sc[v];
   }
-  es = wave_sum_f64_dpp(es);
+  es = red.sum(es);
   const double inv_es = 1.0 / es;
   const double inv_m = 1.0 / fmax(ms, (double)KL_EPS);
   double kl = 0.0;
@@ -87,13 +122,13 @@ __device__ __forceinline__ double sparse_kl_wave(const bool (&ok)[N], const floa
     double t = 0.0;
     if (ok[v]) {
       t = (double)c[v] * inv_m;
-      const double pj = (double)e[v] * inv_es;
+      const double pj = (double)sc[v] * inv_es;
       const float x = (float)(t - pj) * __builtin_amdgcn_rcpf((float)pj + KL_EPS);
       kl += t * (double)log1p_kl(x);
     }
-    tj[v] = (float)t;
+    c[v] = (float)t;   // the teacher value
   }
-  return wave_sum_f64_dpp(kl);
+  return red.sum(kl);
 }
 
 }  // namespace csa

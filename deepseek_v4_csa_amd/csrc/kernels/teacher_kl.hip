@@ -24,35 +24,46 @@
 namespace csa {
 
 // ---------------------------------------------------------------- sparse
-// One wave per row; slot j = v*64 + lane (v < SPL), so every load is issued up front and
-// coalesced except the score gather (one dependent load per slot); the row is finished by
-// sparse_kl_wave.
-template <int SPL>
+// NW waves per row (1, 2 or 4: a row's slots / 64 lanes / NW <= 8, so a lane keeps few
+// registers however long the row); slot j = (v*NW + wr)*64 + lane for wave wr of the row,
+// so every load is issued up front and coalesced except the score gather (one dependent
+// load per slot); the row is finished by sparse_kl_wave, its sums over the row's waves
+// combined through LDS when NW > 1 (every wave then reaches every reduction: rows past T
+// or left out of the loss run them with an empty support).
+template <int SPL, int NW>
 __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
     LayoutDev L, int T, const float *__restrict__ scores, int64_t ld, int selected,
     const int32_t *__restrict__ ids, int k_eff, const float *__restrict__ cmass, float *__restrict__ teacher,
     int64_t ldt, float *__restrict__ kl_row) {
+  constexpr int RPB = 4 / NW;   // rows per workgroup
+  __shared__ float fred[RPB][NW];
+  __shared__ double dred[RPB][NW];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + w;
-  if (t >= T) return;
-  const int32_t *idr = ids + (int64_t)t * k_eff;
-  const float *cm = cmass + (int64_t)t * k_eff;
-  const float *sr = scores + (int64_t)t * ld;
-  float *te = teacher ? teacher + (int64_t)t * ldt : nullptr;
+  const int rw = w / NW, wr = w % NW;   // the wave's row within the workgroup, its index there
+  const int t = blockIdx.x * RPB + rw;
+  if (NW == 1 && t >= T) return;        // (a lone wave has no barrier to meet)
+  const bool live = t < T;
+  const int tt = live ? t : 0;
+  const int32_t *idr = ids + (int64_t)tt * k_eff;
+  const float *cm = cmass + (int64_t)tt * k_eff;
+  const float *sr = scores + (int64_t)tt * ld;
+  float *te = (teacher && live) ? teacher + (int64_t)tt * ldt : nullptr;
   // every load that needs only the row index goes out first (ids, cmass and, in place,
   // the selected scores); the segment search and the score gather follow
   int id[SPL];
   float c[SPL], sc[SPL];
 #pragma unroll
   for (int v = 0; v < SPL; ++v) {
-    const int j = v * 64 + lane;
-    id[v] = j < k_eff ? idr[j] : -1;
-    c[v] = j < k_eff ? cm[j] : 0.f;
-    sc[v] = (selected && j < k_eff) ? sr[j] : 0.f;
+    const int j = (v * NW + wr) * 64 + lane;
+    const bool in = live && j < k_eff;
+    id[v] = in ? idr[j] : -1;
+    c[v] = in ? cm[j] : 0.f;
+    sc[v] = (selected && in) ? sr[j] : 0.f;
   }
-  const RowGeo geo = row_geo(L, t);
-  if (loss_row_empty(L, geo, t)) {
+  const RowGeo geo = row_geo(L, tt);
+  const bool empty = !live || loss_row_empty(L, geo, tt);
+  if (NW == 1 && empty) {
     if (te)
       for (int j = lane; j < k_eff; j += 64) te[j] = 0.f;
     if (lane == 0) kl_row[t] = 0.f;
@@ -61,18 +72,21 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
   bool ok[SPL];
 #pragma unroll
   for (int v = 0; v < SPL; ++v) {
-    ok[v] = id[v] >= 0;
+    ok[v] = !empty && id[v] >= 0;
     // the score of slot j: read in place (selected scores) or gathered from the full row
     if (!selected) sc[v] = ok[v] ? sr[id[v] - geo.k_base] : 0.f;
   }
-  float tj[SPL];
-  const double kl = sparse_kl_wave(ok, c, sc, tj);
+  double kl;   // c now holds the teacher (0 off the support, and on an empty row)
+  if constexpr (NW == 1) kl = sparse_kl_wave(ok, c, sc);
+  else kl = sparse_kl_wave(ok, c, sc, GroupRed<NW>{fred[rw], dred[rw], wr});
   if (te) {
 #pragma unroll
-    for (int v = 0; v < SPL; ++v)
-      if (v * 64 + lane < k_eff) te[v * 64 + lane] = tj[v];
+    for (int v = 0; v < SPL; ++v) {
+      const int j = (v * NW + wr) * 64 + lane;
+      if (j < k_eff) te[j] = c[v];
+    }
   }
-  if (lane == 0) kl_row[t] = (float)kl;
+  if (live && wr == 0 && lane == 0) kl_row[t] = empty ? 0.f : (float)kl;
 }
 
 // ---------------------------------------------------------------- dense
@@ -379,17 +393,19 @@ hipError_t launch_teacher_kl(const LaunchLayout &LL, bool sparse, const float *s
   hipError_t e = hipSuccess;
   if (LL.total_q > 0) {
     if (sparse) {
+      // slots per lane of a one-wave row; rows longer than 8 * 64 slots are shared by
+      // 2 or 4 waves (up to 16 slots per lane at 4 waves: k_eff <= 4096)
       const int spl = (k_eff + 63) / 64;
-      const dim3 grid((unsigned)((LL.total_q + 3) / 4));
-#define CSA_TKS_CASE(V)                                                                              \
-      if (spl <= V) {                                                                                \
-        hipLaunchKernelGGL(teacher_kl_sparse_kernel<V>, grid, dim3(256), 0, st, LL.dev, LL.total_q,  \
-                           scores, ld, selected ? 1 : 0, ids, k_eff, cmass, teacher, ld_teacher,     \
-                           kl_row);                                                                  \
+#define CSA_TKS_CASE(V, NW)                                                                          \
+      if (spl <= V * NW) {                                                                           \
+        const dim3 grid((unsigned)((LL.total_q + 4 / NW - 1) / (4 / NW)));                          \
+        hipLaunchKernelGGL((teacher_kl_sparse_kernel<V, NW>), grid, dim3(256), 0, st, LL.dev,        \
+                           LL.total_q, scores, ld, selected ? 1 : 0, ids, k_eff, cmass, teacher,     \
+                           ld_teacher, kl_row);                                                      \
         e = hipGetLastError();                                                                       \
       } else
-      CSA_TKS_CASE(1) CSA_TKS_CASE(2) CSA_TKS_CASE(4) CSA_TKS_CASE(8) CSA_TKS_CASE(16)
-      CSA_TKS_CASE(32) CSA_TKS_CASE(64) { return hipErrorInvalidValue; }
+      CSA_TKS_CASE(1, 1) CSA_TKS_CASE(2, 1) CSA_TKS_CASE(4, 1) CSA_TKS_CASE(8, 1) CSA_TKS_CASE(8, 2)
+      CSA_TKS_CASE(8, 4) CSA_TKS_CASE(16, 4) { return hipErrorInvalidValue; }
 #undef CSA_TKS_CASE
     } else {
       (void)bf16;

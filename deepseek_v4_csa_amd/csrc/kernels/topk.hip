@@ -55,9 +55,16 @@ __device__ __forceinline__ void block_scan2(int a, int b, int *wsum, int &pa, in
 // taken whole.  Compaction: each wave counts, per v, its keys above the threshold and its
 // ties (ballot popcounts), one block scan over the (v, wave) counts in index order gives
 // every group its offsets, and each lane places its picks with mbcnt ranks.
-template <int VPT>
+// the float whose order-preserving key is k (the inverse of ordered_key)
+__device__ __forceinline__ float float_of_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// SEL: the selected scores are written too (sel, slot-aligned with ids)
+template <int VPT, bool SEL>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const float *__restrict__ scores,
-                                                          int64_t ld, int k_eff, int32_t *__restrict__ ids) {
+                                                          int64_t ld, int k_eff, int32_t *__restrict__ ids,
+                                                          float *__restrict__ sel) {
   static_assert(VPT * TK_WAVES <= TK_THREADS, "one scan entry per (v, wave)");
   __shared__ uint32_t hist[256];
   __shared__ uint32_t red[2 * TK_WAVES];
@@ -70,11 +77,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   const RowGeo g = row_geo(L, t);
   const int n = g.n_valid;
   int32_t *out = ids + (int64_t)t * k_eff;
+  float *sout = SEL ? sel + (int64_t)t * k_eff : nullptr;
+  const float *row = scores + (int64_t)t * ld;
   if (n <= k_eff) {  // every visible key is selected
-    for (int j = tid; j < k_eff; j += TK_THREADS) out[j] = j < n ? g.k_base + j : -1;
+    for (int j = tid; j < k_eff; j += TK_THREADS) {
+      out[j] = j < n ? g.k_base + j : -1;
+      if constexpr (SEL) sout[j] = j < n ? row[j] : -__builtin_inff();
+    }
     return;
   }
-  const float *row = scores + (int64_t)t * ld;
 
   uint32_t key[VPT];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -179,19 +190,22 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     const int eq_before = cnt[1][v * TK_WAVES + w] +
         __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0));
     const bool gt = (bg >> lane) & 1, eq = (be >> lane) & 1;
-    const bool sel = gt || (eq && eq_before < need);
+    const bool sel_ = gt || (eq && eq_before < need);
     const int pos = gt_before + min(eq_before, need);
-    if (sel && pos < k_eff) out[pos] = g.k_base + v * TK_THREADS + tid;
+    if (sel_ && pos < k_eff) {
+      out[pos] = g.k_base + v * TK_THREADS + tid;
+      if constexpr (SEL) sout[pos] = float_of_key(key[v] + kmin);
+    }
   }
 }
 
 // One wave per row (rows up to 64*VPL visible keys): the same selection as above with
 // wave-level primitives only (wave_select), so there is no workgroup barrier.  The row's
 // loads are issued before its geometry is known (every column below max_seqlen_k exists).
-template <int VPL>
+template <int VPL, bool SEL>
 __global__ __launch_bounds__(256) void topk_wave_kernel(LayoutDev L, int T, const float *__restrict__ scores,
                                                         int64_t ld, int max_sk, int k_eff,
-                                                        int32_t *__restrict__ ids) {
+                                                        int32_t *__restrict__ ids, float *__restrict__ sel) {
   __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][256];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -207,25 +221,44 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(LayoutDev L, int T, cons
   const RowGeo g = row_geo(L, t);
   const int n = g.n_valid;
   int32_t *out = ids + (int64_t)t * k_eff;
+  float *sout = SEL ? sel + (int64_t)t * k_eff : nullptr;
   if (n <= k_eff) {  // every visible key is selected
-    for (int j = lane; j < k_eff; j += 64) out[j] = j < n ? g.k_base + j : -1;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int j = v * 64 + lane;
+      if (j < k_eff) {
+        out[j] = j < n ? g.k_base + j : -1;
+        if constexpr (SEL) sout[j] = j < n ? val[v] : -__builtin_inff();
+      }
+    }
     return;
   }
-  wave_select<VPL>(val, n, k_eff, hist_all[w], [&](int pos, int j, int) { out[pos] = g.k_base + j; });
+  if constexpr (SEL) {
+    wave_select<VPL>(val, n, k_eff, hist_all[w], [&](int pos, int j, int v) {
+      out[pos] = g.k_base + j;
+      sout[pos] = val[v];
+    });
+  } else {
+    wave_select<VPL>(val, n, k_eff, hist_all[w], [&](int pos, int j, int) { out[pos] = g.k_base + j; });
+  }
 }
 
 bool topk_supported(int max_seqlen_k, int k_eff) { return max_seqlen_k <= 16384 && k_eff >= 0; }
 
 hipError_t launch_topk(const LaunchLayout &LL, const float *scores, int64_t ld, int k_eff,
-                       int32_t *ids, hipStream_t st) {
+                       int32_t *ids, float *sel, hipStream_t st) {
   if (LL.total_q == 0 || k_eff == 0) return hipSuccess;
   if (LL.max_seqlen_k <= 64 * 64) {  // one wave per row
     const int vpl = (LL.max_seqlen_k + 63) / 64;
     const dim3 wgrid((unsigned)((LL.total_q + 3) / 4));
 #define CSA_TOPKW_CASE(V)                                                                            \
     if (vpl <= V) {                                                                                  \
-      hipLaunchKernelGGL(topk_wave_kernel<V>, wgrid, dim3(256), 0, st, LL.dev, LL.total_q, scores, ld, \
-                         LL.max_seqlen_k, k_eff, ids);                                               \
+      if (sel)                                                                                       \
+        hipLaunchKernelGGL((topk_wave_kernel<V, true>), wgrid, dim3(256), 0, st, LL.dev, LL.total_q, \
+                           scores, ld, LL.max_seqlen_k, k_eff, ids, sel);                            \
+      else                                                                                           \
+        hipLaunchKernelGGL((topk_wave_kernel<V, false>), wgrid, dim3(256), 0, st, LL.dev, LL.total_q, \
+                           scores, ld, LL.max_seqlen_k, k_eff, ids, sel);                            \
       return hipGetLastError();                                                                      \
     }
     CSA_TOPKW_CASE(4)
@@ -239,7 +272,10 @@ hipError_t launch_topk(const LaunchLayout &LL, const float *scores, int64_t ld, 
   dim3 grid((unsigned)LL.total_q), block(TK_THREADS);
 #define CSA_TOPK_CASE(V)                                                                         \
   if (per <= V) {                                                                                \
-    hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, st, LL.dev, scores, ld, k_eff, ids);     \
+    if (sel)                                                                                     \
+      hipLaunchKernelGGL((topk_kernel<V, true>), grid, block, 0, st, LL.dev, scores, ld, k_eff, ids, sel); \
+    else                                                                                         \
+      hipLaunchKernelGGL((topk_kernel<V, false>), grid, block, 0, st, LL.dev, scores, ld, k_eff, ids, sel); \
     return hipGetLastError();                                                                    \
   }
   CSA_TOPK_CASE(1)

@@ -17,7 +17,7 @@ hipError_t launch_indexer_score(const LaunchLayout &L, const void *q_idx, const 
                                 float *scores, int64_t ld, hipStream_t st);
 
 hipError_t launch_topk(const LaunchLayout &L, const float *scores, int64_t ld, int k_eff,
-                       int32_t *ids, hipStream_t st);
+                       int32_t *ids, float *sel /* NULL: ids only */, hipStream_t st);
 
 hipError_t launch_sparse_attn(const LaunchLayout &L, const void *q, const void *kv,
                               const void *ckv, const float *sink, const int32_t *ids, int k_eff,

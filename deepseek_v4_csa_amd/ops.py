@@ -61,7 +61,7 @@ def load():
     lib.csa_indexer_score.restype = ctypes.c_int
     lib.csa_indexer_score.argtypes = [LP, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, P]
     lib.csa_topk.restype = ctypes.c_int
-    lib.csa_topk.argtypes = [LP, P, I64, I32, P, P]
+    lib.csa_topk.argtypes = [LP, P, I64, I32, P, P, P]
     lib.csa_sparse_attn_fwd.restype = ctypes.c_int
     lib.csa_sparse_attn_fwd.argtypes = [LP, P, P, P, P, P, I32, I32, ctypes.c_int, I32, I32, F32,
                                         P, P, P, P, P]
@@ -163,12 +163,14 @@ def csa_indexer_score(layout: Layout, q_idx, k_idx, weights, idx_scale: float, s
     return scores
 
 
-def csa_topk(layout: Layout, scores, topk: int, ids=None):
+def csa_topk(layout: Layout, scores, topk: int, ids=None, sel_scores=None):
+    """ids [T, k_eff]; with sel_scores (a [T, k_eff] fp32 tensor) also the score of each
+    selected id, slot-aligned with ids."""
     ke = k_eff(layout, topk)
     if ids is None:
         ids = torch.empty((scores.shape[0], ke), dtype=torch.int32, device=scores.device)
     _check(load().csa_topk(ctypes.byref(layout.c()), _ptr(scores), scores.stride(0), int(topk),
-                           _ptr(ids), _stream()))
+                           _ptr(ids), _ptr(sel_scores) if sel_scores is not None else None, _stream()))
     return ids
 
 
@@ -329,12 +331,13 @@ def layout_of_inputs(inp) -> Layout:
                   wl.max_seqlen_k, inp.offsets, inp.cu_q_real)
 
 
-def forward(inp, want_teacher=False, fused=False, attn_kl=False):
+def forward(inp, want_teacher=False, fused=False, attn_kl=False, topk_sel=False):
     """The whole path on one Inputs, on the current stream: the four calls, or with
     fused=True (sparse loss) csa_indexer_topk in place of the score and top-k calls, the
     teacher/KL then reading the selected scores (no score matrix: scores is None), and
     with attn_kl=True (sparse loss) csa_sparse_attn_kl_fwd in place of the attention and
-    teacher/KL calls."""
+    teacher/KL calls.  topk_sel=True (sparse loss, two score calls): csa_topk also writes
+    the selected scores and the teacher/KL reads those instead of gathering from the rows."""
     wl = inp.wl
     L = layout_of_inputs(inp)
     sel = row_lse = scores = None
@@ -345,20 +348,23 @@ def forward(inp, want_teacher=False, fused=False, attn_kl=False):
                                              want_lse=True)
     else:
         scores = csa_indexer_score(L, inp.q_idx, inp.k_idx, inp.weights, inp.idx_scale)
-        ids = csa_topk(L, scores, wl.topk)
+        if topk_sel and wl.sparse_loss:
+            sel = torch.empty((wl.total_q, k_eff(L, wl.topk)), dtype=torch.float32, device=scores.device)
+        ids = csa_topk(L, scores, wl.topk, sel_scores=sel)
+    selected = sel is not None
     if attn_kl:
         if not wl.sparse_loss:
             raise RuntimeError("the attention + teacher/KL call serves the sparse loss")
         out, lse, lse_nc, cmass, teacher, kl_row, loss = csa_sparse_attn_kl_fwd(
-            L, inp.q, inp.kv, inp.ckv, inp.sink, ids, wl.window, inp.scale, sel if fused else scores,
-            scores_selected=fused, want_teacher=want_teacher)
+            L, inp.q, inp.kv, inp.ckv, inp.sink, ids, wl.window, inp.scale, sel if selected else scores,
+            scores_selected=selected, want_teacher=want_teacher)
         return dict(scores=scores, ids=ids, out=out, lse=lse, lse_nc=lse_nc, cmass=cmass,
                     teacher=teacher, kl_row=kl_row, loss=loss, sel=sel, row_lse=row_lse)
     out, lse, lse_nc, cmass = csa_sparse_attn_fwd(L, inp.q, inp.kv, inp.ckv, inp.sink, ids, wl.window,
                                                   inp.scale, want_cmass=wl.sparse_loss)
-    teacher, kl_row, loss = csa_indexer_teacher_kl(L, wl.sparse_loss, sel if fused else scores, ids, cmass,
+    teacher, kl_row, loss = csa_indexer_teacher_kl(L, wl.sparse_loss, sel if selected else scores, ids, cmass,
                                                    inp.q, inp.ckv, lse_nc, inp.scale, want_teacher=want_teacher,
-                                                   scores_selected=fused)
+                                                   scores_selected=selected)
     return dict(scores=scores, ids=ids, out=out, lse=lse, lse_nc=lse_nc, cmass=cmass,
                 teacher=teacher, kl_row=kl_row, loss=loss, sel=sel, row_lse=row_lse)
 
@@ -387,8 +393,10 @@ class Prepared:
             self.args_score = (Lp, _ptr(inp.q_idx), _ptr(inp.k_idx), _ptr(inp.weights), _dtype(inp.q_idx),
                                Hi, Di, ctypes.c_float(inp.idx_scale), _ptr(scores),
                                ctypes.c_int64(scores.stride(0)), st)
-            self.args_topk = (Lp, _ptr(scores), ctypes.c_int64(scores.stride(0)), int(topk), _ptr(ids), st)
-        if sel is not None:   # fused score + top-k; the teacher/KL reads the selected scores
+            # with sel, the top-k call also writes the selected scores
+            self.args_topk = (Lp, _ptr(scores), ctypes.c_int64(scores.stride(0)), int(topk), _ptr(ids),
+                              _ptr(sel) if sel is not None else None, st)
+        if sel is not None:   # the teacher/KL reads the selected scores (fused call or top-k's)
             self.args_fused = (Lp, _ptr(inp.q_idx), _ptr(inp.k_idx), _ptr(inp.weights), _dtype(inp.q_idx),
                                Hi, Di, ctypes.c_float(inp.idx_scale), int(topk), _ptr(ids), _ptr(sel), None, st)
         tkl_scores = sel if sel is not None else scores

@@ -123,11 +123,14 @@ csa_status_t csa_indexer_score(const csa_layout_t *L, const void *q_idx, const v
  *   ids: [PR8539] item 1, b*S_k + local for BSHD; flat packed ids for THD), and
  *   ids[t, K_t..k_eff) = -1 ([I5776], csa.py sparse-attention excerpt: picks beyond the
  *   causal limit become -1).  Only columns j < n_valid(t) are read.
- *   scores [T, ld_scores] fp32 (finite or -inf; no NaN);  ids [T, k_eff] int32.
+ *   scores [T, ld_scores] fp32 (finite or -inf; no NaN);  ids [T, k_eff] int32;
+ *   sel_scores [T, k_eff] fp32 or NULL: slot j receives the score of ids[t, j] (-inf at -1
+ *       slots), so that csa_indexer_teacher_kl / csa_indexer_loss_bwd can read the selected
+ *       scores in place (scores_selected = 1) instead of gathering them from the rows.
  * Supported: max_seqlen_k <= 16384, 1 <= topk.
  */
 csa_status_t csa_topk(const csa_layout_t *L, const float *scores, int64_t ld_scores,
-                      int32_t topk, int32_t *ids, void *stream);
+                      int32_t topk, int32_t *ids, float *sel_scores, void *stream);
 
 /*
  * csa_indexer_topk -- csa_indexer_score and csa_topk in one pass that never stores the

@@ -53,7 +53,7 @@ FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case below fails va
 def test_layout_misuse_is_rejected(lib, kw, code):
     from deepseek_v4_csa_amd import ops
     L = _layout(ops, **kw)
-    st = lib.csa_topk(ctypes.byref(L), FAKE, 16, 4, FAKE, None)
+    st = lib.csa_topk(ctypes.byref(L), FAKE, 16, 4, FAKE, None, None)
     assert st == code
     assert lib.csa_last_error().decode().startswith("csa_topk")
 
@@ -62,9 +62,9 @@ def test_argument_misuse_is_rejected(lib):
     from deepseek_v4_csa_amd import ops
     L = _layout(ops)
     B = ctypes.byref
-    assert lib.csa_topk(B(L), FAKE, 16, 0, FAKE, None) == 1                      # topk < 1
-    assert lib.csa_topk(B(L), FAKE, 8, 4, FAKE, None) == 1                       # ld < max_seqlen_k
-    assert lib.csa_topk(B(L), None, 16, 4, FAKE, None) == 1                      # null scores
+    assert lib.csa_topk(B(L), FAKE, 16, 0, FAKE, None, None) == 1                      # topk < 1
+    assert lib.csa_topk(B(L), FAKE, 8, 4, FAKE, None, None) == 1                       # ld < max_seqlen_k
+    assert lib.csa_topk(B(L), None, 16, 4, FAKE, None, None) == 1                      # null scores
     assert lib.csa_indexer_score(B(L), FAKE, FAKE, FAKE, 1, 4, 48, 0.1, FAKE, 16, None) == 2  # Di=48
     assert lib.csa_indexer_score(B(L), FAKE, FAKE, FAKE, 7, 4, 64, 0.1, FAKE, 16, None) == 1  # dtype
     assert lib.csa_sparse_attn_fwd(B(L), FAKE, FAKE, FAKE, FAKE, FAKE, 4, -1, 1, 4, 64, 0.1,
