@@ -87,13 +87,21 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     return;
   }
 
+  // the row through a buffer resource of exactly n floats: the loads are unconditional
+  // (past n they read zeros), so all VPT of them are in flight at once -- a load under a
+  // per-slot branch would be waited for before the next one is issued
+  const __amdgpu_buffer_rsrc_t rrow = make_rsrc(row, (uint32_t)n * 4);
   uint32_t key[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v)
+    key[v] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rrow, (v * TK_THREADS + tid) * 4, 0, 0);
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const int j = v * TK_THREADS + tid;
-    key[v] = j < n ? ordered_key(row[j]) : 0u;
-    if (j < n) { kmin = min(kmin, key[v]); kmax = max(kmax, key[v]); }
+    const bool in = v * TK_THREADS + tid < n;
+    key[v] = in ? ordered_key(__uint_as_float(key[v])) : 0u;
+    kmin = in ? min(kmin, key[v]) : kmin;
+    kmax = in ? max(kmax, key[v]) : kmax;
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -164,14 +172,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     bg = __ballot(valid && (kp > thr || (whole && kp == thr)));
     be = __ballot(valid && !whole && kp == thr);
   };
+  // the wave's counts per v gathered in lane v (no per-v branch), stored by one write each
+  int cg = 0, ce = 0;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     uint64_t bg, be;
     ballots(v, bg, be);
-    if (lane == 0) {
-      cnt[0][v * TK_WAVES + w] = __popcll(bg);
-      cnt[1][v * TK_WAVES + w] = __popcll(be);
-    }
+    cg = lane == v ? __popcll(bg) : cg;
+    ce = lane == v ? __popcll(be) : ce;
+  }
+  if (lane < VPT) {
+    cnt[0][lane * TK_WAVES + w] = cg;
+    cnt[1][lane * TK_WAVES + w] = ce;
   }
   __syncthreads();
   {
@@ -181,13 +193,16 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     if (tid < VPT * TK_WAVES) { cnt[0][tid] = pa; cnt[1][tid] = pb; }
   }
   __syncthreads();
+  // the wave's offsets per v: lane v reads them once, every v takes them by readlane
+  const int og = lane < VPT ? cnt[0][lane * TK_WAVES + w] : 0;
+  const int oe = lane < VPT ? cnt[1][lane * TK_WAVES + w] : 0;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     uint64_t bg, be;
     ballots(v, bg, be);
-    const int gt_before = cnt[0][v * TK_WAVES + w] +
+    const int gt_before = __builtin_amdgcn_readlane(og, v) +
         __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0));
-    const int eq_before = cnt[1][v * TK_WAVES + w] +
+    const int eq_before = __builtin_amdgcn_readlane(oe, v) +
         __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0));
     const bool gt = (bg >> lane) & 1, eq = (be >> lane) & 1;
     const bool sel_ = gt || (eq && eq_before < need);
