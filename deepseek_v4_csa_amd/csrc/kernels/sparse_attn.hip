@@ -382,15 +382,28 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
   const int w_lo = max(geo.q_start, t - window + 1);
   const int nw = window > 0 ? t - w_lo + 1 : 0;
   const int nwc = (nw + 31) >> 5, ncc = (k_eff + 31) >> 5, nch = nwc + ncc;
-  // the row's ids, padded with -1 to whole 32-row chunks
-  for (int i = tid; i < ncc * 32; i += NT) ids_l[i] = i < k_eff ? ids[(int64_t)t * k_eff + i] : -1;
+  // the row's ids, padded with -1 to whole 32-row chunks: unconditional loads through a
+  // buffer resource of exactly k_eff ids, four per thread in flight at once (a load under a
+  // per-element branch is waited for before the next is issued)
+  {
+    const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids + (int64_t)t * k_eff, (uint32_t)k_eff * 4);
+    for (int i0 = tid; i0 < ncc * 32; i0 += 4 * NT) {
+      int x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = __builtin_amdgcn_raw_buffer_load_b32(rid, (i0 + u * NT) * 4, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * NT < ncc * 32) ids_l[i0 + u * NT] = i0 + u * NT < k_eff ? x[u] : -1;
+    }
+  }
   // Q^T operands, MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
+  // (a lane of a head past H loads head 0's row: its logits are masked, the values never used)
   u32x4 qf[NG][NC];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok[gi] ? hh[gi] : 0)) * D) + g;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[gi][c] = h_ok[gi] ? p[4 * c] : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NC; ++c) qf[gi][c] = p[4 * c];
   }
   const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)total_q * ROWB);
   const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * ROWB);
@@ -720,7 +733,7 @@ __global__ __launch_bounds__(256) void sparse_attn_dma_kernel(
   {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok ? h : 0)) * D) + g;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = h_ok ? p[4 * c] : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NC; ++c) qf[c] = p[4 * c];   // (masked where the head is past H)
   }
   // per-lane LDS offsets (relative to a tile)
   const int gg = lane / PIECES, pp = lane % PIECES;   // load: row-in-instruction, piece position
@@ -1026,10 +1039,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
     }
   };
   // MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
+  // (a lane of a head past H loads head 0's row: its logits are masked, the values unused)
   auto load_q = [&](int tq, u32x4 (&f)[NC]) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)tq * H + (h_ok ? h : 0)) * D) + g;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) f[c] = h_ok ? p[4 * c] : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NC; ++c) f[c] = p[4 * c];
   };
   // the NI row loads of step s of a query (window steps first, then compressed steps)
   // into `base`; valid = false requests NI out-of-range loads

@@ -45,21 +45,29 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
   if (NW == 1 && t >= T) return;        // (a lone wave has no barrier to meet)
   const bool live = t < T;
   const int tt = live ? t : 0;
-  const int32_t *idr = ids + (int64_t)tt * k_eff;
-  const float *cm = cmass + (int64_t)tt * k_eff;
   const float *sr = scores + (int64_t)tt * ld;
   float *te = (teacher && live) ? teacher + (int64_t)tt * ldt : nullptr;
   // every load that needs only the row index goes out first (ids, cmass and, in place,
-  // the selected scores); the segment search and the score gather follow
+  // the selected scores), through buffer resources of exactly k_eff elements: the loads
+  // are unconditional (past the end they read zeros) and all in flight at once -- a load
+  // under a per-slot branch is waited for at the branch's end, before the next is issued
+  const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids + (int64_t)tt * k_eff, (uint32_t)k_eff * 4);
+  const __amdgpu_buffer_rsrc_t rcm = make_rsrc(cmass + (int64_t)tt * k_eff, (uint32_t)k_eff * 4);
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(sr, selected ? (uint32_t)k_eff * 4 : 0u);
   int id[SPL];
   float c[SPL], sc[SPL];
 #pragma unroll
   for (int v = 0; v < SPL; ++v) {
     const int j = (v * NW + wr) * 64 + lane;
-    const bool in = live && j < k_eff;
-    id[v] = in ? idr[j] : -1;
-    c[v] = in ? cm[j] : 0.f;
-    sc[v] = (selected && in) ? sr[j] : 0.f;
+    id[v] = __builtin_amdgcn_raw_buffer_load_b32(rid, j * 4, 0, 0);
+    c[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rcm, j * 4, 0, 0));
+    sc[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, j * 4, 0, 0));
+  }
+#pragma unroll
+  for (int v = 0; v < SPL; ++v) {
+    const bool in = live && (v * NW + wr) * 64 + lane < k_eff;
+    id[v] = in ? id[v] : -1;
+    c[v] = in ? c[v] : 0.f;
   }
   const RowGeo geo = row_geo(L, tt);
   const bool empty = !live || loss_row_empty(L, geo, tt);
@@ -71,10 +79,15 @@ __global__ __launch_bounds__(256) void teacher_kl_sparse_kernel(
   }
   bool ok[SPL];
 #pragma unroll
-  for (int v = 0; v < SPL; ++v) {
-    ok[v] = !empty && id[v] >= 0;
-    // the score of slot j: read in place (selected scores) or gathered from the full row
-    if (!selected) sc[v] = ok[v] ? sr[id[v] - geo.k_base] : 0.f;
+  for (int v = 0; v < SPL; ++v) ok[v] = !empty && id[v] >= 0;
+  if (!selected) {
+    // the score of slot j gathered from the full row, unconditionally (a slot off the
+    // support reads past the resource: zero, unused)
+    const __amdgpu_buffer_rsrc_t rrow = make_rsrc(sr, (uint32_t)geo.n_valid * 4);
+#pragma unroll
+    for (int v = 0; v < SPL; ++v)
+      sc[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rrow, ok[v] ? (uint32_t)(id[v] - geo.k_base) * 4 : BUF_OOB, 0, 0));
   }
   double kl;   // c now holds the teacher (0 off the support, and on an empty row)
   if constexpr (NW == 1) kl = sparse_kl_wave(ok, c, sc);
@@ -143,7 +156,7 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   for (int gi = 0; gi < NG; ++gi) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (h_ok[gi] ? hh[gi] : 0)) * D) + g;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[gi][c] = h_ok[gi] ? p[4 * c] : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NC; ++c) qf[gi][c] = p[4 * c];   // (masked where the head is past H)
   }
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(ckv + (int64_t)geo.k_base * D, (uint32_t)n * ROWB);
   const int nch = (n + 31) / 32;
@@ -281,9 +294,27 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   // sums, normalisers and t - p in fp64 (as in the sparse kernel above)
   const float *sr = scores + (int64_t)t * ld;
   __shared__ double dred[2 * 16];
+  // the row's scores in batches of 8 per thread through a buffer resource of exactly n
+  // floats: unconditional loads, all 8 in flight at once (a loop of single guarded loads
+  // would wait for each before the next)
+  constexpr int UB = 8;
+  const __amdgpu_buffer_rsrc_t rsr = make_rsrc(sr, (uint32_t)n * 4);
+  auto load_batch = [&](int base, float (&x)[UB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      x[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsr, (base + u * NT) * 4, 0, 0));
+  };
   float mx = NINF;
   double msum = 0.0;
-  for (int j = tid; j < n; j += NT) { mx = fmaxf(mx, sr[j]); msum += (double)mj[j]; }
+  for (int base = tid; base < n; base += UB * NT) {
+    float x[UB];
+    load_batch(base, x);
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int j = base + u * NT;
+      if (j < n) { mx = fmaxf(mx, x[u]); msum += (double)mj[j]; }
+    }
+  }
   mx = wave_max(mx);
   msum = wave_sum_f64(msum);
   if (lane == 0) { red[w] = mx; dred[w] = msum; }
@@ -292,7 +323,13 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   for (int ww = 1; ww < HG; ++ww) { mx = fmaxf(mx, red[ww]); msum += dred[ww]; }
   __syncthreads();
   double es = 0.0;
-  for (int j = tid; j < n; j += NT) es += (double)fast_exp2((sr[j] - mx) * LOG2E);
+  for (int base = tid; base < n; base += UB * NT) {
+    float x[UB];
+    load_batch(base, x);
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      if (base + u * NT < n) es += (double)fast_exp2((x[u] - mx) * LOG2E);
+  }
   es = wave_sum_f64(es);
   if (lane == 0) dred[16 + w] = es;
   __syncthreads();
@@ -301,12 +338,20 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   const double inv_es = 1.0 / es;
   const double inv_m = 1.0 / fmax(msum, (double)KL_EPS);
   double kl = 0.0;
-  for (int j = tid; j < n; j += NT) {
-    const double tj = (double)mj[j] * inv_m;
-    const double pj = (double)fast_exp2((sr[j] - mx) * LOG2E) * inv_es;
-    const float x = (float)(tj - pj) / ((float)pj + KL_EPS);
-    kl += tj * (double)log1p_kl(x);
-    if (teacher) teacher[(int64_t)t * ldt + j] = (float)tj;
+  for (int base = tid; base < n; base += UB * NT) {
+    float x[UB];
+    load_batch(base, x);
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int j = base + u * NT;
+      if (j < n) {
+        const double tj = (double)mj[j] * inv_m;
+        const double pj = (double)fast_exp2((x[u] - mx) * LOG2E) * inv_es;
+        const float xr = (float)(tj - pj) * __builtin_amdgcn_rcpf((float)pj + KL_EPS);
+        kl += tj * (double)log1p_kl(xr);
+        if (teacher) teacher[(int64_t)t * ldt + j] = (float)tj;
+      }
+    }
   }
   if (teacher)
     for (int j = n + tid; j < ldt; j += NT) teacher[(int64_t)t * ldt + j] = 0.f;
