@@ -332,13 +332,30 @@ __global__ __launch_bounds__(64 * IXL_WAVES) void indexer_score_lds_kernel(
     tile_of(w, bk, tile);
     load_k(tile, kbn);
   }
-  // fp32(w * s_idx), head-major: one 16-byte LDS read gives a lane its 4 tokens
-  for (int e = tid; e < 2 * HI * IXL_TOK; e += NTHR) {
-    const int bk = e >= HI * IXL_TOK, e2 = e - bk * HI * IXL_TOK;
-    const int tt = e2 / HI, h = e2 - tt * HI;
-    const int t = (bk ? tb1 : tb0) + tt;
-    ws[bk][h * IXL_TOK + tt] =
-        (bk < nblk && t < q_len) ? weights[(int64_t)(q_start + t) * HI + h] * idx_scale : 0.f;
+  // fp32(w * s_idx), head-major: one 16-byte LDS read gives a lane its 4 tokens.  The
+  // loads are unconditional (a token past the segment reads its last row, then is zeroed),
+  // so all of a thread's are in flight at once
+  {
+    constexpr int NW8 = (2 * HI * IXL_TOK + NTHR - 1) / NTHR;
+    float x[NW8];
+#pragma unroll
+    for (int k = 0; k < NW8; ++k) {
+      const int e = tid + k * NTHR;
+      const int bk = e >= HI * IXL_TOK, e2 = e - bk * HI * IXL_TOK;
+      const int tt = e2 / HI, h = e2 - tt * HI;
+      const int t = min((bk ? tb1 : tb0) + tt, q_len - 1);
+      x[k] = e < 2 * HI * IXL_TOK ? weights[(int64_t)(q_start + t) * HI + h] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < NW8; ++k) {
+      const int e = tid + k * NTHR;
+      if (e < 2 * HI * IXL_TOK) {
+        const int bk = e >= HI * IXL_TOK, e2 = e - bk * HI * IXL_TOK;
+        const int tt = e2 / HI, h = e2 - tt * HI;
+        const int t = (bk ? tb1 : tb0) + tt;
+        ws[bk][h * IXL_TOK + tt] = (bk < nblk && t < q_len) ? x[k] * idx_scale : 0.f;
+      }
+    }
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -679,10 +696,28 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int c = 0; c < NCD; ++c) kb[n][c] = kp[4 * c];
   }
-  for (int e = tid; e < Hi * HGK_TOK; e += NTHR) {
-    const int tt = e / Hi, h = e - tt * Hi;
-    const int t = t0 + tt;
-    wsl[h * HGK_TOK + tt] = t < q_len ? weights[(int64_t)(q_start + t) * Hi + h] * idx_scale : 0.f;
+  // the block's weights are one contiguous run of rows_w * Hi floats: unconditional loads
+  // through a buffer resource of exactly that run (tokens past the segment read zeros),
+  // eight per thread in flight at once -- a guarded load per element would be waited for
+  // (with every earlier load of the wave) before the next is issued
+  {
+    const int rows_w = min(HGK_TOK, q_len - t0);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(weights + (int64_t)(q_start + t0) * Hi, (uint32_t)(rows_w * Hi) * 4);
+    for (int e0 = tid; e0 < Hi * HGK_TOK; e0 += 8 * NTHR) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        x[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (e0 + u * NTHR) * 4, 0, 0));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * NTHR;
+        if (e < Hi * HGK_TOK) {
+          const int tt = e / Hi, h = e - tt * Hi;
+          wsl[h * HGK_TOK + tt] = x[u] * idx_scale;
+        }
+      }
+    }
   }
   f32x4 acc[4];
 #pragma unroll
