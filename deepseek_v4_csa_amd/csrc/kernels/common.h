@@ -66,11 +66,12 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 // reductions over the 16 lanes of a lane group (lanes with the same l/16), on DPP:
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  These controls
-// are permutations within a 16-lane row (every lane has a source), so the plain DPP move
-// is used: no old value to set up first.
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], quad_perm [3,2,1,0], row_half_mirror,
+// row_mirror.  These controls are permutations within a 16-lane row (every lane has a
+// source), so the plain DPP move is used: no old value to set up first.
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
-  static_assert(CTRL == 0xB1 || CTRL == 0x4E || CTRL == 0x141 || CTRL == 0x140, "a full in-row permutation");
+  static_assert(CTRL == 0xB1 || CTRL == 0x4E || CTRL == 0x1B || CTRL == 0x141 || CTRL == 0x140,
+                "a full in-row permutation");
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 __device__ __forceinline__ float group16_sum(float v) {
@@ -79,6 +80,23 @@ __device__ __forceinline__ float group16_sum(float v) {
   v += dpp<0x141>(v);
   v += dpp<0x140>(v);
   return v;
+}
+// Eight sums over the 16 lanes of a lane group at once, as a reduce-scatter: at each of
+// four exchanges (row_mirror i <-> 15-i, row_half_mirror i <-> 7-i within eight,
+// quad_perm i <-> 3-i, quad_perm i <-> i^1) a lane keeps half of its partial sums and adds
+// the partner's copies of them, so the eight totals cost 22 vector instructions instead of
+// 32 and land spread over the lanes.  Lane r of the group returns the total of value
+// sum8_index(r); lanes r and r ^ 1 return the same one.
+__device__ __forceinline__ int sum8_index(int r) { return 4 * ((r >> 3) & 1) + 2 * ((r >> 2) & 1) + ((r >> 1) & 1); }
+__device__ __forceinline__ float group16_sum8(const float (&v)[8], int r) {
+  const bool u1 = (r & 8) != 0, u2 = (r & 4) != 0, u3 = (r & 2) != 0;
+  float w[4], x[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = (u1 ? v[4 + k] : v[k]) + dpp<0x140>(u1 ? v[k] : v[4 + k]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) x[k] = (u2 ? w[2 + k] : w[k]) + dpp<0x141>(u2 ? w[k] : w[2 + k]);
+  const float y = (u3 ? x[1] : x[0]) + dpp<0x1B>(u3 ? x[0] : x[1]);
+  return y + dpp<0xB1>(y);
 }
 // full-wave reductions on DPP (16-lane rows) plus four readlanes; the result is uniform
 template <int CTRL> __device__ __forceinline__ double dpp_f64(double v) {
@@ -266,10 +284,20 @@ namespace csa {
 // rows of 128 or 384 bytes (D = 64, 192), where consecutive rows already start half a
 // bank row apart, take the 8 values < 8, which also keeps p ^ swz inside a row of 24
 // pieces.  The pattern repeats every 16 rows.
-template <int D> __device__ __forceinline__ int row_swz(int r) {
+template <int D> __host__ __device__ constexpr int row_swz(int r) {
   static_assert(D == 64 || D == 128 || D == 192 || D == 256 || D == 512, "row size");
   if constexpr (D == 64 || D == 192) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
   else return 2 * (r & 7) + ((r >> 3) & 1);
+}
+// A load instruction of 64 lanes x 16 bytes covers RPI = 64 / (D / 8) whole rows when D
+// divides 512; then the swizzle of row i RPI + g (g < RPI) splits into a per-lane and a
+// per-instruction term.
+template <int D> constexpr bool swz_splits() {
+  constexpr int RPI = 512 / D;
+  for (int i = 0; i * RPI < 32; ++i)
+    for (int g = 0; g < RPI; ++g)
+      if (row_swz<D>(i * RPI + g) != (row_swz<D>(g) ^ row_swz<D>(i * RPI))) return false;
+  return true;
 }
 
 // ---------------------------------------------------------------- LDS DMA

@@ -626,14 +626,18 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
       }
     }
     if (crow && ci >= nwc) {
+      // value e of group g is row 16 (e >> 2) + 4g + (e & 3); lane r16 ends with the head
+      // sum of value sum8_index(r16)
+      float ps[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float ps = p[0][e];
+        ps[e] = p[0][e];
 #pragma unroll
-        for (int gi = 1; gi < NG; ++gi) ps += p[gi][e];
-        const float sh = group16_sum(ps);
-        if (r16 == 0) cm_part[n & 1][w][(e < 4 ? 4 * g + e : 16 + 4 * g + e - 4)] = sh;
+        for (int gi = 1; gi < NG; ++gi) ps[e] += p[gi][e];
       }
+      const float sh = group16_sum8(ps, r16);
+      const int el = sum8_index(r16);
+      if ((r16 & 1) == 0) cm_part[n & 1][w][16 * (el >> 2) + 4 * g + (el & 3)] = sh;
     }
   }
   if (nch > 0) {
@@ -981,6 +985,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
   constexpr float RESCALE = 8.f;
   constexpr int NSC = (IDS + 63) / 64;  // 4-byte loads of a row's selected scores (KL)
   static_assert(NI <= 15, "vmcnt");
+  static_assert(swz_splits<D>(), "row_swz(i RPI + g) = row_swz(g) ^ row_swz(i RPI)");
   // per wave: two tiles, two id buffers and (KL) the selected scores of the current query
   __shared__ __attribute__((aligned(16))) char lds_all[4][2 * TILE + 2 * IDS * 4 + (KL ? 4 * 64 * NSC : 0)];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -995,7 +1000,6 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
   const bool h_ok = h < H;
   const bool group_full = H >= 16;
   const int ncc = (k_eff + 31) >> 5;  // compressed steps per query
-  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)total_q * ROWB);
   const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * ROWB);
   const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // bpermute addresses
   const int gg = lane / PIECES, pp = lane % PIECES;   // load: row-in-instruction, piece position
@@ -1046,17 +1050,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
     for (int c = 0; c < NC; ++c) f[c] = p[4 * c];
   };
   // the NI row loads of step s of a query (window steps first, then compressed steps)
-  // into `base`; valid = false requests NI out-of-range loads
+  // into `base`; valid = false requests NI out-of-range loads.  Load i, lane l writes the
+  // 16 bytes of tile row R = i RPI + gg, piece slot pp, which hold the row's logical piece
+  // pp ^ row_swz(R) = (pp ^ row_swz(gg)) ^ row_swz(i RPI): a per-lane byte offset d0 and a
+  // constant per load, so a load costs one or two address instructions.
   auto dma_step = [&](bool valid, const Geo &G, int buf, int s, char *base) {
-    int pps = pp, ggs = gg;
-    asm volatile("" : "+v"(pps), "+v"(ggs));
+    int d0 = 16 * (pp ^ row_swz<D>(gg)), ggs = gg;
+    asm volatile("" : "+v"(d0), "+v"(ggs));
     if (valid && s < G.nwc) {
+      // rows past the query (slot >= nw) lie past the end of this resource: zeros
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(kv, (uint32_t)(G.w_lo + G.nw) * ROWB);
+      const uint32_t wb = (uint32_t)(G.w_lo + 32 * s + ggs) * ROWB;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int R = i * RPI + ggs, slot = 32 * s + R;
-        const uint32_t off = slot < G.nw ? (uint32_t)(G.w_lo + slot) * ROWB + 16 * (pps ^ row_swz<D>(R)) : BUF_OOB;
-        dma16(rkv, base + i * 1024, off);
-      }
+      for (int i = 0; i < NI; ++i)
+        dma16(rw, base + i * 1024, (wb + (uint32_t)(i * RPI * ROWB)) + (uint32_t)(d0 ^ (16 * row_swz<D>(i * RPI))));
     } else {
       int idr[NI];
       if (valid) {
@@ -1067,12 +1074,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
 #pragma unroll
         for (int i = 0; i < NI; ++i) idr[i] = -1;
       }
+      // an id of -1 gives 2^32 - ROWB + (< ROWB): past the end of the resource, zeros
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int R = i * RPI + ggs;
-        const uint32_t off = idr[i] >= 0 ? (uint32_t)idr[i] * ROWB + 16 * (pps ^ row_swz<D>(R)) : BUF_OOB;
-        dma16(rck, base + i * 1024, off);
-      }
+      for (int i = 0; i < NI; ++i)
+        dma16(rck, base + i * 1024, (uint32_t)idr[i] * ROWB + (uint32_t)(d0 ^ (16 * row_swz<D>(i * RPI))));
     }
   };
 
@@ -1101,11 +1106,14 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
   }
   int n = 0;  // stream step index: step n reads tile n & 1
 
-  // KL: each lane holds, for every other step c = 2i + half, the slot 32c + jl (e = r16 & 7
-  // of its lane group's head sums), so the 64 lanes share a row's slots evenly
+  // head sums of a compressed step: lane r16 of group g ends with the one of value
+  // e = sum8_index(r16), slot jl of the step (lanes r16 and r16 ^ 1 hold the same slot).
+  // KL: each lane keeps it for every other step c = 2i + half, so the 64 lanes share a
+  // row's slots evenly
   constexpr int NO = (KC + 1) / 2;
-  const int half = r16 >> 3;
-  const int jl = 16 * ((r16 >> 2) & 1) + 4 * g + (r16 & 3);   // slot within a step
+  const int half = r16 & 1;
+  const int el = sum8_index(r16);
+  const int jl = 16 * (el >> 2) + 4 * g + (el & 3);             // slot within a step
   const int jo = (jl % RPI) * NI + jl / RPI;                    // its place in ids_lds
   int kp_t = -1;          // the query whose teacher and KL are pending (-1: none)
   bool kp_empty = false;  // its row is left out of the loss
@@ -1305,10 +1313,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
         *reinterpret_cast<uint2 *>(orow + 16 * dt) =
             uint2{pack2_bf16(o[dt][0] * inv, o[dt][1] * inv), pack2_bf16(o[dt][2] * inv, o[dt][3] * inv)};
     }
-    // head sums of the compressed probabilities: after the group sum every lane of group
-    // g holds sums[e] of slot 32c + 16 (e >> 2) + 4g + (e & 3).  For the KL each lane
-    // keeps one of them for every other step: e = r16 & 7 of the steps c = 2i + (r16 >> 3)
-    // in own[i], so the 64 lanes share the row's slots evenly.
+    // head sums of the compressed probabilities: value e of a lane of group g is slot
+    // 32c + 16 (e >> 2) + 4g + (e & 3); lane r16 ends with the sum of slot 32c + jl.  For
+    // the KL each lane keeps the steps c = 2i + half in own[i].
     float own[NO];
 #pragma unroll
     for (int i = 0; i < NO; ++i) own[i] = 0.f;
@@ -1317,27 +1324,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         if (c < ncc) {
-          float sums[8];
+          float pv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sums[e] = group16_sum(pk[c][e] * inv);
+          for (int e = 0; e < 8; ++e) pv[e] = pk[c][e] * inv;
+          const float sum = group16_sum8(pv, r16);
           if constexpr (KL) {
-            float v = sums[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) v = (r16 & 7) == e ? sums[e] : v;
-            if (half == (c & 1)) own[c >> 1] = v;
+            if (half == (c & 1)) own[c >> 1] = sum;
           }
-          // lane r16 = tau of group g writes slots 32c + 16*tau + 4g + (0..3)
-          const int slot0 = 32 * c + 16 * r16 + 4 * g;
-          if (crow && r16 < 2) {
-            const f32x4 v = r16 ? f32x4{sums[4], sums[5], sums[6], sums[7]} : f32x4{sums[0], sums[1], sums[2], sums[3]};
-            if (slot0 + 4 <= k_eff) {
-              *reinterpret_cast<f32x4 *>(crow + slot0) = v;
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (slot0 + i < k_eff) crow[slot0 + i] = v[i];
-            }
-          }
+          const int j = 32 * c + jl;
+          if (crow && half == 0 && j < k_eff) crow[j] = sum;
         }
       }
     }

@@ -277,14 +277,18 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
     if (ci > 0) flush(ci - 1);
     float s[NG][8];
     logits(tile(st), ci, s);
+    // value e of group g is key 16 (e >> 2) + 4g + (e & 3); lane hl ends with the head
+    // sum of value sum8_index(hl)
+    float ps[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float ps = fast_exp2(fmaf(s[0][e], scale_log2, nl[0]));
+      ps[e] = fast_exp2(fmaf(s[0][e], scale_log2, nl[0]));
 #pragma unroll
-      for (int gi = 1; gi < NG; ++gi) ps += fast_exp2(fmaf(s[gi][e], scale_log2, nl[gi]));
-      const float sh = group16_sum(ps);
-      if (hl == 0) part[st & 1][w][e < 4 ? 4 * g + e : 16 + 4 * g + e - 4] = sh;
+      for (int gi = 1; gi < NG; ++gi) ps[e] += fast_exp2(fmaf(s[gi][e], scale_log2, nl[gi]));
     }
+    const float sh = group16_sum8(ps, hl);
+    const int el = sum8_index(hl);
+    if ((hl & 1) == 0) part[st & 1][w][16 * (el >> 2) + 4 * g + (el & 3)] = sh;
   }
   __syncthreads();
   if (nch > 0) flush(nch - 1);
