@@ -405,18 +405,26 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[gi][c] = p[4 * c];
   }
-  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)total_q * ROWB);
+  // window rows past the query lie past the end of rkv: they read zeros
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)(t + 1) * ROWB);
   const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * ROWB);
-  // this wave's loads: instruction i = w + k*HG writes tile bytes [1024 i, 1024 i + 1024),
-  // lane l the 16 bytes of piece slot pc of row R (64 i + l = R * PIECES + pc), which
-  // hold the row's logical piece pc ^ swz(R)
-  // (re-derived at every use from an opaque copy of the lane index, so that they are
-  // not kept live across the steps)
-  auto dslot = [&](int k, int ln, int &R, int &off) __attribute__((always_inline)) {
-    const int P = 64 * (w + k * HG) + ln;
-    R = P / PIECES;
-    off = 16 * ((P - R * PIECES) ^ row_swz<D>(R));
-  };
+  // This wave's loads: instruction i = w + k*HG writes tile bytes [1024 i, 1024 i + 1024),
+  // lane l the 16 bytes of piece slot pc of row R (64 i + l = R * PIECES + pc), which hold
+  // the row's logical piece pc ^ swz(R).  An id of -1 gives an offset of 2^32 - ROWB +
+  // (< ROWB), past the end of rck: zeros.
+  // When a load covers whole rows (RPI = 512 / D of them), R = i RPI + l / PIECES and the
+  // swizzle splits into a per-lane and a per-load term, so the lane's part is one value
+  // re-derived at each use from an opaque copy of the lane index; rows of 384 bytes keep,
+  // per load, the lane's row and piece offset packed in one register (R << 16 | offset).
+  constexpr bool SPLIT = 512 % D == 0;
+  constexpr int NPK = SPLIT ? 1 : NIW;
+  uint32_t lpk[NPK];
+#pragma unroll
+  for (int k = 0; k < NPK; ++k) {
+    const int P = 64 * (w + k * HG) + lane, R = P / PIECES;
+    lpk[k] = ((uint32_t)R << 16) | (uint32_t)(16 * ((P - R * PIECES) ^ row_swz<D>(R)));
+  }
+  if constexpr (SPLIT) static_assert(swz_splits<D>(), "row_swz(i RPI + g) = row_swz(g) ^ row_swz(i RPI)");
   // K operand: row r16 (+16), piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3))
   const int ksw = row_swz<D>(r16);
   const int kbase = r16 * ROWB + 16 * (g ^ (ksw & 3)), kx = ksw >> 2;
@@ -427,31 +435,37 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
 
   // rows of chunk ci (window chunks first, then compressed) into tile `buf`
   auto issue = [&](int ci, char *buf) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    if (ci < nwc) {
+    if constexpr (SPLIT) {
+      constexpr int RPI = SPLIT ? 512 / D : 1;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int gl = ln / PIECES;
+      const uint32_t d0 = 16 * ((ln % PIECES) ^ row_swz<D>(gl));   // < ROWB
 #pragma unroll
       for (int k = 0; k < NIW; ++k) {
         const int i = w + k * HG;
         if (NI % HG == 0 || i < NI) {
-          int R, doff;
-          dslot(k, ln, R, doff);
-          const int slot = 32 * ci + R;
-          const uint32_t off = slot < nw ? (uint32_t)(w_lo + slot) * ROWB + doff : BUF_OOB;
-          dma16(rkv, buf + i * 1024, off);
+          const uint32_t sx = 16 * row_swz<D>(i * RPI);
+          if (ci < nwc) {
+            dma16(rkv, buf + i * 1024, (uint32_t)(w_lo + 32 * ci + i * RPI + gl) * ROWB + (d0 ^ sx));
+          } else {
+            const int id = ids_l[32 * (ci - nwc) + i * RPI + gl];
+            dma16(rck, buf + i * 1024, (uint32_t)id * ROWB + (d0 ^ sx));
+          }
         }
       }
     } else {
-      const int *il = ids_l + 32 * (ci - nwc);
 #pragma unroll
       for (int k = 0; k < NIW; ++k) {
         const int i = w + k * HG;
         if (NI % HG == 0 || i < NI) {
-          int R, doff;
-          dslot(k, ln, R, doff);
-          const int id = il[R];
-          const uint32_t off = id >= 0 ? (uint32_t)id * ROWB + doff : BUF_OOB;
-          dma16(rck, buf + i * 1024, off);
+          const uint32_t R = lpk[k] >> 16, off = lpk[k] & 0xffffu;
+          if (ci < nwc) {
+            dma16(rkv, buf + i * 1024, (uint32_t)(w_lo + 32 * ci) * ROWB + R * ROWB + off);
+          } else {
+            const int id = ids_l[32 * (ci - nwc) + R];
+            dma16(rck, buf + i * 1024, (uint32_t)id * ROWB + off);
+          }
         }
       }
     }

@@ -161,6 +161,8 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(ckv + (int64_t)geo.k_base * D, (uint32_t)n * ROWB);
   const int nch = (n + 31) / 32;
   // this wave's loads of chunk ci: instruction i = w + k*HG, lane l -> piece slot 64 i + l
+  // (when a load covers whole rows, RPI = 512 / D of them, the row is i RPI + l / PIECES
+  // and the swizzle splits into a per-lane and a per-load term)
   auto issue = [&](int ci, char *buf) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -168,9 +170,17 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
     for (int k = 0; k < NIW; ++k) {
       const int i = w + k * HG;
       if (NI % HG == 0 || i < NI) {
-        const int P = 64 * i + ln;
-        const int R = P / PIECES, pc = P - R * PIECES;
-        dma16(rk, buf + i * 1024, (uint32_t)(32 * ci + R) * ROWB + 16 * (pc ^ row_swz<D>(R)));
+        if constexpr (512 % D == 0) {
+          static_assert(512 % D != 0 || swz_splits<D>(), "row_swz(i RPI + g) = row_swz(g) ^ row_swz(i RPI)");
+          constexpr int RPI = 512 % D == 0 ? 512 / D : 1;
+          const int gl = ln / PIECES;
+          const uint32_t d0 = 16 * ((ln % PIECES) ^ row_swz<D>(gl)), sx = 16 * row_swz<D>(i * RPI);
+          dma16(rk, buf + i * 1024, (uint32_t)(32 * ci + i * RPI + gl) * ROWB + (d0 ^ sx));
+        } else {
+          const int P = 64 * i + ln;
+          const int R = P / PIECES, pc = P - R * PIECES;
+          dma16(rk, buf + i * 1024, (uint32_t)(32 * ci + R) * ROWB + 16 * (pc ^ row_swz<D>(R)));
+        }
       }
     }
   };
