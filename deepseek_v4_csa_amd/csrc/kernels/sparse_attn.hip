@@ -333,9 +333,12 @@ __global__ __launch_bounds__(64 * HG) void sparse_attn_kernel(
 // ============================================================================
 // Workgroup variant (bf16; any H up to 16*HG; D = 64, 128, 192, 256 or 512; k_eff <= 4096).
 //
-// One workgroup per query row, wave w owning heads [16w, 16w+16), the same two passes as
-// the kernel above (exact per-head max and sum first, then P, O and cmass with lse
-// already final).  The gathered rows are staged 32 at a time into two LDS tiles by
+// One workgroup per query row, wave w owning NG groups of 16 heads, in two passes.  Pass 1
+// runs over every chunk: the per-head sum under a running max shared by a head's lane
+// groups (raised lazily, by at least 2^8), and for the window chunks P V straight into O,
+// rescaled with the max.  Pass 2 runs over the compressed chunks only, with lse final:
+// their probabilities P = exp(s - lse) are formed once, for O and for cmass.  So a window
+// row's logits and exponentials are computed once, a compressed row's twice.  The gathered rows are staged 32 at a time into two LDS tiles by
 // direct buffer->LDS loads: the waves split the D/16 load instructions of a tile between
 // them, and the next tile's loads are issued right after the step's barrier, so they
 // stream in while the current tile is consumed.  Rows are stored with the XOR swizzle
@@ -500,32 +503,31 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
         acc1[gi] = mfma16x16x32(k1, qf[gi][c], acc1[gi]);
       }
     }
-    if (wave_full && bm == 0xffffffffu) {
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi)
+    for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { sv[gi][i] = acc0[gi][i]; sv[gi][4 + i] = acc1[gi][i]; }
-    } else {
+      for (int i = 0; i < 4; ++i) { sv[gi][i] = acc0[gi][i]; sv[gi][4 + i] = acc1[gi][i]; }
+    if (!(wave_full && bm == 0xffffffffu)) {   // masked in place
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
         const uint32_t m0 = h_ok[gi] ? (bm >> (4 * g)) : 0u, m1 = h_ok[gi] ? (bm >> (16 + 4 * g)) : 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sv[gi][i] = ((m0 >> i) & 1) ? acc0[gi][i] : NINF;
-          sv[gi][4 + i] = ((m1 >> i) & 1) ? acc1[gi][i] : NINF;
+          sv[gi][i] = ((m0 >> i) & 1) ? sv[gi][i] : NINF;
+          sv[gi][4 + i] = ((m1 >> i) & 1) ? sv[gi][4 + i] : NINF;
         }
       }
     }
   };
 
   __syncthreads();   // ids in LDS
-  // Steps: pass 1 over the chunks, then pass 2; step n reads tile n & 1 and, right after
-  // its barrier (its own loads have landed, so after the barrier every wave's have, and
-  // every wave has finished reading tile n - 1), requests the rows of step n + 1 into the
-  // other tile, where they stream in while tile n is consumed.  (A third tile, requests
-  // two steps ahead, measured slower on these shapes.)
-  const int ns = 2 * nch;
-  auto chunk_of = [&](int n) { return n < nch ? n : n - nch; };
+  // Steps: pass 1 over every chunk, then pass 2 over the compressed chunks; step n reads
+  // tile n & 1 and, right after its barrier (its own loads have landed, so after the
+  // barrier every wave's have, and every wave has finished reading tile n - 1), requests
+  // the rows of step n + 1 into the other tile, where they stream in while tile n is
+  // consumed.  (A third tile, requests two steps ahead, measured slower on these shapes.)
+  const int ns = nch + ncc;
+  auto chunk_of = [&](int n) { return n < nch ? n : nwc + (n - nch); };
   auto tile = [&](int n) { return wg_dyn + (n & 1) * TILE; };
   auto top = [&](int n) {
     wait_vmcnt<0>();
@@ -534,92 +536,21 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
   };
   if (ns > 0) issue(0, tile(0));
 
-  // ---------------------------------------------------------------- pass 1: max / sum
-  float m[NG], l[NG], m_nc[NG], l_nc[NG];
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const float a2 = h_ok[gi] ? sink[hh[gi]] * LOG2E : NINF;
-    m[gi] = (g == 0) ? a2 : NINF;
-    l[gi] = (g == 0 && a2 > NINF) ? 1.f : 0.f;
-    m_nc[gi] = m[gi];
-    l_nc[gi] = l[gi];
-  }
-  for (int ci = 0; ci < nch; ++ci) {
-    const int n = ci;
-    top(n);
-    if (ci == nwc) {
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi) { m_nc[gi] = m[gi]; l_nc[gi] = l[gi]; }
-    }
-    float sv[NG][8];
-    logits(tile(n), row_mask(ci), sv);
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      float cm = sv[gi][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[gi][e]);
-      const float mn = fmaxf(m[gi], cm * sl2);   // log2 units (sl2 > 0 keeps the order)
-      if (mn > NINF) {
-        float acc = l[gi] * fast_exp2(m[gi] - mn);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += fast_exp2(fmaf(sv[gi][e], sl2, -mn));
-        l[gi] = acc;
-        m[gi] = mn;
-      }
-    }
-  }
-  float lse2[NG], lse2_nc[NG], nl[NG];
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    if (ncc == 0) { m_nc[gi] = m[gi]; l_nc[gi] = l[gi]; }
-    const float M = across_groups_max(m[gi]);
-    const float Ls = across_groups_sum(M > NINF ? l[gi] * fast_exp2(m[gi] - M) : 0.f);
-    const float Mnc = across_groups_max(m_nc[gi]);
-    const float Lnc = across_groups_sum(Mnc > NINF ? l_nc[gi] * fast_exp2(m_nc[gi] - Mnc) : 0.f);
-    lse2[gi] = Ls > 0.f ? M + __log2f(Ls) : NINF;
-    lse2_nc[gi] = Lnc > 0.f ? Mnc + __log2f(Lnc) : NINF;
-    nl[gi] = lse2[gi] > NINF ? -lse2[gi] : NINF;   // exp2(-inf) = 0: no probability at all
-  }
-
-  // ---------------------------------------------------------------- pass 2: P, O, cmass
   f32x4 o[NG][D / 16];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) o[gi][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float *crow = cmass ? cmass + (int64_t)t * k_eff : nullptr;
-  // sums over the waves of the compressed chunk staged at the previous step
-  auto flush = [&](int cprev, int pbuf) {
-    if (crow && cprev >= nwc && tid < 32) {
-      const int slot = 32 * (cprev - nwc) + tid;
-      if (slot < k_eff) {
-        float sum = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < HG; ++ww) sum += cm_part[pbuf][ww][tid];
-        crow[slot] = sum;
-      }
-    }
-  };
-  for (int ci = 0; ci < nch; ++ci) {
-    const int n = nch + ci;
-    top(n);
-    if (ci > 0) flush(ci - 1, (n - 1) & 1);
-    const char *base = tile(n);
-    float sv[NG][8];
-    logits(base, row_mask(ci), sv);
-    float p[NG][8];
+  // O^T += V^T P^T for the tile at `base`: V^T operands in batches of BDT d-tiles (fewer
+  // registers in flight), each feeding the MFMAs of every head group
+  auto pv = [&](const char *base, const float (&p)[NG][8]) __attribute__((always_inline)) {
     u32x4 pb[NG];
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[gi][e] = fast_exp2(fmaf(sv[gi][e], sl2, nl[gi]));
+    for (int gi = 0; gi < NG; ++gi)
       pb[gi] = u32x4{pack2_bf16(p[gi][0], p[gi][1]), pack2_bf16(p[gi][2], p[gi][3]),
                      pack2_bf16(p[gi][4], p[gi][5]), pack2_bf16(p[gi][6], p[gi][7])};
-    }
     int vxs = vx;
     asm volatile("" : "+v"(vxs));
-    // V^T operands in batches of BDT d-tiles (fewer registers in flight); each feeds the
-    // MFMAs of every head group
 #pragma unroll
     for (int hf = 0; hf < D / 16 / BDT; ++hf) {
       uint2 xv[2 * BDT];
@@ -639,7 +570,108 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
         for (int gi = 0; gi < NG; ++gi) o[gi][dt] = mfma16x16x32(a, pb[gi], o[gi][dt]);
       }
     }
-    if (crow && ci >= nwc) {
+  };
+
+  // ------------------------------------------------- pass 1: sums, and P V of the window
+  // One running max per head, shared by its 4 lane groups and raised only when a logit
+  // exceeds it by 2^8 (then the wave agrees on the new per-head max and rescales l and O),
+  // so the window's probabilities exp2(sl2 s - m) <= 2^8 go straight into O.
+  constexpr float RESCALE = 8.f;
+  float m[NG], l[NG], m_nc[NG], l_nc[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float a2 = h_ok[gi] ? sink[hh[gi]] * LOG2E : NINF;
+    m[gi] = a2;
+    l[gi] = (g == 0 && a2 > NINF) ? 1.f : 0.f;   // the sink counted once per head
+    m_nc[gi] = m[gi];
+    l_nc[gi] = l[gi];
+  }
+  for (int ci = 0; ci < nch; ++ci) {
+    const int n = ci;
+    top(n);
+    if (ci == nwc) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) { m_nc[gi] = m[gi]; l_nc[gi] = l[gi]; }
+    }
+    const char *base = tile(n);
+    float sv[NG][8];
+    logits(base, row_mask(ci), sv);
+    float cmx[NG];
+    bool up = false;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      cmx[gi] = sv[gi][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) cmx[gi] = fmaxf(cmx[gi], sv[gi][e]);
+      up = up || cmx[gi] * sl2 > m[gi] + RESCALE;   // log2 units (sl2 > 0 keeps the order)
+    }
+    if (__builtin_expect(__ballot(up) != 0, 0)) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const float cand = across_groups_max(cmx[gi]) * sl2;
+        const float mn = cand > m[gi] + RESCALE ? cand : m[gi];
+        const float alpha = mn == m[gi] ? 1.f : fast_exp2(m[gi] - mn);
+        l[gi] *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) o[gi][i] *= alpha;
+        m[gi] = mn;
+      }
+    }
+    float p[NG][8];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float nms = m[gi] == NINF ? 0.f : -m[gi];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[gi][e] = fast_exp2(fmaf(sv[gi][e], sl2, nms));
+        l[gi] += p[gi][e];
+      }
+    }
+    if (ci < nwc) pv(base, p);
+  }
+  // lse, lse_nc; the window part of O normalised, so pass 2 adds normalised terms to it
+  float lse2[NG], lse2_nc[NG], nl[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    if (ncc == 0) { m_nc[gi] = m[gi]; l_nc[gi] = l[gi]; }
+    const float Ls = across_groups_sum(l[gi]);
+    const float Lnc = across_groups_sum(l_nc[gi]);
+    lse2[gi] = Ls > 0.f ? m[gi] + __log2f(Ls) : NINF;
+    lse2_nc[gi] = Lnc > 0.f ? m_nc[gi] + __log2f(Lnc) : NINF;
+    nl[gi] = lse2[gi] > NINF ? -lse2[gi] : NINF;   // exp2(-inf) = 0: no probability at all
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[gi][i] *= inv;
+  }
+
+  // ------------------------------------------- pass 2: compressed chunks, P, O and cmass
+  float *crow = cmass ? cmass + (int64_t)t * k_eff : nullptr;
+  // sums over the waves of the compressed chunk staged at the previous step
+  auto flush = [&](int cprev, int pbuf) {
+    if (crow && cprev >= nwc && tid < 32) {
+      const int slot = 32 * (cprev - nwc) + tid;
+      if (slot < k_eff) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < HG; ++ww) sum += cm_part[pbuf][ww][tid];
+        crow[slot] = sum;
+      }
+    }
+  };
+  for (int cc = 0; cc < ncc; ++cc) {
+    const int ci = nwc + cc, n = nch + cc;
+    top(n);
+    if (cc > 0) flush(ci - 1, (n - 1) & 1);
+    const char *base = tile(n);
+    float sv[NG][8];
+    logits(base, row_mask(ci), sv);
+    float p[NG][8];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[gi][e] = fast_exp2(fmaf(sv[gi][e], sl2, nl[gi]));
+    pv(base, p);
+    if (crow) {
       // value e of group g is row 16 (e >> 2) + 4g + (e & 3); lane r16 ends with the head
       // sum of value sum8_index(r16)
       float ps[8];
@@ -654,7 +686,7 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
       if ((r16 & 1) == 0) cm_part[n & 1][w][16 * (el >> 2) + 4 * g + (el & 3)] = sh;
     }
   }
-  if (nch > 0) {
+  if (ncc > 0) {
     __syncthreads();
     flush(nch - 1, (ns - 1) & 1);
   }
@@ -1214,15 +1246,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
         acc0 = mfma16x16x32(k0, qf[c], acc0);
         acc1 = mfma16x16x32(k1, qf[c], acc1);
       }
-      if (group_full && bm == 0xffffffffu) {
+      // (masked in place: the common full-tile path then needs no register copies)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { raw[i] = acc0[i]; raw[4 + i] = acc1[i]; }
-      } else {
+      for (int i = 0; i < 4; ++i) { raw[i] = acc0[i]; raw[4 + i] = acc1[i]; }
+      if (!(group_full && bm == 0xffffffffu)) {
         const uint32_t m0 = h_ok ? (bm >> (4 * g)) : 0u, m1 = h_ok ? (bm >> (16 + 4 * g)) : 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          raw[i] = ((m0 >> i) & 1) ? acc0[i] : NINF;
-          raw[4 + i] = ((m1 >> i) & 1) ? acc1[i] : NINF;
+          raw[i] = ((m0 >> i) & 1) ? raw[i] : NINF;
+          raw[4 + i] = ((m1 >> i) & 1) ? raw[4 + i] : NINF;
         }
       }
       // Common path without cross-lane traffic: each lane tests its logits against the
