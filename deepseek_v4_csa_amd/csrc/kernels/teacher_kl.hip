@@ -234,38 +234,50 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
 
   // pass 1: l_h = log2(2^{u_h} + sum_j 2^{c_hj})   (base-2 logits; scale_log2 > 0, so the
   // maximum of the unscaled products is the maximum of the logits)
+  // (one running max per head, shared by its 4 lane groups and raised only when a logit
+  // exceeds it by 2^8, so the common chunk needs no rescaling and no cross-lane traffic)
+  constexpr float RESCALE = 8.f;
   float m[NG], l[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const float u2 = h_ok[gi] ? lse_nc[(int64_t)t * H + hh[gi]] * LOG2E : NINF;
-    m[gi] = g == 0 ? u2 : NINF;
-    l[gi] = (g == 0 && u2 > NINF) ? 1.f : 0.f;
+    m[gi] = u2;
+    l[gi] = (g == 0 && u2 > NINF) ? 1.f : 0.f;   // e^{u_h} counted once per head
   }
   for (int ci = 0; ci < nch; ++ci) {
     top(ci);
     float s[NG][8];
     logits(tile(ci), ci, s);
+    float cmx[NG];
+    bool up = false;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      float cmx = s[gi][0];
+      cmx[gi] = s[gi][0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) cmx = fmaxf(cmx, s[gi][e]);
-      const float mn = fmaxf(m[gi], cmx * scale_log2);
-      if (mn > NINF) {
-        float acc = l[gi] * fast_exp2(m[gi] - mn);
+      for (int e = 1; e < 8; ++e) cmx[gi] = fmaxf(cmx[gi], s[gi][e]);
+      up = up || cmx[gi] * scale_log2 > m[gi] + RESCALE;
+    }
+    if (__builtin_expect(__ballot(up) != 0, 0)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc += fast_exp2(fmaf(s[gi][e], scale_log2, -mn));
-        l[gi] = acc;
+      for (int gi = 0; gi < NG; ++gi) {
+        const float cand = across_groups_max(cmx[gi]) * scale_log2;
+        const float mn = cand > m[gi] + RESCALE ? cand : m[gi];
+        l[gi] *= mn == m[gi] ? 1.f : fast_exp2(m[gi] - mn);
         m[gi] = mn;
       }
+    }
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const float nms = m[gi] == NINF ? 0.f : -m[gi];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l[gi] += fast_exp2(fmaf(s[gi][e], scale_log2, nms));
     }
   }
   float nl[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    const float M = across_groups_max(m[gi]);
-    const float Ls = across_groups_sum(M > NINF ? l[gi] * fast_exp2(m[gi] - M) : 0.f);
-    const float ell2 = Ls > 0.f ? M + __log2f(Ls) : NINF;
+    const float Ls = across_groups_sum(l[gi]);
+    const float ell2 = Ls > 0.f ? m[gi] + __log2f(Ls) : NINF;
     nl[gi] = ell2 > NINF ? -ell2 : NINF;   // exp2(-inf) = 0: no mass at all
   }
 
