@@ -47,10 +47,10 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="path: score and top-k as two calls (the score matrix stored) even where "
                          "the fused call applies")
-    ap.add_argument("--attn-kl", action="store_true",
-                    help="path: attention, teacher and KL as one call (csa_sparse_attn_kl_fwd, then "
-                         "csa_loss_reduce) instead of csa_sparse_attn_fwd + csa_indexer_teacher_kl "
-                         "(measured about 1%% slower on bshd-b2-s4096, so not the default)")
+    ap.add_argument("--two-call-attn", action="store_true",
+                    help="path: csa_sparse_attn_fwd + csa_indexer_teacher_kl even where the one-call "
+                         "attention + teacher/KL kernel applies (csa_sparse_attn_kl_fwd, then "
+                         "csa_loss_reduce: the default there, ~2%% faster on bshd-b2-s4096)")
     ap.add_argument("--cp", type=int, default=8, help="cp-share: CP size")
     ap.add_argument("--rank", type=int, default=0, help="cp-share: rank")
     return ap.parse_args()
@@ -406,9 +406,11 @@ def main():
             fused, sel = False, None
     if fused:
         scores = None
-    # --attn-kl (sparse loss): attention, teacher and KL in one call, the loss reduced by
-    # its own call
-    attn_kl = wl.sparse_loss and args.attn_kl
+    # sparse loss on shapes the one-wave-per-query kernel takes (bf16, H <= 16, D of 64 or
+    # 128, a window, k_eff <= 256, the selected scores of the fused top-k): attention,
+    # teacher and KL in one call, the loss reduced by its own call
+    attn_kl = (wl.sparse_loss and not args.two_call_attn and sel is not None and wl.dtype != "f32"
+               and wl.H <= 16 and wl.D in (64, 128) and wl.window > 0 and k_eff <= 256)
     att_name = "sparse_attn_kl" if attn_kl else "sparse_attn"
     names = (("indexer_topk",) if fused else ("indexer_score", "topk")) + \
         ((att_name, "loss_reduce") if attn_kl else (att_name, "teacher_kl"))
