@@ -384,20 +384,31 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
   const RowGeo geo = row_geo(L, t);
   const int w_lo = max(geo.q_start, t - window + 1);
   const int nw = window > 0 ? t - w_lo + 1 : 0;
-  const int nwc = (nw + 31) >> 5, ncc = (k_eff + 31) >> 5, nch = nwc + ncc;
+  const int nwc = (nw + 31) >> 5, ncc_all = (k_eff + 31) >> 5;
   // the row's ids, padded with -1 to whole 32-row chunks: unconditional loads through a
   // buffer resource of exactly k_eff ids, four per thread in flight at once (a load under a
-  // per-element branch is waited for before the next is issued)
+  // per-element branch is waited for before the next is issued).  The last slot holding
+  // an id (jlast) bounds the compressed chunks: those after it have no row, contribute
+  // nothing, and are skipped (top-k rows with fewer causal keys than k_eff end in -1s).
+  __shared__ int jlast;
+  if (tid == 0) jlast = -1;
+  __syncthreads();
   {
     const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids + (int64_t)t * k_eff, (uint32_t)k_eff * 4);
-    for (int i0 = tid; i0 < ncc * 32; i0 += 4 * NT) {
+    int jl = -1;
+    for (int i0 = tid; i0 < ncc_all * 32; i0 += 4 * NT) {
       int x[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) x[u] = __builtin_amdgcn_raw_buffer_load_b32(rid, (i0 + u * NT) * 4, 0, 0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (i0 + u * NT < ncc * 32) ids_l[i0 + u * NT] = i0 + u * NT < k_eff ? x[u] : -1;
+      for (int u = 0; u < 4; ++u) {
+        const int j = i0 + u * NT;
+        const int id = j < k_eff ? x[u] : -1;
+        if (j < ncc_all * 32) ids_l[j] = id;
+        if (id >= 0) jl = j;   // j grows with u and i0
+      }
     }
+    if (jl >= 0) atomicMax(&jlast, jl);
   }
   // Q^T operands, MFMA K index <-> feature: piece c of lane group g holds features [(4c+g)*8, +8)
   // (a lane of a head past H loads head 0's row: its logits are masked, the values never used)
@@ -520,7 +531,10 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
     }
   };
 
-  __syncthreads();   // ids in LDS
+  __syncthreads();   // ids and jlast in LDS
+  const int ncc = (jlast + 32) >> 5, nch = nwc + ncc;
+  if (cmass != nullptr)   // the skipped chunks' slots hold no id: mass 0
+    for (int j = 32 * ncc + tid; j < k_eff; j += NT) cmass[(int64_t)t * k_eff + j] = 0.f;
   // Steps: pass 1 over every chunk, then pass 2 over the compressed chunks; step n reads
   // tile n & 1 and, right after its barrier (its own loads have landed, so after the
   // barrier every wave's have, and every wave has finished reading tile n - 1), requests
