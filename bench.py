@@ -1,14 +1,16 @@
 """Throughput of the CSA forward hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bshd-b2-s4096]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long-64k]
                     [--row path|backward|cp-share]
 
 One step = the four calls of the path (indexer scores, top-k, window+top-k sparse
 attention with sink and teacher masses, teacher + KL + loss) over one batch of seeded
-synthetic inputs already resident in HBM.  Prints one JSON line: query tokens/s over K
-timed steps, the roofline of the dominant kernel (HIP events on the launch stream,
-around the attention launch inside the timed region) and the CPU oracle timed on a
-bounded row sample of the same workload (cpu_baseline).
+synthetic inputs already resident in HBM.  The default workload is the largest one that
+fits one GPU: one 65,536-token sequence, 128 heads over a shared 512-wide latent KV, 64
+indexer heads x 128, top-2048 of 16,384 compressed keys, window 128.  Prints one JSON
+line: query tokens/s over K timed steps, the roofline of the dominant kernel (HIP events
+on the launch stream, around the attention launch inside the timed region) and the CPU
+oracle timed on a bounded row sample of the same workload (cpu_baseline).
 
 The steps after the path are measured the same way, one JSON line each:
   --row backward   one step = csa_indexer_loss_bwd (score gradients, dq_idx/dweights,
@@ -17,6 +19,18 @@ The steps after the path are measured the same way, one JSON line each:
                    context-parallel scoring (csa_cp_plan): the 65,536-token sequence at
                    CP = 8, rank 0 (chunks 0 and 15, 8,192 rows, key prefixes cropped at
                    the chunk ends).
+
+Measurement tools (the profiles' summaries are made with these):
+  python bench.py copy-probe
+        a plain 1 GiB device copy, three times: profiled beside the path, it calibrates
+        the FETCH_SIZE / WRITE_SIZE counters (a copy's bytes are known exactly);
+  python bench.py prof-summary stats <stats_dir> <out.txt> --cmd "<command>"
+  python bench.py prof-summary traffic <workload> <fetch_dir> <write_dir> \
+        <copy_fetch_dir> <copy_write_dir> <out_prefix> --cmd "<command>"
+        rocprofv3 CSV output (run_kernel_stats.csv of --kernel-trace --stats;
+        run_counter_collection.csv of one --pmc FETCH_SIZE or WRITE_SIZE pass) turned
+        into the short summaries of profiles/ and the per-kernel HBM traffic table that
+        the JSON line's roofline.traffic reads.
 """
 from __future__ import annotations
 
@@ -38,9 +52,9 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="bshd-b2-s4096")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long-64k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--row", default="path", choices=("path", "backward", "cp-share"))
@@ -104,26 +118,29 @@ def traffic_of(wl_name, kernel):
     return d.get("hbm_bytes_per_launch")
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, seconds):
-    """The CPU oracle (as it stands) on a seeded uniform sample of rows of the workload."""
+    """The CPU oracle (as it stands) on a seeded uniform sample of rows of the workload.
+    Only the sampled rows of the per-row tensors (q, q_idx, weights) are copied to the
+    host; the key/value tensors are copied whole.  Uniform rows carry the average work of
+    a row, so rows/s is the oracle's query tokens/s on the whole workload."""
     import numpy as np
-    import torch
     import oracle
     from deepseek_v4_csa_amd.inputs import uniform_rows
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     wl = inp.wl
-    h = lambda x: x.detach().to("cpu", torch.float64).numpy()
-    L = oracle.Layout(cu_q=inp.cu_q.cpu().numpy(), cu_k=inp.cu_k.cpu().numpy(), ratio=wl.ratio,
-                      off=inp.offsets.cpu().numpy())
-    P = oracle.Problem(layout=L, q=h(inp.q), kv=h(inp.kv), ckv=h(inp.ckv), q_idx=h(inp.q_idx),
-                       k_idx=h(inp.k_idx), weights=h(inp.weights), sink=h(inp.sink), topk=wl.topk,
-                       window=wl.window, scale=inp.scale, idx_scale=inp.idx_scale,
-                       sparse_loss=wl.sparse_loss)
-    order = uniform_rows(wl.total_q, wl.total_q, seed=11)
+    # at most ~512 MB of q rows on the host
+    n = min(wl.total_q, 4096, max(256, int(5e8 / (wl.H * wl.D * 8))))
+    order = uniform_rows(wl.total_q, n, seed=11)
+    P = _oracle_problem(inp, order)
     rng = np.random.default_rng(11)
     rng.shuffle(order)
     t0 = time.perf_counter()
@@ -134,7 +151,8 @@ def cpu_baseline(inp, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": done / el, "unit": "query tokens/s", "cores": int(_threads()), "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"{done} uniformly drawn rows of {wl.total_q} ({wl.name}), every step of the path "
                       f"per row in NumPy float64, {el:.1f} s"}
 
@@ -459,14 +477,29 @@ def main():
     value = T * args.steps / elapsed
     wm = work_model(wl)
 
-    # the attention's algorithmic bytes; with the teacher/KL finished in its epilogue also
-    # the selected scores it reads and kl_row (ids and cmass are already in attn_bytes)
+    # The attention's roofline: algorithmic bytes on the gather model (each query's
+    # window and selected KV rows counted once per query, plus q, out and the per-row
+    # statistics; with the teacher/KL finished in its epilogue also the selected scores it
+    # reads and kl_row) against the HBM peak, and its algorithmic FLOP (4 H D per gathered
+    # row) against the MFMA peak; the binding resource is the one with the larger ideal
+    # time.  The unique KV rows are small enough for the caches, so the DRAM bytes the
+    # counters see (traffic) stay below the gather-model bytes.
     att_bytes = wm["attn_bytes"] + ((4 * T * k_eff + 4 * T) if attn_kl else 0)
-    roof = {"kernel": att_name, "bound": "hbm",
-            "achieved": att_bytes / (att_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    mfma_peak = FP32_MFMA_PEAK_TFLOPS if wl.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
+    att_sec = att_ms * 1e-3
+    hbm = {"achieved": att_bytes / att_sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    mfma = {"achieved": wm["attn_flop"] / att_sec / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"}
+    hbm_bound = att_bytes / (HBM_PEAK_GBS * 1e9) >= wm["attn_flop"] / (mfma_peak * 1e12)
+    roof = {"kernel": att_name, "bound": "hbm" if hbm_bound else "mfma", **(hbm if hbm_bound else mfma),
             "traffic": traffic_of(wl.name, att_name)}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    idx_peak = FP32_MFMA_PEAK_TFLOPS if wl.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
+    roof["model"] = "gather: every query's window and selected KV rows counted once, plus q, out and row statistics"
+    roof["algorithmic"] = {"bytes": att_bytes, "flop": wm["attn_flop"]}
+    roof["frac_mfma"] = mfma["achieved"] / mfma["peak"]
+    roof["frac_hbm_gather"] = hbm["achieved"] / hbm["peak"]
+    if roof["traffic"] is not None:
+        roof["frac_hbm_counters"] = roof["traffic"] / att_sec / 1e9 / HBM_PEAK_GBS
+    idx_peak = mfma_peak
     kernels = {}
     if fused:
         kernels["indexer_topk"] = {
@@ -480,8 +513,8 @@ def main():
             "frac_mfma_peak": wm["indexer_flop"] / (per_kernel_ms["indexer_score"] * 1e-3) / 1e12 / idx_peak}
         kernels["topk"] = {"us": per_kernel_ms["topk"] * 1e3,
                            "gbs": wm["topk_bytes"] / (per_kernel_ms["topk"] * 1e-3) / 1e9}
-    kernels[att_name] = {"us": att_ms * 1e3, "gbs_gather_model": roof["achieved"],
-                         "tflops": wm["attn_flop"] / (att_ms * 1e-3) / 1e12}
+    kernels[att_name] = {"us": att_ms * 1e3, "gbs_gather_model": hbm["achieved"], "tflops": mfma["achieved"],
+                         "frac_mfma_peak": roof["frac_mfma"]}
     if attn_kl:
         kernels["loss_reduce"] = {"us": per_kernel_ms["loss_reduce"] * 1e3}
     else:
@@ -506,5 +539,137 @@ def main():
     print(json.dumps(line))
 
 
+# ------------------------------------------------------------------ measurement tools
+COPY_BYTES = 1 << 30
+KSRC = os.path.join(ROOT, "deepseek_v4_csa_amd", "csrc", "kernels")
+# kernel family -> (name prefix in the trace, source file)
+FAMILIES = {
+    "indexer_topk": ("csa::indexer_score_lds_kernel", "indexer_score.hip"),
+    "indexer_score": ("csa::indexer_score", "indexer_score.hip"),
+    "topk": ("csa::topk", "topk.hip"),
+    "sparse_attn": ("csa::sparse_attn", "sparse_attn.hip"),
+    "sparse_attn_kl": ("csa::sparse_attn_pipe_kernel", "sparse_attn.hip"),
+    "teacher_kl": ("csa::teacher_kl", "teacher_kl.hip"),
+    "loss_reduce": ("csa::loss_reduce", "teacher_kl.hip"),
+}
+
+
+def copy_probe():
+    """A plain device copy of COPY_BYTES, three times (counter calibration)."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x3")
+
+
+def _short(name: str) -> str:
+    import re
+    name = re.sub(r"^void ", "", name)
+    return re.sub(r"\(.*", "", name)
+
+
+def _family_of(name: str):
+    # the attention kernel that also finishes the teacher and KL (csa_sparse_attn_kl_fwd)
+    if "csa::sparse_attn_pipe_kernel" in name and ", true>" in name:
+        return "sparse_attn_kl"
+    # the fused score + top-k instance of the paired-block indexer kernel
+    if "csa::indexer_score_lds_kernel" in name and ", true," in name:
+        return "indexer_topk"
+    for fam, (prefix, _) in FAMILIES.items():
+        if fam != "indexer_topk" and prefix in name:
+            return fam
+    return None
+
+
+def _sha256(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def prof_stats(stats_dir: str, out: str, cmd: str) -> None:
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
+    lines = ["# rocprofv3 kernel statistics", f"# command: {cmd}", "",
+             f"{'kernel':<58} {'calls':>6} {'avg us':>9} {'min us':>9} {'max us':>9} {'% time':>7}"]
+    for r in rows:
+        lines.append(f"{_short(r['Name'])[:58]:<58} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                     f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>7.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def _counter_means(d: str, counter: str):
+    import collections
+    import csv
+    acc = collections.defaultdict(list)
+    for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+        if r["Counter_Name"] == counter:
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def _copy_scale(d: str, counter: str) -> float:
+    """Bytes per counter unit, from the plain copy kernel of copy-probe."""
+    means, _ = _counter_means(d, counter)
+    copies = {k: v for k, v in means.items() if "copyBuffer" in k}
+    if len(copies) != 1:
+        raise SystemExit(f"{d}: expected one copy kernel, found {list(copies)}")
+    return COPY_BYTES / next(iter(copies.values()))
+
+
+def prof_traffic(wl: str, fdir: str, wdir: str, cfdir: str, cwdir: str, prefix: str, cmd: str) -> None:
+    fs, ws = _copy_scale(cfdir, "FETCH_SIZE"), _copy_scale(cwdir, "WRITE_SIZE")
+    fm, fn = _counter_means(fdir, "FETCH_SIZE")
+    wm, _ = _counter_means(wdir, "WRITE_SIZE")
+    table = {}
+    lines = [f"# HBM traffic per launch, workload {wl}", f"# command: {cmd}",
+             f"# scale: FETCH_SIZE x {fs:.4f} B/unit, WRITE_SIZE x {ws:.4f} B/unit "
+             f"(copy of {COPY_BYTES} B)", "",
+             f"{'kernel':<50} {'n':>4} {'FETCH KiB':>11} {'WRITE KiB':>11} {'read MB':>9} {'write MB':>9}"]
+    for name, fv in sorted(fm.items()):
+        fam = _family_of(name)
+        if fam is None:
+            continue
+        wv = wm.get(name, 0.0)
+        rd, wr = fv * fs, wv * ws
+        src = os.path.join(KSRC, FAMILIES[fam][1])
+        table[fam] = {"kernel": _short(name), "dispatches": fn[name], "fetch_counter": fv, "write_counter": wv,
+                      "read_bytes": rd, "write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
+                      "source": os.path.relpath(src, ROOT), "source_sha256": _sha256(src)}
+        lines.append(f"{_short(name)[:50]:<50} {fn[name]:>4} {fv:>11.1f} {wv:>11.1f} {rd / 1e6:>9.2f} {wr / 1e6:>9.2f}")
+    doc = {"workload": wl, "command": cmd, "fetch_scale": fs, "write_scale": ws, "kernels": table}
+    json.dump(doc, open(prefix + ".json", "w"), indent=1)
+    open(prefix + ".txt", "w").write("\n".join(lines) + "\n")
+
+
+def tools_main(argv):
+    ap = argparse.ArgumentParser(prog="bench.py")
+    sub = ap.add_subparsers(dest="tool", required=True)
+    sub.add_parser("copy-probe")
+    ps = sub.add_parser("prof-summary")
+    pm = ps.add_subparsers(dest="mode", required=True)
+    s = pm.add_parser("stats")
+    s.add_argument("stats_dir")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    t = pm.add_parser("traffic")
+    for a in ("workload", "fetch_dir", "write_dir", "copy_fetch_dir", "copy_write_dir", "out_prefix"):
+        t.add_argument(a)
+    t.add_argument("--cmd", required=True)
+    a = ap.parse_args(argv)
+    if a.tool == "copy-probe":
+        copy_probe()
+    elif a.mode == "stats":
+        prof_stats(a.stats_dir, a.out, a.cmd)
+    else:
+        prof_traffic(a.workload, a.fetch_dir, a.write_dir, a.copy_fetch_dir, a.copy_write_dir, a.out_prefix,
+                     a.cmd)
+
+
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] in ("copy-probe", "prof-summary"):
+        tools_main(sys.argv[1:])
+    else:
+        main()

@@ -1186,7 +1186,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
 #pragma unroll
       for (int i = 0; i < NO; ++i) kp_own[i] = 0.f;
     } else {
-      kl = sparse_kl_wave(kp_ok, kp_own, kp_sc);   // kp_own now holds the teacher
+      kl = sparse_kl_wave<NO, WaveRed, true>(kp_ok, kp_own, kp_sc);   // kp_own now holds the teacher
     }
     if (te) {
 #pragma unroll

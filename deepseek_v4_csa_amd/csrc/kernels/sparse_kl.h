@@ -13,8 +13,6 @@
 
 namespace csa {
 
-constexpr float KL_EPS = 1e-10f;
-
 // What a kernel that finishes the sparse loss itself needs besides its own outputs:
 // the scores at the selected slots (slot j of row t holds the score of ids[t, j], row
 // stride ld), the teacher output (NULL: not written; row stride ldt) and kl_row [T].
@@ -26,25 +24,31 @@ struct KlArgs {
   float *kl_row;
 };
 
-// log(1 + x) for x > -1: |x| < 1/2 by the series 2 atanh(u), u = x / (2 + x) (|u| < 1/3,
-// terms through u^15: truncation below 3e-9 relative; the quotient by the hardware
-// reciprocal, 1 ulp); otherwise the hardware log of 1 + x, where 1 + x is exact enough
-// (relative error ~1e-7 of the result).
-__device__ __forceinline__ float log1p_kl(float x) {
-  if (fabsf(x) < 0.5f) {
-    const float u = x * __builtin_amdgcn_rcpf(2.f + x);
-    const float u2 = u * u;
-    float p = 1.f / 15.f;
-    p = fmaf(p, u2, 1.f / 13.f);
-    p = fmaf(p, u2, 1.f / 11.f);
-    p = fmaf(p, u2, 1.f / 9.f);
-    p = fmaf(p, u2, 1.f / 7.f);
-    p = fmaf(p, u2, 1.f / 5.f);
-    p = fmaf(p, u2, 1.f / 3.f);
-    p = fmaf(p, u2, 1.f);
-    return 2.f * u * p;
+// The predictor's exponential e^(s - mx) in fp64 (s and mx are fp32, so the difference is
+// exact) and one KL term t (log(t + eps) - log(p + eps)) = t log1p((t - p) / (p + eps))
+// in fp64, with the device library's exp and log1p.  For nearly equal t and p the KL is
+// second order in t - p, so p must carry far more than fp32's 24 bits for the KL of such a
+// row to keep 1e-5 relative accuracy; an error in the sum of the e_j shifts the KL by the
+// same amount in absolute terms.
+constexpr double KL_EPS = 1e-10;
+__device__ __forceinline__ double pred_exp(float s, float mx) { return exp((double)s - (double)mx); }
+// log(1 + x), x > -1.  For |x| < 1/2 from log(1 + x) = 2 atanh(u), u = x / (2 + x), |u| < 1/3:
+// 2 (u + u^3/3 + ... + u^27/27), truncation below 1e-14 relative (the log-ratios of a KL row
+// are small, so this is the common case); otherwise the device library's log1p.
+__device__ __forceinline__ double log1p_kl(double x) {
+  if (fabs(x) < 0.5) {
+    const double u = x / (2.0 + x), u2 = u * u;
+    double p = 1.0 / 27;
+#pragma unroll
+    for (int k = 25; k >= 1; k -= 2) p = fma(p, u2, 1.0 / k);
+    return 2.0 * u * p;
   }
-  return __log2f(1.f + x) * LN2;
+  return log1p(x);
+}
+template <bool SERIES = true>
+__device__ __forceinline__ double kl_term(double t, double p) {
+  const double x = (t - p) / (p + KL_EPS);
+  return t * (SERIES ? log1p_kl(x) : log1p(x));
 }
 
 // Reductions over the lanes that hold one row: a whole wave (WaveRed), or NW waves of one
@@ -84,18 +88,16 @@ template <int NW> struct GroupRed {
 // The lanes that hold a row hold its support slots, N per lane in any arrangement: ok[v] marks a slot
 // of the support (a valid id), c[v] its head-summed mass m_j, sc[v] its indexer score.
 // Returns the row's KL (the same value in every lane) and leaves the teacher value of each
-// slot in c[v] (0 off the support); sc[v] is overwritten (the predictor's exponentials
-// take its place: the arrays are reused so that long rows keep few registers).  Every lane
-// of the wave must take part.
+// slot in c[v] (0 off the support, the array reused so that long rows keep few registers).
+// Every lane of the wave must take part.
 //
-// The KL of two nearly equal distributions is a second-order quantity, so the normalisers
-// and the log-ratios are finished in fp64: an fp32 error in either normaliser would shift
-// the KL by about that relative error.  The predictor terms are fp32 (an independent
-// relative error d_j of e_j moves the KL only through sum_j (t_j - p_j) d_j).
-// log(t + eps) - log(p + eps) is taken as log1p(x), x = (t - p) / (p + eps), with t - p in
-// fp64 and the rest in fp32 (the quotient by the hardware reciprocal, 1 ulp), so the KL
-// moves by ~1e-7 * sum_j t_j |x_j|.
-template <int N, class Red = WaveRed>
+// The KL of two nearly equal distributions is a second-order quantity, so everything after
+// the inputs is fp64: the teacher normaliser, the predictor's exponentials and their sum,
+// and the log-ratios (pred_exp, kl_term).
+// LEAN = false keeps the N exponentials in registers between the two loops (2N VGPRs) and
+// takes the log-ratios from the series; a kernel short of registers passes LEAN = true and
+// recomputes the exponentials and calls the library's log1p.
+template <int N, class Red = WaveRed, bool LEAN = false>
 __device__ __forceinline__ double sparse_kl_wave(const bool (&ok)[N], float (&c)[N], float (&sc)[N],
                                                  const Red &red = Red()) {
   float mx = -__builtin_inff();
@@ -107,24 +109,24 @@ __device__ __forceinline__ double sparse_kl_wave(const bool (&ok)[N], float (&c)
   }
   mx = red.max(mx);
   ms = red.sum(ms);
-  double es = 0.0;
+  constexpr bool KEEP_E = !LEAN;
+  double es = 0.0, e[KEEP_E ? N : 1];
 #pragma unroll
   for (int v = 0; v < N; ++v) {
-    sc[v] = ok[v] ? fast_exp2((sc[v] - mx) * LOG2E) : 0.f;   // e_j from here on
-    es += (double)sc[v];
+    const double x = ok[v] ? pred_exp(sc[v], mx) : 0.0;
+    if constexpr (KEEP_E) e[v] = x;
+    es += x;
   }
   es = red.sum(es);
   const double inv_es = 1.0 / es;
-  const double inv_m = 1.0 / fmax(ms, (double)KL_EPS);
+  const double inv_m = 1.0 / fmax(ms, KL_EPS);
   double kl = 0.0;
 #pragma unroll
   for (int v = 0; v < N; ++v) {
     double t = 0.0;
     if (ok[v]) {
       t = (double)c[v] * inv_m;
-      const double pj = (double)sc[v] * inv_es;
-      const float x = (float)(t - pj) * __builtin_amdgcn_rcpf((float)pj + KL_EPS);
-      kl += t * (double)log1p_kl(x);
+      kl += kl_term<!LEAN>(t, (KEEP_E ? e[v] : pred_exp(sc[v], mx)) * inv_es);
     }
     c[v] = (float)t;   // the teacher value
   }

@@ -316,8 +316,8 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   if (nch > 0) flush(nch - 1);
   __syncthreads();   // m_j complete
 
-  // predictor over j < n, teacher normalisation, KL: exponentials and log1p in fp32, the
-  // sums, normalisers and t - p in fp64 (as in the sparse kernel above)
+  // predictor over j < n, teacher normalisation, KL: all in fp64 from the fp32 scores and
+  // masses (pred_exp, kl_term: the same arithmetic as the sparse loss)
   const float *sr = scores + (int64_t)t * ld;
   __shared__ double dred[2 * 16];
   // the row's scores in batches of 8 per thread through a buffer resource of exactly n
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
     load_batch(base, x);
 #pragma unroll
     for (int u = 0; u < UB; ++u)
-      if (base + u * NT < n) es += (double)fast_exp2((x[u] - mx) * LOG2E);
+      if (base + u * NT < n) es += pred_exp(x[u], mx);
   }
   es = wave_sum_f64(es);
   if (lane == 0) dred[16 + w] = es;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
   es = 0.0;
   for (int ww = 0; ww < HG; ++ww) es += dred[16 + ww];
   const double inv_es = 1.0 / es;
-  const double inv_m = 1.0 / fmax(msum, (double)KL_EPS);
+  const double inv_m = 1.0 / fmax(msum, KL_EPS);
   double kl = 0.0;
   for (int base = tid; base < n; base += UB * NT) {
     float x[UB];
@@ -372,9 +372,7 @@ __global__ __launch_bounds__(64 * HG) void teacher_kl_dense_kernel(
       const int j = base + u * NT;
       if (j < n) {
         const double tj = (double)mj[j] * inv_m;
-        const double pj = (double)fast_exp2((x[u] - mx) * LOG2E) * inv_es;
-        const float xr = (float)(tj - pj) * __builtin_amdgcn_rcpf((float)pj + KL_EPS);
-        kl += tj * (double)log1p_kl(xr);
+        kl += kl_term<true>(tj, pred_exp(x[u], mx) * inv_es);
         if (teacher) teacher[(int64_t)t * ldt + j] = (float)tj;
       }
     }

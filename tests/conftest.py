@@ -19,3 +19,19 @@ def gpu_ok():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return True
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Worst parity figures of the GPU checks that ran (errors against the oracle, and
+    each error over its tolerance where the tolerance is per element)."""
+    try:
+        from tests import gpu_check
+    except Exception:  # pragma: no cover
+        return
+    if not gpu_check.WORST:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "worst parity figures against the oracle")
+    for tag in sorted(gpu_check.WORST):
+        vals = gpu_check.WORST[tag]
+        tr.write_line(f"{tag}: " + ", ".join(f"{k}={v:.3g}" for k, v in sorted(vals.items())))

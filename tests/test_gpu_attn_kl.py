@@ -28,7 +28,7 @@ def _ops():
     return ops
 
 
-def _close(a, b, rel=1e-5, abs_=1e-8):
+def _close(a, b, rel=1e-5, abs_=1e-12):
     a = a.double()
     b = b.double()
     return bool(((a - b).abs() <= rel * b.abs() + abs_).all())
@@ -36,8 +36,8 @@ def _close(a, b, rel=1e-5, abs_=1e-8):
 
 def _run_both(inp, fused_scores=True):
     ops = _ops()
-    r2 = ops.forward(inp, want_teacher=True, fused=fused_scores)
-    rk = ops.forward(inp, want_teacher=True, fused=fused_scores, attn_kl=True)
+    r2 = ops.forward(inp, want_teacher=True, poison=True, fused=fused_scores)
+    rk = ops.forward(inp, want_teacher=True, poison=True, fused=fused_scores, attn_kl=True)
     torch.cuda.synchronize()
     return r2, rk
 
@@ -64,7 +64,7 @@ def _check(inp, r2, rk, rows, epilogue=True):
     # the oracle on identical ids (the full score rows give the oracle's score check)
     res = dict(rk)
     res["scores"] = _scores_for_oracle(inp)
-    C.check_rows(inp, res, rows)
+    C.check_rows(inp, res, rows, tag=f"attn-kl-{inp.wl.name}", loss_rows=(len(rows) == inp.wl.total_q))
 
 
 SMALL = {
@@ -140,7 +140,7 @@ def test_attn_kl_full_workload(gpu_ok):
     r2, rk = _run_both(inp)
     rows = I.sample_rows(wl, 24)
     _check(inp, r2, rk, rows)
-    again = _ops().forward(inp, want_teacher=True, fused=True, attn_kl=True)
+    again = _ops().forward(inp, want_teacher=True, poison=True, fused=True, attn_kl=True)
     torch.cuda.synchronize()
     for k in ("teacher", "kl_row", "loss"):
         assert torch.equal(again[k], rk[k]), k

@@ -50,7 +50,7 @@ def nan_workspaces(ops, L, inp):
 def _gpu(inp, grad_loss=1.0, per_token=False, res=None):
     ops = _ops()
     if res is None:
-        res = ops.forward(inp, want_teacher=True)
+        res = ops.forward(inp, want_teacher=True, poison=True)
     L = ops.layout_of_inputs(inp)
     g, ws = nan_workspaces(ops, L, inp)
     dq, dw, dk = ops.csa_indexer_loss_bwd(L, inp.wl.sparse_loss, inp.q_idx, inp.k_idx, inp.weights,

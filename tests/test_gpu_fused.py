@@ -131,15 +131,15 @@ def test_fused_full_workload_forward_and_backward(gpu_ok, index):
     wl = I.WORKLOADS[index]
     inp = I.make_inputs(wl, device="cuda")
     L = ops.layout_of_inputs(inp)
-    r2 = ops.forward(inp, want_teacher=True)
-    rf = ops.forward(inp, want_teacher=True, fused=True)
+    r2 = ops.forward(inp, want_teacher=True, poison=True)
+    rf = ops.forward(inp, want_teacher=True, poison=True, fused=True)
     torch.cuda.synchronize()
     rows = I.sample_rows(wl, 24)
     _check_against_two_calls(L, inp, r2["scores"], r2["ids"], rf["ids"], rf["sel"], rf["row_lse"], rows)
     for k in ("out", "lse", "cmass", "teacher", "kl_row", "loss"):
         assert torch.equal(rf[k], r2[k]), k
     # the oracle's top-k of the two-call scores on sampled rows (scores within the band)
-    C.check_rows(inp, r2, rows)
+    C.check_rows(inp, r2, rows, tag="fused-" + wl.name)
     g, ws = nan_workspaces(ops, L, inp)
     a = ops.csa_indexer_loss_bwd(L, True, inp.q_idx, inp.k_idx, inp.weights, inp.idx_scale, r2["scores"],
                                  r2["ids"], r2["teacher"], grad_scores=g, workspace=ws)

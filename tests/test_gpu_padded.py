@@ -35,7 +35,7 @@ def _ops():
 
 
 def _fwd(inp):
-    res = _ops().forward(inp, want_teacher=True)
+    res = _ops().forward(inp, want_teacher=True, poison=True)
     torch.cuda.synchronize()
     return res
 
@@ -77,7 +77,7 @@ def test_padded_small_every_row(gpu_ok, name):
     inp = I.make_inputs(wl, device="cuda")
     pad = I.pad_inputs(inp, n_pad, dummy=dummy)
     res, resp = _fwd(inp), _fwd(pad)
-    rep = C.check_rows(pad, resp, list(range(pad.wl.total_q)))
+    rep = C.check_rows(pad, resp, list(range(pad.wl.total_q)), tag=f"padded-{name}", loss_rows=True)
     print(name, dict(rep), flush=True)
     _check_against_unpadded(inp, pad, res, resp)
 
@@ -113,7 +113,7 @@ def test_padded_full_thd_workload(gpu_ok):
     pad = I.pad_inputs(inp, 1024, dummy=True)
     res, resp = _fwd(inp), _fwd(pad)
     rows = sorted(set(I.sample_rows(wl, 24)) | set(range(wl.total_q, wl.total_q + 1024, 97)))
-    rep = C.check_rows(pad, resp, rows)
+    rep = C.check_rows(pad, resp, rows, tag="thd-varlen-16k-padded")
     print("thd-varlen-16k padded", dict(rep), flush=True)
     _check_against_unpadded(inp, pad, res, resp)
     del res, resp

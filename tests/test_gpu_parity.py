@@ -25,7 +25,7 @@ def _ops():
 
 
 def _run(inp):
-    res = _ops().forward(inp, want_teacher=True)
+    res = _ops().forward(inp, want_teacher=True, poison=True)
     torch.cuda.synchronize()
     return res
 
@@ -45,7 +45,8 @@ def test_small_workloads_every_row(gpu_ok, name, family):
     wl = SMALL[name]
     inp = I.make_inputs(wl, device="cuda", family=family)
     res = _run(inp)
-    rep = C.check_rows(inp, res, list(range(wl.total_q)), exact_scores=(family == "exact"))
+    rep = C.check_rows(inp, res, list(range(wl.total_q)), exact_scores=(family == "exact"),
+                       tag=f"{name}-{family}", loss_rows=True)
     print(name, family, dict(rep), flush=True)
     # the loss is the documented reduction of kl_row (mean over every physical row)
     kl = res["kl_row"].double()
@@ -58,7 +59,10 @@ def test_full_workloads_sampled_rows(gpu_ok, index):
     inp = I.make_inputs(wl, device="cuda")
     res = _run(inp)
     rows = I.sample_rows(wl, 40 if index != 3 else 24)
-    rep = C.check_rows(inp, res, rows)
+    if index == 3:
+        # rows with fewer causal keys than k_eff (their compressed chunks end early)
+        rows = sorted(set(rows) | set(range(37, 8192, 331)))
+    rep = C.check_rows(inp, res, rows, tag=wl.name)
     mean, mn = C.recall_all_rows(inp, res)
     print(wl.name, dict(rep), "recall", mean, mn, flush=True)
     assert mean == 1.0 and mn == 1.0
@@ -206,10 +210,9 @@ def test_chunk_offsets_and_negative_control(gpu_ok):
 # ----------------------------------------------------------------------------- edge cases
 def test_edge_layouts(gpu_ok):
     """Empty and short segments, lengths not divisible by the ratio (negative default
-    offsets), window 0, top-k above every segment's key count, a sink of -inf."""
+    offsets), window 0, top-k above every segment's key count, a sink of -inf; every row
+    against the oracle (tolerances of tests/gpu_check.py, the loss included)."""
     ops = _ops()
-    import oracle
-    from tests.oracle_bridge import host
     rng = torch.Generator(device="cuda")
     rng.manual_seed(5)
     seg_q = [70, 0, 3, 129, 1]
@@ -218,7 +221,7 @@ def test_edge_layouts(gpu_ok):
     H, D, Hi, Di = 16, 128, 4, 64
     T, Tk = sum(seg_q), sum(seg_k)
     for window, topk, sink_val in ((0, 8, None), (5, 64, -float("inf")), (3, 2, None)):
-        L = ops.Layout.from_lengths(seg_q, seg_k, ratio)     # default (bottom-right) offsets
+        L = ops.Layout.from_lengths(seg_q, seg_k, ratio)     # NULL offsets: the bottom-right default
         rnd = lambda *s: (torch.randn(*s, generator=rng, device="cuda") / 8).to(torch.bfloat16)
         q, kv, ckv = rnd(T, H, D), rnd(T, D), rnd(Tk, D)
         qi, ki = rnd(T, Hi, Di), rnd(Tk, Di)
@@ -226,28 +229,20 @@ def test_edge_layouts(gpu_ok):
         sink = torch.randn(H, generator=rng, device="cuda")
         if sink_val is not None:
             sink[:] = sink_val
-        sc = ops.csa_indexer_score(L, qi, ki, w, 0.125)
-        ids = ops.csa_topk(L, sc, topk)
-        out, lse, lse_nc, cm = ops.csa_sparse_attn_fwd(L, q, kv, ckv, sink, ids, window, D ** -0.5)
-        te, klr, loss = ops.csa_indexer_teacher_kl(L, True, sc, ids, cm, q, ckv, lse_nc, D ** -0.5,
-                                                   want_teacher=True)
+        with ops.poisoned_outputs():
+            sc = ops.csa_indexer_score(L, qi, ki, w, 0.125)
+            ids = ops.csa_topk(L, sc, topk)
+            out, lse, lse_nc, cm = ops.csa_sparse_attn_fwd(L, q, kv, ckv, sink, ids, window, D ** -0.5)
+            te, klr, loss = ops.csa_indexer_teacher_kl(L, True, sc, ids, cm, q, ckv, lse_nc, D ** -0.5,
+                                                       want_teacher=True)
         torch.cuda.synchronize()
-        Lo = oracle.Layout(cu_q=L.cu_q.cpu().numpy(), cu_k=L.cu_k.cpu().numpy(), ratio=ratio, off=None)
-        P = oracle.Problem(layout=Lo, q=host(q), kv=host(kv), ckv=host(ckv), q_idx=host(qi), k_idx=host(ki),
-                           weights=host(w), sink=host(sink), topk=topk, window=window, scale=D ** -0.5,
-                           idx_scale=0.125)
-        k_eff = oracle.k_eff_of(Lo, topk)
-        assert ids.shape[1] == k_eff
-        g_sc, g_ids, g_out = host(sc), ids.cpu().numpy(), host(out)
-        g_lse, g_lnc, g_kl = host(lse), host(lse_nc), host(klr)
-        for t in range(T):
-            gg = oracle.row_geometry(Lo, t)
-            assert np.array_equal(g_ids[t], oracle.topk_row(g_sc[t], gg.n_valid, k_eff, gg.k_base))
-            r = oracle.run_row(P, t, ids_override=g_ids[t])
-            fin = np.isfinite(r.attn.lse)
-            assert np.array_equal(np.isfinite(g_lse[t]), fin)
-            assert np.all(np.abs(g_lse[t][fin] - r.attn.lse[fin]) <= 1e-5 * np.abs(r.attn.lse[fin]) + 1e-6)
-            assert np.all(np.abs(g_lnc[t][np.isfinite(r.attn.lse_nc)] - r.attn.lse_nc[np.isfinite(r.attn.lse_nc)]) <= 1e-5)
-            assert np.max(np.abs(g_out[t] - r.attn.out)) <= C.TOL_OUT
-            assert abs(g_kl[t] - r.kl) <= 1e-5 * abs(r.kl) + 1e-8, (t, g_kl[t], r.kl)
-        assert np.isfinite(float(loss[0]))
+        wl = I.scaled_down(I.WORKLOADS[1], seg_q, H=H, D=D, Hi=Hi, Di=Di, topk=topk, window=window,
+                           name=f"edge-w{window}-k{topk}")
+        # the oracle takes the offsets explicitly: seg_k * ratio - seg_q
+        off = torch.tensor([k * ratio - n for n, k in zip(seg_q, seg_k)], dtype=torch.int32, device="cuda")
+        inp = I.Inputs(wl, L.cu_q, L.cu_k, off, q, kv, ckv, qi, ki, w, sink, 0.125, D ** -0.5)
+        assert ids.shape[1] == min(topk, max(seg_k))
+        res = dict(scores=sc, ids=ids, out=out, lse=lse, lse_nc=lse_nc, cmass=cm, teacher=te, kl_row=klr,
+                   loss=loss)
+        rep = C.check_rows(inp, res, list(range(T)), tag="edge-layouts", loss_rows=True)
+        print(wl.name, dict(rep), flush=True)

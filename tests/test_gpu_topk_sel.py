@@ -58,9 +58,9 @@ def test_teacher_kl_from_topk_selected_scores(gpu_ok, name):
     ops = _ops()
     wl, seed = CASES[name]
     inp = I.make_inputs(wl, device="cuda", seed=seed)
-    a = ops.forward(inp, want_teacher=True)
+    a = ops.forward(inp, want_teacher=True, poison=True)
     a = {k: (v.clone() if v is not None else None) for k, v in a.items()}
-    b = ops.forward(inp, want_teacher=True, topk_sel=True)
+    b = ops.forward(inp, want_teacher=True, poison=True, topk_sel=True)
     torch.cuda.synchronize()
     for key in ("ids", "out", "lse", "lse_nc", "cmass", "teacher", "kl_row", "loss"):
         assert torch.equal(a[key], b[key]), key
