@@ -74,6 +74,39 @@ bool scale_ok(float s) { return s > 0.f && s <= 3.4e38f; }
 
 int k_eff_of(const csa_layout_t *L, int topk) { return topk < L->max_seqlen_k ? topk : L->max_seqlen_k; }
 
+// Checks shared by the two backward entry points (everything but the workspaces).
+csa_status_t check_bwd(const csa_layout_t *L, const char *fn, csa::LaunchLayout *LL, int32_t sparse_loss,
+                       const void *q_idx, const void *k_idx, const float *weights, csa_dtype_t dt, int32_t Hi,
+                       int32_t Di, const float *scores, int64_t ld_scores, int32_t scores_selected,
+                       const int32_t *ids, int32_t k_eff, const float *teacher, int64_t ld_teacher,
+                       const float *dq_idx, const float *dweights, const float *dk_idx) {
+  csa_status_t st = check_layout(L, fn, LL);
+  if (st != CSA_OK) return st;
+  if (!q_idx || !k_idx || !weights || !scores || !teacher || !dq_idx || !dweights || !dk_idx)
+    return fail(CSA_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
+  if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
+  if (Hi < 1 || Di < 1) return fail(CSA_ERR_INVALID, "%s: Hi=%d, Di=%d must be >= 1", fn, Hi, Di);
+  if (scores_selected && !sparse_loss)
+    return fail(CSA_ERR_INVALID, "%s: selected scores need the sparse loss", fn);
+  if (ld_scores < (scores_selected ? k_eff : L->max_seqlen_k))
+    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld too small (max_seqlen_k=%d, k_eff=%d)", fn,
+                (long long)ld_scores, L->max_seqlen_k, k_eff);
+  if (sparse_loss) {
+    if (k_eff < 1 || k_eff > L->max_seqlen_k)
+      return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [1, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
+    if (!ids) return fail(CSA_ERR_INVALID, "%s: sparse loss needs ids", fn);
+    if (ld_teacher < k_eff)
+      return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < k_eff=%d", fn, (long long)ld_teacher, k_eff);
+  } else if (ld_teacher < L->max_seqlen_k) {
+    return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < max_seqlen_k=%d", fn, (long long)ld_teacher,
+                L->max_seqlen_k);
+  }
+  if (!csa::indexer_bwd_supported(dt == CSA_BF16, Hi, Di, k_eff, sparse_loss != 0, L->max_seqlen_k))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d Hi=%d Di=%d k_eff=%d", fn, (int)dt, Hi, Di,
+                k_eff);
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,30 +328,12 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, co
                                   void *stream) {
   const char *fn = "csa_indexer_loss_bwd";
   csa::LaunchLayout LL;
-  csa_status_t st = check_layout(L, fn, &LL);
+  csa_status_t st = check_bwd(L, fn, &LL, sparse_loss, q_idx, k_idx, weights, dt, Hi, Di, scores, ld_scores,
+                              scores_selected, ids, k_eff, teacher, ld_teacher, dq_idx, dweights, dk_idx);
   if (st != CSA_OK) return st;
-  if (!q_idx || !k_idx || !weights || !scores || !teacher || !grad_scores || !dq_idx || !dweights || !dk_idx)
-    return fail(CSA_ERR_INVALID, "%s: a tensor pointer is NULL", fn);
-  if (!dtype_ok(dt)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, (int)dt);
-  if (Hi < 1 || Di < 1) return fail(CSA_ERR_INVALID, "%s: Hi=%d, Di=%d must be >= 1", fn, Hi, Di);
-  if (scores_selected && !sparse_loss)
-    return fail(CSA_ERR_INVALID, "%s: selected scores need the sparse loss", fn);
-  if (ld_scores < (scores_selected ? k_eff : L->max_seqlen_k) || ld_grad < L->max_seqlen_k)
-    return fail(CSA_ERR_INVALID, "%s: ld_scores=%lld / ld_grad=%lld too small (max_seqlen_k=%d, k_eff=%d)",
-                fn, (long long)ld_scores, (long long)ld_grad, L->max_seqlen_k, k_eff);
-  if (sparse_loss) {
-    if (k_eff < 1 || k_eff > L->max_seqlen_k)
-      return fail(CSA_ERR_INVALID, "%s: k_eff=%d outside [1, max_seqlen_k=%d]", fn, k_eff, L->max_seqlen_k);
-    if (!ids) return fail(CSA_ERR_INVALID, "%s: sparse loss needs ids", fn);
-    if (ld_teacher < k_eff)
-      return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < k_eff=%d", fn, (long long)ld_teacher, k_eff);
-  } else if (ld_teacher < L->max_seqlen_k) {
-    return fail(CSA_ERR_INVALID, "%s: ld_teacher=%lld < max_seqlen_k=%d", fn, (long long)ld_teacher,
-                L->max_seqlen_k);
-  }
-  if (!csa::indexer_bwd_supported(dt == CSA_BF16, Hi, Di, k_eff, sparse_loss != 0, L->max_seqlen_k))
-    return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d Hi=%d Di=%d k_eff=%d", fn, (int)dt, Hi,
-                Di, k_eff);
+  if (!grad_scores) return fail(CSA_ERR_INVALID, "%s: grad_scores is NULL", fn);
+  if (ld_grad < L->max_seqlen_k)
+    return fail(CSA_ERR_INVALID, "%s: ld_grad=%lld < max_seqlen_k=%d", fn, (long long)ld_grad, L->max_seqlen_k);
   const int64_t need = csa::indexer_bwd_workspace_bytes(L->num_seqs, L->total_k, L->max_seqlen_q,
                                                         L->max_seqlen_k, Di);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -330,6 +345,39 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss, co
                                                   k_eff, teacher,
                                                   ld_teacher, gscale, grad_scores, ld_grad, dq_idx,
                                                   dweights, dk_idx, workspace,
+                                                  static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+csa_status_t csa_indexer_loss_bwd_noalloc(const csa_layout_t *L, int32_t sparse_loss, const void *q_idx,
+                                          const void *k_idx, const float *weights, csa_dtype_t dt, int32_t Hi,
+                                          int32_t Di, float idx_scale, const float *scores, int64_t ld_scores,
+                                          int32_t scores_selected, const int32_t *ids, int32_t k_eff,
+                                          const float *teacher, int64_t ld_teacher, float grad_loss,
+                                          int32_t per_token_loss, float *dq_idx, float *dweights, float *dk_idx,
+                                          void *stream) {
+  const char *fn = "csa_indexer_loss_bwd_noalloc";
+  csa::LaunchLayout LL;
+  csa_status_t st = check_bwd(L, fn, &LL, sparse_loss, q_idx, k_idx, weights, dt, Hi, Di, scores, ld_scores,
+                              scores_selected, ids, k_eff, teacher, ld_teacher, dq_idx, dweights, dk_idx);
+  if (st != CSA_OK) return st;
+  const csa::NoallocPlan plan = csa::noalloc_plan(L->num_seqs, L->total_q, L->total_k, L->max_seqlen_q,
+                                                  L->max_seqlen_k, Di);
+  if (plan.bytes > csa::NOALLOC_SCRATCH_BYTES)
+    return fail(CSA_ERR_INVALID,
+                "%s: this layout needs %lld bytes of scratch (score gradients and dk partials), above the "
+                "library's %lld; use csa_indexer_loss_bwd with caller workspaces",
+                fn, (long long)plan.bytes, (long long)csa::NOALLOC_SCRATCH_BYTES);
+  void *base = nullptr;
+  st = hip_status(csa::noalloc_scratch_ptr(&base), fn);
+  if (st != CSA_OK) return st;
+  char *b = static_cast<char *>(base);
+  const float gscale = per_token_loss ? grad_loss : (L->total_q > 0 ? grad_loss / (float)L->total_q : 0.f);
+  return hip_status(csa::launch_indexer_loss_bwd(LL, sparse_loss != 0, q_idx, k_idx, weights, Hi, Di,
+                                                  idx_scale, scores, ld_scores, scores_selected != 0, ids,
+                                                  k_eff, teacher, ld_teacher, gscale,
+                                                  reinterpret_cast<float *>(b), plan.ld_grad, dq_idx,
+                                                  dweights, dk_idx, b + plan.ws_offset,
                                                   static_cast<hipStream_t>(stream)),
                     fn);
 }

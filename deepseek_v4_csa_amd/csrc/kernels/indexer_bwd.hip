@@ -30,6 +30,7 @@
 // come from LDS through the transposing 64-bit read.  No atomics: every output element
 // is written once, in a fixed summation order.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "../launch.h"
@@ -653,6 +654,48 @@ bool indexer_bwd_supported(bool bf16, int Hi, int Di, int k_eff, bool sparse, in
   if (Di == 64) return Hi == 4 || Hi == 8 || Hi == 16 || Hi == 32;
   if (Di == 128) return Hi == 4 || Hi == 8 || Hi == 16;
   return false;
+}
+
+// ---------------------------------------------------------------- the no-allocation route
+// Device scratch of the backward for callers that cannot allocate: the score-gradient
+// matrix G and the dk chunk partials live in this file-scope array instead of caller
+// workspaces.  Each GPU the library runs on holds its own copy for the life of the
+// process.  Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol); it passes the device address that hipGetSymbolAddress returns
+// for the current device, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t noalloc_scratch_ptr(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// The scratch layout of a call: G [total_q, ld] fp32 with ld = max_seqlen_k rounded up to
+// 64 floats, then the dk partials at the next 256-byte boundary.
+NoallocPlan noalloc_plan(int num_seqs, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Di) {
+  NoallocPlan p;
+  p.ld_grad = ((int64_t)max_seqlen_k + 63) / 64 * 64;
+  p.ws_offset = ((int64_t)total_q * p.ld_grad * 4 + 255) / 256 * 256;
+  p.bytes = p.ws_offset + indexer_bwd_workspace_bytes(num_seqs, total_k, max_seqlen_q, max_seqlen_k, Di);
+  return p;
 }
 
 }  // namespace csa

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "../../include/csa.h"
 #include "kernels/common.h"
 #include "kernels/sparse_kl.h"
 
@@ -47,6 +48,17 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &L, bool sparse, const voi
                                   float *dq, float *dw, float *dk, void *workspace, hipStream_t st);
 // device workspace of the indexer-loss backward (dk partials per token-block chunk; 0: none)
 int64_t indexer_bwd_workspace_bytes(int num_seqs, int total_k, int max_seqlen_q, int max_seqlen_k, int Di);
+
+// the no-allocation backward: G and the dk partials in the library's static device scratch
+constexpr int64_t NOALLOC_SCRATCH_BYTES = CSA_NOALLOC_SCRATCH_BYTES;
+struct NoallocPlan {
+  int64_t ld_grad;    // row stride of G (floats)
+  int64_t ws_offset;  // byte offset of the dk partials
+  int64_t bytes;      // scratch bytes the call needs
+};
+NoallocPlan noalloc_plan(int num_seqs, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Di);
+// device address of this device's scratch (looked up on the first call per device)
+hipError_t noalloc_scratch_ptr(void **ptr);
 
 hipError_t launch_indexer_topk(const LaunchLayout &L, const void *q_idx, const void *k_idx,
                                const float *weights, int Hi, int Di, float idx_scale, int k_eff,

@@ -37,7 +37,8 @@ class _CLayout(ctypes.Structure):
 
 EXPORTS = ("csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
            "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd", "csa_indexer_loss_bwd_workspace",
-           "csa_cp_plan", "csa_indexer_topk", "csa_sparse_attn_kl_fwd", "csa_loss_reduce")
+           "csa_cp_plan", "csa_indexer_topk", "csa_sparse_attn_kl_fwd", "csa_loss_reduce",
+           "csa_indexer_loss_bwd_noalloc")
 
 
 def lib_path() -> str:
@@ -71,6 +72,9 @@ def load():
     lib.csa_indexer_loss_bwd.restype = ctypes.c_int
     lib.csa_indexer_loss_bwd.argtypes = [LP, I32, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, I32, P,
                                          I32, P, I64, F32, I32, P, I64, P, P, P, P, I64, P]
+    lib.csa_indexer_loss_bwd_noalloc.restype = ctypes.c_int
+    lib.csa_indexer_loss_bwd_noalloc.argtypes = [LP, I32, P, P, P, ctypes.c_int, I32, I32, F32, P, I64, I32, P,
+                                                 I32, P, I64, F32, I32, P, P, P, P]
     lib.csa_indexer_loss_bwd_workspace.restype = I64
     lib.csa_indexer_loss_bwd_workspace.argtypes = [LP, I32, I32]
     lib.csa_indexer_topk.restype = ctypes.c_int
@@ -326,6 +330,22 @@ def csa_indexer_loss_bwd(layout: Layout, sparse_loss: bool, q_idx, k_idx, weight
         _ptr(ids) if ids is not None else None, k_eff_, _ptr(teacher), teacher.stride(0),
         float(grad_loss), 1 if per_token else 0, _ptr(grad_scores), grad_scores.stride(0),
         _ptr(dq_idx), _ptr(dweights), _ptr(dk_idx), _ptr(workspace), workspace.numel(), _stream()))
+    return dq_idx, dweights, dk_idx
+
+
+def csa_indexer_loss_bwd_noalloc(layout: Layout, sparse_loss: bool, q_idx, k_idx, weights, idx_scale: float,
+                                 scores, ids, teacher, dq_idx, dweights, dk_idx, grad_loss: float = 1.0,
+                                 per_token: bool = False, scores_selected: bool = False):
+    """csa_indexer_loss_bwd with the library's static device scratch in place of the
+    grad_scores and workspace buffers: the C call allocates nothing, so the outputs
+    (fp32 dq_idx [T, Hi, Di], dweights [T, Hi], dk_idx [T_k, Di]) are the caller's."""
+    T, Hi, Di = q_idx.shape
+    k_eff_ = ids.shape[1] if ids is not None else 0
+    _check(load().csa_indexer_loss_bwd_noalloc(
+        ctypes.byref(layout.c()), 1 if sparse_loss else 0, _ptr(q_idx), _ptr(k_idx), _ptr(weights),
+        _dtype(q_idx), Hi, Di, float(idx_scale), _ptr(scores), scores.stride(0), 1 if scores_selected else 0,
+        _ptr(ids) if ids is not None else None, k_eff_, _ptr(teacher), teacher.stride(0),
+        float(grad_loss), 1 if per_token else 0, _ptr(dq_idx), _ptr(dweights), _ptr(dk_idx), _stream()))
     return dq_idx, dweights, dk_idx
 
 

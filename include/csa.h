@@ -304,6 +304,33 @@ csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss,
                                   int64_t ld_grad, float *dq_idx, float *dweights, float *dk_idx,
                                   void *workspace, int64_t workspace_bytes, void *stream);
 
+/*
+ * csa_indexer_loss_bwd_noalloc -- csa_indexer_loss_bwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same gradients from the same arguments, with no grad_scores and no
+ * workspace argument.  The score-gradient matrix and the dk chunk partials live in a
+ * static device array of the library, CSA_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held
+ * by each GPU the library runs on until the process ends; its device address is looked up
+ * on the first call on each device (with that device current).  The call allocates and
+ * frees nothing.  Outputs dq_idx, dweights, dk_idx are caller-owned as in
+ * csa_indexer_loss_bwd and equal its outputs bit for bit.
+ * Scratch needed: total_q * ld * 4 bytes (ld = max_seqlen_k rounded up to 64) rounded up to
+ * 256, plus csa_indexer_loss_bwd_workspace(L, Hi, Di); a layout needing more than
+ * CSA_NOALLOC_SCRATCH_BYTES is CSA_ERR_INVALID before anything is enqueued (use
+ * csa_indexer_loss_bwd with caller workspaces then).
+ * Every call on one GPU uses that GPU's one array and leaves its contents behind: calls
+ * that overlap on one GPU (two streams, two threads) race and must be serialised by the
+ * caller.  Nothing in the array has to start at a particular value.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (128ll << 20)
+csa_status_t csa_indexer_loss_bwd_noalloc(const csa_layout_t *L, int32_t sparse_loss,
+                                          const void *q_idx, const void *k_idx, const float *weights,
+                                          csa_dtype_t dt, int32_t Hi, int32_t Di, float idx_scale,
+                                          const float *scores, int64_t ld_scores, int32_t scores_selected,
+                                          const int32_t *ids, int32_t k_eff, const float *teacher,
+                                          int64_t ld_teacher, float grad_loss, int32_t per_token_loss,
+                                          float *dq_idx, float *dweights, float *dk_idx, void *stream);
+
 /* Bytes of device workspace csa_indexer_loss_bwd needs for this layout and indexer
  * shape (0: none); -1 for an invalid layout or an unsupported shape (message in
  * csa_last_error).  Host-only: reads nothing on the device. */

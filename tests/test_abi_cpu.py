@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"csa_last_error", "csa_k_eff", "csa_indexer_score", "csa_topk",
                           "csa_sparse_attn_fwd", "csa_indexer_teacher_kl", "csa_indexer_loss_bwd",
                           "csa_indexer_loss_bwd_workspace", "csa_cp_plan", "csa_indexer_topk",
-                          "csa_sparse_attn_kl_fwd", "csa_loss_reduce"}
+                          "csa_sparse_attn_kl_fwd", "csa_loss_reduce", "csa_indexer_loss_bwd_noalloc"}
     from deepseek_v4_csa_amd import ops
     assert set(ops.EXPORTS) == set(names)
     for n in names:
