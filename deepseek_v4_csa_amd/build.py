@@ -25,6 +25,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "indexer_score.hip"),
     os.path.join(CSRC, "kernels", "topk.hip"),
     os.path.join(CSRC, "kernels", "sparse_attn.hip"),
+    os.path.join(CSRC, "kernels", "sparse_attn_wide.hip"),
     os.path.join(CSRC, "kernels", "teacher_kl.hip"),
     os.path.join(CSRC, "kernels", "indexer_bwd.hip"),
 ]

@@ -277,17 +277,23 @@ __device__ __forceinline__ float bperm(int addr, float v) {
 
 namespace csa {
 // Row tiles of D bf16 (D*2 bytes per row) staged in LDS: 16-byte piece p of tile row R is
-// stored at piece position p ^ row_swz<D>(R).  With 64 LDS banks of 4 bytes (256 bytes
-// per bank row), this keeps conflict-free the row-operand reads (16 lanes = rows 0..15,
-// one piece each), the transposing reads (32 lanes = 8 rows x 2 pieces x 2 halves) and
-// the row-staging writes.  Rows of 256*k bytes (D = 128, 256, 512) take all 16 values;
-// rows of 128 or 384 bytes (D = 64, 192), where consecutive rows already start half a
-// bank row apart, take the 8 values < 8, which also keeps p ^ swz inside a row of 24
-// pieces.  The pattern repeats every 16 rows.
+// stored at piece position p ^ row_swz<D>(R).  The LDS of gfx950 (measured with the bank
+// conflict counter on access patterns of their own): 16-byte reads are served a quarter
+// wave per cycle, the quarter being half-wave h = lane >> 5 and parity
+// bit2 ^ bit3 ^ bit4 of the lane index (lanes 0-3, 12-15, 20-23, 24-27 together); two of
+// its lanes conflict when they hit the same 16-byte slot (address bits 7:4) at different
+// addresses.  8-byte transposing reads are served a half wave (32 consecutive lanes) per
+// cycle over the 32 8-byte words of a 256-byte line.  The swizzle is linear in the bits of
+// R and keeps conflict-free, for every MFMA K-chunk and d-tile: the row-operand reads
+// (lane (g, r) reads piece 4c + g of row r), the transposing reads (lane (g, r) reads
+// pieces 2dt, 2dt + 1 of row 4g + r / 4) and the row-staging writes (whole rows).  Rows
+// of 256*k bytes (D = 128, 256, 512) take 16 values; rows of 128 or 384 bytes (D = 64,
+// 192), which start half a line apart, take 8 values (p ^ swz then stays inside the row's
+// 8-piece group).  The pattern repeats every 16 rows.
 template <int D> __host__ __device__ constexpr int row_swz(int r) {
   static_assert(D == 64 || D == 128 || D == 192 || D == 256 || D == 512, "row size");
-  if constexpr (D == 64 || D == 192) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-  else return 2 * (r & 7) + ((r >> 3) & 1);
+  if constexpr (D == 64 || D == 192) return (2 * ((r >> 1) & 3)) ^ (5 * ((r >> 3) & 1));
+  else return (2 * (r & 7)) ^ (9 * ((r >> 3) & 1));
 }
 // A load instruction of 64 lanes x 16 bytes covers RPI = 64 / (D / 8) whole rows when D
 // divides 512; then the swizzle of row i RPI + g (g < RPI) splits into a per-lane and a

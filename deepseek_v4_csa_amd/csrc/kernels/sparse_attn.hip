@@ -1595,7 +1595,7 @@ hipError_t launch_sparse_attn(const LaunchLayout &LL, const void *q, const void 
       case 128: return launch_wg<128>(CSA_ARGS);
       case 192: return launch_wg<192>(CSA_ARGS);
       case 256: return launch_wg<256>(CSA_ARGS);
-      case 512: return launch_wg<512>(CSA_ARGS);
+      case 512: return launch_sparse_attn_wide(CSA_ARGS);
     }
   }
   if (bf16) {

@@ -25,6 +25,12 @@ hipError_t launch_sparse_attn(const LaunchLayout &L, const void *q, const void *
                               int window, bool bf16, int H, int D, float scale, void *out,
                               float *lse, float *lse_nc, float *cmass, hipStream_t st);
 
+// the D = 512 workgroup attention (P.V split over the output columns; bf16, H <= 128)
+hipError_t launch_sparse_attn_wide(const LaunchLayout &L, const void *q, const void *kv, const void *ckv,
+                                   const float *sink, const int32_t *ids, int k_eff, int window, int H,
+                                   float scale, void *out, float *lse, float *lse_nc, float *cmass,
+                                   hipStream_t st);
+
 // attention whose epilogue also finishes the sparse teacher and KL (kl_row, teacher)
 // from the selected scores; only for shapes where attn_kl_fused_supported holds
 hipError_t launch_sparse_attn_kl(const LaunchLayout &L, const void *q, const void *kv,

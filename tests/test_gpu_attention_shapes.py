@@ -4,8 +4,10 @@ The workloads exercise one head shape each; this file covers the shapes in betwe
 that every kernel the launcher can pick is checked against the oracle's attention_row:
   persistent gather kernel   bf16, H <= 16, D in {64, 128}, 1 <= k_eff <= 256, window > 0
   gather kernel              bf16, H <= 16, D in {64, 128}, 1 <= k_eff <= 256, window = 0
-  workgroup kernel           other bf16 shapes: H up to 128 (not a multiple of 16 too),
-                             D in {64, 128, 192, 256, 512}, k_eff up to 4096
+  workgroup kernel           other bf16 shapes with D in {64, 128, 192, 256}: H up to
+                             128 (not a multiple of 16 too), k_eff up to 4096
+  wide workgroup kernel      bf16, D = 512, any H up to 128 (P.V split over the output
+                             columns, P shared through LDS)
   register-staged kernel     fp32 inputs
 The ids are drawn directly (ascending distinct visible keys of the row's segment with
 random -1 holes, -1 padding past the visible count), so the selection is not involved;
@@ -36,7 +38,11 @@ CASES = [
     ("wg-h20-d64", torch.bfloat16, 20, 64, 300, 40, (150, 1300)),
     ("wg-h40-d192", torch.bfloat16, 40, 192, 77, 33, (97, 500)),
     ("wg-h64-d256-nowin", torch.bfloat16, 64, 256, 520, 0, (64, 2200)),
-    ("wg-h128-d512", torch.bfloat16, 128, 512, 130, 64, (200, 700)),
+    ("wide-h128-d512", torch.bfloat16, 128, 512, 130, 64, (200, 700)),
+    ("wide-h128-d512-k600", torch.bfloat16, 128, 512, 600, 64, (300, 2600)),
+    ("wide-h112-d512", torch.bfloat16, 112, 512, 300, 130, (150, 1300)),
+    ("wide-h40-d512-nowin", torch.bfloat16, 40, 512, 77, 0, (97, 500)),
+    ("wide-h8-d512-k1", torch.bfloat16, 8, 512, 1, 1, (40, 90)),
     ("wg-h33-d128-k1", torch.bfloat16, 33, 128, 1, 1, (40, 90)),
     ("f32-h4-d64", torch.float32, 4, 64, 16, 32, (100, 256)),
     ("f32-h20-d128", torch.float32, 20, 128, 300, 40, (150, 1300)),
