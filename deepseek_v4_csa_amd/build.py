@@ -34,13 +34,17 @@ SOURCES = [
 # does not know the feature, which is harmless
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# MFMA results in VGPRs (the kernels keep at most 256 registers per lane), except in the
+# wide attention kernel, whose single wave per SIMD keeps its output accumulators in AGPRs
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+AGPR_SOURCES = {"sparse_attn_wide.hip"}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    extra = [] if os.path.basename(src) in AGPR_SOURCES else VGPR_FORM
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -249,6 +249,14 @@ template <int N> __device__ __forceinline__ void lds_tr16_wait(uint2 (&v)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
 }
+// The same with LATER LDS operations allowed to stay outstanding: for reads issued after the
+// transposing reads (LDS operations complete in order, so lgkmcnt(LATER) covers these).
+template <int LATER, int N> __device__ __forceinline__ void lds_tr16_wait_but(uint2 (&v)[N]) {
+  static_assert(LATER >= 0 && LATER <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(LATER) : "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
 }  // namespace csa
 
 namespace csa {
@@ -320,6 +328,13 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds_base, u
 }
 // s_waitcnt with only vmcnt constrained (expcnt 7 and lgkmcnt 15 = no wait); the 6-bit
 // count is split over bits 3:0 and 15:14 of the immediate
+// Workgroup barrier of the LDS-staged pipelines: the wave's own LDS reads and writes are
+// waited for (lgkmcnt 0), then s_barrier.  __syncthreads() would also wait for every direct
+// buffer->LDS load still in flight (its workgroup-scope release fence counts them as LDS
+// writes), which drains the tiles requested ahead at every step; the kernels instead wait
+// for each tile's own loads with wait_vmcnt before this barrier.  The memory clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));

@@ -9,27 +9,26 @@
 //   out = (sum_window e^w kv[t'] + sum_ids e^c ckv[id]) / Z_h,  lse = log Z_h,
 //   lse_nc = log(exp(sink_h) + sum_window e^w),  cmass[t, j] = sum_h exp(c_hj - lse_h).
 //
-// One workgroup (8 waves) per query row; the row's KV rows are staged 32 at a time (one
+// One workgroup of four waves (one per SIMD, each with the whole 512-entry register file:
+// 256 VGPRs and 256 AGPRs) per query row.  The row's KV rows are staged 32 at a time (one
 // "chunk", 32 KiB) in a ring of three or four LDS tiles by direct buffer->LDS loads, the
-// chunk one or two steps ahead requested right after each step's barrier.  With one KV row shared by every head
-// the cost that matters is LDS reads per MFMA, so the two passes are organised to read
-// each operand from LDS as few times as the registers allow:
+// chunk one or two steps ahead requested right after each step's barrier.  With one KV
+// row shared by every head, the cost that matters is LDS reads per MFMA; a wave holding
+// the Q rows of 32 heads in registers reads each K operand once for four MFMAs:
 //
-//  pass 1 (lse and lse_nc, no output accumulators needed): waves 2p and 2p+1 share 32
-//    heads (their own 16 and their partner's 16) and split every chunk's keys between
-//    them (rows 0..15 / 16..31): each K operand read feeds two MFMAs and each wave reads
-//    half a chunk.  Each keeps a running max (raised lazily, by 2^8 or more) and sum per
-//    head; the two halves are combined through LDS at the end.
-//  pass 2 (P, out and cmass, with lse final): wave w forms P = exp(s - lse) of its own 16
-//    heads over the whole chunk (S^T = K Q^T on MFMA), writes it as bf16 to an LDS
-//    buffer holding the chunk's P for all 128 heads, and adds its head sums into cmass.
-//    One step later (behind the next barrier) wave w accumulates the output columns
-//    [64 w, 64 w + 64) of every head: O^T[d, h] += V^T[d, j] P^T[j, h], V^T read with the
-//    transposing LDS read (4 KiB per chunk) and P^T with 16-byte reads (8 KiB per chunk),
-//    instead of every wave reading all 32 KiB of the chunk's V for its own heads.
+//  pass 1 (lse and lse_nc): wave w takes heads [32 w, 32 w + 32) over all 32 keys of every
+//    chunk (S^T = K Q^T on MFMA), with a running max per head (raised lazily, by 2^8 or
+//    more) and a running sum.
+//  pass 2 (P, out and cmass, lse final): the same S^T again, P = exp(s - lse) written as
+//    bf16 to an LDS buffer holding the chunk's P for all 128 heads, its head sums added
+//    into cmass.  One step later (behind the next barrier) wave w accumulates the output
+//    columns [128 w, 128 w + 128) of every head in AGPRs: O^T[d, h] += V^T[d, j] P^T[j, h],
+//    V^T read with the transposing LDS read (8 KiB per chunk) and P^T with 16-byte reads
+//    (8 KiB per chunk).  Those 64 MFMAs do not depend on the chunk's softmax, so the two
+//    are interleaved.
 //
-// LDS per query and 32-key chunk: pass 1 reads 128 KiB of K, pass 2 256 KiB of K plus
-// 96 KiB of V and P; the 16-byte pieces of a tile row are XOR-swizzled (row_swz) so the K
+// LDS per query and 32-key chunk: pass 1 reads 128 KiB of K, pass 2 128 KiB of K plus
+// 64 KiB of V and P; the 16-byte pieces of a tile row are XOR-swizzled (row_swz) so the K
 // reads, the transposing V reads and the staging writes are free of bank conflicts, and
 // P row h keeps its 16-byte key blocks XOR-swizzled by a function of h for the same reason
 // (16 lanes reading 16 rows of 64 bytes).
@@ -42,31 +41,32 @@ namespace csa {
 
 namespace {
 constexpr int WD = 512;                 // head dim
-constexpr int WHG = 8;                  // waves per workgroup
-constexpr int WNT = 64 * WHG;           // threads
+constexpr int WW = 4;                   // waves per workgroup
+constexpr int WNT = 64 * WW;            // threads
 constexpr int WROWB = WD * 2;           // bytes per KV row (1 KiB)
 constexpr int WTILE = 32 * WROWB;       // one 32-row chunk (32 KiB)
 constexpr int WPROW = 64;               // bytes per P row (32 keys, bf16)
 constexpr int WPBUF = 128 * WPROW;      // P of one chunk for 128 heads (8 KiB)
 constexpr int WNC = WD / 32;            // MFMA K-chunks per row
+constexpr int WRPW = 32 / WW;           // rows each wave stages per chunk
 #ifndef WIDE_NTILE_MAX
 #define WIDE_NTILE_MAX 4
 #endif
-#ifndef WIDE_LA1
-#define WIDE_LA1 4
+#ifndef WIDE_LA
+#define WIDE_LA 3
 #endif
-#ifndef WIDE_LA2
-#define WIDE_LA2 3
+constexpr int LA = WIDE_LA;             // K operand pairs requested ahead of their MFMAs
+#ifndef WIDE_VPRE
+#define WIDE_VPRE 2
 #endif
-#ifndef WIDE_LAP
-#define WIDE_LAP 2
+constexpr int VPRE = WIDE_VPRE;         // V^T d-tiles of P.V read during the QK MFMAs
+#ifndef WIDE_QKVALU
+#define WIDE_QKVALU 0
 #endif
-constexpr int LA1 = WIDE_LA1;   // pass 1: K operands requested ahead (one per K-chunk)
-constexpr int LA2 = WIDE_LA2;   // pass 2: K operand pairs requested ahead
-constexpr int LAP = WIDE_LAP;   // P.V: P^T operands requested ahead
-// Scheduling groups for the compiler's machine scheduler: the instructions of a region are
-// placed in the order of these calls (DS reads issued ahead of the MFMAs that consume them)
-constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
+constexpr int QKVALU = WIDE_QKVALU;     // vector ALU slots after each MFMA pair of QK
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DS_READ = 0x100;
+// the compiler's machine scheduler places the instructions of a region in the order of
+// these groups (used to interleave independent MFMAs and vector ALU work)
 template <int MASK, int N> __device__ __forceinline__ void sched_group() {
   __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
 }
@@ -80,7 +80,7 @@ size_t wide_attn_lds_bytes(int ntile, int k_eff) {
 }
 
 template <int NTILE>
-__global__ __launch_bounds__(WNT, 2) void sparse_attn_wide_kernel(
+__global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
     LayoutDev L, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
     const uint16_t *__restrict__ ckv, const float *__restrict__ sink,
     const int32_t *__restrict__ ids, int k_eff, int window, int H, int total_q, int total_k,
@@ -92,21 +92,20 @@ __global__ __launch_bounds__(WNT, 2) void sparse_attn_wide_kernel(
   constexpr int DIST = NTILE - 2;          // request distance in steps
   char *pbufs = wide_dyn + NTILE * WTILE;
   int *ids_l = reinterpret_cast<int *>(pbufs + 2 * WPBUF);
-  __shared__ float cm_part[2][WHG][33];   // slot 32: spare target of stores not needed
-  __shared__ float4 stat[2][128];   // per key half and head: m, L, m_nc, L_nc (log2 units)
+  __shared__ float cm_part[2][WW][33];   // slot 32: spare target of stores not needed
   __shared__ int jlast;
 
   const int t = blockIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-  const int kh = w & 1;                         // pass 1: key half of every chunk
-  // pass 1 head groups: gi = 0 the wave's own heads 16 w + r16, gi = 1 its partner's
-  int h1[2];
-  bool ok1[2];
-  h1[0] = 16 * w + r16;
-  h1[1] = 16 * (w ^ 1) + r16;
-  ok1[0] = h1[0] < H;
-  ok1[1] = h1[1] < H;
+  // the wave's heads: tile hi holds heads 32 w + 16 hi + r16
+  int hh[2];
+  bool ok[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    hh[hi] = 32 * w + 16 * hi + r16;
+    ok[hi] = hh[hi] < H;
+  }
   const RowGeo geo = row_geo(L, t);
   const int w_lo = max(geo.q_start, t - window + 1);
   const int nw = window > 0 ? t - w_lo + 1 : 0;
@@ -134,35 +133,17 @@ __global__ __launch_bounds__(WNT, 2) void sparse_attn_wide_kernel(
     }
     if (jl >= 0) atomicMax(&jlast, jl);
   }
-  // Q^T operands of both head groups; piece c of lane group g holds features
+  // Q^T operands of both head tiles; piece c of lane group g holds features
   // [(4c+g)*8, +8) (a head past H loads head 0's row: its logits are masked)
   u32x4 qf[2][WNC];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (ok1[gi] ? h1[gi] : 0)) * WD) + g;
+  for (int hi = 0; hi < 2; ++hi) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q + ((int64_t)t * H + (ok[hi] ? hh[hi] : 0)) * WD) + g;
 #pragma unroll
-    for (int c = 0; c < WNC; ++c) qf[gi][c] = p[4 * c];
+    for (int c = 0; c < WNC; ++c) qf[hi][c] = p[4 * c];
   }
   const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)(t + 1) * WROWB);   // rows past t: zeros
   const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * WROWB);  // id -1: past the end
-  // loads of chunk ci: instruction i = w + 8k moves row i (1 KiB); lane l writes slot l,
-  // which holds the row's piece l ^ row_swz(i)
-  auto issue = [&](int ci, char *buf) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const uint32_t d0 = 16 * ln;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = w + WHG * k;
-      const uint32_t off = d0 ^ (uint32_t)(16 * row_swz<WD>(i));
-      if (ci < nwc) {
-        dma16(rkv, buf + i * 1024, (uint32_t)(w_lo + 32 * ci + i) * WROWB + off);
-      } else {
-        const int id = ids_l[32 * (ci - nwc) + i];
-        dma16(rck, buf + i * 1024, (uint32_t)id * WROWB + off);
-      }
-    }
-  };
   auto row_mask = [&](int ci) -> uint32_t {
     if (ci < nwc) {
       const int n = nw - 32 * ci;
@@ -186,158 +167,220 @@ __global__ __launch_bounds__(WNT, 2) void sparse_attn_wide_kernel(
   const int ns = 2 * nch;   // steps: pass 1 over every chunk, then pass 2
   auto chunk_of = [&](int n) { return n < nch ? n : n - nch; };
   auto tile = [&](int n) { return wide_dyn + (n % NTILE) * WTILE; };
-  // Every wave issues exactly 4 row loads per step, so with DIST steps requested ahead
-  // "at most 4 (DIST - 1) vector-memory operations outstanding" means step n's rows have
-  // landed (loads complete in order; stores issued in between only make the wait stricter).
-  // After the barrier every wave has finished step n - 1, the last reader (P.V) of the tile
-  // of step n - 2 = n + DIST - NTILE, which the new request reuses.
-  auto top = [&](int n) {
-    if (n + DIST - 1 < ns) wait_vmcnt<4 * (DIST - 1)>();
+  // Loads of the chunk of step n: instruction k of wave w moves row i = w + 4k (1 KiB);
+  // lane l writes slot l, which holds the row's piece l ^ row_swz(i).  A step issues the
+  // rows it requests one at a time between its QK MFMAs: a burst of eight 1 KiB loads
+  // would hold the wave until the memory pipeline's queue takes them.
+  struct ChunkReq {
+    __amdgpu_buffer_rsrc_t r;
+    char *buf;
+    int myrow;   // lane l (< 32) holds the KV or compressed row that is chunk row l
+  };
+  const __amdgpu_buffer_rsrc_t rnone = make_rsrc(kv, 0);   // every load out of range: zeros
+  uint32_t d0 = 16 * lane;
+  asm volatile("" : "+v"(d0));
+  auto request = [&](int n) -> ChunkReq {
+    ChunkReq rq;
+    rq.buf = tile(n);
+    const int ci = chunk_of(n);
+    if (n >= ns) {   // nothing left to load: zeros into the free tile
+      rq.r = rnone;
+      rq.myrow = 0;
+    } else if (ci < nwc) {
+      rq.r = rkv;
+      rq.myrow = w_lo + 32 * ci + (lane & 31);
+    } else {
+      rq.r = rck;
+      rq.myrow = ids_l[32 * (ci - nwc) + (lane & 31)];
+    }
+    return rq;
+  };
+  auto issue_row = [&](const ChunkReq &rq, int k) __attribute__((always_inline)) {
+    const int i = w + WW * k;
+    const uint32_t off = d0 ^ (uint32_t)(16 * row_swz<WD>(i));
+    dma16(rq.r, rq.buf + i * WROWB, (uint32_t)__builtin_amdgcn_readlane(rq.myrow, i) * WROWB + off);
+  };
+  // Every wave issues exactly WRPW row loads per step (before the next step's barrier), so
+  // with DIST steps requested ahead
+  // "at most WRPW (DIST - 1) vector-memory operations outstanding" means step n's rows
+  // have landed (loads complete in order; stores issued in between only make the wait
+  // stricter).  After the barrier every wave has finished step n - 1, the last reader
+  // (P.V) of the tile of step n - 2 = n + DIST - NTILE, which the new request reuses.
+  auto top = [&](int n) -> ChunkReq {
+    if (n + DIST - 1 < ns) wait_vmcnt<WRPW * (DIST - 1)>();
     else wait_vmcnt<0>();
-    __syncthreads();
-    if (n + DIST < ns) issue(chunk_of(n + DIST), tile(n + DIST));
+    lds_barrier();
+    return request(n + DIST);
   };
 #pragma unroll
-  for (int k = 0; k < DIST; ++k)
-    if (k < ns) issue(chunk_of(k), tile(k));
+  for (int k = 0; k < DIST; ++k) {
+    const ChunkReq rq = request(k);
+#pragma unroll
+    for (int r = 0; r < WRPW; ++r) issue_row(rq, r);
+  }
+
+  // S^T of the chunk of step n for the wave's 32 heads: acc[kt][hi][i] is the logit of
+  // key 16 kt + 4 g + i and head 32 w + 16 hi + r16 (unscaled)
+  // mid() is called once the last K operands are requested (P.V operand reads of pass 2);
+  // vector ALU work placed before the call in the same block runs between the MFMAs
+  auto qk = [&](int n, f32x4 (&acc)[2][2], const ChunkReq &rq, auto &&mid) __attribute__((always_inline)) {
+    const char *kb = tile(n) + kbase;
+    int kxs = kx;
+    asm volatile("" : "+v"(kxs));
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) acc[kt][hi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 kr[LA][2];
+    auto kread = [&](int c, u32x4 (&dst)[2]) __attribute__((always_inline)) {
+      const char *kp = kb + 64 * (c ^ kxs);
+      dst[0] = *reinterpret_cast<const u32x4 *>(kp);
+      dst[1] = *reinterpret_cast<const u32x4 *>(kp + 16 * WROWB);
+    };
+#pragma unroll
+    for (int c = 0; c < LA; ++c) kread(c, kr[c]);
+    sched_group<SG_DS_READ, 2 * LA>();
+#pragma unroll
+    for (int c = 0; c < WNC; ++c) {
+      const u32x4 k0 = kr[c % LA][0], k1 = kr[c % LA][1];
+      if (c + LA < WNC) kread(c + LA, kr[c % LA]);
+      if (c + LA == WNC - 1) mid();
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        acc[0][hi] = mfma16x16x32(k0, qf[hi][c], acc[0][hi]);
+        acc[1][hi] = mfma16x16x32(k1, qf[hi][c], acc[1][hi]);
+      }
+      if (c % 2 == 1) issue_row(rq, c / 2);
+      sched_group<SG_MFMA, 2>();
+      if (QKVALU) sched_group<SG_VALU, QKVALU>();
+      if (c + LA < WNC) sched_group<SG_DS_READ, 2>();
+      sched_group<SG_MFMA, 2>();
+      if (QKVALU) sched_group<SG_VALU, QKVALU>();
+      if (c % 2 == 1) sched_group<SG_VMEM, 1>();
+    }
+  };
 
   // ------------------------------------------------------------------ pass 1: lse, lse_nc
   float m[2], l[2], m_nc[2], l_nc[2];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const float a2 = ok1[gi] ? sink[h1[gi]] * LOG2E : NINF;
-    m[gi] = a2;
-    l[gi] = (g == 0 && kh == 0 && a2 > NINF) ? 1.f : 0.f;   // the sink counted once per head
-    m_nc[gi] = m[gi];
-    l_nc[gi] = l[gi];
+  for (int hi = 0; hi < 2; ++hi) {
+    const float a2 = ok[hi] ? sink[hh[hi]] * LOG2E : NINF;
+    m[hi] = a2;
+    l[hi] = (g == 0 && a2 > NINF) ? 1.f : 0.f;   // the sink counted once per head
+    m_nc[hi] = m[hi];
+    l_nc[hi] = l[hi];
   }
-  for (int ci = 0; ci < nch; ++ci) {
-    top(ci);
-    if (ci == nwc) {
+  // The logits of a chunk (masked, unscaled) are folded into the running max and sums at
+  // the next step, while that step's MFMAs run: the max is raised first (rarely; a branch),
+  // then the exponentials are summed beside the MFMAs.
+  float sv[2][8];
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) { m_nc[gi] = m[gi]; l_nc[gi] = l[gi]; }
-    }
-    // this wave's 16 keys (rows 16 kh + 4g + i) for both head groups, unscaled
-    const char *kb = tile(ci) + kbase + 16 * kh * WROWB;
-    int kxs = kx;
-    asm volatile("" : "+v"(kxs));
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    u32x4 kr[LA1];   // K operands requested LA1 K-chunks ahead
+  for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-    for (int c = 0; c < LA1; ++c) kr[c] = *reinterpret_cast<const u32x4 *>(kb + 64 * (c ^ kxs));
-    sched_group<SG_DS_READ, LA1>();
-#pragma unroll
-    for (int c = 0; c < WNC; ++c) {
-      const u32x4 k0 = kr[c % LA1];
-      if (c + LA1 < WNC) {
-        kr[c % LA1] = *reinterpret_cast<const u32x4 *>(kb + 64 * ((c + LA1) ^ kxs));
-        sched_group<SG_DS_READ, 1>();
-      }
-      acc[0] = mfma16x16x32(k0, qf[0][c], acc[0]);
-      acc[1] = mfma16x16x32(k0, qf[1][c], acc[1]);
-      sched_group<SG_MFMA, 2>();
-    }
-    const uint32_t bm = (row_mask(ci) >> (16 * kh)) >> (4 * g);
-    float sv[2][4];
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[gi][i] = (ok1[gi] && ((bm >> i) & 1)) ? acc[gi][i] : NINF;
+    for (int e = 0; e < 8; ++e) sv[hi][e] = NINF;
+  auto raise_max = [&]() __attribute__((always_inline)) {
     float cmx[2];
     bool up = false;
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      cmx[gi] = fmaxf(fmaxf(sv[gi][0], sv[gi][1]), fmaxf(sv[gi][2], sv[gi][3]));
-      up = up || cmx[gi] * sl2 > m[gi] + RESCALE;   // log2 units (sl2 > 0 keeps the order)
+    for (int hi = 0; hi < 2; ++hi) {
+      cmx[hi] = sv[hi][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) cmx[hi] = fmaxf(cmx[hi], sv[hi][e]);
+      up = up || cmx[hi] * sl2 > m[hi] + RESCALE;   // log2 units (sl2 > 0 keeps the order)
     }
     if (__builtin_expect(__ballot(up) != 0, 0)) {
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        const float cand = across_groups_max(cmx[gi]) * sl2;
-        const float mn = cand > m[gi] + RESCALE ? cand : m[gi];
-        l[gi] *= mn == m[gi] ? 1.f : fast_exp2(m[gi] - mn);
-        m[gi] = mn;
+      for (int hi = 0; hi < 2; ++hi) {
+        const float cand = across_groups_max(cmx[hi]) * sl2;
+        const float mn = cand > m[hi] + RESCALE ? cand : m[hi];
+        l[hi] *= mn == m[hi] ? 1.f : fast_exp2(m[hi] - mn);
+        m[hi] = mn;
       }
     }
+  };
+  auto add_sums = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const float nms = m[gi] == NINF ? 0.f : -m[gi];
+    for (int hi = 0; hi < 2; ++hi) {
+      const float nms = m[hi] == NINF ? 0.f : -m[hi];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l[gi] += fast_exp2(fmaf(sv[gi][i], sl2, nms));
+      for (int e = 0; e < 8; ++e) l[hi] += fast_exp2(fmaf(sv[hi][e], sl2, nms));
     }
+  };
+  for (int ci = 0; ci < nch; ++ci) {
+    const ChunkReq rq = top(ci);
+    raise_max();   // chunk ci - 1
+    add_sums();
+    f32x4 acc[2][2];
+    qk(ci, acc, rq, [] {});
+    if (ci == nwc) {   // every window chunk folded
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
+    }
+    const uint32_t bm = row_mask(ci) >> (4 * g);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sv[hi][e] = (ok[hi] && ((bm >> (16 * (e >> 2) + (e & 3))) & 1)) ? acc[e >> 2][hi][e & 3] : NINF;
   }
+  raise_max();   // the last chunk
+  add_sums();
   if (ncc == 0) {
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) { m_nc[gi] = m[gi]; l_nc[gi] = l[gi]; }
+    for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
   }
+  // lse of the wave's heads (log2 units), -inf for a head with no probability at all
+  float nl[2];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const float Ls = across_groups_sum(l[gi]), Lnc = across_groups_sum(l_nc[gi]);
-    if (g == 0 && ok1[gi]) stat[kh][h1[gi]] = make_float4(m[gi], Ls, m_nc[gi], Lnc);
-  }
-  __syncthreads();   // both key halves' sums of every head
-  // lse of the wave's own heads (pass 2): the two halves combined
-  const bool ok2 = ok1[0];
-  float lse2 = NINF, lse2_nc = NINF;
-  if (ok2) {
-    const float4 a = stat[0][h1[0]], b = stat[1][h1[0]];
-    auto comb = [&](float ma, float la, float mb, float lb) {
-      const float mm = fmaxf(ma, mb);
-      if (mm == NINF) return NINF;
-      const float s = (ma == NINF ? 0.f : la * fast_exp2(ma - mm)) + (mb == NINF ? 0.f : lb * fast_exp2(mb - mm));
-      return s > 0.f ? mm + __log2f(s) : NINF;
-    };
-    lse2 = comb(a.x, a.y, b.x, b.y);
-    lse2_nc = comb(a.z, a.w, b.z, b.w);
-  }
-  const float nl = lse2 > NINF ? -lse2 : NINF;   // exp2(-inf) = 0: no probability at all
-  if (ok2 && g == 0) {
-    lse[(int64_t)t * H + h1[0]] = lse2 * LN2;
-    lse_nc[(int64_t)t * H + h1[0]] = lse2_nc * LN2;
+  for (int hi = 0; hi < 2; ++hi) {
+    const float Ls = across_groups_sum(l[hi]), Lnc = across_groups_sum(l_nc[hi]);
+    const float lse2 = (m[hi] > NINF && Ls > 0.f) ? m[hi] + __log2f(Ls) : NINF;
+    const float lse2_nc = (m_nc[hi] > NINF && Lnc > 0.f) ? m_nc[hi] + __log2f(Lnc) : NINF;
+    nl[hi] = (ok[hi] && lse2 > NINF) ? -lse2 : NINF;   // exp2(-inf) = 0
+    if (ok[hi] && g == 0) {
+      lse[(int64_t)t * H + hh[hi]] = lse2 * LN2;
+      lse_nc[(int64_t)t * H + hh[hi]] = lse2_nc * LN2;
+    }
   }
 
   // ------------------------------------------------------- pass 2: P, cmass, then P.V
-  f32x4 o[8][4];   // O^T[d = 64 w + 16 dt + 4g + i][head 16 ht + r16]
+  f32x4 o[8][8];   // O^T[d = 128 w + 16 dt + 4 g + i][head 16 ht + r16]
 #pragma unroll
   for (int ht = 0; ht < 8; ++ht)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 8; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // P row swizzle of rows 16x + r16 (16-byte key block b at position b ^ psw): with the
   // 16-byte read service order of the LDS every quarter wave hits 16 distinct slots
   const int psw = (2 * ((r16 >> 2) & 1)) ^ (3 * ((r16 >> 3) & 1));
   auto pbuf = [&](int n) { return pbufs + (n & 1) * WPBUF; };
-  // O^T += V^T P^T for the chunk of step n (its tile and P buffer)
-  auto pv = [&](int n) __attribute__((always_inline)) {
+  // P.V operands of the chunk of step n: V^T of the wave's 8 d-tiles (transposing reads)
+  // and P^T of the 8 head tiles
+  u32x4 va[8], pb[8];
+  uint2 xv[16];
+  auto pv_read_v = [&](int n, int dt0, int dt1) __attribute__((always_inline)) {
     const char *base = tile(n);
     int vxs = vx;
     asm volatile("" : "+v"(vxs));
-    uint2 xv[8];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const uint32_t va = lds_addr_of(base + vbase + 32 * ((4 * w + dt) ^ vxs));
-      xv[2 * dt] = lds_read_tr16_nowait_off<0>(va);
-      xv[2 * dt + 1] = lds_read_tr16_nowait_off<16 * WROWB>(va);
+    for (int dt = dt0; dt < dt1; ++dt) {
+      const uint32_t a = lds_addr_of(base + vbase + 32 * ((8 * w + dt) ^ vxs));
+      xv[2 * dt] = lds_read_tr16_nowait_off<0>(a);
+      xv[2 * dt + 1] = lds_read_tr16_nowait_off<16 * WROWB>(a);
     }
-    lds_tr16_wait(xv);
-    u32x4 a[4];
+  };
+  auto pv_read_p = [&](int n) __attribute__((always_inline)) {
+    const char *pr = pbuf(n) + r16 * WPROW + 16 * (g ^ psw);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) a[dt] = u32x4{xv[2 * dt].x, xv[2 * dt].y, xv[2 * dt + 1].x, xv[2 * dt + 1].y};
-    const char *pb = pbuf(n) + r16 * WPROW + 16 * (g ^ psw);
-    u32x4 br[LAP];   // P^T operands requested LAP head tiles ahead
+    for (int ht = 0; ht < 8; ++ht) pb[ht] = *reinterpret_cast<const u32x4 *>(pr + 16 * ht * WPROW);
+    lds_tr16_wait_but<8>(xv);   // the P^T reads may still be in flight
 #pragma unroll
-    for (int ht = 0; ht < LAP; ++ht) br[ht] = *reinterpret_cast<const u32x4 *>(pb + 16 * ht * WPROW);
-    sched_group<SG_DS_READ, LAP>();
+    for (int dt = 0; dt < 8; ++dt) va[dt] = u32x4{xv[2 * dt].x, xv[2 * dt].y, xv[2 * dt + 1].x, xv[2 * dt + 1].y};
+  };
+  auto pv_mma = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ht = 0; ht < 8; ++ht) {
-      const u32x4 b = br[ht % LAP];
-      if (ht + LAP < 8) {
-        br[ht % LAP] = *reinterpret_cast<const u32x4 *>(pb + 16 * (ht + LAP) * WPROW);
-        sched_group<SG_DS_READ, 1>();
-      }
+    for (int ht = 0; ht < 8; ++ht)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[ht][dt] = mfma16x16x32(a[dt], b, o[ht][dt]);
-      sched_group<SG_MFMA, 4>();
-    }
+      for (int dt = 0; dt < 8; ++dt) o[ht][dt] = mfma16x16x32(va[dt], pb[ht], o[ht][dt]);
   };
   auto flush = [&](int cprev, int nprev) {
     if (crow && cprev >= nwc && tid < 32) {
@@ -345,7 +388,7 @@ __global__ __launch_bounds__(WNT, 2) void sparse_attn_wide_kernel(
       if (slot < k_eff) {
         float sum = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < WHG; ++ww) sum += cm_part[nprev & 1][ww][tid];
+        for (int ww = 0; ww < WW; ++ww) sum += cm_part[nprev & 1][ww][tid];
         crow[slot] = sum;
       }
     }
@@ -356,65 +399,56 @@ __global__ __launch_bounds__(WNT, 2) void sparse_attn_wide_kernel(
     for (int i = tid; i < WPBUF / 16; i += WNT) reinterpret_cast<u32x4 *>(pbuf(nch - 1))[i] = u32x4{0, 0, 0, 0};
   for (int ci = 0; ci < nch; ++ci) {
     const int n = nch + ci;
-    top(n);
+    const ChunkReq rq = top(n);
     if (ci > 0) flush(ci - 1, n - 1);
-    // S^T for the 32 rows of the chunk and the wave's 16 heads
-    const char *base = tile(n);
-    int kxs = kx;
-    asm volatile("" : "+v"(kxs));
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-    // K operands requested LA K-chunks ahead of their MFMAs (a ring of LA pairs), so that
-    // LDS latency overlaps the MFMAs instead of being paid before each of them
-    u32x4 kr[LA2][2];
-    auto kread = [&](int c, u32x4 (&dst)[2]) __attribute__((always_inline)) {
-      const char *kp = base + kbase + 64 * (c ^ kxs);
-      dst[0] = *reinterpret_cast<const u32x4 *>(kp);
-      dst[1] = *reinterpret_cast<const u32x4 *>(kp + 16 * WROWB);
-    };
+    // P.V operands of the chunk before (at the first step: a zeroed P buffer): VPRE of the
+    // V^T tiles read during the last QK MFMAs, the rest and P^T after them
+    f32x4 acc[2][2];
+    qk(n, acc, rq, [&] { pv_read_v(n - 1, 0, VPRE); });
+    pv_read_v(n - 1, VPRE, 8);
+    pv_read_p(n - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // P = exp2(s sl2 - lse) of the chunk, its bf16 copy for P.V and the head sums for
+    // cmass, interleaved with the P.V MFMAs of the chunk before (no dependence either way;
+    // stores the step does not need go to a spare slot, so the block has no branch)
+    const uint32_t bm = row_mask(ci) >> (4 * g);
+    float p[2][8];   // [hi][4 kt + i]
 #pragma unroll
-    for (int c = 0; c < LA2; ++c) kread(c, kr[c]);
-    sched_group<SG_DS_READ, 2 * LA2>();
+    for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-    for (int c = 0; c < WNC; ++c) {
-      const u32x4 k0 = kr[c % LA2][0], k1 = kr[c % LA2][1];
-      if (c + LA2 < WNC) {
-        kread(c + LA2, kr[c % LA2]);
-        sched_group<SG_DS_READ, 2>();
+      for (int e = 0; e < 8; ++e) {
+        const float s = ((bm >> (16 * (e >> 2) + (e & 3))) & 1) ? acc[e >> 2][hi][e & 3] : NINF;
+        p[hi][e] = fast_exp2(fmaf(s, sl2, nl[hi]));
       }
-      acc0 = mfma16x16x32(k0, qf[0][c], acc0);
-      acc1 = mfma16x16x32(k1, qf[0][c], acc1);
-      sched_group<SG_MFMA, 2>();
-    }
-    // Masking, P, its bf16 copy for P.V, the head sums for cmass and the P.V of the chunk
-    // before form one branch-free block (stores the step does not need go to a spare
-    // slot), so the compiler can overlap the vector work of this chunk with the MFMAs of
-    // the previous chunk's P.V.
-    const uint32_t bm = row_mask(ci);
-    const uint32_t m0 = ok2 ? (bm >> (4 * g)) : 0u, m1 = ok2 ? (bm >> (16 + 4 * g)) : 0u;
-    float p[8];
+    // P row 32 w + 16 hi + r16, key block g (MFMA k order: keys 4g..4g+3, 16+4g..16+4g+3)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = ((m0 >> i) & 1) ? acc0[i] : NINF;
-      p[4 + i] = ((m1 >> i) & 1) ? acc1[i] : NINF;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(p[e], sl2, nl));
-    // P row 16 w + r16, key block g (MFMA k order: keys 4g..4g+3, 16+4g..16+4g+3)
-    *reinterpret_cast<u32x4 *>(pbuf(n) + (16 * w + r16) * WPROW + 16 * (g ^ psw)) =
-        u32x4{pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]), pack2_bf16(p[6], p[7])};
-    // value e of group g is row 16 (e >> 2) + 4g + (e & 3); lane r16 ends with the head sum
+    for (int hi = 0; hi < 2; ++hi)
+      *reinterpret_cast<u32x4 *>(pbuf(n) + (32 * w + 16 * hi + r16) * WPROW + 16 * (g ^ psw)) =
+          u32x4{pack2_bf16(p[hi][0], p[hi][1]), pack2_bf16(p[hi][2], p[hi][3]), pack2_bf16(p[hi][4], p[hi][5]),
+                pack2_bf16(p[hi][6], p[hi][7])};
+    // value e of group g is key 16 (e >> 2) + 4g + (e & 3); lane r16 ends with the head sum
     // of value sum8_index(r16); window chunks and odd lanes store to the spare slot 32
-    const float sh = group16_sum8(p, r16);
+    float ps[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ps[e] = p[0][e] + p[1][e];
+    const float sh = group16_sum8(ps, r16);
     const int el = sum8_index(r16);
     const bool cm_on = crow != nullptr && ci >= nwc && (r16 & 1) == 0;
     cm_part[n & 1][w][cm_on ? 16 * (el >> 2) + 4 * g + (el & 3) : 32] = sh;
-    // P.V of the chunk before (at the first step: a zeroed P buffer)
-    pv(n - 1);
+    pv_mma();
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+      sched_group<SG_MFMA, 1>();
+      sched_group<SG_VALU, 2>();
+    }
   }
+  wait_vmcnt<0>();   // no load into the LDS outlives the workgroup
   if (nch > 0) {
     __syncthreads();   // the last chunk's P and cmass partials of every wave
     flush(nch - 1, ns - 1);
-    pv(ns - 1);
+    pv_read_v(ns - 1, 0, 8);
+    pv_read_p(ns - 1);
+    pv_mma();
   }
 
   // ---------------------------------------------------------------- outputs
@@ -422,9 +456,9 @@ __global__ __launch_bounds__(WNT, 2) void sparse_attn_wide_kernel(
   for (int ht = 0; ht < 8; ++ht) {
     const int h = 16 * ht + r16;
     if (h < H) {
-      uint16_t *orow = out + ((int64_t)t * H + h) * WD + 64 * w + 4 * g;
+      uint16_t *orow = out + ((int64_t)t * H + h) * WD + 128 * w + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 8; ++dt)
         *reinterpret_cast<uint2 *>(orow + 16 * dt) =
             uint2{pack2_bf16(o[ht][dt][0], o[ht][dt][1]), pack2_bf16(o[ht][dt][2], o[ht][dt][3])};
     }
@@ -453,7 +487,7 @@ hipError_t launch_sparse_attn_wide(const LaunchLayout &LL, const void *q, const 
                                    const float *sink, const int32_t *ids, int k_eff, int window, int H,
                                    float scale, void *out, float *lse, float *lse_nc, float *cmass,
                                    hipStream_t st) {
-  constexpr size_t LDS_CU = 160 * 1024, STATIC = 8 * 1024;
+  constexpr size_t LDS_CU = 160 * 1024, STATIC = 2 * 1024;   // cm_part and jlast
   if (WIDE_NTILE_MAX >= 4 && wide_attn_lds_bytes(4, k_eff) + STATIC <= LDS_CU)
     return launch_wide_t<WIDE_NTILE_MAX>(LL, q, kv, ckv, sink, ids, k_eff, window, H, scale, out, lse, lse_nc,
                                          cmass, st);
