@@ -151,9 +151,12 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
     }
     return (uint32_t)__ballot(ids_l[32 * (ci - nwc) + (lane & 31)] >= 0);
   };
-  // K operand: row r16 (+16), piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3))
+  // K operand: row r16 (+16), piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3));
+  // with c = 4 (c >> 2) + j that is byte 256 (c >> 2) + kbj[j] of the row
   const int ksw = row_swz<WD>(r16);
-  const int kbase = r16 * WROWB + 16 * (g ^ (ksw & 3)), kx = ksw >> 2;
+  int kbj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kbj[j] = r16 * WROWB + 16 * (g ^ (ksw & 3)) + 64 * (j ^ (ksw >> 2));
   // V^T operand: rows rho (+16), piece (2dt + hb) ^ swz = 2 (dt ^ (swz >> 1)) + (hb ^ (swz & 1))
   const int rho = 4 * g + (r16 >> 2);
   const int vsw = row_swz<WD>(rho);
@@ -224,16 +227,14 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   // mid() is called once the last K operands are requested (P.V operand reads of pass 2);
   // vector ALU work placed before the call in the same block runs between the MFMAs
   auto qk = [&](int n, f32x4 (&acc)[2][2], const ChunkReq &rq, auto &&mid) __attribute__((always_inline)) {
-    const char *kb = tile(n) + kbase;
-    int kxs = kx;
-    asm volatile("" : "+v"(kxs));
+    const char *tb = tile(n);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) acc[kt][hi] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 kr[LA][2];
     auto kread = [&](int c, u32x4 (&dst)[2]) __attribute__((always_inline)) {
-      const char *kp = kb + 64 * (c ^ kxs);
+      const char *kp = tb + kbj[c & 3] + 256 * (c >> 2);   // the rest of the offset is immediate
       dst[0] = *reinterpret_cast<const u32x4 *>(kp);
       dst[1] = *reinterpret_cast<const u32x4 *>(kp + 16 * WROWB);
     };
@@ -316,12 +317,20 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
     }
-    const uint32_t bm = row_mask(ci) >> (4 * g);
+    // a head past H keeps finite garbage statistics that are never written
+    const uint32_t bm_all = row_mask(ci), bm = bm_all >> (4 * g);
+    if (bm_all == 0xffffffffu) {
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi)
+      for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sv[hi][e] = (ok[hi] && ((bm >> (16 * (e >> 2) + (e & 3))) & 1)) ? acc[e >> 2][hi][e & 3] : NINF;
+        for (int e = 0; e < 8; ++e) sv[hi][e] = acc[e >> 2][hi][e & 3];
+    } else {
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sv[hi][e] = ((bm >> (16 * (e >> 2) + (e & 3))) & 1) ? acc[e >> 2][hi][e & 3] : NINF;
+    }
   }
   raise_max();   // the last chunk
   add_sums();
@@ -411,15 +420,19 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
     // P = exp2(s sl2 - lse) of the chunk, its bf16 copy for P.V and the head sums for
     // cmass, interleaved with the P.V MFMAs of the chunk before (no dependence either way;
     // stores the step does not need go to a spare slot, so the block has no branch)
-    const uint32_t bm = row_mask(ci) >> (4 * g);
-    float p[2][8];   // [hi][4 kt + i]
+    const uint32_t bm_all = row_mask(ci), bm = bm_all >> (4 * g);
+    float p[2][8];   // [hi][4 kt + i]; a head past H has nl = -inf: P = 0
+    if (bm_all != 0xffffffffu) {
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!((bm >> (16 * (e >> 2) + (e & 3))) & 1)) acc[e >> 2][hi][e & 3] = NINF;
+    }
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = ((bm >> (16 * (e >> 2) + (e & 3))) & 1) ? acc[e >> 2][hi][e & 3] : NINF;
-        p[hi][e] = fast_exp2(fmaf(s, sl2, nl[hi]));
-      }
+      for (int e = 0; e < 8; ++e) p[hi][e] = fast_exp2(fmaf(acc[e >> 2][hi][e & 3], sl2, nl[hi]));
     // P row 32 w + 16 hi + r16, key block g (MFMA k order: keys 4g..4g+3, 16+4g..16+4g+3)
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
