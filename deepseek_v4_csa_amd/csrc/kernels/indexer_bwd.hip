@@ -185,25 +185,32 @@ __device__ __forceinline__ void dma_q_block(const uint16_t *q_idx, int row0, int
 }
 
 // ---------------------------------------------------------------- 2. dq / dweights
-// HPW heads per wave per pass; 4 waves; passes = HI / (4 * HPW).
-template <int DI, int HI, int HPW>
+// A workgroup takes HW of the HI heads (head group hg of HI / HW; the q slice of those
+// heads, HW * DI * 2 bytes of each token row, is what it stages); HPW heads per wave per
+// pass; 4 waves; passes = HW / (4 * HPW).  The head groups of a token block are
+// independent: each recomputes the block's key tiles for its own heads.
+template <int DI, int HI, int HPW, int HW>
 __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
     LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const float *__restrict__ weights, float idx_scale, const float *__restrict__ grad, int64_t ldg,
     int max_sk, int total_q, int nqb, float *__restrict__ dq, float *__restrict__ dw) {
-  constexpr int RB = HI * DI * 2, CPR = RB / 16;
+  constexpr int RB = HI * DI * 2;      // bytes of a token's q row
+  constexpr int SB = HW * DI * 2, CPR = SB / 16;   // staged bytes of it
+  static_assert(HI % HW == 0, "head groups");
   constexpr int NCD = DI / 32;         // MFMA 16x16x32 K-chunks per dot product
   constexpr int NDT = DI / 16;         // 16-dim output tiles
   constexpr int ROWB = DI * 2;         // bytes per key row
   constexpr int PIECES = DI / 8, RPI = 64 / PIECES, NI = 64 / RPI;   // key-tile DMA shape
   constexpr int KT = 64 * ROWB;        // one 64-key tile
-  constexpr int PASSES = HI / (4 * HPW);
-  static_assert(HI % (4 * HPW) == 0, "heads per pass");
+  constexpr int PASSES = HW / (4 * HPW);
+  static_assert(HW % (4 * HPW) == 0, "heads per pass");
   __shared__ __attribute__((aligned(16))) u32x4 qs[BWD_TOK * CPR];
   __shared__ __attribute__((aligned(16))) char kt_lds[2][KT];
 
   const int seg = blockIdx.x % L.num_seqs;
-  const int qb = nqb - 1 - (int)(blockIdx.x / L.num_seqs);   // heaviest blocks first
+  const int bi = (int)(blockIdx.x / L.num_seqs);
+  const int hg0 = (bi % (HI / HW)) * HW;          // first head of the group
+  const int qb = nqb - 1 - bi / (HI / HW);        // heaviest blocks first
   const int q_start = __ldg(L.cu_q + seg);
   const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
   const int t0 = qb * BWD_TOK;
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
   const bool t_ok = t < q_len;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_idx + (int64_t)k_base * DI, (uint32_t)(max(s_k, 0) * ROWB));
 
-  dma_q_block<RB>(q_idx, q_start + t0, total_q, reinterpret_cast<char *>(qs), w, 4, lane);
+  dma_rows<RB, SB>(q_idx, q_start + t0, total_q, hg0 * DI * 2, reinterpret_cast<char *>(qs), w, 4, lane);
   // key tile kt -> buffer b: NI instructions of RPI rows, dealt over the 4 waves
   const int kgg = lane / PIECES, kpp = lane % PIECES;
   auto dma_k = [&](int kt, int b) {
@@ -229,8 +236,8 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
       dma16(rk, kt_lds[b] + i * 1024, o);
     }
   };
-  const char *qrow = reinterpret_cast<const char *>(qs) + r16 * RB;
-  auto a_frag = [&](int h, int c) -> u32x4 {   // Q_h^T operand: token r16, piece 4c+g
+  const char *qrow = reinterpret_cast<const char *>(qs) + r16 * SB;
+  auto a_frag = [&](int h, int c) -> u32x4 {   // Q_h^T operand (h within the group): token r16, piece 4c+g
     const int q = h * (DI / 8) + 4 * c + g;
     return *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
   };
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
         }
 #pragma unroll
         for (int k = 0; k < HPW; ++k) {
-          const int h = pass * 4 * HPW + k * 4 + w;
+          const int h = pass * 4 * HPW + k * 4 + w;   // within the group
           float e[8];
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
@@ -328,7 +335,7 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
     // outputs: lane (token r16, group g) holds dims 16dt + 4g + i of U_h^T
 #pragma unroll
     for (int k = 0; k < HPW; ++k) {
-      const int h = pass * 4 * HPW + k * 4 + w;
+      const int h = hg0 + pass * 4 * HPW + k * 4 + w;
       float s = dwa[k];
       s += __shfl_xor(s, 16, 64);
       s += __shfl_xor(s, 32, 64);
@@ -578,7 +585,7 @@ int64_t indexer_bwd_workspace_bytes(int num_seqs, int total_k, int max_seqlen_q,
   return ns > 1 ? (int64_t)ns * total_k * Di * (int64_t)sizeof(float) : 0;
 }
 
-template <int DI, int HI, int HPW>
+template <int DI, int HI, int HPW, int HW = HI>
 static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
                                const float *weights, float idx_scale, const float *grad, int64_t ldg,
                                float *dq, float *dw, float *dk, float *ws, hipStream_t st) {
@@ -587,7 +594,8 @@ static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const 
   int ch, ns;
   indexer_bwd_dk_split(LL.num_seqs, LL.max_seqlen_q, LL.max_seqlen_k, &ch, &ns);
   if (LL.total_q > 0) {
-    hipLaunchKernelGGL((idx_bwd_dq_kernel<DI, HI, HPW>), dim3((unsigned)(LL.num_seqs * nqb)), dim3(256), 0, st,
+    hipLaunchKernelGGL((idx_bwd_dq_kernel<DI, HI, HPW, HW>), dim3((unsigned)(LL.num_seqs * nqb * (HI / HW))),
+                       dim3(256), 0, st,
                        LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
                        weights, idx_scale, grad, ldg, LL.max_seqlen_k, LL.total_q, nqb, dq, dw);
     hipError_t e = hipGetLastError();
@@ -636,12 +644,15 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const vo
       case 8: return launch_bwd_t<64, 8, 2>(CSA_BWD_ARGS);
       case 16: return launch_bwd_t<64, 16, 4>(CSA_BWD_ARGS);
       case 32: return launch_bwd_t<64, 32, 4>(CSA_BWD_ARGS);
+      case 64: return launch_bwd_t<64, 64, 4, 32>(CSA_BWD_ARGS);
     }
   } else if (Di == 128) {
     switch (Hi) {
       case 4: return launch_bwd_t<128, 4, 1>(CSA_BWD_ARGS);
       case 8: return launch_bwd_t<128, 8, 2>(CSA_BWD_ARGS);
       case 16: return launch_bwd_t<128, 16, 2>(CSA_BWD_ARGS);
+      case 32: return launch_bwd_t<128, 32, 2, 16>(CSA_BWD_ARGS);
+      case 64: return launch_bwd_t<128, 64, 2, 16>(CSA_BWD_ARGS);
     }
   }
 #undef CSA_BWD_ARGS
@@ -651,8 +662,8 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const vo
 bool indexer_bwd_supported(bool bf16, int Hi, int Di, int k_eff, bool sparse, int max_seqlen_k) {
   if (!bf16) return false;
   if ((sparse ? k_eff : max_seqlen_k) > 64 * 64) return false;   // score-gradient slots per row
-  if (Di == 64) return Hi == 4 || Hi == 8 || Hi == 16 || Hi == 32;
-  if (Di == 128) return Hi == 4 || Hi == 8 || Hi == 16;
+  if (Di == 64) return Hi == 4 || Hi == 8 || Hi == 16 || Hi == 32 || Hi == 64;
+  if (Di == 128) return Hi == 4 || Hi == 8 || Hi == 16 || Hi == 32 || Hi == 64;
   return false;
 }
 

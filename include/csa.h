@@ -291,8 +291,8 @@ csa_status_t csa_loss_reduce(const float *kl_row, int32_t total_q, int32_t per_t
  *   Hi, Di) bytes (may be NULL when that is 0), caller-owned, contents undefined after
  *   the call; it holds per-chunk partial sums of dk_idx, which a last kernel adds in a
  *   fixed order.  A smaller workspace is CSA_ERR_INVALID.
- * Supported: dt = CSA_BF16; Di = 64 with Hi in {4, 8, 16, 32}, or Di = 128 with Hi in
- * {4, 8, 16}; sparse k_eff <= 4096, dense max_seqlen_k <= 4096.
+ * Supported: dt = CSA_BF16; Di in {64, 128} with Hi in {4, 8, 16, 32, 64}; sparse
+ * k_eff <= 4096, dense max_seqlen_k <= 4096.
  */
 csa_status_t csa_indexer_loss_bwd(const csa_layout_t *L, int32_t sparse_loss,
                                   const void *q_idx, const void *k_idx, const float *weights,

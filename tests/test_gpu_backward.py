@@ -62,18 +62,20 @@ def _gpu(inp, grad_loss=1.0, per_token=False, res=None):
 
 
 def _oracle_rows(P, res, rows):
-    """RowResults of `rows` on the GPU's scores and ids, with the GPU's teacher."""
+    """RowResults of `rows` on the GPU's scores and ids, with the GPU's teacher (host copies
+    of those rows only)."""
     L = P.layout
-    ids = res["ids"].cpu().numpy().astype(np.int64)
-    sc = B.host(res["scores"])
-    te = B.host(res["teacher"])
+    ids = B.RowMap(res["ids"], rows)
+    sc = B.RowMap(res["scores"], rows)
+    te = B.RowMap(res["teacher"], rows)
     out = []
     for t in rows:
         g = oracle.row_geometry(L, t)
         s_k = int(L.cu_k[g.seg + 1] - L.cu_k[g.seg])
-        r = oracle.run_row(P, t, ids_override=ids[t], scores_override=sc[t, :s_k])
+        ids_t = ids[t].astype(np.int64)
+        r = oracle.run_row(P, t, ids_override=ids_t, scores_override=sc[t][:s_k])
         if g.n_valid > 0:
-            r.teacher = te[t, :ids.shape[1]].copy() if P.sparse_loss else te[t, :g.n_valid].copy()
+            r.teacher = te[t][:ids_t.shape[0]].copy() if P.sparse_loss else te[t][:g.n_valid].copy()
         out.append(r)
     return out
 
@@ -102,7 +104,8 @@ def test_small_workloads_every_element(gpu_ok, name):
     _close(f"{name} dk", B.host(dk), rdk)
 
 
-@pytest.mark.parametrize("Hi,Di", [(4, 64), (8, 64), (32, 64), (4, 128), (8, 128), (16, 128)])
+@pytest.mark.parametrize("Hi,Di", [(4, 64), (8, 64), (32, 64), (64, 64), (4, 128), (8, 128), (16, 128),
+                                   (32, 128), (64, 128)])
 def test_every_supported_indexer_shape(gpu_ok, Hi, Di):
     """Each (Hi, Di) the backward supports, every element, on a ragged two-segment batch
     (q rows of 4 x 64 bf16 are 512 bytes: the staging path for rows under 1 KiB)."""
@@ -205,3 +208,54 @@ def test_full_workloads_sampled(gpu_ok, index):
         for c, v in zip(cols[sel], dk_c):
             ref[kpos[int(c)]] += v
     _close(f"{wl.name} dk keys", B.host(dk[keys]), ref)
+
+
+def test_long_context_sampled(gpu_ok):
+    """The long-context workload (64 indexer heads x 128 dims, 16384 compressed keys, top-k
+    2048): dq/dweights on sampled rows, dk on keys of the tail of the key range (each seen
+    by a few thousand rows' supports), from host copies of only the rows involved."""
+    wl = I.WORKLOADS[3]
+    inp = I.make_inputs(wl, device="cuda")
+    res, dq, dw, dk = _gpu(inp)
+    T = wl.total_q
+    rows = I.sample_rows(wl, 16)
+    P = B.problem_of(inp, rows)
+    rdq, rdw = [], []
+    for r in _oracle_rows(P, res, rows):
+        cols, tch, prd = oracle.loss_support(P, r)
+        g = r.geom
+        seg_k = slice(g.k_base, int(P.layout.cu_k[g.seg + 1]))
+        gs = oracle.kl_grad_scores(tch, prd) / T
+        dq_t, dw_t, _ = oracle.indexer_grads_row(P.q_idx[r.t], P.weights[r.t], P.k_idx[seg_k],
+                                                 P.idx_scale, cols, gs)
+        rdq.append(dq_t)
+        rdw.append(dw_t)
+    idx = torch.tensor(rows, device="cuda")
+    _close("long-64k dq rows", B.host(dq.index_select(0, idx)), np.stack(rdq))
+    _close("long-64k dw rows", B.host(dw.index_select(0, idx)), np.stack(rdw))
+    # dk: every row whose support holds one of the keys, found on the GPU
+    keys = [12000, 16000, 16383]
+    kt = torch.tensor(keys, device="cuda", dtype=res["ids"].dtype)
+    hit = (res["ids"].unsqueeze(-1) == kt).any(-1).any(-1)
+    krows = torch.nonzero(hit).flatten().tolist()
+    assert len(krows) > 100, len(krows)
+    k_idx = B.host(inp.k_idx)
+    ref = np.zeros((len(keys), k_idx.shape[1]))
+    kpos = {k: i for i, k in enumerate(keys)}
+    for b0 in range(0, len(krows), 1024):
+        part = krows[b0:b0 + 1024]
+        pi = torch.tensor(part, device="cuda")
+        ids_p = res["ids"].index_select(0, pi)
+        sc_p = B.host(torch.gather(res["scores"].index_select(0, pi), 1, ids_p.clamp(min=0).long()))
+        te_p = B.host(res["teacher"].index_select(0, pi)[:, :ids_p.shape[1]])
+        q_p, w_p = B.host(inp.q_idx.index_select(0, pi)), B.host(inp.weights.index_select(0, pi))
+        ids_p = ids_p.cpu().numpy().astype(np.int64)
+        for i in range(len(part)):
+            valid = ids_p[i] >= 0
+            cols = ids_p[i][valid]          # one segment: global ids are local ids
+            sel = np.isin(cols, keys)
+            gs = oracle.kl_grad_scores(te_p[i][valid], oracle.predictor(sc_p[i][valid])) / T
+            _, _, dk_c = oracle.indexer_grads_row(q_p[i], w_p[i], k_idx, inp.idx_scale, cols[sel], gs[sel])
+            for c, v in zip(cols[sel], dk_c):
+                ref[kpos[int(c)]] += v
+    _close("long-64k dk keys", B.host(dk[keys]), ref)
