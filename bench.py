@@ -27,10 +27,12 @@ Measurement tools (the profiles' summaries are made with these):
   python bench.py prof-summary stats <stats_dir> <out.txt> --cmd "<command>"
   python bench.py prof-summary traffic <workload> <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <out_prefix> --cmd "<command>"
+  python bench.py prof-summary counters <workload> <counter_dir> <out.txt> --cmd "<command>"
         rocprofv3 CSV output (run_kernel_stats.csv of --kernel-trace --stats;
         run_counter_collection.csv of one --pmc FETCH_SIZE or WRITE_SIZE pass) turned
         into the short summaries of profiles/ and the per-kernel HBM traffic table that
-        the JSON line's roofline.traffic reads.
+        the JSON line's roofline.traffic reads; a --pmc pass of the SQ counters into the
+        per-kernel LDS bank-conflict ratio and MFMA busy fraction.
 """
 from __future__ import annotations
 
@@ -634,7 +636,7 @@ def prof_traffic(wl: str, fdir: str, wdir: str, cfdir: str, cwdir: str, prefix: 
             continue
         wv = wm.get(name, 0.0)
         rd, wr = fv * fs, wv * ws
-        src = os.path.join(KSRC, FAMILIES[fam][1])
+        src = os.path.join(KSRC, "sparse_attn_wide.hip" if "sparse_attn_wide" in name else FAMILIES[fam][1])
         table[fam] = {"kernel": _short(name), "dispatches": fn[name], "fetch_counter": fv, "write_counter": wv,
                       "read_bytes": rd, "write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
                       "source": os.path.relpath(src, ROOT), "source_sha256": _sha256(src)}
@@ -642,6 +644,32 @@ def prof_traffic(wl: str, fdir: str, wdir: str, cfdir: str, cwdir: str, prefix: 
     doc = {"workload": wl, "command": cmd, "fetch_scale": fs, "write_scale": ws, "kernels": table}
     json.dump(doc, open(prefix + ".json", "w"), indent=1)
     open(prefix + ".txt", "w").write("\n".join(lines) + "\n")
+
+
+# SQ counters of the counter summaries; the MFMA busy fraction is
+# SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES) (busy cycles summed over the 4 SIMDs of
+# every CU against the busy cycles summed over the CUs)
+SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
+               "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS")
+
+
+def prof_counters(wl: str, cdir: str, out: str, cmd: str) -> None:
+    """Per-kernel means per dispatch of the SQ counters of one --pmc pass, with the LDS
+    bank-conflict ratio and the MFMA busy fraction."""
+    means = {c: _counter_means(cdir, c) for c in SQ_COUNTERS}
+    names = sorted({k for m, _ in means.values() for k in m if _family_of(k)})
+    lines = [f"# SQ counters per launch, workload {wl}", f"# command: {cmd}",
+             "# lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE;"
+             " mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES)", ""]
+    for k in names:
+        v = {c: means[c][0].get(k, 0.0) for c in SQ_COUNTERS}
+        n = max(means[c][1].get(k, 0) for c in SQ_COUNTERS)
+        conf = v["SQ_LDS_BANK_CONFLICT"] / v["SQ_LDS_IDX_ACTIVE"] if v["SQ_LDS_IDX_ACTIVE"] else 0.0
+        busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * v["SQ_BUSY_CU_CYCLES"]) if v["SQ_BUSY_CU_CYCLES"] else 0.0
+        lines.append(f"{_short(k)}  (dispatches {n})")
+        lines.append(f"    lds_conflict {conf:.4f}   mfma_busy {busy:.3f}")
+        lines.append("    " + "  ".join(f"{c[3:]}={v[c]:.4g}" for c in SQ_COUNTERS))
+    open(out, "w").write("\n".join(lines) + "\n")
 
 
 def tools_main(argv):
@@ -658,11 +686,17 @@ def tools_main(argv):
     for a in ("workload", "fetch_dir", "write_dir", "copy_fetch_dir", "copy_write_dir", "out_prefix"):
         t.add_argument(a)
     t.add_argument("--cmd", required=True)
+    c = pm.add_parser("counters")
+    for a_ in ("workload", "counter_dir", "out"):
+        c.add_argument(a_)
+    c.add_argument("--cmd", required=True)
     a = ap.parse_args(argv)
     if a.tool == "copy-probe":
         copy_probe()
     elif a.mode == "stats":
         prof_stats(a.stats_dir, a.out, a.cmd)
+    elif a.mode == "counters":
+        prof_counters(a.workload, a.counter_dir, a.out, a.cmd)
     else:
         prof_traffic(a.workload, a.fetch_dir, a.write_dir, a.copy_fetch_dir, a.copy_write_dir, a.out_prefix,
                      a.cmd)

@@ -625,6 +625,11 @@ hipError_t launch_indexer_topk(const LaunchLayout &LL, const void *q_idx, const 
 constexpr int HGK_TOK = 64;
 constexpr int HGK_KEYS = 128;
 constexpr int HGK_WAVES = 8;
+// The staged weights [Hi][64 tokens]: token tt of head h sits at h * 64 + (tt ^ wsw(h)).
+// The staging writes go across heads (lane = head), which without the XOR would put all 64
+// lanes on one LDS bank; the XOR is a multiple of 4, so the 4 tokens a lane reads as one
+// f32x4 stay one aligned group.
+__device__ __forceinline__ int wsw(int h) { return 4 * (h & 15); }
 
 template <int DI>
 __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(4))) void indexer_score_hg_kernel(
@@ -638,7 +643,7 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   constexpr int NTHR = 64 * HGK_WAVES;
   static_assert(PB == 512 && CPP >= 16, "512-byte staged rows");
   __shared__ __attribute__((aligned(16))) u32x4 qs[2][HGK_TOK * CPP];
-  extern __shared__ __attribute__((aligned(16))) float wsl[];   // [Hi][HGK_TOK]
+  extern __shared__ __attribute__((aligned(16))) float wsl[];   // [Hi][HGK_TOK], tokens XOR wsw(h)
 
   // Workgroup id -> tile, XCD-aware: workgroups are dealt to the 8 XCDs round-robin by id,
   // so id = 8 * slot + xcd; token block b goes to XCD b % 8, and an XCD's consecutive slots
@@ -714,7 +719,7 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
         const int e = e0 + u * NTHR;
         if (e < Hi * HGK_TOK) {
           const int tt = e / Hi, h = e - tt * Hi;
-          wsl[h * HGK_TOK + tt] = x[u] * idx_scale;
+          wsl[h * HGK_TOK + (tt ^ wsw(h))] = x[u] * idx_scale;
         }
       }
     }
@@ -742,7 +747,8 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
       for (int c = 0; c < NCD; ++c)
 #pragma unroll
         for (int n = 0; n < 4; ++n) d[n] = mfma16x16x32(qa[c], kb[n][c], d[n]);
-      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsl + (grp * HG + hl) * HGK_TOK + tw * 16 + 4 * g);
+      const int hw = grp * HG + hl;
+      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsl + hw * HGK_TOK + ((tw * 16 + 4 * g) ^ wsw(hw)));
 #pragma unroll
       for (int n = 0; n < 4; ++n)
 #pragma unroll

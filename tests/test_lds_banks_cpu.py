@@ -1,0 +1,252 @@
+"""CPU model of the gfx950 LDS bank rules, checked against the LDS layouts of the kernels.
+
+The rules, measured on MI355X with the SQ_LDS_BANK_CONFLICT counter on probe kernels of
+their own (and restated in csrc/kernels/common.h beside row_swz):
+
+* 16-byte accesses (ds_read_b128 / ds_write_b128) are served a quarter wave per cycle;
+  the quarter of lane l is (l >> 5, parity of bits 2, 3 and 4 of l), i.e. lanes
+  {0-3, 12-15, 20-23, 24-27} and {4-11, 16-19, 28-31} of each half wave.  Two lanes of a
+  quarter conflict when they address the same 16-byte slot of a 256-byte line
+  ((addr >> 4) & 15) at different addresses (one address read by several lanes is a
+  broadcast).
+* 8-byte transposing reads (ds_read_b64_tr_b16) are served 32 consecutive lanes per cycle
+  over the 32 8-byte words of a line ((addr >> 3) & 31).
+* 4-byte accesses (not probed; the usual model): 64 lanes per cycle over 64 banks of
+  4 bytes ((addr >> 2) & 63).
+
+Each pattern below restates a kernel's address arithmetic (the file and the names are
+given) and checks two things: the lane reads the element the kernel means (the storage
+rule: 16-byte piece p of tile row R at piece slot p ^ row_swz(R)), and the access takes
+the minimum number of cycles.  A plausible slip (a dropped swizzle term, a row of the
+wrong half) fails one of them; tests plant such slips to show it.
+"""
+import pytest
+
+
+# ---------------------------------------------------------------- the rules
+def quarter_of(lane):
+    return (lane >> 5, ((lane >> 2) ^ (lane >> 3) ^ (lane >> 4)) & 1)
+
+
+def cycles_b128(addrs):
+    """Cycles of one 16-byte access of the 64 lanes (lane l accesses addrs[l]; None = off)."""
+    groups = {}
+    for lane, a in enumerate(addrs):
+        if a is not None:
+            groups.setdefault(quarter_of(lane), []).append(a)
+    total = 0
+    for lst in groups.values():
+        per_slot = {}
+        for a in lst:
+            per_slot.setdefault((a >> 4) & 15, set()).add(a)
+        total += max(len(v) for v in per_slot.values())
+    return total
+
+
+def cycles_tr64(addrs):
+    total = 0
+    for h in (0, 1):
+        per_word = {}
+        for lane in range(32 * h, 32 * h + 32):
+            a = addrs[lane]
+            per_word.setdefault((a >> 3) & 31, set()).add(a)
+        total += max(len(v) for v in per_word.values())
+    return total
+
+
+def cycles_b32(addrs):
+    per_bank = {}
+    for a in addrs:
+        if a is not None:
+            per_bank.setdefault((a >> 2) & 63, set()).add(a)
+    return max(len(v) for v in per_bank.values())
+
+
+def quarters_used(addrs):
+    return len({quarter_of(l) for l, a in enumerate(addrs) if a is not None})
+
+
+# ---------------------------------------------------------------- the layouts
+def row_swz(D, r):
+    """row_swz<D> of csrc/kernels/common.h."""
+    if D in (64, 192):
+        return (2 * ((r >> 1) & 3)) ^ (5 * ((r >> 3) & 1))
+    return (2 * (r & 7)) ^ (9 * ((r >> 3) & 1))
+
+
+def slot_of(D, R, piece):
+    """Byte offset in a tile of the 16-byte piece `piece` of row R."""
+    return R * 2 * D + 16 * (piece ^ row_swz(D, R))
+
+
+LANES = range(64)
+D_ALL = (64, 128, 192, 256, 512)
+
+
+# ---------------------------------------------------------------- generic row_swz claims
+@pytest.mark.parametrize("D", D_ALL)
+def test_row_operand_reads(D):
+    """Lane (g, r) reads piece 4c + g of row r (and of row r + 16): the MFMA K operand."""
+    for c in range(D // 32):
+        for r0 in (0, 16):
+            addrs = [slot_of(D, r0 + (l & 15), 4 * c + (l >> 4)) for l in LANES]
+            assert cycles_b128(addrs) == quarters_used(addrs), (D, c, r0)
+
+
+@pytest.mark.parametrize("D", D_ALL)
+def test_transposing_reads(D):
+    """Lane (g, r) reads 8 bytes of piece 2dt + ((r & 3) >> 1) of row 4g + r // 4 (and of
+    the row 16 below): the V^T operand of O^T += V^T P^T."""
+    for dt in range(D // 16):
+        for r0 in (0, 16):
+            addrs = []
+            for l in LANES:
+                g, r = l >> 4, l & 15
+                R = r0 + 4 * g + (r >> 2)
+                addrs.append(slot_of(D, R, 2 * dt + ((r & 3) >> 1)) + 8 * (r & 1))
+            assert cycles_tr64(addrs) == 2, (D, dt, r0)
+
+
+@pytest.mark.parametrize("D", (64, 128, 256, 512))
+def test_row_staging_writes(D):
+    """A 1 KiB buffer->LDS load covering whole rows: lane l writes piece l % (D/8) of row
+    i * RPI + l // (D/8)."""
+    ppr, rpi = D // 8, 512 // D
+    for i in range(32 // rpi):
+        addrs = [slot_of(D, i * rpi + l // ppr, l % ppr) for l in LANES]
+        assert cycles_b128(addrs) == 4, (D, i)
+
+
+# ---------------------------------------------------------------- sparse_attn_wide.hip
+def wide_k_read(lane, c, kt, swz=row_swz):
+    """sparse_attn_wide.hip qk(): tile + kbj[c & 3] + 256 (c >> 2) (+ 16 rows for kt = 1)."""
+    g, r16 = lane >> 4, lane & 15
+    ksw = swz(512, r16)
+    kbj = 16 * (g ^ (ksw & 3)) + 64 * ((c & 3) ^ (ksw >> 2))
+    return r16 * 1024 + kbj + 256 * (c >> 2) + kt * 16 * 1024
+
+
+def wide_v_read(lane, w, dt, half, swz=row_swz):
+    """sparse_attn_wide.hip pv_read_v(): vbase + 32 ((8 w + dt) ^ vx) (+ 16 rows)."""
+    g, r16 = lane >> 4, lane & 15
+    rho = 4 * g + (r16 >> 2)
+    vsw = swz(512, rho)
+    vbase = rho * 1024 + 16 * (((r16 & 3) >> 1) ^ (vsw & 1)) + 8 * (r16 & 1)
+    return vbase + 32 * ((8 * w + dt) ^ (vsw >> 1)) + half * 16 * 1024
+
+
+def psw(r16):
+    """sparse_attn_wide.hip: P row swizzle of rows 16x + r16."""
+    return (2 * ((r16 >> 2) & 1)) ^ (3 * ((r16 >> 3) & 1))
+
+
+def test_wide_k_reads_address_and_banks():
+    for c in range(16):
+        for kt in (0, 1):
+            addrs = [wide_k_read(l, c, kt) for l in LANES]
+            want = [slot_of(512, 16 * kt + (l & 15), 4 * c + (l >> 4)) for l in LANES]
+            assert addrs == want, (c, kt)
+            assert cycles_b128(addrs) == 4, (c, kt)
+
+
+def test_wide_v_reads_address_and_banks():
+    for w in range(4):
+        for dt in range(8):
+            for half in (0, 1):
+                addrs = [wide_v_read(l, w, dt, half) for l in LANES]
+                want = []
+                for l in LANES:
+                    g, r = l >> 4, l & 15
+                    R = 16 * half + 4 * g + (r >> 2)
+                    want.append(slot_of(512, R, 2 * (8 * w + dt) + ((r & 3) >> 1)) + 8 * (r & 1))
+                assert addrs == want, (w, dt, half)
+                assert cycles_tr64(addrs) == 2, (w, dt, half)
+
+
+def test_wide_p_buffer_reads_and_writes():
+    """P [128 heads][32 keys] bf16, 64-byte rows, 16-byte key block b of row h at b ^ psw:
+    the P^T operand reads (lane (g, r16): block g of row 16 ht + r16) and the writes of
+    the wave's two head tiles (row 32 w + 16 hi + r16, block g)."""
+    for ht in range(8):
+        addrs = [(16 * ht + (l & 15)) * 64 + 16 * ((l >> 4) ^ psw(l & 15)) for l in LANES]
+        assert cycles_b128(addrs) == 4, ht
+    for w in range(4):
+        for hi in range(2):
+            addrs = [(32 * w + 16 * hi + (l & 15)) * 64 + 16 * ((l >> 4) ^ psw(l & 15)) for l in LANES]
+            assert cycles_b128(addrs) == 4, (w, hi)
+            # every (row, block) written once: the reads find what the writes put there
+            assert len(set(addrs)) == 64
+
+
+def test_wide_cmass_partials():
+    """cm_part[w][slot]: lane r16 (even) of group g stores the head sum of key
+    16 (el >> 2) + 4 g + (el & 3), el = sum8_index(r16); the other lanes store to the
+    spare slot 32.  The 32 keys are written once each over the wave, and the cross-wave
+    flush (lane tid < 32 reads slot tid of every wave) is one bank per lane."""
+    def sum8_index(r):
+        return 4 * ((r >> 3) & 1) + 2 * ((r >> 2) & 1) + ((r >> 1) & 1)
+    slots = []
+    for l in LANES:
+        g, r16 = l >> 4, l & 15
+        el = sum8_index(r16)
+        slots.append(16 * (el >> 2) + 4 * g + (el & 3) if r16 % 2 == 0 else 32)
+    assert sorted(s for s in slots if s != 32) == list(range(32))
+    for w in range(4):
+        reads = [(w * 33 + t) * 4 if t < 32 else None for t in LANES]
+        assert cycles_b32(reads) == 1
+
+
+# ---------------------------------------------------------------- indexer_score.hip
+def test_indexer_hg_q_operand_reads():
+    """indexer_score_hg_kernel: staged q rows of 512 bytes, chunk q of token row r at
+    slot q ^ (r % 16); lane (g, r16) reads chunk hl * Di / 8 + 4 c + g of row 16 tw + r16."""
+    for Di in (64, 128):
+        for tw in range(4):
+            for hl in range(256 // Di):
+                for c in range(Di // 32):
+                    addrs = [(16 * tw + (l & 15)) * 512 + 16 * ((hl * Di // 8 + 4 * c + (l >> 4)) ^ (l & 15))
+                             for l in LANES]
+                    assert cycles_b128(addrs) == 4, (Di, tw, hl, c)
+
+
+def wsw(h):
+    """indexer_score.hip: token XOR of the staged weights of head h."""
+    return 4 * (h & 15)
+
+
+def test_indexer_hg_weight_staging():
+    """The staged weights [Hi][64 tokens]: the staging writes (64 consecutive elements of
+    the [tokens, Hi] run, head fastest) spread over at least 16 banks, and each lane's
+    f32x4 read of tokens 16 tw + 4 g .. + 3 of head h is one aligned group holding exactly
+    those tokens."""
+    for Hi in (32, 64):
+        for e0 in range(0, Hi * 64, 64):
+            addrs = []
+            for e in range(e0, e0 + 64):
+                tt, h = divmod(e, Hi)
+                addrs.append(4 * (h * 64 + (tt ^ wsw(h))))
+            assert cycles_b32(addrs) <= 4, (Hi, e0)
+            # the unswizzled layout: every lane of a 64-head run on one bank
+            if Hi == 64:
+                assert cycles_b32([4 * (h * 64 + e0 // 64) for h in range(64)]) == 64
+        for h in range(Hi):
+            for tw in range(4):
+                for g in range(4):
+                    base = (16 * tw + 4 * g) ^ wsw(h)
+                    assert base % 4 == 0
+                    assert {(base + i) ^ wsw(h) for i in range(4)} == {16 * tw + 4 * g + i for i in range(4)}
+
+
+# ---------------------------------------------------------------- the model catches slips
+def test_planted_slips_are_caught():
+    """A dropped swizzle term, a K row taken from the wrong half, or a P row swizzle of
+    zero each fail one of the checks above."""
+    no_swz = lambda D, r: 0
+    conflicted = any(cycles_b128([wide_k_read(l, c, 0, no_swz) for l in LANES]) > 4 for c in range(16))
+    assert conflicted
+    wrong_half = [wide_k_read(l, 0, 1) - 16 * 1024 * ((l >> 4) & 1) for l in LANES]
+    assert wrong_half != [slot_of(512, 16 + (l & 15), l >> 4) for l in LANES]
+    p_plain = [(l & 15) * 64 + 16 * (l >> 4) for l in LANES]
+    assert cycles_b128(p_plain) > 4
+    tr_noswz = any(cycles_tr64([wide_v_read(l, 0, dt, 0, no_swz) for l in LANES]) > 2 for dt in range(8))
+    assert tr_noswz
