@@ -63,10 +63,12 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="path: score and top-k as two calls (the score matrix stored) even where "
                          "the fused call applies")
-    ap.add_argument("--two-call-attn", action="store_true",
-                    help="path: csa_sparse_attn_fwd + csa_indexer_teacher_kl even where the one-call "
-                         "attention + teacher/KL kernel applies (csa_sparse_attn_kl_fwd, then "
-                         "csa_loss_reduce: the default there, ~2%% faster on bshd-b2-s4096)")
+    ap.add_argument("--one-call-attn", action="store_true",
+                    help="path: the one-call attention + teacher/KL kernel (csa_sparse_attn_kl_fwd, then "
+                         "csa_loss_reduce) where it applies, instead of csa_sparse_attn_fwd + "
+                         "csa_indexer_teacher_kl (the default: on bshd-b2-s4096 the two calls' kernels "
+                         "take 82 us against 88 us, since the fp64 predictor and log-ratios of the KL "
+                         "cost the one-wave-per-query kernel more than the teacher kernel)")
     ap.add_argument("--cp", type=int, default=8, help="cp-share: CP size")
     ap.add_argument("--rank", type=int, default=0, help="cp-share: rank")
     return ap.parse_args()
@@ -429,7 +431,7 @@ def main():
     # sparse loss on shapes the one-wave-per-query kernel takes (bf16, H <= 16, D of 64 or
     # 128, a window, k_eff <= 256, the selected scores of the fused top-k): attention,
     # teacher and KL in one call, the loss reduced by its own call
-    attn_kl = (wl.sparse_loss and not args.two_call_attn and sel is not None and wl.dtype != "f32"
+    attn_kl = (wl.sparse_loss and args.one_call_attn and sel is not None and wl.dtype != "f32"
                and wl.H <= 16 and wl.D in (64, 128) and wl.window > 0 and k_eff <= 256)
     att_name = "sparse_attn_kl" if attn_kl else "sparse_attn"
     names = (("indexer_topk",) if fused else ("indexer_score", "topk")) + \

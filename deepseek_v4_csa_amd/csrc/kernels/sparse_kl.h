@@ -26,12 +26,31 @@ struct KlArgs {
 
 // The predictor's exponential e^(s - mx) in fp64 (s and mx are fp32, so the difference is
 // exact) and one KL term t (log(t + eps) - log(p + eps)) = t log1p((t - p) / (p + eps))
-// in fp64, with the device library's exp and log1p.  For nearly equal t and p the KL is
-// second order in t - p, so p must carry far more than fp32's 24 bits for the KL of such a
-// row to keep 1e-5 relative accuracy; an error in the sum of the e_j shifts the KL by the
-// same amount in absolute terms.
+// in fp64.  For nearly equal t and p the KL is second order in t - p, so p must carry far
+// more than fp32's 24 bits for the KL of such a row to keep 1e-5 relative accuracy; an
+// error in the sum of the e_j shifts the KL by the same amount in absolute terms.
 constexpr double KL_EPS = 1e-10;
-__device__ __forceinline__ double pred_exp(float s, float mx) { return exp((double)s - (double)mx); }
+// e^d for d <= 0: d log2(e) = n + f with n = rint(d log2(e)) and |f| <= 1/2, so
+// e^d = 2^n e^x with x = f ln 2, |x| <= 0.35, and e^x is its Taylor series to degree 10
+// (truncation below 3e-13 relative); arguments below -1100 log 2 give 0.
+__device__ __forceinline__ double exp_nonpos_f64(double d) {
+  const double y = fmax(d * 1.4426950408889634074, -1100.0);
+  const double n = rint(y);
+  const double x = (y - n) * 0.69314718055994530942;
+  double p = 1.0 / 3628800.0;
+  p = fma(p, x, 1.0 / 362880.0);
+  p = fma(p, x, 1.0 / 40320.0);
+  p = fma(p, x, 1.0 / 5040.0);
+  p = fma(p, x, 1.0 / 720.0);
+  p = fma(p, x, 1.0 / 120.0);
+  p = fma(p, x, 1.0 / 24.0);
+  p = fma(p, x, 1.0 / 6.0);
+  p = fma(p, x, 0.5);
+  p = fma(p, x, 1.0);
+  p = fma(p, x, 1.0);
+  return ldexp(p, (int)n);
+}
+__device__ __forceinline__ double pred_exp(float s, float mx) { return exp_nonpos_f64((double)s - (double)mx); }
 // log(1 + x), x > -1.  For |x| < 1/2 from log(1 + x) = 2 atanh(u), u = x / (2 + x), |u| < 1/3:
 // 2 (u + u^3/3 + ... + u^27/27), truncation below 1e-14 relative (the log-ratios of a KL row
 // are small, so this is the common case); otherwise the device library's log1p.
