@@ -141,8 +141,9 @@ def cpu_baseline(inp, seconds):
     import oracle
     from deepseek_v4_csa_amd.inputs import uniform_rows
     wl = inp.wl
-    # at most ~512 MB of q rows on the host
-    n = min(wl.total_q, 4096, max(256, int(5e8 / (wl.H * wl.D * 8))))
+    # enough rows for the time target on every workload, at most ~1.6 GB of fp64 q rows
+    # on the host (long-64k: 3,051 rows of 512 KiB)
+    n = min(wl.total_q, 4096, max(256, int(1.6e9 / (wl.H * wl.D * 8))))
     order = uniform_rows(wl.total_q, n, seed=11)
     P = _oracle_problem(inp, order)
     rng = np.random.default_rng(11)
