@@ -177,7 +177,8 @@ csa_status_t csa_indexer_topk(const csa_layout_t *L, const void *q_idx, const vo
   if (!csa::indexer_topk_supported(dt == CSA_BF16, Hi, Di, L->max_seqlen_k))
     return fail(CSA_ERR_UNSUPPORTED,
                 "%s: no fused kernel for dtype=%d Hi=%d Di=%d max_seqlen_k=%d (bf16 (Hi, Di) in {(8,64), "
-                "(16,64), (4,128), (8,128)} with the score rows of two 16-token blocks in 160 KiB of LDS)",
+                "(16,64), (4,128), (8,128), (32,64), (64,64), (16,128), (32,128)} with the block's score "
+                "rows in 160 KiB of LDS)",
                 fn, (int)dt, Hi, Di, L->max_seqlen_k);
   return hip_status(csa::launch_indexer_topk(LL, q_idx, k_idx, weights, Hi, Di, idx_scale, k_eff_of(L, topk),
                                              ids, sel_scores, row_lse, static_cast<hipStream_t>(stream)),

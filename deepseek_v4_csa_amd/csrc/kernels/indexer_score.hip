@@ -587,6 +587,273 @@ static hipError_t launch_fused_v(const LaunchLayout &LL, const void *q_idx, cons
   return hipErrorInvalidValue;
 }
 
+
+// ---------------------------------------------------------------- fused, head-grouped
+// Fused score + top-k for q rows too long for the paired-block kernel to stage whole
+// (HI * DI * 2 above 2 KiB: thd-varlen-16k's 32 x 64).  One workgroup (8 waves) per
+// 16-token block, heaviest blocks first.  The heads are taken HGF at a time: the block's q
+// slice of a head group is staged in LDS (chunk q of row r at slot q ^ r, as in the
+// paired-block kernel), and every wave runs the group's heads over its key tiles,
+// continuing each (token, key) accumulator from the block's LDS score row where the
+// previous group left it -- so the heads are summed in the same order, with the same
+// fused multiply-adds, as in the score kernels, and the scores are bit-identical.  Then
+// one wave per row selects from LDS (wave_select, as in the paired-block kernel).
+template <int DI, int HI, int HGF> constexpr int grouped_static_bytes() {
+  return IXL_TOK * HGF * DI * 2 + HI * IXL_TOK * 4;
+}
+
+template <int DI, int HI, int HGF, int VPL>
+__global__ __launch_bounds__(64 * IXL_WAVES) void indexer_topk_grouped_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
+    const float *__restrict__ weights, float idx_scale, int max_sk, int total_q, TopkOut to) {
+  constexpr int RB = HI * DI * 2;     // bytes of one token's q_idx row
+  constexpr int GB = HGF * DI * 2;    // bytes of it in one head group
+  constexpr int CPG = GB / 16;        // 16-byte chunks per staged row
+  constexpr int PPG = GB / 1024;      // 1 KiB pieces per staged row
+  constexpr int CH = DI / 8;          // 16-byte chunks per head
+  constexpr int NCD = DI / 32;
+  constexpr int NG = HI / HGF;
+  constexpr int NTHR = 64 * IXL_WAVES;
+  static_assert(HI % HGF == 0 && GB % 1024 == 0 && CPG >= 16, "head groups of whole KiB pieces");
+  __shared__ __attribute__((aligned(16))) u32x4 qs[IXL_TOK * CPG];
+  __shared__ __attribute__((aligned(16))) float ws[HI * IXL_TOK];   // [h][token]
+  extern __shared__ __attribute__((aligned(16))) float score_lds[];  // rows, then histograms
+
+  const int seg = blockIdx.x % L.num_seqs;
+  const int rev = (int)(blockIdx.x / L.num_seqs);
+  const int q_start = __ldg(L.cu_q + seg);
+  const int q_len = __ldg(L.cu_q + seg + 1) - q_start;
+  const int nqb = (q_len + IXL_TOK - 1) / IXL_TOK;
+  if (rev >= nqb) return;
+  const int t0 = (nqb - 1 - rev) * IXL_TOK;
+  const int k_base = __ldg(L.cu_k + seg);
+  const int s_k = __ldg(L.cu_k + seg + 1) - k_base;
+  const int off = seg_offset(L, seg, q_len, s_k);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nlive = (n_valid_of(min(t0 + IXL_TOK, q_len) - 1, off, L.ratio, s_k) + 63) / 64;
+  if (nlive == 0) {   // no row of the block sees a key: -1 ids, -inf scores and lse
+    for (int e = tid; e < IXL_TOK * to.k_eff; e += NTHR) {
+      const int r = e / to.k_eff, c = e - r * to.k_eff;
+      if (t0 + r < q_len) {
+        to.ids[(int64_t)(q_start + t0 + r) * to.k_eff + c] = -1;
+        to.sel[(int64_t)(q_start + t0 + r) * to.k_eff + c] = -__builtin_inff();
+      }
+    }
+    if (to.lse && tid < IXL_TOK && t0 + tid < q_len) to.lse[q_start + t0 + tid] = -__builtin_inff();
+    return;
+  }
+  const int str = nlive * 64 + 4;   // score row stride (the four token groups of a store hit different banks)
+  auto row_ptr = [&](int r) { return score_lds + r * str; };
+
+  const int rows_left = min(IXL_TOK, total_q - (q_start + t0));
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(q_idx + (int64_t)(q_start + t0) * (RB / 2), (uint32_t)(rows_left * RB));
+  auto stage = [&](int gi) {   // head group gi of the block's 16 rows -> qs
+    for (int m = w; m < IXL_TOK * PPG; m += IXL_WAVES) {
+      const int r = m / PPG, q0 = (m - r * PPG) * 64;
+      dma16(rq, reinterpret_cast<char *>(qs) + (size_t)(r * CPG + q0) * 16,
+            (uint32_t)(r * RB + gi * GB + (((q0 + lane) ^ r) << 4)));
+    }
+  };
+  stage(0);
+  // fp32(w * s_idx), head-major (unconditional loads: a token past the segment reads its
+  // last row, then is zeroed)
+  {
+    constexpr int NW = (HI * IXL_TOK + NTHR - 1) / NTHR;
+    float x[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int e = tid + k * NTHR;
+      const int tt = e / HI, h = e - tt * HI;
+      const int t = min(t0 + tt, q_len - 1);
+      x[k] = e < HI * IXL_TOK ? weights[(int64_t)(q_start + t) * HI + h] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int e = tid + k * NTHR;
+      if (e < HI * IXL_TOK) {
+        const int tt = e / HI, h = e - tt * HI;
+        ws[h * IXL_TOK + tt] = t0 + tt < q_len ? x[k] * idx_scale : 0.f;
+      }
+    }
+  }
+  // key tile fragments (MFMA B operand: lane column r16 = key, piece 4c+g); keys past the
+  // segment are clamped to its last key (their scores are never selected)
+  auto load_k = [&](int tile, u32x4 (&kb)[4][NCD]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int j = min(tile * 64 + 16 * n + r16, s_k - 1);
+      const u32x4 *kp = reinterpret_cast<const u32x4 *>(k_idx + (int64_t)(k_base + j) * DI) + g;
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) kb[n][c] = kp[4 * c];
+    }
+  };
+  const char *qrow = reinterpret_cast<const char *>(qs) + r16 * CPG * 16;
+  const float *wsp = ws + 4 * g;
+  for (int gi = 0; gi < NG; ++gi) {
+    if (gi > 0) {
+      __syncthreads();   // every wave is done with the previous group's q rows
+      stage(gi);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();     // group gi staged (and, the first time, the weights)
+    u32x4 kb[4][NCD], kbn[4][NCD];
+    if (w < nlive) load_k(w, kbn);
+    for (int u = w; u < nlive; u += IXL_WAVES) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int c = 0; c < NCD; ++c) kb[n][c] = kbn[n][c];
+      if (u + IXL_WAVES < nlive) load_k(u + IXL_WAVES, kbn);
+      // the accumulators continue where the previous head group left them
+      f32x4 acc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float *src = row_ptr(4 * g + i) + u * 64 + r16;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[n][i] = gi > 0 ? src[16 * n] : 0.f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      auto a_frag = [&](int hl, u32x4 (&qa)[NCD]) {
+#pragma unroll
+        for (int c = 0; c < NCD; ++c)
+          qa[c] = *reinterpret_cast<const u32x4 *>(qrow + (((hl * CH + 4 * c + g) ^ r16) << 4));
+      };
+      auto head_mfma = [&](const u32x4 (&qa)[NCD], f32x4 (&d)[4]) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) d[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCD; ++c)
+#pragma unroll
+          for (int n = 0; n < 4; ++n) d[n] = mfma16x16x32(qa[c], kb[n][c], d[n]);
+      };
+      auto epilogue = [&](const f32x4 (&d)[4], const f32x4 &wv) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[n][i] = fmaf(wv[i], relu_bits(d[n][i]), acc[n][i]);
+          asm volatile("" : "+v"(acc[n]));   // the epilogue of head h stays in its iteration
+        }
+      };
+      auto interleave = [&]() {
+#pragma unroll
+        for (int m = 0; m < 4 * NCD; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 32 / (4 * NCD), 0);  // then VALU
+        }
+      };
+      // two register sets alternate between "MFMAs in flight" and "epilogue"
+      u32x4 qa0[NCD], qa1[NCD];
+      f32x4 d0[4], d1[4];
+      a_frag(0, qa0);
+      head_mfma(qa0, d0);
+      if (HGF > 1) a_frag(1, qa1);
+#pragma unroll
+      for (int hl = 0; hl < HGF; hl += 2) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(wsp + (gi * HGF + hl) * IXL_TOK);
+        if (hl + 1 < HGF) {
+          head_mfma(qa1, d1);
+          if (hl + 2 < HGF) a_frag(hl + 2, qa0);
+        }
+        epilogue(d0, w0);
+        if (hl + 1 < HGF) interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        if (hl + 1 < HGF) {
+          const f32x4 w1 = *reinterpret_cast<const f32x4 *>(wsp + (gi * HGF + hl + 1) * IXL_TOK);
+          if (hl + 2 < HGF) {
+            head_mfma(qa0, d0);
+            if (hl + 3 < HGF) a_frag(hl + 3, qa1);
+          }
+          epilogue(d1, w1);
+          if (hl + 2 < HGF) interleave();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // lane (token 4g+i, key u*64 + 16n + r16) -> the block's LDS score row
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float *dst = row_ptr(4 * g + i) + u * 64 + r16;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) dst[16 * n] = acc[n][i];
+      }
+    }
+  }
+  __syncthreads();   // every score tile of the block is in LDS
+  uint32_t *hist = reinterpret_cast<uint32_t *>(score_lds + IXL_TOK * str) + 256 * w;
+  for (int r = w; r < IXL_TOK; r += IXL_WAVES) {
+    const int t = t0 + r;
+    if (t >= q_len) continue;
+    const int n = n_valid_of(t, off, L.ratio, s_k);
+    const float *row = row_ptr(r);
+    float val[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int j = v * 64 + lane;
+      val[v] = j < n ? row[j] : -__builtin_inff();
+    }
+    const int64_t o = (int64_t)(q_start + t) * to.k_eff;
+    if (to.lse) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) m = fmaxf(m, val[v]);
+      m = wave_max_dpp(m);
+      double sum = 0.0;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (v * 64 + lane < n) sum += (double)__expf(val[v] - m);
+      sum = wave_sum_f64_dpp(sum);
+      if (lane == 0) to.lse[q_start + t] = n > 0 ? m + (float)log(sum) : -__builtin_inff();
+    }
+    if (n <= to.k_eff) {   // every visible key is selected
+      for (int c = lane; c < to.k_eff; c += 64) {
+        to.ids[o + c] = c < n ? k_base + c : -1;
+        to.sel[o + c] = c < n ? row[c] : -__builtin_inff();
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rid = make_rsrc(to.ids + o, (uint32_t)to.k_eff * 4);
+      const __amdgpu_buffer_rsrc_t rsel = make_rsrc(to.sel + o, (uint32_t)to.k_eff * 4);
+      wave_select<VPL>(val, n, to.k_eff, hist, [&](int pos, int j, int v) {
+        __builtin_amdgcn_raw_buffer_store_b32(k_base + j, rid, pos * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[v]), rsel, pos * 4, 0, 0);
+      });
+    }
+  }
+}
+
+static int grouped_dyn_bytes(int max_sk) { return (IXL_TOK * ((max_sk + 63) / 64 * 64 + 4) + 256 * IXL_WAVES) * 4; }
+
+template <int DI, int HI, int HGF, int VPL>
+static hipError_t launch_grouped_t(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+                                   const float *weights, float idx_scale, const TopkOut &to, hipStream_t st) {
+  const int nqb = (LL.max_seqlen_q + IXL_TOK - 1) / IXL_TOK;
+  const int64_t grid = (int64_t)LL.num_seqs * nqb;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int dyn = grouped_dyn_bytes(LL.max_seqlen_k);
+  auto kern = indexer_topk_grouped_kernel<DI, HI, HGF, VPL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * IXL_WAVES), dyn, st, LL.dev,
+                     static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx), weights,
+                     idx_scale, LL.max_seqlen_k, LL.total_q, to);
+  return hipGetLastError();
+}
+
+template <int DI, int HI, int HGF>
+static hipError_t launch_grouped_v(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+                                   const float *weights, float idx_scale, const TopkOut &to, hipStream_t st) {
+  const int vpl = (LL.max_seqlen_k + 63) / 64;
+  if (vpl <= 4) return launch_grouped_t<DI, HI, HGF, 4>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (vpl <= 8) return launch_grouped_t<DI, HI, HGF, 8>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (vpl <= 16) return launch_grouped_t<DI, HI, HGF, 16>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (vpl <= 32) return launch_grouped_t<DI, HI, HGF, 32>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  return hipErrorInvalidValue;
+}
+
+// head-group size of the grouped kernel: 2 KiB of each q row per group
+template <int DI> constexpr int grouped_hgf() { return 1024 / DI; }
+
 bool indexer_topk_supported(bool bf16, int Hi, int Di, int max_seqlen_k) {
   // rows up to 2048 keys (Di = 64) or 512 keys (Di = 128: longer rows would spill the
   // selection's registers)
@@ -596,6 +863,10 @@ bool indexer_topk_supported(bool bf16, int Hi, int Di, int max_seqlen_k) {
   else if (Di == 64 && Hi == 16) stat = lds_static_bytes<64, 16>();
   else if (Di == 128 && Hi == 4) stat = lds_static_bytes<128, 4>();
   else if (Di == 128 && Hi == 8) stat = lds_static_bytes<128, 8>();
+  else if (Di == 64 && Hi == 32) return grouped_static_bytes<64, 32, grouped_hgf<64>()>() + grouped_dyn_bytes(max_seqlen_k) <= LDS_PER_CU;
+  else if (Di == 64 && Hi == 64) return grouped_static_bytes<64, 64, grouped_hgf<64>()>() + grouped_dyn_bytes(max_seqlen_k) <= LDS_PER_CU;
+  else if (Di == 128 && Hi == 16) return grouped_static_bytes<128, 16, grouped_hgf<128>()>() + grouped_dyn_bytes(max_seqlen_k) <= LDS_PER_CU;
+  else if (Di == 128 && Hi == 32) return grouped_static_bytes<128, 32, grouped_hgf<128>()>() + grouped_dyn_bytes(max_seqlen_k) <= LDS_PER_CU;
   else return false;
   return stat + fused_dyn_bytes(max_seqlen_k) <= LDS_PER_CU;
 }
@@ -609,6 +880,10 @@ hipError_t launch_indexer_topk(const LaunchLayout &LL, const void *q_idx, const 
   if (Di == 64 && Hi == 16) return launch_fused_v<64, 16>(LL, q_idx, k_idx, weights, idx_scale, to, st);
   if (Di == 128 && Hi == 4) return launch_fused_v<128, 4>(LL, q_idx, k_idx, weights, idx_scale, to, st);
   if (Di == 128 && Hi == 8) return launch_fused_v<128, 8>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (Di == 64 && Hi == 32) return launch_grouped_v<64, 32, grouped_hgf<64>()>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (Di == 64 && Hi == 64) return launch_grouped_v<64, 64, grouped_hgf<64>()>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (Di == 128 && Hi == 16) return launch_grouped_v<128, 16, grouped_hgf<128>()>(LL, q_idx, k_idx, weights, idx_scale, to, st);
+  if (Di == 128 && Hi == 32) return launch_grouped_v<128, 32, grouped_hgf<128>()>(LL, q_idx, k_idx, weights, idx_scale, to, st);
   return hipErrorInvalidValue;
 }
 

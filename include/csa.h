@@ -144,10 +144,15 @@ csa_status_t csa_topk(const csa_layout_t *L, const float *scores, int64_t ld_sco
  *       csa_indexer_teacher_kl / csa_indexer_loss_bwd with scores_selected = 1);
  *   row_lse [T] fp32 or NULL: log sum_{j < n_valid(t)} exp(scores[t, j]) (-inf when
  *       n_valid(t) = 0), the dense-mode predictor's normaliser.
- * Inputs as csa_indexer_score.  Supported: dt = CSA_BF16 with (Hi, Di) in {(8, 64),
- * (16, 64), (4, 128), (8, 128)}, max_seqlen_k <= 2048 (512 for Di = 128), and the q rows
- * of two 16-token blocks plus 16 score rows of 64 * (ceil(max_seqlen_k / 64) + 1) floats
- * within the 160 KiB of LDS of a compute unit (for (16, 64): max_seqlen_k <= 1024);
+ * Inputs as csa_indexer_score.  Supported: dt = CSA_BF16, max_seqlen_k <= 2048 (512 for
+ * Di = 128), and (Hi, Di) in
+ *   {(8, 64), (16, 64), (4, 128), (8, 128)} (two 16-token blocks per workgroup): the q
+ *       rows of both blocks plus 16 score rows of 64 * (ceil(max_seqlen_k / 64) + 1)
+ *       floats within the 160 KiB of LDS of a compute unit (for (16, 64):
+ *       max_seqlen_k <= 1024);
+ *   {(32, 64), (64, 64), (16, 128), (32, 128)} (one block per workgroup, the heads taken
+ *       in groups of 2 KiB of q row): 16 score rows of 64 * ceil(max_seqlen_k / 64) + 4
+ *       floats within the LDS (max_seqlen_k <= 1856 for (32, 64), <= 1792 for (64, 64));
  * other shapes return CSA_ERR_UNSUPPORTED (use the two calls).
  */
 csa_status_t csa_indexer_topk(const csa_layout_t *L, const void *q_idx, const void *k_idx,

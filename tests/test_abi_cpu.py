@@ -119,11 +119,12 @@ def test_argument_misuse_is_rejected(lib):
     fz = lib.csa_indexer_topk
     assert fz(B(L), FAKE, FAKE, FAKE, 1, 16, 64, 0.1, 0, FAKE, FAKE, None, None) == 1   # topk < 1
     assert fz(B(L), FAKE, FAKE, FAKE, 1, 16, 64, 0.1, 4, FAKE, None, None, None) == 1   # null sel
-    assert fz(B(L), FAKE, FAKE, FAKE, 1, 32, 64, 0.1, 4, FAKE, FAKE, None, None) == 2   # Hi = 32
+    assert fz(B(L), FAKE, FAKE, FAKE, 1, 24, 64, 0.1, 4, FAKE, FAKE, None, None) == 2   # Hi = 24
     assert fz(B(L), FAKE, FAKE, FAKE, 0, 16, 64, 0.1, 4, FAKE, FAKE, None, None) == 2   # fp32
     Lw = _layout(ops, total_q=8192, max_seqlen_q=8192, total_k=2048, max_seqlen_k=2048)
     assert fz(B(Lw), FAKE, FAKE, FAKE, 1, 16, 64, 0.1, 4, FAKE, FAKE, None, None) == 2  # rows too long
     assert "fused" in lib.csa_last_error().decode()
+    assert fz(B(Lw), FAKE, FAKE, FAKE, 1, 32, 64, 0.1, 4, FAKE, FAKE, None, None) == 2  # grouped: too long
     # attention + teacher/KL in one call
     akl = lib.csa_sparse_attn_kl_fwd
     args = [B(L), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 4, 64, 0.1, FAKE, 4, 1, 0,

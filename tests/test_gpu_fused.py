@@ -63,7 +63,7 @@ def _check_against_two_calls(L, inp, s, ids, fid, sel, lse, rows=None):
         assert abs(lse_h[t] - ref) <= band + 1e-6 * abs(ref) + 1e-6, (t, lse_h[t], ref)
 
 
-SHAPES = [(8, 64), (16, 64), (4, 128), (8, 128)]
+SHAPES = [(8, 64), (16, 64), (4, 128), (8, 128), (32, 64), (64, 64), (16, 128), (32, 128)]
 
 
 @pytest.mark.parametrize("Hi,Di", SHAPES)
@@ -123,10 +123,11 @@ def test_fused_two_phase_chunk_offsets(gpu_ok):
     assert torch.equal(fid, idf[c0:])
 
 
-@pytest.mark.parametrize("index", [1])
+@pytest.mark.parametrize("index", [1, 2])
 def test_fused_full_workload_forward_and_backward(gpu_ok, index):
-    """bshd-b2-s4096: fused ids / selected scores / KL / loss / backward equal the two-call
-    path bit for bit on every row; row_lse against the oracle on sampled rows."""
+    """bshd-b2-s4096 (two blocks per workgroup) and thd-varlen-16k (32 x 64: one block per
+    workgroup, heads in groups): fused ids / selected scores / KL / loss / backward equal
+    the two-call path bit for bit on every row; row_lse against the oracle on sampled rows."""
     ops = _ops()
     wl = I.WORKLOADS[index]
     inp = I.make_inputs(wl, device="cuda")
