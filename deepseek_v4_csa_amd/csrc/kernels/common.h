@@ -223,40 +223,53 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char *lds_ptr) {
   v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
   return __builtin_bit_cast(uint2, v);
 }
-// The same read issued as inline assembly.  The compiler then does not treat it as an
-// LDS access that might alias buffer-to-LDS loads still in flight (for the builtin it
-// inserts a full vmcnt wait, which would also wait for the next tile's prefetch).  The
-// result is not tracked either: the caller waits on lgkmcnt with lds_tr16_wait before use.
-__device__ __forceinline__ uint2 lds_read_tr16_nowait(const char *lds_ptr) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const lds_v4i16 *)(lds_ptr);
-  uint2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a) : "memory");
-  return r;
-}
-// the same with a constant byte offset added in the instruction's offset field
-template <int OFF> __device__ __forceinline__ uint2 lds_read_tr16_nowait_off(uint32_t lds_addr) {
-  uint2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF) : "memory");
-  return r;
-}
 __device__ __forceinline__ uint32_t lds_addr_of(const void *lds_ptr) {
   return (uint32_t)(uintptr_t)(const lds_v4i16 *)(lds_ptr);
 }
-// lgkmcnt(0), then every given value is re-defined after the wait (empty volatile asm
-// with a read-write operand), so no instruction using them can be scheduled earlier.
-template <int N> __device__ __forceinline__ void lds_tr16_wait(uint2 (&v)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+// A batch of N pairs of transposing reads (read 2k at LDS byte address a[k], read 2k + 1 at
+// a[k] + OFF2) and the wait for them, in one asm block: the results are complete when the
+// block ends, so the compiler may move or reuse their registers freely.  (For the builtin
+// read above the compiler first waits for every buffer->LDS load still in flight, the next
+// tiles' prefetch included; the asm form is not taken for such an LDS access.)  The wait is
+// lgkmcnt(0): LDS operations issued before the block complete with it.
+#define CSA_TRP(k)                                                   \
+  "ds_read_b64_tr_b16 %[o" #k "a], %[a" #k "]\n\t"                   \
+  "ds_read_b64_tr_b16 %[o" #k "b], %[a" #k "] offset:%[off]\n\t"
+#define CSA_TRO(k) [o##k##a] "=&v"(v[2 * k]), [o##k##b] "=&v"(v[2 * k + 1])
+#define CSA_TRI(k) [a##k] "v"(a[k])
+template <int> constexpr bool tr_pairs_unsupported = false;
+template <int OFF2, int N>
+__device__ __forceinline__ void lds_read_tr16_pairs(uint2 (&v)[2 * N], const uint32_t (&a)[N]) {
+  static_assert(OFF2 >= 0 && OFF2 < 65536, "ds offset field");
+  if constexpr (N == 2) {
+    asm volatile(CSA_TRP(0) CSA_TRP(1) "s_waitcnt lgkmcnt(0)"
+                 : CSA_TRO(0), CSA_TRO(1)
+                 : CSA_TRI(0), CSA_TRI(1), [off] "i"(OFF2)
+                 : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(CSA_TRP(0) CSA_TRP(1) CSA_TRP(2) CSA_TRP(3) "s_waitcnt lgkmcnt(0)"
+                 : CSA_TRO(0), CSA_TRO(1), CSA_TRO(2), CSA_TRO(3)
+                 : CSA_TRI(0), CSA_TRI(1), CSA_TRI(2), CSA_TRI(3), [off] "i"(OFF2)
+                 : "memory");
+  } else if constexpr (N == 6) {
+    asm volatile(CSA_TRP(0) CSA_TRP(1) CSA_TRP(2) CSA_TRP(3) CSA_TRP(4) CSA_TRP(5) "s_waitcnt lgkmcnt(0)"
+                 : CSA_TRO(0), CSA_TRO(1), CSA_TRO(2), CSA_TRO(3), CSA_TRO(4), CSA_TRO(5)
+                 : CSA_TRI(0), CSA_TRI(1), CSA_TRI(2), CSA_TRI(3), CSA_TRI(4), CSA_TRI(5), [off] "i"(OFF2)
+                 : "memory");
+  } else if constexpr (N == 8) {
+    asm volatile(CSA_TRP(0) CSA_TRP(1) CSA_TRP(2) CSA_TRP(3) CSA_TRP(4) CSA_TRP(5) CSA_TRP(6) CSA_TRP(7)
+                 "s_waitcnt lgkmcnt(0)"
+                 : CSA_TRO(0), CSA_TRO(1), CSA_TRO(2), CSA_TRO(3), CSA_TRO(4), CSA_TRO(5), CSA_TRO(6), CSA_TRO(7)
+                 : CSA_TRI(0), CSA_TRI(1), CSA_TRI(2), CSA_TRI(3), CSA_TRI(4), CSA_TRI(5), CSA_TRI(6), CSA_TRI(7),
+                   [off] "i"(OFF2)
+                 : "memory");
+  } else {
+    static_assert(tr_pairs_unsupported<N>, "pairs per batch: 2, 4, 6 or 8");
+  }
 }
-// The same with LATER LDS operations allowed to stay outstanding: for reads issued after the
-// transposing reads (LDS operations complete in order, so lgkmcnt(LATER) covers these).
-template <int LATER, int N> __device__ __forceinline__ void lds_tr16_wait_but(uint2 (&v)[N]) {
-  static_assert(LATER >= 0 && LATER <= 15, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(LATER) : "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
-}
+#undef CSA_TRP
+#undef CSA_TRO
+#undef CSA_TRI
 }  // namespace csa
 
 namespace csa {

@@ -568,14 +568,10 @@ __global__ __launch_bounds__(64 * HG, (D == 192 || D == 512) ? 2 : 3) void spars
 #pragma unroll
     for (int hf = 0; hf < D / 16 / BDT; ++hf) {
       uint2 xv[2 * BDT];
+      uint32_t va[BDT];
 #pragma unroll
-      for (int k = 0; k < BDT; ++k) {
-        const int dt = hf * BDT + k;
-        const uint32_t va = lds_addr_of(base + vbase + 32 * (dt ^ vxs));
-        xv[2 * k] = lds_read_tr16_nowait_off<0>(va);
-        xv[2 * k + 1] = lds_read_tr16_nowait_off<16 * ROWB>(va);
-      }
-      lds_tr16_wait(xv);
+      for (int k = 0; k < BDT; ++k) va[k] = lds_addr_of(base + vbase + 32 * ((hf * BDT + k) ^ vxs));
+      lds_read_tr16_pairs<16 * ROWB>(xv, va);
 #pragma unroll
       for (int k = 0; k < BDT; ++k) {
         const int dt = hf * BDT + k;
@@ -1305,14 +1301,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_pipe_kernel(
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         uint2 xv[D / 16];
+        uint32_t va[D / 32];
 #pragma unroll
-        for (int k = 0; k < D / 32; ++k) {
-          const int dt = hf * (D / 32) + k;
-          const uint32_t va = lds_addr_of(base + vbase + 32 * (dt ^ vxs));
-          xv[2 * k] = lds_read_tr16_nowait_off<0>(va);
-          xv[2 * k + 1] = lds_read_tr16_nowait_off<16 * ROWB>(va);
-        }
-        lds_tr16_wait(xv);
+        for (int k = 0; k < D / 32; ++k) va[k] = lds_addr_of(base + vbase + 32 * ((hf * (D / 32) + k) ^ vxs));
+        lds_read_tr16_pairs<16 * ROWB>(xv, va);
 #pragma unroll
         for (int k = 0; k < D / 32; ++k) {
           const int dt = hf * (D / 32) + k;

@@ -56,19 +56,32 @@ constexpr int WRPW = 32 / WW;           // rows each wave stages per chunk
 #define WIDE_LA 3
 #endif
 constexpr int LA = WIDE_LA;             // K operand pairs requested ahead of their MFMAs
-#ifndef WIDE_VPRE
-#define WIDE_VPRE 2
-#endif
-constexpr int VPRE = WIDE_VPRE;         // V^T d-tiles of P.V read during the QK MFMAs
-#ifndef WIDE_QKVALU
-#define WIDE_QKVALU 0
-#endif
-constexpr int QKVALU = WIDE_QKVALU;     // vector ALU slots after each MFMA pair of QK
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DS_READ = 0x100;
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_TRANS = 0x400;
 // the compiler's machine scheduler places the instructions of a region in the order of
 // these groups (used to interleave independent MFMAs and vector ALU work)
 template <int MASK, int N> __device__ __forceinline__ void sched_group() {
   __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+// S^T products on the 16x16x32 bf16 MFMA with C and D in VGPRs.  The builtin takes the
+// accumulator form the output tiles need (AGPRs, all 256 of them), which pushes 16 output
+// registers into VGPRs and copies them through AGPRs around every step; as asm statements
+// the S^T tiles stay in VGPRs.  The compiler does not pad hazards it does not see, so:
+//  * D is read only after mfma_v_fence: 16 wait states (this shape needs 8 before a vector
+//    instruction reads its result and 3 before one overwrites a C operand still being read);
+//  * C is the constant 0 or exactly D of the chain's previous MFMA (an exactly overlapping
+//    accumulation chain needs no wait states);
+//  * A and B are results of LDS and global loads, which the compiler waits for (it tracks the
+//    registers an asm statement reads); no vector instruction writes them.
+// Being volatile, the statements keep their order among themselves and with every memory
+// access, so the LDS reads and row requests issue where the source places them.
+__device__ __forceinline__ void mfma_v_first(f32x4 &d, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x4 &d, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_fence(f32x4 (&d)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(d[0][0]), "+v"(d[0][1]), "+v"(d[1][0]), "+v"(d[1][1]));
 }
 }  // namespace
 
@@ -223,15 +236,14 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   }
 
   // S^T of the chunk of step n for the wave's 32 heads: acc[kt][hi][i] is the logit of
-  // key 16 kt + 4 g + i and head 32 w + 16 hi + r16 (unscaled)
-  // mid() is called once the last K operands are requested (P.V operand reads of pass 2);
-  // vector ALU work placed before the call in the same block runs between the MFMAs
-  auto qk = [&](int n, f32x4 (&acc)[2][2], const ChunkReq &rq, auto &&mid) __attribute__((always_inline)) {
+  // key 16 kt + 4 g + i and head 32 w + 16 hi + r16 (unscaled).  at(c, j) runs after MFMA
+  // j of K-chunk c, at(-1, 0) before the first (once the first K operands are requested):
+  // vector work there runs beside the MFMAs when its inputs and results are tied to that
+  // place by empty asm statements, which keep their order with the MFMA statements.  One
+  // wave issues in order, so a window between two MFMAs holds best one short instruction
+  // or one exponential, none depending on another of the same window.
+  auto qk = [&](int n, f32x4 (&acc)[2][2], const ChunkReq &rq, auto &&at) __attribute__((always_inline)) {
     const char *tb = tile(n);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) acc[kt][hi] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 kr[LA][2];
     auto kread = [&](int c, u32x4 (&dst)[2]) __attribute__((always_inline)) {
       const char *kp = tb + kbj[c & 3] + 256 * (c >> 2);   // the rest of the offset is immediate
@@ -240,25 +252,21 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
     };
 #pragma unroll
     for (int c = 0; c < LA; ++c) kread(c, kr[c]);
-    sched_group<SG_DS_READ, 2 * LA>();
+    at(-1, 0);
 #pragma unroll
     for (int c = 0; c < WNC; ++c) {
       const u32x4 k0 = kr[c % LA][0], k1 = kr[c % LA][1];
       if (c + LA < WNC) kread(c + LA, kr[c % LA]);
-      if (c + LA == WNC - 1) mid();
 #pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        acc[0][hi] = mfma16x16x32(k0, qf[hi][c], acc[0][hi]);
-        acc[1][hi] = mfma16x16x32(k1, qf[hi][c], acc[1][hi]);
+      for (int j = 0; j < 4; ++j) {   // acc[kt = j & 1][hi = j >> 1]
+        const u32x4 &kk = (j & 1) ? k1 : k0;
+        if (c == 0) mfma_v_first(acc[j & 1][j >> 1], kk, qf[j >> 1][c]);
+        else mfma_v(acc[j & 1][j >> 1], kk, qf[j >> 1][c]);
+        at(c, j);
       }
       if (c % 2 == 1) issue_row(rq, c / 2);
-      sched_group<SG_MFMA, 2>();
-      if (QKVALU) sched_group<SG_VALU, QKVALU>();
-      if (c + LA < WNC) sched_group<SG_DS_READ, 2>();
-      sched_group<SG_MFMA, 2>();
-      if (QKVALU) sched_group<SG_VALU, QKVALU>();
-      if (c % 2 == 1) sched_group<SG_VMEM, 1>();
     }
+    mfma_v_fence(acc);
   };
 
   // ------------------------------------------------------------------ pass 1: lse, lse_nc
@@ -299,26 +307,47 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
       }
     }
   };
-  auto add_sums = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const float nms = m[hi] == NINF ? 0.f : -m[hi];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) l[hi] += fast_exp2(fmaf(sv[hi][e], sl2, nms));
+  // The sum of value v (head tile v / 8) of the 16: its FMA, exponential and addition in
+  // three windows of K-chunk v (j = 0, 1, 3; the sums keep their order)
+  float fx[16];
+  auto add_sums_step = [&](int v, int j) __attribute__((always_inline)) {
+    const int hi = v >> 3, e = v & 7;
+    if (j == 0) {
+      asm volatile("" : "+v"(sv[hi][e]));
+      fx[v] = fmaf(sv[hi][e], sl2, m[hi] == NINF ? 0.f : -m[hi]);
+      asm volatile("" : "+v"(fx[v]));
+    } else if (j == 1) {
+      asm volatile("" : "+v"(fx[v]));
+      fx[v] = fast_exp2(fx[v]);
+      asm volatile("" : "+v"(fx[v]));
+    } else if (j == 3) {
+      asm volatile("" : "+v"(fx[v]));
+      l[hi] += fx[v];
+      asm volatile("" : "+v"(l[hi]));
     }
   };
   for (int ci = 0; ci < nch; ++ci) {
     const ChunkReq rq = top(ci);
-    raise_max();   // chunk ci - 1
-    add_sums();
+    const uint32_t bm_all = row_mask(ci), bm = bm_all >> (4 * g);   // read before the products
     f32x4 acc[2][2];
-    qk(ci, acc, rq, [] {});
+    qk(ci, acc, rq, [&](int c, int j) __attribute__((always_inline)) {
+      if (c < 0) {   // chunk ci - 1 into the running max, beside the first K reads
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(sv[hi][e]));
+        raise_max();
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) asm volatile("" : "+v"(m[hi]), "+v"(l[hi]));
+      } else {
+        add_sums_step(c, j);
+      }
+    });
     if (ci == nwc) {   // every window chunk folded
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
     }
     // a head past H keeps finite garbage statistics that are never written
-    const uint32_t bm_all = row_mask(ci), bm = bm_all >> (4 * g);
     if (bm_all == 0xffffffffu) {
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi)
@@ -333,7 +362,10 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
     }
   }
   raise_max();   // the last chunk
-  add_sums();
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) add_sums_step(v, j);
   if (ncc == 0) {
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
@@ -362,28 +394,27 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   // 16-byte read service order of the LDS every quarter wave hits 16 distinct slots
   const int psw = (2 * ((r16 >> 2) & 1)) ^ (3 * ((r16 >> 3) & 1));
   auto pbuf = [&](int n) { return pbufs + (n & 1) * WPBUF; };
-  // P.V operands of the chunk of step n: V^T of the wave's 8 d-tiles (transposing reads)
-  // and P^T of the 8 head tiles
+  // P.V operands of the chunk of step n: V^T of the wave's 8 d-tiles by transposing reads
+  // (one batch with its wait, at the end of step n: the wait overlaps the step barrier that
+  // follows; the tile stays until step n + 2 requests rows) and P^T of the 8 head tiles
+  // (read during the last QK MFMAs of step n + 1, behind the barrier that publishes them)
   u32x4 va[8], pb[8];
-  uint2 xv[16];
-  auto pv_read_v = [&](int n, int dt0, int dt1) __attribute__((always_inline)) {
+  auto v_read = [&](int n) __attribute__((always_inline)) {
     const char *base = tile(n);
     int vxs = vx;
     asm volatile("" : "+v"(vxs));
+    uint32_t a[8];
 #pragma unroll
-    for (int dt = dt0; dt < dt1; ++dt) {
-      const uint32_t a = lds_addr_of(base + vbase + 32 * ((8 * w + dt) ^ vxs));
-      xv[2 * dt] = lds_read_tr16_nowait_off<0>(a);
-      xv[2 * dt + 1] = lds_read_tr16_nowait_off<16 * WROWB>(a);
-    }
+    for (int dt = 0; dt < 8; ++dt) a[dt] = lds_addr_of(base + vbase + 32 * ((8 * w + dt) ^ vxs));
+    uint2 xv[16];
+    lds_read_tr16_pairs<16 * WROWB>(xv, a);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) va[dt] = u32x4{xv[2 * dt].x, xv[2 * dt].y, xv[2 * dt + 1].x, xv[2 * dt + 1].y};
   };
   auto pv_read_p = [&](int n) __attribute__((always_inline)) {
     const char *pr = pbuf(n) + r16 * WPROW + 16 * (g ^ psw);
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht) pb[ht] = *reinterpret_cast<const u32x4 *>(pr + 16 * ht * WPROW);
-    lds_tr16_wait_but<8>(xv);   // the P^T reads may still be in flight
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) va[dt] = u32x4{xv[2 * dt].x, xv[2 * dt].y, xv[2 * dt + 1].x, xv[2 * dt + 1].y};
   };
   auto pv_mma = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -404,23 +435,25 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   };
   // the P buffer the first pass-2 step's P.V reads (there is no chunk before it) holds
   // zeros; its tile holds the last pass-1 chunk's finite rows
-  if (nch > 0)
+  if (nch > 0) {
     for (int i = tid; i < WPBUF / 16; i += WNT) reinterpret_cast<u32x4 *>(pbuf(nch - 1))[i] = u32x4{0, 0, 0, 0};
+    v_read(nch - 1);
+  }
   for (int ci = 0; ci < nch; ++ci) {
     const int n = nch + ci;
     const ChunkReq rq = top(n);
     if (ci > 0) flush(ci - 1, n - 1);
-    // P.V operands of the chunk before (at the first step: a zeroed P buffer): VPRE of the
-    // V^T tiles read during the last QK MFMAs, the rest and P^T after them
+    // P^T of the chunk before (at the first step: the zeroed P buffer) read during the last
+    // QK MFMAs; its V^T operands are in registers since the end of the step before
+    const uint32_t bm_all = row_mask(ci), bm = bm_all >> (4 * g);   // read before the products
     f32x4 acc[2][2];
-    qk(n, acc, rq, [&] { pv_read_v(n - 1, 0, VPRE); });
-    pv_read_v(n - 1, VPRE, 8);
-    pv_read_p(n - 1);
+    qk(n, acc, rq, [&](int c, int j) __attribute__((always_inline)) {
+      if (c == WNC - 2 && j == 0) pv_read_p(n - 1);
+    });
     __builtin_amdgcn_sched_barrier(0);
     // P = exp2(s sl2 - lse) of the chunk, its bf16 copy for P.V and the head sums for
     // cmass, interleaved with the P.V MFMAs of the chunk before (no dependence either way;
     // stores the step does not need go to a spare slot, so the block has no branch)
-    const uint32_t bm_all = row_mask(ci), bm = bm_all >> (4 * g);
     float p[2][8];   // [hi][4 kt + i]; a head past H has nl = -inf: P = 0
     if (bm_all != 0xffffffffu) {
 #pragma unroll
@@ -449,17 +482,26 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
     const bool cm_on = crow != nullptr && ci >= nwc && (r16 & 1) == 0;
     cm_part[n & 1][w][cm_on ? 16 * (el >> 2) + 4 * g + (el & 3) : 32] = sh;
     pv_mma();
+    // one exponential per MFMA (each holds the vector unit for four FMA issue slots), then
+    // two other vector instructions per MFMA
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
+    for (int k = 0; k < 16; ++k) {
+      sched_group<SG_MFMA, 1>();
+      sched_group<SG_TRANS, 1>();
+      sched_group<SG_VALU, 1>();
+    }
+#pragma unroll
+    for (int k = 16; k < 64; ++k) {
       sched_group<SG_MFMA, 1>();
       sched_group<SG_VALU, 2>();
     }
+    __builtin_amdgcn_sched_barrier(0);
+    v_read(n);
   }
   wait_vmcnt<0>();   // no load into the LDS outlives the workgroup
   if (nch > 0) {
     __syncthreads();   // the last chunk's P and cmass partials of every wave
     flush(nch - 1, ns - 1);
-    pv_read_v(ns - 1, 0, 8);
     pv_read_p(ns - 1);
     pv_mma();
   }
