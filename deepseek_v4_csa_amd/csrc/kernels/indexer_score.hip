@@ -889,22 +889,24 @@ hipError_t launch_indexer_topk(const LaunchLayout &LL, const void *q_idx, const 
 
 // ============================================================================
 // Head-grouped variant for long q_idx rows (bf16, Hi * Di * 2 above what the paired-block
-// kernel stages).  One workgroup (8 waves) = 64 tokens x 128 keys; wave w = 16 tokens
-// (w % 4) x 64 keys (w / 4), its key fragments in registers for the whole head loop.  The
-// q rows are staged in LDS one head group at a time (HG heads = 512 bytes of each token
-// row, 32 KiB per group, double-buffered, buffer->LDS loads of 1 KiB = two rows each),
-// chunk q of token row r at slot q ^ (r % 16) so the 16 lanes of an A-operand read hit 16
-// bank groups; fp32(w * s_idx) of every head is staged once.  Per head: Di/32 x 4
-// MFMAs, then the ReLU x weight accumulate.  Each staged byte of q feeds 128 keys.
+// kernel stages).  One workgroup (8 waves) = 16 tokens x 512 keys; wave w = the 16 tokens
+// x 64 keys (64 w), its key fragments in registers for the whole head loop.  The q rows
+// are staged in LDS one head group at a time (HG heads = 512 bytes of each token row,
+// 8 KiB per group: one 1 KiB buffer->LDS load, two rows, per wave), chunk q of token row
+// r at slot q ^ r so the 16 lanes of an A-operand read hit 16 bank groups, in a ring of
+// four buffers requested three groups ahead (a group's MFMAs take far less time than its
+// rows take to arrive from L2); fp32(w * s_idx) of every head is staged once.  Per head:
+// Di/32 x 4 MFMAs, then the ReLU x weight accumulate.  Each staged byte of q feeds 512 keys.
 // ============================================================================
-constexpr int HGK_TOK = 64;
-constexpr int HGK_KEYS = 128;
+constexpr int HGK_TOK = 16;
+constexpr int HGK_KEYS = 512;
 constexpr int HGK_WAVES = 8;
-// The staged weights [Hi][64 tokens]: token tt of head h sits at h * 64 + (tt ^ wsw(h)).
-// The staging writes go across heads (lane = head), which without the XOR would put all 64
-// lanes on one LDS bank; the XOR is a multiple of 4, so the 4 tokens a lane reads as one
-// f32x4 stay one aligned group.
-__device__ __forceinline__ int wsw(int h) { return 4 * (h & 15); }
+constexpr int HGK_NBUF = 4;
+// The staged weights [Hi][16 tokens]: token tt of head h sits at h * 16 + (tt ^ wsw(h)).
+// The staging writes go across heads (lane = head), which without the XOR would put 4
+// lanes on one LDS bank per row of 16 heads; the XOR is a multiple of 4, so the 4 tokens a
+// lane reads as one f32x4 stay one aligned group.
+__device__ __forceinline__ int wsw(int h) { return 4 * ((h >> 2) & 3); }
 
 template <int DI>
 __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(4))) void indexer_score_hg_kernel(
@@ -916,13 +918,13 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   constexpr int CPP = PB / 16;        // 16-byte chunks per staged row
   constexpr int NCD = DI / 32;
   constexpr int NTHR = 64 * HGK_WAVES;
-  static_assert(PB == 512 && CPP >= 16, "512-byte staged rows");
-  __shared__ __attribute__((aligned(16))) u32x4 qs[2][HGK_TOK * CPP];
+  static_assert(PB == 512 && CPP == 32 && HGK_TOK * PB == HGK_WAVES * 1024, "one 1 KiB load per wave and group");
+  __shared__ __attribute__((aligned(16))) u32x4 qs[HGK_NBUF][HGK_TOK * CPP];
   extern __shared__ __attribute__((aligned(16))) float wsl[];   // [Hi][HGK_TOK], tokens XOR wsw(h)
 
   // Workgroup id -> tile, XCD-aware: workgroups are dealt to the 8 XCDs round-robin by id,
   // so id = 8 * slot + xcd; token block b goes to XCD b % 8, and an XCD's consecutive slots
-  // walk all key tiles of one of its token blocks before the next.  The 64 q rows of a
+  // walk all key tiles of one of its token blocks before the next.  The 16 q rows of a
   // block (Hi * Di * 2 bytes each) are then fetched from HBM about once and re-read from
   // that XCD's L2 by the block's key tiles, instead of once per key tile.
   const int nkb = (max_sk + HGK_KEYS - 1) / HGK_KEYS;
@@ -942,7 +944,7 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int j0 = kt * HGK_KEYS;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tw = w & 3, jw = j0 + 64 * (w >> 2);
+  const int jw = j0 + 64 * w;
   const int nv_last = n_valid_of(min(t0 + HGK_TOK, q_len) - 1, off, L.ratio, s_k);
 
   if (j0 >= nv_last) {   // the whole tile is above the causal limit
@@ -956,16 +958,16 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int rows_left = min(HGK_TOK, total_q - (q_start + t0));
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(q_idx + (int64_t)(q_start + t0) * Hi * DI, (uint32_t)(rows_left * RB));
-  auto stage = [&](int grp, int buf) {   // 64 rows x 512 bytes: 32 instructions, 4 per wave
-#pragma unroll
-    for (int k = 0; k < 32 / HGK_WAVES; ++k) {
-      const int m = k * HGK_WAVES + w;
-      const int r = 2 * m + (lane >> 5), c = lane & 31;
-      dma16(rq, reinterpret_cast<char *>(qs[buf]) + (size_t)m * 1024,
-            (uint32_t)(r * RB + grp * PB + ((c ^ (r & 15)) << 4)));
-    }
+  // group grp's rows into buffer grp % NBUF: wave w moves rows 2w and 2w + 1 (lane >> 5)
+  const int srow = 2 * w + (lane >> 5), sc = lane & 31;
+  const uint32_t soff = (uint32_t)(srow * RB + ((sc ^ (srow & 15)) << 4));
+  auto stage = [&](int grp) {
+    dma16(rq, reinterpret_cast<char *>(qs[grp % HGK_NBUF]) + (size_t)w * 1024, soff + (uint32_t)(grp * PB));
   };
-  stage(0, 0);
+  const int ngrp = Hi / HG;
+#pragma unroll
+  for (int k = 0; k < HGK_NBUF - 1; ++k)
+    if (k < ngrp) stage(k);
   // key fragments (B operand: lane column r16 = key, piece 4c+g); keys past the segment
   // are clamped to its last key (their scores are masked)
   u32x4 kb[4][NCD];
@@ -978,19 +980,19 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   }
   // the block's weights are one contiguous run of rows_w * Hi floats: unconditional loads
   // through a buffer resource of exactly that run (tokens past the segment read zeros),
-  // eight per thread in flight at once -- a guarded load per element would be waited for
-  // (with every earlier load of the wave) before the next is issued
+  // several per thread in flight at once -- a guarded load per element would be waited
+  // for (with every earlier load of the wave) before the next is issued
   {
     const int rows_w = min(HGK_TOK, q_len - t0);
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(weights + (int64_t)(q_start + t0) * Hi, (uint32_t)(rows_w * Hi) * 4);
-    for (int e0 = tid; e0 < Hi * HGK_TOK; e0 += 8 * NTHR) {
-      float x[8];
+    for (int e0 = tid; e0 < Hi * HGK_TOK; e0 += 2 * NTHR) {
+      float x[2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 2; ++u)
         x[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (e0 + u * NTHR) * 4, 0, 0));
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 2; ++u) {
         const int e = e0 + u * NTHR;
         if (e < Hi * HGK_TOK) {
           const int tt = e / Hi, h = e - tt * Hi;
@@ -1002,13 +1004,17 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   f32x4 acc[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ngrp = Hi / HG;
-  const int rrow = (tw * 16 + r16) * PB;
+  const int rrow = r16 * PB;
   for (int grp = 0; grp < ngrp; ++grp) {
-    wait_vmcnt<0>();
-    __syncthreads();   // group grp staged (and, first time, the weights)
-    if (grp + 1 < ngrp) stage(grp + 1, (grp + 1) & 1);   // its buffer was last read at grp - 1
-    const char *qb = reinterpret_cast<const char *>(qs[grp & 1]) + rrow;
+    // group grp's rows have landed once at most the loads of the groups after it that were
+    // requested (one per wave and group) are outstanding; the barrier publishes every
+    // wave's rows (and, first time, the weights) and frees the buffer of group grp - 1
+    if (grp + 2 < ngrp) wait_vmcnt<2>();
+    else if (grp + 1 < ngrp) wait_vmcnt<1>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (grp + HGK_NBUF - 1 < ngrp) stage(grp + HGK_NBUF - 1);
+    const char *qb = reinterpret_cast<const char *>(qs[grp % HGK_NBUF]) + rrow;
 #pragma unroll
     for (int hl = 0; hl < HG; ++hl) {
       u32x4 qa[NCD];
@@ -1023,17 +1029,17 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int n = 0; n < 4; ++n) d[n] = mfma16x16x32(qa[c], kb[n][c], d[n]);
       const int hw = grp * HG + hl;
-      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsl + hw * HGK_TOK + ((tw * 16 + 4 * g) ^ wsw(hw)));
+      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsl + hw * HGK_TOK + ((4 * g) ^ wsw(hw)));
 #pragma unroll
       for (int n = 0; n < 4; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[n][i] = fmaf(wv[i], relu_bits(d[n][i]), acc[n][i]);
     }
   }
-  // lane (token tw*16 + 4g + i, key jw + 16n + r16)
+  // lane (token 4g + i, key jw + 16n + r16)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t = t0 + tw * 16 + 4 * g + i;
+    const int t = t0 + 4 * g + i;
     if (t >= q_len) continue;
     const int nv = n_valid_of(t, off, L.ratio, s_k);
     float *dst = scores + (int64_t)(q_start + t) * ld;

@@ -198,43 +198,39 @@ def test_wide_cmass_partials():
 
 # ---------------------------------------------------------------- indexer_score.hip
 def test_indexer_hg_q_operand_reads():
-    """indexer_score_hg_kernel: staged q rows of 512 bytes, chunk q of token row r at
-    slot q ^ (r % 16); lane (g, r16) reads chunk hl * Di / 8 + 4 c + g of row 16 tw + r16."""
+    """indexer_score_hg_kernel: 16 staged q rows of 512 bytes, chunk q of token row r at
+    slot q ^ r; lane (g, r16) reads chunk hl * Di / 8 + 4 c + g of row r16."""
     for Di in (64, 128):
-        for tw in range(4):
-            for hl in range(256 // Di):
-                for c in range(Di // 32):
-                    addrs = [(16 * tw + (l & 15)) * 512 + 16 * ((hl * Di // 8 + 4 * c + (l >> 4)) ^ (l & 15))
-                             for l in LANES]
-                    assert cycles_b128(addrs) == 4, (Di, tw, hl, c)
+        for hl in range(256 // Di):
+            for c in range(Di // 32):
+                addrs = [(l & 15) * 512 + 16 * ((hl * Di // 8 + 4 * c + (l >> 4)) ^ (l & 15)) for l in LANES]
+                assert cycles_b128(addrs) == 4, (Di, hl, c)
 
 
 def wsw(h):
     """indexer_score.hip: token XOR of the staged weights of head h."""
-    return 4 * (h & 15)
+    return 4 * ((h >> 2) & 3)
 
 
 def test_indexer_hg_weight_staging():
-    """The staged weights [Hi][64 tokens]: the staging writes (64 consecutive elements of
-    the [tokens, Hi] run, head fastest) spread over at least 16 banks, and each lane's
-    f32x4 read of tokens 16 tw + 4 g .. + 3 of head h is one aligned group holding exactly
-    those tokens."""
-    for Hi in (32, 64):
-        for e0 in range(0, Hi * 64, 64):
+    """The staged weights [Hi][16 tokens]: the staging writes (64 consecutive elements of
+    the [tokens, Hi] run, head fastest) take at most 4 cycles (16 without the XOR), and each
+    lane's f32x4 read of tokens 4 g .. 4 g + 3 of head h is one aligned group holding
+    exactly those tokens."""
+    for Hi in (16, 32, 64, 128):
+        for e0 in range(0, Hi * 16, 64):
             addrs = []
             for e in range(e0, e0 + 64):
                 tt, h = divmod(e, Hi)
-                addrs.append(4 * (h * 64 + (tt ^ wsw(h))))
+                addrs.append(4 * (h * 16 + (tt ^ wsw(h))))
             assert cycles_b32(addrs) <= 4, (Hi, e0)
-            # the unswizzled layout: every lane of a 64-head run on one bank
-            if Hi == 64:
-                assert cycles_b32([4 * (h * 64 + e0 // 64) for h in range(64)]) == 64
+        if Hi == 64:
+            assert cycles_b32([4 * (h * 16 + 0) for h in range(64)]) == 16
         for h in range(Hi):
-            for tw in range(4):
-                for g in range(4):
-                    base = (16 * tw + 4 * g) ^ wsw(h)
-                    assert base % 4 == 0
-                    assert {(base + i) ^ wsw(h) for i in range(4)} == {16 * tw + 4 * g + i for i in range(4)}
+            for g in range(4):
+                base = (4 * g) ^ wsw(h)
+                assert base % 4 == 0
+                assert {(base + i) ^ wsw(h) for i in range(4)} == {4 * g + i for i in range(4)}
 
 
 # ---------------------------------------------------------------- the model catches slips
