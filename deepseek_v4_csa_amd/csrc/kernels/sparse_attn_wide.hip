@@ -157,12 +157,17 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   }
   const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)(t + 1) * WROWB);   // rows past t: zeros
   const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * WROWB);  // id -1: past the end
+  // key masks of the compressed chunks (bit b of chunk c: slot 32 c + b holds an id), lane
+  // c of cbits[h] holding chunk 64 h + c; built once from the staged ids below, so a step
+  // takes its mask by a lane read instead of an LDS round trip before its first products
+  uint32_t cbits[2] = {0u, 0u};
   auto row_mask = [&](int ci) -> uint32_t {
     if (ci < nwc) {
       const int n = nw - 32 * ci;
       return n >= 32 ? 0xffffffffu : (1u << n) - 1u;
     }
-    return (uint32_t)__ballot(ids_l[32 * (ci - nwc) + (lane & 31)] >= 0);
+    const int cc = ci - nwc;
+    return (uint32_t)__builtin_amdgcn_readlane(cc < 64 ? cbits[0] : cbits[1], cc & 63);
   };
   // K operand: row r16 (+16), piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3));
   // with c = 4 (c >> 2) + j that is byte 256 (c >> 2) + kbj[j] of the row
@@ -176,6 +181,21 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   const int vbase = rho * WROWB + 16 * (((r16 & 3) >> 1) ^ (vsw & 1)) + 8 * (r16 & 1), vx = vsw >> 1;
 
   __syncthreads();   // ids and jlast in LDS
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = 64 * h + lane;
+    if (c < ncc_all) {   // lane c reads the 32 ids of chunk c (eight 16-byte reads, rotated by lane)
+      uint32_t m = 0;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int vv = (v + lane) & 7;
+        const int4 x = reinterpret_cast<const int4 *>(ids_l + 32 * c)[vv];
+        m |= (uint32_t)(x.x >= 0) << (4 * vv) | (uint32_t)(x.y >= 0) << (4 * vv + 1) |
+             (uint32_t)(x.z >= 0) << (4 * vv + 2) | (uint32_t)(x.w >= 0) << (4 * vv + 3);
+      }
+      cbits[h] = m;
+    }
+  }
   const int ncc = (jlast + 32) >> 5, nch = nwc + ncc;
   float *crow = cmass ? cmass + (int64_t)t * k_eff : nullptr;
   if (crow)   // the skipped chunks' slots hold no id: mass 0
