@@ -108,7 +108,7 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   __shared__ float cm_part[2][WW][33];   // slot 32: spare target of stores not needed
   __shared__ int jlast;
 
-  const int t = blockIdx.x;
+  const int t = total_q - 1 - (int)blockIdx.x;   // the longest rows (last) first: a lighter tail
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   // the wave's heads: tile hi holds heads 32 w + 16 hi + r16
