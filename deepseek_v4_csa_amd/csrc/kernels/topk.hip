@@ -6,7 +6,7 @@
 // are -1 in its sparse-attention excerpt); ids are global, cu_k[s] + j (page
 // "Megatron-LM pull request 8539", item 1).
 //
-// One workgroup (256 threads) per row; the row's visible scores sit in registers as
+// One workgroup (512 threads) per row; the row's visible scores sit in registers as
 // order-preserving uint32 keys.  The k-th largest key is found by radix selection on
 // (key - row_min_key), starting at the highest set bit of (max - min) so the first
 // 8-bit digit already spreads the values over the histogram (the raw top byte of
@@ -19,7 +19,7 @@
 
 namespace csa {
 
-constexpr int TK_THREADS = 256;
+constexpr int TK_THREADS = 512;   // 256 and 1,024 measured slower on 16k-key rows
 constexpr int TK_WAVES = TK_THREADS / 64;
 
 // Exclusive prefix sums over the block (thread order) of two counts at once, with
@@ -49,8 +49,8 @@ __device__ __forceinline__ void block_scan2(int a, int b, int *wsum, int &pa, in
   pb = bb + ib - b;
 }
 
-// One workgroup per row (rows above 4096 keys).  Key j = v*256 + tid sits in key[v] of
-// thread tid, so every load instruction reads 1 KiB of the row contiguously, and index
+// One workgroup per row (rows above 4096 keys).  Key j = v*512 + tid sits in key[v] of
+// thread tid, so every load instruction reads 2 KiB of the row contiguously, and index
 // order is v, then wave, then lane.  The radix passes stop as soon as the threshold bin is
 // taken whole.  Compaction: each wave counts, per v, its keys above the threshold and its
 // ties (ballot popcounts), one block scan over the (v, wave) counts in index order gives
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   while (cur > 0) {
     const int width = cur < 8 ? cur : 8;
     const int sh = cur - width;
-    hist[tid] = 0;  // TK_THREADS == 256 bins
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
