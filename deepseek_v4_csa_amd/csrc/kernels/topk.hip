@@ -22,39 +22,13 @@ namespace csa {
 constexpr int TK_THREADS = 512;   // 256 and 1,024 measured slower on 16k-key rows
 constexpr int TK_WAVES = TK_THREADS / 64;
 
-// Exclusive prefix sums over the block (thread order) of two counts at once, with
-// their totals; two barriers.  wsum: 2 * TK_WAVES words of LDS.
-__device__ __forceinline__ void block_scan2(int a, int b, int *wsum, int &pa, int &pb, int &ta, int &tb) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int ia = a, ib = b;   // inclusive scans within the wave
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int ya = __shfl_up(ia, o, 64), yb = __shfl_up(ib, o, 64);
-    if (lane >= o) { ia += ya; ib += yb; }
-  }
-  if (lane == 63) { wsum[w] = ia; wsum[TK_WAVES + w] = ib; }
-  __syncthreads();
-  int ba = 0, bb = 0;
-  ta = tb = 0;
-#pragma unroll
-  for (int i = 0; i < TK_WAVES; ++i) {
-    const int ca = wsum[i], cb = wsum[TK_WAVES + i];
-    ba += i < w ? ca : 0;
-    bb += i < w ? cb : 0;
-    ta += ca;
-    tb += cb;
-  }
-  __syncthreads();
-  pa = ba + ia - a;
-  pb = bb + ib - b;
-}
-
-// One workgroup per row (rows above 4096 keys).  Key j = v*512 + tid sits in key[v] of
-// thread tid, so every load instruction reads 2 KiB of the row contiguously, and index
-// order is v, then wave, then lane.  The radix passes stop as soon as the threshold bin is
-// taken whole.  Compaction: each wave counts, per v, its keys above the threshold and its
-// ties (ballot popcounts), one block scan over the (v, wave) counts in index order gives
-// every group its offsets, and each lane places its picks with mbcnt ranks.
+// One workgroup per row (rows above 4096 keys).  Wave w owns the contiguous run of keys
+// j = 64 VPT w + 64 v + lane (key[v] of the lane), so every load instruction reads 256
+// bytes of the row contiguously and index order is wave, then v, then lane.  The radix
+// passes stop as soon as the threshold bin is taken whole.  Compaction: each wave counts
+// its keys above the threshold and its ties (ballot popcounts), the waves' totals pass
+// through LDS once, and each lane places its picks at its wave's offset plus the running
+// counts of the wave's earlier v plus its mbcnt rank.
 // the float whose order-preserving key is k (the inverse of ordered_key)
 __device__ __forceinline__ float float_of_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -65,17 +39,16 @@ template <int VPT, bool SEL>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const float *__restrict__ scores,
                                                           int64_t ld, int k_eff, int32_t *__restrict__ ids,
                                                           float *__restrict__ sel) {
-  static_assert(VPT * TK_WAVES <= TK_THREADS, "one scan entry per (v, wave)");
   __shared__ uint32_t hist[256];
   __shared__ uint32_t red[2 * TK_WAVES];
-  __shared__ int wsum[2 * TK_WAVES];
-  __shared__ int cnt[2][VPT * TK_WAVES];
+  __shared__ int wtot[2 * TK_WAVES];
   __shared__ uint32_t sel_digit, sel_above, sel_cnt;
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const RowGeo g = row_geo(L, t);
   const int n = g.n_valid;
+  auto jof = [&](int v) { return 64 * VPT * w + 64 * v + lane; };
   int32_t *out = ids + (int64_t)t * k_eff;
   float *sout = SEL ? sel + (int64_t)t * k_eff : nullptr;
   const float *row = scores + (int64_t)t * ld;
@@ -94,11 +67,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   uint32_t key[VPT];
 #pragma unroll
   for (int v = 0; v < VPT; ++v)
-    key[v] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rrow, (v * TK_THREADS + tid) * 4, 0, 0);
+    key[v] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rrow, jof(v) * 4, 0, 0);
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const bool in = v * TK_THREADS + tid < n;
+    const bool in = jof(v) < n;
     key[v] = in ? ordered_key(__uint_as_float(key[v])) : 0u;
     kmin = in ? min(kmin, key[v]) : kmin;
     kmax = in ? max(kmax, key[v]) : kmax;
@@ -128,7 +101,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-      const bool in_play = v * TK_THREADS + tid < n && (cur >= 32 || (key[v] >> cur) == thr);
+      const bool in_play = jof(v) < n && (cur >= 32 || (key[v] >> cur) == thr);
       if (in_play) atomicAdd(&hist[(key[v] >> sh) & ((1u << width) - 1u)], 1u);
     }
     __syncthreads();
@@ -167,48 +140,41 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   // (the ballots are taken twice rather than kept: 2 * VPT 64-bit masks would not fit the
   // scalar registers)
   auto ballots = [&](int v, uint64_t &bg, uint64_t &be) __attribute__((always_inline)) {
-    const bool valid = v * TK_THREADS + tid < n;
+    const bool valid = jof(v) < n;
     const uint32_t kp = key[v] >> cur;
     bg = __ballot(valid && (kp > thr || (whole && kp == thr)));
     be = __ballot(valid && !whole && kp == thr);
   };
-  // the wave's counts per v gathered in lane v (no per-v branch), stored by one write each
-  int cg = 0, ce = 0;
+  // the wave's totals, then every wave's offset from the waves before it
+  int tg = 0, te = 0;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     uint64_t bg, be;
     ballots(v, bg, be);
-    cg = lane == v ? __popcll(bg) : cg;
-    ce = lane == v ? __popcll(be) : ce;
+    tg += __popcll(bg);
+    te += __popcll(be);
   }
-  if (lane < VPT) {
-    cnt[0][lane * TK_WAVES + w] = cg;
-    cnt[1][lane * TK_WAVES + w] = ce;
-  }
+  if (lane == 0) { wtot[w] = tg; wtot[TK_WAVES + w] = te; }
   __syncthreads();
-  {
-    const int a = tid < VPT * TK_WAVES ? cnt[0][tid] : 0, b2 = tid < VPT * TK_WAVES ? cnt[1][tid] : 0;
-    int pa, pb, ta, tb;
-    block_scan2(a, b2, wsum, pa, pb, ta, tb);
-    if (tid < VPT * TK_WAVES) { cnt[0][tid] = pa; cnt[1][tid] = pb; }
+  int og = 0, oe = 0;
+#pragma unroll
+  for (int i = 0; i < TK_WAVES; ++i) {
+    og += i < w ? wtot[i] : 0;
+    oe += i < w ? wtot[TK_WAVES + i] : 0;
   }
-  __syncthreads();
-  // the wave's offsets per v: lane v reads them once, every v takes them by readlane
-  const int og = lane < VPT ? cnt[0][lane * TK_WAVES + w] : 0;
-  const int oe = lane < VPT ? cnt[1][lane * TK_WAVES + w] : 0;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     uint64_t bg, be;
     ballots(v, bg, be);
-    const int gt_before = __builtin_amdgcn_readlane(og, v) +
-        __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0));
-    const int eq_before = __builtin_amdgcn_readlane(oe, v) +
-        __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0));
+    const int gt_before = og + __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0));
+    const int eq_before = oe + __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0));
     const bool gt = (bg >> lane) & 1, eq = (be >> lane) & 1;
     const bool sel_ = gt || (eq && eq_before < need);
     const int pos = gt_before + min(eq_before, need);
+    og += __popcll(bg);
+    oe += __popcll(be);
     if (sel_ && pos < k_eff) {
-      out[pos] = g.k_base + v * TK_THREADS + tid;
+      out[pos] = g.k_base + jof(v);
       if constexpr (SEL) sout[pos] = float_of_key(key[v] + kmin);
     }
   }
