@@ -43,6 +43,9 @@ CASES = [
     ("wide-h112-d512", torch.bfloat16, 112, 512, 300, 130, (150, 1300)),
     ("wide-h40-d512-nowin", torch.bfloat16, 40, 512, 77, 0, (97, 500)),
     ("wide-h8-d512-k1", torch.bfloat16, 8, 512, 1, 1, (40, 90)),
+    # 125 compressed chunks: key masks of chunks 64 and up, and the three-tile ring (four
+    # 32 KiB tiles no longer fit the LDS beside 4,000 staged ids)
+    ("wide-h16-d512-k4000", torch.bfloat16, 16, 512, 4000, 64, (16400,)),
     ("wg-h33-d128-k1", torch.bfloat16, 33, 128, 1, 1, (40, 90)),
     ("f32-h4-d64", torch.float32, 4, 64, 16, 32, (100, 256)),
     ("f32-h20-d128", torch.float32, 20, 128, 300, 40, (150, 1300)),
