@@ -26,6 +26,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "topk.hip"),
     os.path.join(CSRC, "kernels", "sparse_attn.hip"),
     os.path.join(CSRC, "kernels", "sparse_attn_wide.hip"),
+    os.path.join(CSRC, "kernels", "sparse_attn_wide_lse.hip"),
     os.path.join(CSRC, "kernels", "teacher_kl.hip"),
     os.path.join(CSRC, "kernels", "indexer_bwd.hip"),
 ]

@@ -9,29 +9,28 @@
 //   out = (sum_window e^w kv[t'] + sum_ids e^c ckv[id]) / Z_h,  lse = log Z_h,
 //   lse_nc = log(exp(sink_h) + sum_window e^w),  cmass[t, j] = sum_h exp(c_hj - lse_h).
 //
+// Two kernels per call.  sparse_attn_wide_lse.hip forms every logit once for lse and
+// lse_nc; this kernel forms them again for P = exp(s - lse), the output and cmass.
+//
 // One workgroup of four waves (one per SIMD, each with the whole 512-entry register file:
 // 256 VGPRs and 256 AGPRs) per query row.  The row's KV rows are staged 32 at a time (one
 // "chunk", 32 KiB) in a ring of three or four LDS tiles by direct buffer->LDS loads, the
-// chunk one or two steps ahead requested right after each step's barrier.  With one KV
+// chunk two or three steps ahead requested right after each step's barrier.  With one KV
 // row shared by every head, the cost that matters is LDS reads per MFMA; a wave holding
-// the Q rows of 32 heads in registers reads each K operand once for four MFMAs:
+// the Q rows of 32 heads in registers reads each K operand once for four MFMAs.  Per chunk:
+// S^T = K Q^T for the wave's heads [32 w, 32 w + 32) over all 32 keys, P = exp(s - lse)
+// written as bf16 to an LDS buffer holding the chunk's P for all 128 heads, its head sums
+// added into cmass.  One step later (behind the next barrier) wave w accumulates the
+// output columns [128 w, 128 w + 128) of every head in AGPRs: O^T[d, h] += V^T[d, j] P^T[j, h],
+// V^T read with the transposing LDS read (8 KiB per chunk, at the end of the chunk's own
+// step) and P^T with 16-byte reads (8 KiB per chunk).  Those 64 MFMAs do not depend on the
+// chunk's softmax, so the two are interleaved.
 //
-//  pass 1 (lse and lse_nc): wave w takes heads [32 w, 32 w + 32) over all 32 keys of every
-//    chunk (S^T = K Q^T on MFMA), with a running max per head (raised lazily, by 2^8 or
-//    more) and a running sum.
-//  pass 2 (P, out and cmass, lse final): the same S^T again, P = exp(s - lse) written as
-//    bf16 to an LDS buffer holding the chunk's P for all 128 heads, its head sums added
-//    into cmass.  One step later (behind the next barrier) wave w accumulates the output
-//    columns [128 w, 128 w + 128) of every head in AGPRs: O^T[d, h] += V^T[d, j] P^T[j, h],
-//    V^T read with the transposing LDS read (8 KiB per chunk) and P^T with 16-byte reads
-//    (8 KiB per chunk).  Those 64 MFMAs do not depend on the chunk's softmax, so the two
-//    are interleaved.
-//
-// LDS per query and 32-key chunk: pass 1 reads 128 KiB of K, pass 2 128 KiB of K plus
-// 64 KiB of V and P; the 16-byte pieces of a tile row are XOR-swizzled (row_swz) so the K
-// reads, the transposing V reads and the staging writes are free of bank conflicts, and
-// P row h keeps its 16-byte key blocks XOR-swizzled by a function of h for the same reason
-// (16 lanes reading 16 rows of 64 bytes).
+// LDS per query and 32-key chunk: 128 KiB of K reads plus 64 KiB of V and P; the 16-byte
+// pieces of a tile row are XOR-swizzled (row_swz) so the K reads, the transposing V reads
+// and the staging writes are free of bank conflicts, and P row h keeps its 16-byte key
+// blocks XOR-swizzled by a function of h for the same reason (16 lanes reading 16 rows of
+// 64 bytes).
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -49,6 +48,7 @@ constexpr int WPROW = 64;               // bytes per P row (32 keys, bf16)
 constexpr int WPBUF = 128 * WPROW;      // P of one chunk for 128 heads (8 KiB)
 constexpr int WNC = WD / 32;            // MFMA K-chunks per row
 constexpr int WRPW = 32 / WW;           // rows each wave stages per chunk
+constexpr int WIDS = 8;                 // ids per thread in the first batch (2,048 slots)
 #ifndef WIDE_NTILE_MAX
 #define WIDE_NTILE_MAX 4
 #endif
@@ -85,28 +85,28 @@ __device__ __forceinline__ void mfma_v_fence(f32x4 (&d)[2][2]) {
 }
 }  // namespace
 
-// NTILE tiles in the ring: 3 requests the next chunk one step ahead, 4 two steps ahead
-// (pass 2 still reads a tile one step after its own, for P.V)
+// NTILE tiles in the ring: chunks are requested NTILE - 1 steps ahead (a tile is last read
+// at the end of its own step, by the V^T reads)
+// (the id slots: whole chunks, at least the first batch's WIDS * WNT)
 size_t wide_attn_lds_bytes(int ntile, int k_eff) {
   const int ncc = (k_eff + 31) / 32;
-  return (size_t)ntile * WTILE + 2 * (size_t)WPBUF + (size_t)ncc * 32 * sizeof(int);
+  return (size_t)ntile * WTILE + 2 * (size_t)WPBUF + (size_t)max(ncc * 32, WIDS * WNT) * sizeof(int);
 }
 
 template <int NTILE>
 __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
     LayoutDev L, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
-    const uint16_t *__restrict__ ckv, const float *__restrict__ sink,
-    const int32_t *__restrict__ ids, int k_eff, int window, int H, int total_q, int total_k,
-    float sl2, uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ lse_nc,
+    const uint16_t *__restrict__ ckv, const int32_t *__restrict__ ids, int k_eff, int window, int H,
+    int total_q, int total_k, float sl2, const float *__restrict__ lse, uint16_t *__restrict__ out,
     float *__restrict__ cmass) {
   constexpr float NINF = -__builtin_inff();
-  constexpr float RESCALE = 8.f;
   extern __shared__ __attribute__((aligned(16))) char wide_dyn[];   // tiles, P buffers, ids
-  constexpr int DIST = NTILE - 2;          // request distance in steps
+  constexpr int DIST = NTILE - 1;          // request distance in steps
   char *pbufs = wide_dyn + NTILE * WTILE;
   int *ids_l = reinterpret_cast<int *>(pbufs + 2 * WPBUF);
   __shared__ float cm_part[2][WW][33];   // slot 32: spare target of stores not needed
   __shared__ int jlast;
+  __shared__ uint32_t cmask[128];   // key masks of the compressed chunks
 
   const int t = total_q - 1 - (int)blockIdx.x;   // the longest rows (last) first: a lighter tail
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -124,28 +124,18 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   const int nw = window > 0 ? t - w_lo + 1 : 0;
   const int nwc = (nw + 31) >> 5, ncc_all = (k_eff + 31) >> 5;
 
-  // the row's ids, padded with -1 to whole chunks, through a buffer resource of exactly
-  // k_eff ids (unconditional loads, four per thread in flight); jlast = the last slot that
-  // holds an id: compressed chunks after it have no row and are skipped
+  // Requested in order, so that each wait covers only what it needs: the first kernel's lse
+  // of the wave's heads, the first WIDS ids of each thread, the Q^T operands; only then are
+  // the ids stored (slots past k_eff hold -1; a buffer load past k_eff returns 0)
+  float lsev[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) lsev[hi] = lse[(int64_t)t * H + (ok[hi] ? hh[hi] : 0)];
   if (tid == 0) jlast = -1;
-  __syncthreads();
-  {
-    const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids + (int64_t)t * k_eff, (uint32_t)k_eff * 4);
-    int jl = -1;
-    for (int i0 = tid; i0 < ncc_all * 32; i0 += 4 * WNT) {
-      int x[4];
+  const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids + (int64_t)t * k_eff, (uint32_t)k_eff * 4);
+  int x[WIDS];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = __builtin_amdgcn_raw_buffer_load_b32(rid, (i0 + u * WNT) * 4, 0, 0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = i0 + u * WNT;
-        const int id = j < k_eff ? x[u] : -1;
-        if (j < ncc_all * 32) ids_l[j] = id;
-        if (id >= 0) jl = j;
-      }
-    }
-    if (jl >= 0) atomicMax(&jlast, jl);
-  }
+  for (int u = 0; u < WIDS; ++u) x[u] = __builtin_amdgcn_raw_buffer_load_b32(rid, (tid + u * WNT) * 4, 0, 0);
+  asm volatile("" ::: "memory");
   // Q^T operands of both head tiles; piece c of lane group g holds features
   // [(4c+g)*8, +8) (a head past H loads head 0's row: its logits are masked)
   u32x4 qf[2][WNC];
@@ -155,19 +145,45 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
 #pragma unroll
     for (int c = 0; c < WNC; ++c) qf[hi][c] = p[4 * c];
   }
+  asm volatile("" ::: "memory");
+  lds_barrier();   // jlast initialised
+  {
+    // jlast = the last slot that holds an id (compressed chunks after it have no row and are
+    // skipped): the wave's maximum, then one LDS atomic per wave
+    int jl = -1;
+    auto put = [&](int j, int v) __attribute__((always_inline)) {   // no branch: the loads stay above Q's
+      const int id = j < k_eff ? v : -1;
+      ids_l[j] = id;
+      jl = id >= 0 ? j : jl;
+    };
+#pragma unroll
+    for (int u = 0; u < WIDS; ++u) put(tid + u * WNT, x[u]);
+    for (int j = tid + WIDS * WNT; j < ncc_all * 32; j += WNT) put(j, __builtin_amdgcn_raw_buffer_load_b32(rid, j * 4, 0, 0));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) jl = max(jl, __shfl_xor(jl, m, 64));
+    if (lane == 0 && jl >= 0) atomicMax(&jlast, jl);
+  }
+  // exp2 offsets of the wave's heads (-inf for a head with no probability at all, or past
+  // H: P = 0), complete before the steps (whose waits count only the row loads)
+  float nl[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const float l2 = ok[hi] ? lsev[hi] * LOG2E : NINF;
+    nl[hi] = l2 > NINF ? -l2 : NINF;
+    asm volatile("" : "+v"(nl[hi]));
+  }
   const __amdgpu_buffer_rsrc_t rkv = make_rsrc(kv, (uint32_t)(t + 1) * WROWB);   // rows past t: zeros
   const __amdgpu_buffer_rsrc_t rck = make_rsrc(ckv, (uint32_t)total_k * WROWB);  // id -1: past the end
-  // key masks of the compressed chunks (bit b of chunk c: slot 32 c + b holds an id), lane
-  // c of cbits[h] holding chunk 64 h + c; built once from the staged ids below, so a step
-  // takes its mask by a lane read instead of an LDS round trip before its first products
-  uint32_t cbits[2] = {0u, 0u};
-  auto row_mask = [&](int ci) -> uint32_t {
-    if (ci < nwc) {
-      const int n = nw - 32 * ci;
-      return n >= 32 ? 0xffffffffu : (1u << n) - 1u;
-    }
-    const int cc = ci - nwc;
-    return (uint32_t)__builtin_amdgcn_readlane(cc < 64 ? cbits[0] : cbits[1], cc & 63);
+  // key mask of chunk ci (bit b: slot b holds a row): the window chunks' from nw, the
+  // compressed chunks' from a table built once from the staged ids below (cmask, at most
+  // 128 chunks).  No branch: the table is read at a clamped index every time (cmask_raw,
+  // issued by a step before its V^T batch, whose wait covers it) and the choice is a select
+  auto cmask_raw = [&](int ci) -> uint32_t { return cmask[(ci - nwc) & 127]; };
+  auto row_mask = [&](int ci, uint32_t raw) -> uint32_t {
+    const int n = max(min(nw - 32 * ci, 32), 0);
+    const uint32_t win = (uint32_t)(((uint64_t)1 << n) - 1);
+    const uint32_t cm = (uint32_t)__builtin_amdgcn_readfirstlane(raw);
+    return ci < nwc ? win : cm;
   };
   // K operand: row r16 (+16), piece (4c + g) ^ swz = 4 (c ^ (swz >> 2)) + (g ^ (swz & 3));
   // with c = 4 (c >> 2) + j that is byte 256 (c >> 2) + kbj[j] of the row
@@ -180,11 +196,11 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   const int vsw = row_swz<WD>(rho);
   const int vbase = rho * WROWB + 16 * (((r16 & 3) >> 1) ^ (vsw & 1)) + 8 * (r16 & 1), vx = vsw >> 1;
 
-  __syncthreads();   // ids and jlast in LDS
+  lds_barrier();   // ids and jlast in LDS (the Q loads stay in flight)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c = 64 * h + lane;
-    if (c < ncc_all) {   // lane c reads the 32 ids of chunk c (eight 16-byte reads, rotated by lane)
+    if (c < ncc_all && w == 0) {   // lane c reads the 32 ids of chunk c (eight 16-byte reads, rotated by lane)
       uint32_t m = 0;
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
@@ -193,15 +209,14 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
         m |= (uint32_t)(x.x >= 0) << (4 * vv) | (uint32_t)(x.y >= 0) << (4 * vv + 1) |
              (uint32_t)(x.z >= 0) << (4 * vv + 2) | (uint32_t)(x.w >= 0) << (4 * vv + 3);
       }
-      cbits[h] = m;
+      cmask[c] = m;
     }
   }
   const int ncc = (jlast + 32) >> 5, nch = nwc + ncc;
   float *crow = cmass ? cmass + (int64_t)t * k_eff : nullptr;
   if (crow)   // the skipped chunks' slots hold no id: mass 0
     for (int j = 32 * ncc + tid; j < k_eff; j += WNT) crow[j] = 0.f;
-  const int ns = 2 * nch;   // steps: pass 1 over every chunk, then pass 2
-  auto chunk_of = [&](int n) { return n < nch ? n : n - nch; };
+  const int ns = nch;   // one step per chunk
   auto tile = [&](int n) { return wide_dyn + (n % NTILE) * WTILE; };
   // Loads of the chunk of step n: instruction k of wave w moves row i = w + 4k (1 KiB);
   // lane l writes slot l, which holds the row's piece l ^ row_swz(i).  A step issues the
@@ -218,16 +233,15 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   auto request = [&](int n) -> ChunkReq {
     ChunkReq rq;
     rq.buf = tile(n);
-    const int ci = chunk_of(n);
     if (n >= ns) {   // nothing left to load: zeros into the free tile
       rq.r = rnone;
       rq.myrow = 0;
-    } else if (ci < nwc) {
+    } else if (n < nwc) {
       rq.r = rkv;
-      rq.myrow = w_lo + 32 * ci + (lane & 31);
+      rq.myrow = w_lo + 32 * n + (lane & 31);
     } else {
       rq.r = rck;
-      rq.myrow = ids_l[32 * (ci - nwc) + (lane & 31)];
+      rq.myrow = ids_l[32 * (n - nwc) + (lane & 31)];
     }
     return rq;
   };
@@ -240,8 +254,8 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   // with DIST steps requested ahead
   // "at most WRPW (DIST - 1) vector-memory operations outstanding" means step n's rows
   // have landed (loads complete in order; stores issued in between only make the wait
-  // stricter).  After the barrier every wave has finished step n - 1, the last reader
-  // (P.V) of the tile of step n - 2 = n + DIST - NTILE, which the new request reuses.
+  // stricter).  After the barrier every wave has finished step n - 1, whose tile (read last
+  // by the V^T reads at that step's end) the new request reuses: n + DIST - NTILE = n - 1.
   auto top = [&](int n) -> ChunkReq {
     if (n + DIST - 1 < ns) wait_vmcnt<WRPW * (DIST - 1)>();
     else wait_vmcnt<0>();
@@ -289,122 +303,7 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
     mfma_v_fence(acc);
   };
 
-  // ------------------------------------------------------------------ pass 1: lse, lse_nc
-  float m[2], l[2], m_nc[2], l_nc[2];
-#pragma unroll
-  for (int hi = 0; hi < 2; ++hi) {
-    const float a2 = ok[hi] ? sink[hh[hi]] * LOG2E : NINF;
-    m[hi] = a2;
-    l[hi] = (g == 0 && a2 > NINF) ? 1.f : 0.f;   // the sink counted once per head
-    m_nc[hi] = m[hi];
-    l_nc[hi] = l[hi];
-  }
-  // The logits of a chunk (masked, unscaled) are folded into the running max and sums at
-  // the next step, while that step's MFMAs run: the max is raised first (rarely; a branch),
-  // then the exponentials are summed beside the MFMAs.
-  float sv[2][8];
-#pragma unroll
-  for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sv[hi][e] = NINF;
-  auto raise_max = [&]() __attribute__((always_inline)) {
-    float cmx[2];
-    bool up = false;
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      cmx[hi] = sv[hi][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) cmx[hi] = fmaxf(cmx[hi], sv[hi][e]);
-      up = up || cmx[hi] * sl2 > m[hi] + RESCALE;   // log2 units (sl2 > 0 keeps the order)
-    }
-    if (__builtin_expect(__ballot(up) != 0, 0)) {
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        const float cand = across_groups_max(cmx[hi]) * sl2;
-        const float mn = cand > m[hi] + RESCALE ? cand : m[hi];
-        l[hi] *= mn == m[hi] ? 1.f : fast_exp2(m[hi] - mn);
-        m[hi] = mn;
-      }
-    }
-  };
-  // The sum of value v (head tile v / 8) of the 16: its FMA, exponential and addition in
-  // three windows of K-chunk v (j = 0, 1, 3; the sums keep their order)
-  float fx[16];
-  auto add_sums_step = [&](int v, int j) __attribute__((always_inline)) {
-    const int hi = v >> 3, e = v & 7;
-    if (j == 0) {
-      asm volatile("" : "+v"(sv[hi][e]));
-      fx[v] = fmaf(sv[hi][e], sl2, m[hi] == NINF ? 0.f : -m[hi]);
-      asm volatile("" : "+v"(fx[v]));
-    } else if (j == 1) {
-      asm volatile("" : "+v"(fx[v]));
-      fx[v] = fast_exp2(fx[v]);
-      asm volatile("" : "+v"(fx[v]));
-    } else if (j == 3) {
-      asm volatile("" : "+v"(fx[v]));
-      l[hi] += fx[v];
-      asm volatile("" : "+v"(l[hi]));
-    }
-  };
-  for (int ci = 0; ci < nch; ++ci) {
-    const ChunkReq rq = top(ci);
-    const uint32_t bm_all = row_mask(ci), bm = bm_all >> (4 * g);   // read before the products
-    f32x4 acc[2][2];
-    qk(ci, acc, rq, [&](int c, int j) __attribute__((always_inline)) {
-      if (c < 0) {   // chunk ci - 1 into the running max, beside the first K reads
-#pragma unroll
-        for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(sv[hi][e]));
-        raise_max();
-#pragma unroll
-        for (int hi = 0; hi < 2; ++hi) asm volatile("" : "+v"(m[hi]), "+v"(l[hi]));
-      } else {
-        add_sums_step(c, j);
-      }
-    });
-    if (ci == nwc) {   // every window chunk folded
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
-    }
-    // a head past H keeps finite garbage statistics that are never written
-    if (bm_all == 0xffffffffu) {
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sv[hi][e] = acc[e >> 2][hi][e & 3];
-    } else {
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sv[hi][e] = ((bm >> (16 * (e >> 2) + (e & 3))) & 1) ? acc[e >> 2][hi][e & 3] : NINF;
-    }
-  }
-  raise_max();   // the last chunk
-#pragma unroll
-  for (int v = 0; v < 16; ++v)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) add_sums_step(v, j);
-  if (ncc == 0) {
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
-  }
-  // lse of the wave's heads (log2 units), -inf for a head with no probability at all
-  float nl[2];
-#pragma unroll
-  for (int hi = 0; hi < 2; ++hi) {
-    const float Ls = across_groups_sum(l[hi]), Lnc = across_groups_sum(l_nc[hi]);
-    const float lse2 = (m[hi] > NINF && Ls > 0.f) ? m[hi] + __log2f(Ls) : NINF;
-    const float lse2_nc = (m_nc[hi] > NINF && Lnc > 0.f) ? m_nc[hi] + __log2f(Lnc) : NINF;
-    nl[hi] = (ok[hi] && lse2 > NINF) ? -lse2 : NINF;   // exp2(-inf) = 0
-    if (ok[hi] && g == 0) {
-      lse[(int64_t)t * H + hh[hi]] = lse2 * LN2;
-      lse_nc[(int64_t)t * H + hh[hi]] = lse2_nc * LN2;
-    }
-  }
-
-  // ------------------------------------------------------- pass 2: P, cmass, then P.V
+  // ------------------------------------------------------- P, cmass, then P.V
   f32x4 o[8][8];   // O^T[d = 128 w + 16 dt + 4 g + i][head 16 ht + r16]
 #pragma unroll
   for (int ht = 0; ht < 8; ++ht)
@@ -415,8 +314,8 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
   const int psw = (2 * ((r16 >> 2) & 1)) ^ (3 * ((r16 >> 3) & 1));
   auto pbuf = [&](int n) { return pbufs + (n & 1) * WPBUF; };
   // P.V operands of the chunk of step n: V^T of the wave's 8 d-tiles by transposing reads
-  // (one batch with its wait, at the end of step n: the wait overlaps the step barrier that
-  // follows; the tile stays until step n + 2 requests rows) and P^T of the 8 head tiles
+  // (one batch with its wait, at the end of step n: the next step's request reuses the
+  // tile) and P^T of the 8 head tiles
   // (read during the last QK MFMAs of step n + 1, behind the barrier that publishes them)
   u32x4 va[8], pb[8];
   auto v_read = [&](int n) __attribute__((always_inline)) {
@@ -453,19 +352,20 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
       }
     }
   };
-  // the P buffer the first pass-2 step's P.V reads (there is no chunk before it) holds
-  // zeros; its tile holds the last pass-1 chunk's finite rows
-  if (nch > 0) {
-    for (int i = tid; i < WPBUF / 16; i += WNT) reinterpret_cast<u32x4 *>(pbuf(nch - 1))[i] = u32x4{0, 0, 0, 0};
-    v_read(nch - 1);
-  }
+  // the first step's P.V (there is no chunk before it) multiplies zeros: its P buffer
+  // (that of step -1) is cleared, its V^T operands are zero
+  for (int i = tid; i < WPBUF / 16; i += WNT) reinterpret_cast<u32x4 *>(pbuf(-1))[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) va[dt] = u32x4{0, 0, 0, 0};
+  lds_barrier();   // the mask table (written by wave 0)
+  uint32_t raw_next = cmask_raw(0);
   for (int ci = 0; ci < nch; ++ci) {
-    const int n = nch + ci;
+    const int n = ci;
     const ChunkReq rq = top(n);
     if (ci > 0) flush(ci - 1, n - 1);
     // P^T of the chunk before (at the first step: the zeroed P buffer) read during the last
     // QK MFMAs; its V^T operands are in registers since the end of the step before
-    const uint32_t bm_all = row_mask(ci), bm = bm_all >> (4 * g);   // read before the products
+    const uint32_t bm_all = row_mask(ci, raw_next), bm = bm_all >> (4 * g);
     f32x4 acc[2][2];
     qk(n, acc, rq, [&](int c, int j) __attribute__((always_inline)) {
       if (c == WNC - 2 && j == 0) pv_read_p(n - 1);
@@ -516,34 +416,52 @@ __global__ __launch_bounds__(WNT, 1) void sparse_attn_wide_kernel(
       sched_group<SG_VALU, 2>();
     }
     __builtin_amdgcn_sched_barrier(0);
+    // LDS reads before the V^T batch, whose wait covers them: the next chunk's key mask
+    // (past the last: unused) and the cmass partials of the chunk before (published by this
+    // step's barrier, overwritten only after the next one)
+    raw_next = cmask_raw(ci + 1);
     v_read(n);
   }
   wait_vmcnt<0>();   // no load into the LDS outlives the workgroup
+  // every wave's loads have landed and its tile reads are done: the tiles are free below
+  __syncthreads();   // (also: the last chunk's P and cmass partials of every wave)
   if (nch > 0) {
-    __syncthreads();   // the last chunk's P and cmass partials of every wave
     flush(nch - 1, ns - 1);
     pv_read_p(ns - 1);
     pv_mma();
   }
 
   // ---------------------------------------------------------------- outputs
+  // O^T of the wave's d-quarter goes through its own 16 KiB of the freed tiles, 64 heads at
+  // a time: bf16 rows [head][128 d] of 256 bytes whose 16-byte pieces are XOR-swizzled by
+  // head (the 8-byte writes of 32 lanes then cover all 64 banks once), read back 16 bytes
+  // per lane, so that each store writes four whole 256-byte row segments (stores of
+  // 16 head rows x 32 bytes each were several times slower)
+  char *ob = wide_dyn + w * (64 * 256);
 #pragma unroll
-  for (int ht = 0; ht < 8; ++ht) {
-    const int h = 16 * ht + r16;
-    if (h < H) {
-      uint16_t *orow = out + ((int64_t)t * H + h) * WD + 128 * w + 4 * g;
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int hq = 0; hq < 4; ++hq) {
+      const int ht = 4 * half + hq;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<uint2 *>(orow + 16 * dt) =
+        *reinterpret_cast<uint2 *>(ob + (16 * hq + r16) * 256 + 16 * ((2 * dt + (g >> 1)) ^ r16) + 8 * (g & 1)) =
             uint2{pack2_bf16(o[ht][dt][0], o[ht][dt][1]), pack2_bf16(o[ht][dt][2], o[ht][dt][3])};
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {   // rows 4 i + (lane >> 4), logical piece lane & 15
+      const int row = 4 * i + (lane >> 4), pc = lane & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * 256 + 16 * (pc ^ (row & 15)));
+      const int h = 64 * half + row;
+      if (h < H) *reinterpret_cast<u32x4 *>(out + ((int64_t)t * H + h) * WD + 128 * w + 8 * pc) = v;
     }
   }
 }
 
 template <int NTILE>
 static hipError_t launch_wide_t(const LaunchLayout &LL, const void *q, const void *kv, const void *ckv,
-                                const float *sink, const int32_t *ids, int k_eff, int window, int H, float scale,
-                                void *out, float *lse, float *lse_nc, float *cmass, hipStream_t st) {
+                                const int32_t *ids, int k_eff, int window, int H, float scale, const float *lse,
+                                void *out, float *cmass, hipStream_t st) {
   const size_t dyn = wide_attn_lds_bytes(NTILE, k_eff);
   auto kern = sparse_attn_wide_kernel<NTILE>;
   const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -551,22 +469,24 @@ static hipError_t launch_wide_t(const LaunchLayout &LL, const void *q, const voi
   if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL(kern, dim3((unsigned)LL.total_q), dim3(WNT), dyn, st, LL.dev,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
-                     static_cast<const uint16_t *>(ckv), sink, ids, k_eff, window, H, LL.total_q, LL.total_k,
-                     scale * LOG2E, static_cast<uint16_t *>(out), lse, lse_nc, cmass);
+                     static_cast<const uint16_t *>(ckv), ids, k_eff, window, H, LL.total_q, LL.total_k,
+                     scale * LOG2E, lse, static_cast<uint16_t *>(out), cmass);
   return hipGetLastError();
 }
 
-// four tiles (two chunks requested ahead) where the LDS holds them beside the P buffers,
-// the ids and the static arrays, else three
+// lse and lse_nc first (their own kernel), then P, out and cmass: four tiles (three chunks
+// requested ahead) where the LDS holds them beside the P buffers, the ids and the static
+// arrays, else three
 hipError_t launch_sparse_attn_wide(const LaunchLayout &LL, const void *q, const void *kv, const void *ckv,
                                    const float *sink, const int32_t *ids, int k_eff, int window, int H,
                                    float scale, void *out, float *lse, float *lse_nc, float *cmass,
                                    hipStream_t st) {
+  const hipError_t e = launch_sparse_attn_wide_lse(LL, q, kv, ckv, sink, ids, k_eff, window, H, scale, lse, lse_nc, st);
+  if (e != hipSuccess) return e;
   constexpr size_t LDS_CU = 160 * 1024, STATIC = 2 * 1024;   // cm_part and jlast
   if (WIDE_NTILE_MAX >= 4 && wide_attn_lds_bytes(4, k_eff) + STATIC <= LDS_CU)
-    return launch_wide_t<WIDE_NTILE_MAX>(LL, q, kv, ckv, sink, ids, k_eff, window, H, scale, out, lse, lse_nc,
-                                         cmass, st);
-  return launch_wide_t<3>(LL, q, kv, ckv, sink, ids, k_eff, window, H, scale, out, lse, lse_nc, cmass, st);
+    return launch_wide_t<WIDE_NTILE_MAX>(LL, q, kv, ckv, ids, k_eff, window, H, scale, lse, out, cmass, st);
+  return launch_wide_t<3>(LL, q, kv, ckv, ids, k_eff, window, H, scale, lse, out, cmass, st);
 }
 
 }  // namespace csa

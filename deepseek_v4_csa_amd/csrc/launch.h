@@ -31,6 +31,11 @@ hipError_t launch_sparse_attn_wide(const LaunchLayout &L, const void *q, const v
                                    float scale, void *out, float *lse, float *lse_nc, float *cmass,
                                    hipStream_t st);
 
+// its first pass: lse and lse_nc of every row (also bf16, D = 512, H <= 128)
+hipError_t launch_sparse_attn_wide_lse(const LaunchLayout &L, const void *q, const void *kv, const void *ckv,
+                                       const float *sink, const int32_t *ids, int k_eff, int window, int H,
+                                       float scale, float *lse, float *lse_nc, hipStream_t st);
+
 // attention whose epilogue also finishes the sparse teacher and KL (kl_row, teacher)
 // from the selected scores; only for shapes where attn_kl_fused_supported holds
 hipError_t launch_sparse_attn_kl(const LaunchLayout &L, const void *q, const void *kv,
