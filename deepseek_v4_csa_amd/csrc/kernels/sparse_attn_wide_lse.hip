@@ -18,7 +18,8 @@
 // rows are staged a chunk (32 rows, 32 KiB) at a time in two LDS tiles by direct
 // buffer->LDS loads, the next chunk requested right after each step's barrier, 16-byte
 // pieces XOR-swizzled by row_swz as in the other D = 512 kernel.  Each wave keeps a
-// running maximum per head (raised lazily, by 2^8 or more) and the sum of exponentials.
+// running maximum per head (raised lazily, by 2^8 or more) and the sum of exponentials,
+// folding a chunk's logits in while the next chunk's MFMAs run.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -192,6 +193,39 @@ __global__ __launch_bounds__(LNT, 1) void sparse_attn_wide_lse_kernel(
     m_nc[hi] = m[hi];
     l_nc[hi] = l[hi];
   }
+  // The masked logits of a chunk (sv) are folded one step later, beside the next chunk's
+  // MFMAs: the running maximum first (raised only when a logit passes it by RESCALE, in log2
+  // units; rarely, a branch), then one value's exponential per K-chunk
+  float sv[2][8];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[hi][e] = NINF;
+  auto raise_max = [&]() __attribute__((always_inline)) {
+    float cmx[2];
+    bool up = false;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      cmx[hi] = sv[hi][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) cmx[hi] = fmaxf(cmx[hi], sv[hi][e]);
+      up = up || cmx[hi] * sl2 > m[hi] + RESCALE;   // sl2 > 0 keeps the order
+    }
+    if (__builtin_expect(__ballot(up) != 0, 0)) {
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const float cand = across_groups_max(cmx[hi]) * sl2;
+        const float mn = cand > m[hi] + RESCALE ? cand : m[hi];
+        l[hi] *= mn == m[hi] ? 1.f : fast_exp2(m[hi] - mn);
+        m[hi] = mn;
+      }
+    }
+  };
+  float nm[2];
+  auto add_one = [&](int v) __attribute__((always_inline)) {
+    const int hi = v >> 3, e = v & 7;
+    l[hi] += fast_exp2(fmaf(sv[hi][e], sl2, nm[hi]));
+  };
   for (int n = 0; n < nch; ++n) {
     // the wave's loads of chunk n are the only ones in flight (the Q loads are older): then
     // the barrier publishes every wave's rows and frees the tile of chunk n - 1, which the
@@ -199,6 +233,9 @@ __global__ __launch_bounds__(LNT, 1) void sparse_attn_wide_lse_kernel(
     wait_vmcnt<0>();
     lds_barrier();
     const ChunkReq rq = request(n + 1);
+    raise_max();   // chunk n - 1
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) nm[hi] = m[hi] == NINF ? 0.f : -m[hi];
     // S^T = K Q^T of the chunk's 32 keys and the wave's 32 heads: acc[kt][hi][i] is the
     // logit (unscaled) of key 16 kt + 4 g + i and head 32 w + 16 hi + r16
     const char *tb = tile(n);
@@ -221,47 +258,29 @@ __global__ __launch_bounds__(LNT, 1) void sparse_attn_wide_lse_kernel(
         acc[0][hi] = mfma16x16x32(k0, qf[hi][c], c ? acc[0][hi] : z);
         acc[1][hi] = mfma16x16x32(k1, qf[hi][c], c ? acc[1][hi] : z);
       }
+      add_one(c);   // chunk n - 1, value c
       if (c % 2 == 1) issue_row(rq, c / 2);
     }
-    // masked logits into the running maximum (raised only when a logit passes it by
-    // RESCALE, in log2 units) and the sum of exponentials
-    const uint32_t bm = row_mask(n) >> (4 * g);
-    float sv[2][8], cmx[2];
-    bool up = false;
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sv[hi][e] = ((bm >> (16 * (e >> 2) + (e & 3))) & 1) ? acc[e >> 2][hi][e & 3] : NINF;
-      cmx[hi] = sv[hi][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) cmx[hi] = fmaxf(cmx[hi], sv[hi][e]);
-      up = up || cmx[hi] * sl2 > m[hi] + RESCALE;   // sl2 > 0 keeps the order
-    }
-    if (__builtin_expect(__ballot(up) != 0, 0)) {
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        const float cand = across_groups_max(cmx[hi]) * sl2;
-        const float mn = cand > m[hi] + RESCALE ? cand : m[hi];
-        l[hi] *= mn == m[hi] ? 1.f : fast_exp2(m[hi] - mn);
-        m[hi] = mn;
-      }
-    }
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const float nm = m[hi] == NINF ? 0.f : -m[hi];
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        s0 += fast_exp2(fmaf(sv[hi][e], sl2, nm));
-        s1 += fast_exp2(fmaf(sv[hi][e + 1], sl2, nm));
-      }
-      l[hi] += s0 + s1;
-    }
-    if (n + 1 == nwc) {   // every window chunk folded
+    if (n == nwc && n > 0) {   // every window chunk folded
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
     }
+    const uint32_t bm = row_mask(n) >> (4 * g);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sv[hi][e] = ((bm >> (16 * (e >> 2) + (e & 3))) & 1) ? acc[e >> 2][hi][e & 3] : NINF;
+  }
+  // the last chunk
+  raise_max();
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) nm[hi] = m[hi] == NINF ? 0.f : -m[hi];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) add_one(v);
+  if (nch == nwc && nch > 0) {
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
   }
   wait_vmcnt<0>();   // no load into the LDS outlives the workgroup
 
