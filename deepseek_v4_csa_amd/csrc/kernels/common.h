@@ -34,6 +34,27 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+// The same 16x16x32 bf16 product as asm statements, C and D in VGPRs: vector work placed
+// between them (tied to its place by empty asm statements, which keep their order with
+// these) runs beside the MFMAs.  The compiler does not pad hazards it does not see, so:
+//  * D is read only after mfma_v_fence: 16 wait states (this shape needs 8 before a vector
+//    instruction reads its result and 3 before one overwrites a C operand still being read);
+//  * C is the constant 0 or exactly D of the chain's previous MFMA (an exactly overlapping
+//    accumulation chain needs no wait states);
+//  * A and B are results of LDS and global loads, which the compiler waits for (it tracks the
+//    registers an asm statement reads); no vector instruction writes them.
+// Being volatile, the statements keep their order among themselves and with every memory
+// access, so the LDS reads and row requests issue where the source places them.
+// tests/test_mfma_hazards_cpu.py checks the compiled kernels against these rules.
+__device__ __forceinline__ void mfma_v_first(f32x4 &d, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x4 &d, const u32x4 &a, const u32x4 &b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_fence(f32x4 (&d)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(d[0][0]), "+v"(d[0][1]), "+v"(d[1][0]), "+v"(d[1][1]));
+}
 // 16x16x16 bf16: lane l supplies A[l%16][(l/16)*4 + e] and B[(l/16)*4 + e][l%16],
 // e = 0..3 (4 bf16 in two dwords); same C layout.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));

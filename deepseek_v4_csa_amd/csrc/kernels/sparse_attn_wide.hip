@@ -62,27 +62,10 @@ constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_TRANS = 0x400;
 template <int MASK, int N> __device__ __forceinline__ void sched_group() {
   __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
 }
-// S^T products on the 16x16x32 bf16 MFMA with C and D in VGPRs.  The builtin takes the
-// accumulator form the output tiles need (AGPRs, all 256 of them), which pushes 16 output
-// registers into VGPRs and copies them through AGPRs around every step; as asm statements
-// the S^T tiles stay in VGPRs.  The compiler does not pad hazards it does not see, so:
-//  * D is read only after mfma_v_fence: 16 wait states (this shape needs 8 before a vector
-//    instruction reads its result and 3 before one overwrites a C operand still being read);
-//  * C is the constant 0 or exactly D of the chain's previous MFMA (an exactly overlapping
-//    accumulation chain needs no wait states);
-//  * A and B are results of LDS and global loads, which the compiler waits for (it tracks the
-//    registers an asm statement reads); no vector instruction writes them.
-// Being volatile, the statements keep their order among themselves and with every memory
-// access, so the LDS reads and row requests issue where the source places them.
-__device__ __forceinline__ void mfma_v_first(f32x4 &d, const u32x4 &a, const u32x4 &b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v(f32x4 &d, const u32x4 &a, const u32x4 &b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v_fence(f32x4 (&d)[2][2]) {
-  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(d[0][0]), "+v"(d[0][1]), "+v"(d[1][0]), "+v"(d[1][1]));
-}
+// S^T products: the asm-statement MFMAs of common.h (mfma_v_first, mfma_v, mfma_v_fence).
+// The builtin would take the accumulator form the output tiles need (AGPRs, all 256 of
+// them), which pushes 16 output registers into VGPRs and copies them through AGPRs around
+// every step; as asm statements the S^T tiles stay in VGPRs.
 }  // namespace
 
 // NTILE tiles in the ring: chunks are requested NTILE - 1 steps ahead (a tile is last read

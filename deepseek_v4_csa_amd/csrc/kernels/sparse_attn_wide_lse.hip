@@ -221,10 +221,24 @@ __global__ __launch_bounds__(LNT, 1) void sparse_attn_wide_lse_kernel(
       }
     }
   };
-  float nm[2];
-  auto add_one = [&](int v) __attribute__((always_inline)) {
+  float nm[2], fx[16];
+  // the sum of value v (head tile v / 8): its FMA, exponential and addition in three MFMA
+  // windows of K-chunk v (j = 0, 1, 3), tied there by empty asm statements
+  auto add_step = [&](int v, int j) __attribute__((always_inline)) {
     const int hi = v >> 3, e = v & 7;
-    l[hi] += fast_exp2(fmaf(sv[hi][e], sl2, nm[hi]));
+    if (j == 0) {
+      asm volatile("" : "+v"(sv[hi][e]));
+      fx[v] = fmaf(sv[hi][e], sl2, nm[hi]);
+      asm volatile("" : "+v"(fx[v]));
+    } else if (j == 1) {
+      asm volatile("" : "+v"(fx[v]));
+      fx[v] = fast_exp2(fx[v]);
+      asm volatile("" : "+v"(fx[v]));
+    } else if (j == 3) {
+      asm volatile("" : "+v"(fx[v]));
+      l[hi] += fx[v];
+      asm volatile("" : "+v"(l[hi]));
+    }
   };
   for (int n = 0; n < nch; ++n) {
     // the wave's loads of chunk n are the only ones in flight (the Q loads are older): then
@@ -247,20 +261,23 @@ __global__ __launch_bounds__(LNT, 1) void sparse_attn_wide_lse_kernel(
     };
 #pragma unroll
     for (int c = 0; c < LLA; ++c) kread(c, kr[c]);
-    f32x4 acc[2][2];
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) asm volatile("" : "+v"(nm[hi]), "+v"(l[hi]));
+    f32x4 acc[2][2];   // acc[kt][hi]
 #pragma unroll
     for (int c = 0; c < LNC; ++c) {
       const u32x4 k0 = kr[c % LLA][0], k1 = kr[c % LLA][1];
       if (c + LLA < LNC) kread(c + LLA, kr[c % LLA]);
 #pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        acc[0][hi] = mfma16x16x32(k0, qf[hi][c], c ? acc[0][hi] : z);
-        acc[1][hi] = mfma16x16x32(k1, qf[hi][c], c ? acc[1][hi] : z);
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 &kk = (j & 1) ? k1 : k0;
+        if (c == 0) mfma_v_first(acc[j & 1][j >> 1], kk, qf[j >> 1][c]);
+        else mfma_v(acc[j & 1][j >> 1], kk, qf[j >> 1][c]);
+        add_step(c, j);   // chunk n - 1, value c
       }
-      add_one(c);   // chunk n - 1, value c
       if (c % 2 == 1) issue_row(rq, c / 2);
     }
+    mfma_v_fence(acc);
     if (n == nwc && n > 0) {   // every window chunk folded
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }
@@ -277,7 +294,9 @@ __global__ __launch_bounds__(LNT, 1) void sparse_attn_wide_lse_kernel(
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi) nm[hi] = m[hi] == NINF ? 0.f : -m[hi];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) add_one(v);
+  for (int v = 0; v < 16; ++v)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) add_step(v, j);
   if (nch == nwc && nch > 0) {
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) { m_nc[hi] = m[hi]; l_nc[hi] = l[hi]; }

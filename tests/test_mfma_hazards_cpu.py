@@ -1,7 +1,8 @@
-"""The wide attention kernel forms S^T with VGPR-form MFMAs written as asm statements
-(sparse_attn_wide.hip: mfma_v_first, mfma_v, mfma_v_fence), so the compiler pads no
-hazard for them.  This test compiles the kernel to gfx950 assembly with the library's own
-flags and checks, instruction by instruction, the rules the source relies on:
+"""The two D = 512 attention kernels form S^T with VGPR-form MFMAs written as asm
+statements (common.h: mfma_v_first, mfma_v, mfma_v_fence), so the compiler pads no hazard
+for them.  This test compiles both files (sparse_attn_wide.hip, sparse_attn_wide_lse.hip)
+to gfx950 assembly with the library's own flags and checks, instruction by instruction,
+the rules the source relies on:
 
 * each such MFMA and the fence after its chain (one asm statement of two `s_nop 7`, 16 wait
   states; this MFMA shape needs 8 before a vector instruction reads its result) lie in one
@@ -21,25 +22,29 @@ import pytest
 
 from deepseek_v4_csa_amd import build as B
 
-SRC = os.path.join(B.CSRC, "kernels", "sparse_attn_wide.hip")
-KERNEL_RE = re.compile(r"^(_ZN3csa23sparse_attn_wide_kernelILi\d+EE\S*):")
+SOURCES = {   # file: (extra flags as the library builds it, kernel symbol pattern)
+    "sparse_attn_wide.hip": ([], r"^(_ZN3csa23sparse_attn_wide_kernelILi\d+EE\S*):"),
+    "sparse_attn_wide_lse.hip": (B.VGPR_FORM, r"^(_ZN3csa27sparse_attn_wide_lse_kernel\S*):"),
+}
 
 
-def compile_asm(tmp_path):
-    out = tmp_path / "wide.s"
-    cmd = [B.HIPCC, *B.FLAGS, "--cuda-device-only", "-S", "-x", "hip", SRC, "-o", str(out)]
+def compile_asm(tmp_path, name="sparse_attn_wide.hip"):
+    out = tmp_path / (name + ".s")
+    src = os.path.join(B.CSRC, "kernels", name)
+    cmd = [B.HIPCC, *B.FLAGS, *SOURCES[name][0], "--cuda-device-only", "-S", "-x", "hip", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         pytest.fail(r.stderr[-2000:])
     return out.read_text()
 
 
-def kernels(asm):
+def kernels(asm, pattern):
     """{name: [(kind, text)]} with kind 'I' (instruction), 'L' (label), 'AS'/'AE' (asm
     statement start / end markers)."""
     res, cur = {}, None
+    kre = re.compile(pattern)
     for line in asm.split("\n"):
-        m = KERNEL_RE.match(line)
+        m = kre.match(line)
         if m:
             cur = res.setdefault(m.group(1), [])
             continue
@@ -160,8 +165,11 @@ def findings(ins):
 def wide_kernels(tmp_path_factory):
     if not os.path.exists(B.HIPCC):
         pytest.skip("hipcc not available")
-    ks = kernels(compile_asm(tmp_path_factory.mktemp("asm")))
-    assert len(ks) >= 2, "expected the three- and four-tile instantiations"
+    ks = {}
+    for name, (_, pattern) in SOURCES.items():
+        ks.update(kernels(compile_asm(tmp_path_factory.mktemp("asm"), name), pattern))
+    # the three- and four-tile instantiations of the second kernel, and the lse kernel
+    assert len(ks) >= 3, sorted(ks)
     return ks
 
 
