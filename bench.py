@@ -107,18 +107,18 @@ def work_model(wl):
 
 
 def traffic_of(wl_name, kernel):
-    """HBM bytes per launch of ``kernel`` from the committed counter table of the
-    workload (FETCH_SIZE / WRITE_SIZE scaled by a copy of known size), if it was taken
-    on the current source of the kernel; otherwise None."""
+    """HBM bytes per call of ``kernel`` (every kernel the call launches) from the committed
+    counter table of the workload (FETCH_SIZE / WRITE_SIZE scaled by a copy of known size),
+    if it was taken on the current sources of those kernels; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"csa_path_{wl_name}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path)).get("kernels", {}).get(kernel)
-    if not d:
+    if not d or not d.get("sources"):
         return None
-    sha = hashlib.sha256(open(os.path.join(ROOT, d["source"]), "rb").read()).hexdigest()
-    if d.get("source_sha256") != sha:
-        return None
+    for src, want in d["sources"].items():
+        if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != want:
+            return None
     return d.get("hbm_bytes_per_launch")
 
 
@@ -577,6 +577,14 @@ def _short(name: str) -> str:
     return re.sub(r"\(.*", "", name)
 
 
+def _source_of(name: str, fam: str) -> str:
+    if "sparse_attn_wide_lse" in name:
+        return "sparse_attn_wide_lse.hip"
+    if "sparse_attn_wide" in name:
+        return "sparse_attn_wide.hip"
+    return FAMILIES[fam][1]
+
+
 def _family_of(name: str):
     # the attention kernel that also finishes the teacher and KL (csa_sparse_attn_kl_fwd)
     if "csa::sparse_attn_pipe_kernel" in name and ", true>" in name:
@@ -639,10 +647,17 @@ def prof_traffic(wl: str, fdir: str, wdir: str, cfdir: str, cwdir: str, prefix: 
             continue
         wv = wm.get(name, 0.0)
         rd, wr = fv * fs, wv * ws
-        src = os.path.join(KSRC, "sparse_attn_wide.hip" if "sparse_attn_wide" in name else FAMILIES[fam][1])
-        table[fam] = {"kernel": _short(name), "dispatches": fn[name], "fetch_counter": fv, "write_counter": wv,
-                      "read_bytes": rd, "write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
-                      "source": os.path.relpath(src, ROOT), "source_sha256": _sha256(src)}
+        src = os.path.join(KSRC, _source_of(name, fam))
+        # one call may launch several kernels of the family (the D = 512 attention: the lse
+        # kernel, then the output kernel): their bytes add up per call
+        e = table.setdefault(fam, {"kernels": [], "read_bytes": 0.0, "write_bytes": 0.0,
+                                   "hbm_bytes_per_launch": 0.0, "sources": {}})
+        e["kernels"].append({"kernel": _short(name), "dispatches": fn[name], "fetch_counter": fv,
+                             "write_counter": wv, "read_bytes": rd, "write_bytes": wr})
+        e["read_bytes"] += rd
+        e["write_bytes"] += wr
+        e["hbm_bytes_per_launch"] += rd + wr
+        e["sources"][os.path.relpath(src, ROOT)] = _sha256(src)
         lines.append(f"{_short(name)[:50]:<50} {fn[name]:>4} {fv:>11.1f} {wv:>11.1f} {rd / 1e6:>9.2f} {wr / 1e6:>9.2f}")
     doc = {"workload": wl, "command": cmd, "fetch_scale": fs, "write_scale": ws, "kernels": table}
     json.dump(doc, open(prefix + ".json", "w"), indent=1)
