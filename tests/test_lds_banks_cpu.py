@@ -13,6 +13,8 @@ their own (and restated in csrc/kernels/common.h beside row_swz):
   over the 32 8-byte words of a line ((addr >> 3) & 31).
 * 4-byte accesses (not probed; the usual model): 64 lanes per cycle over 64 banks of
   4 bytes ((addr >> 2) & 63).
+* 8-byte accesses (not probed; the same model): 32 consecutive lanes per cycle over the 64
+  banks.
 
 Each pattern below restates a kernel's address arithmetic (the file and the names are
 given) and checks two things: the lane reads the element the kernel means (the storage
@@ -60,6 +62,18 @@ def cycles_b32(addrs):
         if a is not None:
             per_bank.setdefault((a >> 2) & 63, set()).add(a)
     return max(len(v) for v in per_bank.values())
+
+
+def cycles_b64(addrs):
+    total = 0
+    for h in (0, 1):
+        per_bank = {}
+        for lane in range(32 * h, 32 * h + 32):
+            a = addrs[lane]
+            for b in (a, a + 4):
+                per_bank.setdefault((b >> 2) & 63, set()).add(b)
+        total += max(len(v) for v in per_bank.values())
+    return total
 
 
 def quarters_used(addrs):
@@ -194,6 +208,43 @@ def test_wide_cmass_partials():
     for w in range(4):
         reads = [(w * 33 + t) * 4 if t < 32 else None for t in LANES]
         assert cycles_b32(reads) == 1
+
+
+def wide_out_write(lane, hq, dt, swz=True):
+    """sparse_attn_wide.hip outputs: lane (g, r16) writes bf16 d = 16 dt + 4 g .. + 3 of
+    staged head row 16 hq + r16 (256-byte rows) at piece (2 dt + g / 2) ^ r16, half g % 2."""
+    g, r16 = lane >> 4, lane & 15
+    piece = (2 * dt + (g >> 1)) ^ (r16 if swz else 0)
+    return (16 * hq + r16) * 256 + 16 * piece + 8 * (g & 1)
+
+
+def wide_out_read(lane, i, swz=True):
+    """Lane l reads 16 bytes, logical piece l % 16 of staged row 4 i + l / 16."""
+    row, pc = 4 * i + (lane >> 4), lane & 15
+    return row * 256 + 16 * (pc ^ ((row & 15) if swz else 0))
+
+
+def test_wide_output_staging():
+    """The output staging of the second D = 512 kernel: every read returns the 8 d values
+    8 pc .. 8 pc + 7 of its row that the writes put there, and both sides are free of bank
+    conflicts (a dropped head swizzle is not)."""
+    where = {}
+    for hq in range(4):
+        for dt in range(8):
+            addrs = [wide_out_write(l, hq, dt) for l in LANES]
+            assert cycles_b64(addrs) == 2, (hq, dt)
+            for l, a in enumerate(addrs):
+                g, r16 = l >> 4, l & 15
+                for k in range(4):   # bf16 value k of the lane's 8 bytes
+                    where[a + 2 * k] = (16 * hq + r16, 16 * dt + 4 * g + k)
+    assert len(where) == 64 * 128
+    for i in range(16):
+        addrs = [wide_out_read(l, i) for l in LANES]
+        assert cycles_b128(addrs) == 4, i
+        for l, a in enumerate(addrs):
+            row, pc = 4 * i + (l >> 4), l & 15
+            assert [where[a + 2 * k] for k in range(8)] == [(row, 8 * pc + k) for k in range(8)]
+    assert any(cycles_b64([wide_out_write(l, 0, dt, swz=False) for l in LANES]) > 2 for dt in range(8))
 
 
 # ---------------------------------------------------------------- indexer_score.hip
