@@ -352,6 +352,216 @@ __global__ __launch_bounds__(256) void idx_bwd_dq_kernel(
   }
 }
 
+// ---------------------------------------------------------------- 2'. dq / dweights, sparse loss
+// With the sparse loss a token's score gradients are zero off its K_t selected keys, so
+// this kernel gathers those key rows (as the attention does) instead of walking every key
+// tile below the causal limit (at 2,048 of 16,384 keys, an eighth of the work).  Per token
+// the products are the dense kernel's with heads in the place of tokens: D^T = K Q^T over
+// a chunk of 32 selected keys (keys x heads), E = G o [D > 0], U^T += K^T E (the MFMA k
+// index 8g + e <-> key 4g + e of the first 16-key tile, e < 4, or of the second, e >= 4,
+// so that D^T's output layout is E's operand layout); dq = ws * U, dweights = s_idx *
+// sum_j G max(D, 0).
+// A workgroup of 4 waves takes SP_TOK = 4 / WPT tokens; the WPT waves of a token split
+// its heads (32 each at Hi = 64) and share its LDS: the token's ids, two buffers of 32
+// gathered key rows (16-byte pieces XOR-swizzled by row_swz) and two of the 32 gathered
+// score gradients.  Each step: wait for the chunk's rows, one barrier, then the next
+// chunk's gradient gather and row loads (in that order: the gather's value is waited for
+// at the step's end without waiting for the rows), the products, the gradients into LDS.
+constexpr int SP_CH = 32;   // selected keys per step
+template <int DI, int HI>
+struct SparseDqShape {
+  static constexpr int WPT = HI == 64 ? 2 : 1;          // waves per token
+  static constexpr int TOK = 4 / WPT;                   // tokens per workgroup
+  static constexpr int HPW = HI / WPT;                  // heads per wave (<= 32)
+  static constexpr int NHT = HPW > 16 ? 2 : 1;          // 16-head MFMA tiles per wave
+  static constexpr int ROWB = DI * 2;
+  static constexpr int RB = SP_CH * ROWB;               // one chunk of rows
+  static constexpr int RPI = 1024 / ROWB;               // rows per 1 KiB load
+  static constexpr int NLD = SP_CH / RPI;               // loads per chunk
+  static_assert(NLD % WPT == 0, "the loads of a chunk split over the token's waves");
+};
+size_t sparse_dq_token_bytes(int DI, int k_eff) {
+  const int nsl = (k_eff + SP_CH - 1) / SP_CH * SP_CH;
+  return (size_t)2 * SP_CH * DI * 2 + (size_t)2 * SP_CH * 4 + (size_t)nsl * 4;
+}
+
+template <int DI, int HI>
+__global__ __launch_bounds__(256) void idx_bwd_dq_sparse_kernel(
+    LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
+    const float *__restrict__ weights, float idx_scale, const int32_t *__restrict__ ids, int k_eff,
+    const float *__restrict__ grad, int64_t ldg, int total_q, int total_k, float *__restrict__ dq,
+    float *__restrict__ dw) {
+  using S = SparseDqShape<DI, HI>;
+  constexpr int NCD = DI / 32, NDT = DI / 16, PIECES = DI / 8;
+  extern __shared__ __attribute__((aligned(16))) char sp_dyn[];
+  __shared__ int nch_wg;
+  const int nsl = (k_eff + SP_CH - 1) / SP_CH * SP_CH;
+  const int tokb = 2 * S::RB + 2 * SP_CH * 4 + nsl * 4;   // bytes per token (a multiple of 16)
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tk = w / S::WPT, wt = w % S::WPT;             // token of the workgroup, wave within it
+  const int t = total_q - 1 - ((int)blockIdx.x * S::TOK + tk);   // the longest rows first
+  const bool t_ok = t >= 0;
+  char *rows = sp_dyn + tk * tokb;                         // [2][SP_CH][ROWB]
+  float *gbuf = reinterpret_cast<float *>(rows + 2 * S::RB);   // [2][SP_CH]
+  int *ids_l = reinterpret_cast<int *>(gbuf + 2 * SP_CH);       // [nsl]
+  const int tq = t_ok ? t : 0;
+  const RowGeo geo = row_geo(L, tq);
+
+  // the token's ids (-1 past k_eff or for a token past the end) and its last valid slot
+  if (tid == 0) nch_wg = 0;
+  __syncthreads();
+  {
+    const __amdgpu_buffer_rsrc_t rid = make_rsrc(ids + (int64_t)tq * k_eff, t_ok ? (uint32_t)k_eff * 4 : 0u);
+    int jl = -1;
+    for (int j = 64 * wt + lane; j < nsl; j += 64 * S::WPT) {
+      const int x = __builtin_amdgcn_raw_buffer_load_b32(rid, j * 4, 0, 0);
+      const int id = j < k_eff && t_ok ? x : -1;
+      ids_l[j] = id;
+      jl = id >= 0 ? j : jl;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) jl = max(jl, __shfl_xor(jl, m, 64));
+    if (lane == 0 && jl >= 0) atomicMax(&nch_wg, jl / SP_CH + 1);
+  }
+  // Q^T operands of the wave's head tiles: piece c of lane group g holds features
+  // [(4c + g) 8, +8) of head h0 + 16 ht + r16 (a head past the wave's loads head 0's row:
+  // its outputs are not written)
+  const int h0 = wt * S::HPW;
+  u32x4 qf[S::NHT][NCD];
+#pragma unroll
+  for (int ht = 0; ht < S::NHT; ++ht) {
+    const int hl = 16 * ht + r16;
+    const int h = hl < S::HPW ? h0 + hl : 0;
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(q_idx + ((int64_t)tq * HI + h) * DI) + g;
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) qf[ht][c] = p[4 * c];
+  }
+  __syncthreads();   // ids and nch_wg
+  const int nch = nch_wg;   // steps of every token of the workgroup (its longest)
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_idx, (uint32_t)total_k * S::ROWB);   // id -1: past the end
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(grad + (int64_t)tq * ldg, t_ok ? (uint32_t)ldg * 4 : 0u);
+  // the score gradient of slot 32 c + (lane & 31) (0 at a -1 slot): one load per lane of
+  // the token's first wave
+  auto g_load = [&](int c) -> float {
+    const int id = ids_l[SP_CH * c + (lane & 31)];
+    const uint32_t off = id >= 0 ? (uint32_t)(id - geo.k_base) * 4 : BUF_OOB;
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rg, (int)off, 0, 0));
+  };
+  // rows of chunk c into buffer c & 1: load k (of NLD) moves rows k RPI .. k RPI + RPI - 1,
+  // lane l writes piece l % PIECES of row k RPI + l / PIECES at slot piece ^ row_swz(row)
+  const int kgg = lane / PIECES, kpp = lane % PIECES;
+  auto rows_load = [&](int c) {
+    char *dst = rows + (c & 1) * S::RB;
+#pragma unroll
+    for (int k = wt; k < S::NLD; k += S::WPT) {
+      const int R = k * S::RPI + kgg;
+      const int id = ids_l[SP_CH * c + R];
+      const uint32_t o = id >= 0 ? (uint32_t)id * S::ROWB + 16 * (kpp ^ row_swz<DI>(R)) : BUF_OOB;
+      dma16(rk, dst + k * 1024, o);
+    }
+  };
+  if (nch > 0) {
+    float gv0 = 0.f;
+    if (wt == 0) gv0 = g_load(0);
+    asm volatile("" ::: "memory");   // the gather before the row loads (waited for alone)
+    rows_load(0);
+    if (wt == 0 && lane < 32) gbuf[lane] = gv0;
+  }
+
+  f32x4 u[S::NHT][NDT];
+  float dwa[S::NHT];
+#pragma unroll
+  for (int ht = 0; ht < S::NHT; ++ht) {
+    dwa[ht] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) u[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // K^T operand rows: lane (g, r16) reads row 4g + r16 / 4 (+ 16), 8 bytes at piece
+  // 2 dt + ((r16 & 3) >> 1), half r16 & 1
+  const int rr = 4 * g + (r16 >> 2);
+  const int trb = rr * S::ROWB + 8 * (r16 & 1), trsw = row_swz<DI>(rr), trh = (r16 & 3) >> 1;
+  for (int c = 0; c < nch; ++c) {
+    wait_vmcnt<0>();   // the wave's rows of chunk c (the only loads in flight)
+    lds_barrier();     // every wave's rows and the gradients of chunk c; chunk c - 1's buffers free
+    float gnext = 0.f;
+    if (c + 1 < nch) {
+      if (wt == 0) gnext = g_load(c + 1);
+      asm volatile("" ::: "memory");
+      rows_load(c + 1);
+    }
+    const char *kb = rows + (c & 1) * S::RB;
+    const float *gb = gbuf + (c & 1) * SP_CH;
+    // D^T = K Q^T for the 32 keys (two 16-key tiles s) and the wave's head tiles
+    f32x4 d[2][S::NHT];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int R = 16 * s + r16;
+      u32x4 ka[NCD];
+#pragma unroll
+      for (int cc = 0; cc < NCD; ++cc)
+        ka[cc] = *reinterpret_cast<const u32x4 *>(kb + R * S::ROWB + 16 * ((4 * cc + g) ^ row_swz<DI>(R)));
+#pragma unroll
+      for (int ht = 0; ht < S::NHT; ++ht) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < NCD; ++cc) acc = mfma16x16x32(ka[cc], qf[ht][cc], acc);
+        d[s][ht] = acc;
+      }
+    }
+    // G of keys 16 s + 4 g + i
+    const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gb + 4 * g);
+    const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gb + 16 + 4 * g);
+    u32x4 ehi[S::NHT], elo[S::NHT];
+#pragma unroll
+    for (int ht = 0; ht < S::NHT; ++ht) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = d[0][ht][i] > 0.f ? g0[i] : 0.f;
+        e[4 + i] = d[1][ht][i] > 0.f ? g1[i] : 0.f;
+        dwa[ht] = fmaf(g0[i], fmaxf(d[0][ht][i], 0.f), dwa[ht]);
+        dwa[ht] = fmaf(g1[i], fmaxf(d[1][ht][i], 0.f), dwa[ht]);
+      }
+      split_bf16x8(e, ehi[ht], elo[ht]);
+    }
+    // K^T operands of the NDT dim tiles (one batch of transposing reads with its wait; the
+    // rows requested ahead stay in flight)
+    uint32_t ta[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) ta[dt] = lds_addr_of(kb + trb + 16 * ((2 * dt + trh) ^ trsw));
+    uint2 tv[2 * NDT];
+    lds_read_tr16_pairs<16 * S::ROWB, NDT>(tv, ta);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const u32x4 kt_op = u32x4{tv[2 * dt].x, tv[2 * dt].y, tv[2 * dt + 1].x, tv[2 * dt + 1].y};
+#pragma unroll
+      for (int ht = 0; ht < S::NHT; ++ht) {
+        u[ht][dt] = mfma16x16x32(kt_op, ehi[ht], u[ht][dt]);
+        u[ht][dt] = mfma16x16x32(kt_op, elo[ht], u[ht][dt]);
+      }
+    }
+    if (wt == 0 && lane < 32 && c + 1 < nch) gbuf[((c + 1) & 1) * SP_CH + lane] = gnext;
+  }
+  wait_vmcnt<0>();   // no load into the LDS outlives the workgroup
+  // outputs: lane (head r16 of tile ht, group g) holds dims 16 dt + 4 g + i of U^T
+#pragma unroll
+  for (int ht = 0; ht < S::NHT; ++ht) {
+    float sdw = dwa[ht];
+    sdw += __shfl_xor(sdw, 16, 64);
+    sdw += __shfl_xor(sdw, 32, 64);
+    const int hl = 16 * ht + r16;
+    if (t_ok && hl < S::HPW) {
+      const int64_t row = (int64_t)t * HI + h0 + hl;
+      const float ws = weights[row] * idx_scale;
+      float *dst = dq + row * DI + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = u[ht][dt] * ws;
+      if (g == 0) dw[row] = sdw * idx_scale;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- 3. dk
 // First 16-token block of a segment holding a token that sees key j0: n_valid(t) > j0
 // exactly when the token's position i = t + 1 + off reaches (j0 + 1) * ratio.  The number
@@ -585,15 +795,30 @@ int64_t indexer_bwd_workspace_bytes(int num_seqs, int total_k, int max_seqlen_q,
   return ns > 1 ? (int64_t)ns * total_k * Di * (int64_t)sizeof(float) : 0;
 }
 
+// dq / dweights: the selected keys' rows gathered per token (sparse loss), else every
+// causal key tile per 16-token block
 template <int DI, int HI, int HPW, int HW = HI>
-static hipError_t launch_bwd_t(const LaunchLayout &LL, const void *q_idx, const void *k_idx,
+static hipError_t launch_bwd_t(const LaunchLayout &LL, bool sparse, const int32_t *ids, int k_eff,
+                               const void *q_idx, const void *k_idx,
                                const float *weights, float idx_scale, const float *grad, int64_t ldg,
                                float *dq, float *dw, float *dk, float *ws, hipStream_t st) {
   const int nqb = (LL.max_seqlen_q + BWD_TOK - 1) / BWD_TOK;
   const int nkt = (LL.max_seqlen_k + DK_TILE - 1) / DK_TILE;
   int ch, ns;
   indexer_bwd_dk_split(LL.num_seqs, LL.max_seqlen_q, LL.max_seqlen_k, &ch, &ns);
-  if (LL.total_q > 0) {
+  if (LL.total_q > 0 && sparse) {
+    using S = SparseDqShape<DI, HI>;
+    const size_t dyn = (size_t)S::TOK * sparse_dq_token_bytes(DI, k_eff);
+    auto kern = idx_bwd_dq_sparse_kernel<DI, HI>;
+    const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (ea != hipSuccess) return ea;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((LL.total_q + S::TOK - 1) / S::TOK)), dim3(256), dyn, st, LL.dev,
+                       static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx), weights,
+                       idx_scale, ids, k_eff, grad, ldg, LL.total_q, LL.total_k, dq, dw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (LL.total_q > 0) {
     hipLaunchKernelGGL((idx_bwd_dq_kernel<DI, HI, HPW, HW>), dim3((unsigned)(LL.num_seqs * nqb * (HI / HW))),
                        dim3(256), 0, st,
                        LL.dev, static_cast<const uint16_t *>(q_idx), static_cast<const uint16_t *>(k_idx),
@@ -636,7 +861,7 @@ hipError_t launch_indexer_loss_bwd(const LaunchLayout &LL, bool sparse, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#define CSA_BWD_ARGS LL, q_idx, k_idx, weights, idx_scale, grad, ld_grad, dq, dw, dk, \
+#define CSA_BWD_ARGS LL, sparse, ids, k_eff, q_idx, k_idx, weights, idx_scale, grad, ld_grad, dq, dw, dk, \
                      static_cast<float *>(workspace), st
   if (Di == 64) {
     switch (Hi) {
