@@ -4,7 +4,7 @@
 // compressed-only teacher ...": the proposal comment keeps a custom backward that
 // recomputes from saved tensors and returns gradients only for the indexer q, weights
 // and k, the teacher being detached; page "Megatron-LM pull request 8539", item 1: the
-// sparse path's ids are global).  Three kernels:
+// sparse path's ids are global).  The kernels:
 //
 //  1. score gradients, one wave per row: with the forward's predictor p = softmax of the
 //     scores over the support and the given teacher t,
@@ -13,10 +13,12 @@
 //     row's 16-token block reaches -- every column the next two kernels read (the sparse
 //     mode writes the zeros, waits for them, then scatters).  Normalisers and g in fp64,
 //     like the forward's KL.
-//  2. dq / dweights, one workgroup per 16-token block: for every 64-key tile below the
-//     block's causal limit and every indexer head h, D^T = K Q_h^T (keys x tokens) is
-//     recomputed on MFMA, E = G o [D > 0], and U_h^T += K^T E on MFMA; at the end
-//     dq = ws * U and dweights = s_idx * sum_j G max(D, 0).
+//  2. dq / dweights.  Sparse loss: per token, its selected key rows gathered 32 at a time
+//     (idx_bwd_dq_sparse_kernel, heads in the place of tokens below).  Dense loss: one
+//     workgroup per 16-token block: for every 64-key tile below the block's causal limit
+//     and every indexer head h, D^T = K Q_h^T (keys x tokens) is recomputed on MFMA,
+//     E = G o [D > 0], and U_h^T += K^T E on MFMA; at the end dq = ws * U and
+//     dweights = s_idx * sum_j G max(D, 0).
 //  3. dk, one workgroup per (128-key tile of a segment, chunk of 16-token blocks) (wave =
 //     2 x 16 keys): for every block of the chunk with a token that sees the tile,
 //     D = Q_h K^T, E'' = G * ws o [D > 0], and dK^T += Q_h^T E'' on MFMA, summed over
