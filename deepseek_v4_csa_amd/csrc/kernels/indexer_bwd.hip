@@ -162,9 +162,10 @@ __device__ __forceinline__ void dma_rows(const uint16_t *base, int row0, int tot
                                          int w, int nw, int lane) {
   constexpr int CPP = PB / 16;
   static_assert(CPP >= BWD_TOK && (PB % 512) == 0, "the XOR swizzle needs 16-chunk rows");
-  const int rows_left = min(BWD_TOK, total_rows - row0);
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc(base + (int64_t)row0 * (RB / 2), (uint32_t)(max(rows_left, 0) * RB));
+  // uniform, but v_med3 computes it in a VGPR: without readfirstlane the descriptor is
+  // taken as divergent and every load below gets a waterfall loop
+  const int rows_left = __builtin_amdgcn_readfirstlane(max(min(BWD_TOK, total_rows - row0), 0));
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(base + (int64_t)row0 * (RB / 2), (uint32_t)(rows_left * RB));
   if constexpr (PB >= 1024) {
     constexpr int IPR = PB / 1024;
     for (int m = w; m < BWD_TOK * IPR; m += nw) {
@@ -577,10 +578,14 @@ __device__ __forceinline__ int first_block_seeing(int j0, int off, int ratio, in
 // grid: num_seqs x nkt x nsplit (segment fastest); a workgroup owns a DK_TILE-key tile
 // (wave = two 16-key sub-tiles, so every LDS operand read feeds both) and the blocks
 // [s*ch, (s+1)*ch) of split s that see it, and writes its sum to out + s*split_stride
-// (split_stride 0 with one split: out is dk itself).  Each block is taken in NG steps of
-// HG heads, so only 16 rows x HG heads of q (16 KiB) sit in each LDS buffer.
+// (split_stride 0 with one split: out is dk itself).  The blocks are taken in pairs, so
+// that dK^T += Q_h^T E'' contracts 32 tokens per MFMA (the 16x16x32 form; MFMA k index
+// 8g + e <-> token 4g + e of the pair's first block, e < 4, or of its second, e >= 4 --
+// exactly the two blocks' D output layouts); a pair is taken in NG steps of HG heads, so
+// only 2 x 16 rows x HG heads of q sit in each LDS buffer.  A second block past the
+// workgroup's range contributes nothing (its G is 0).
 template <int DI, int HI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DI == 64 ? 4 : 2))) void idx_bwd_dk_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void idx_bwd_dk_kernel(
     LayoutDev L, const uint16_t *__restrict__ q_idx, const uint16_t *__restrict__ k_idx,
     const float *__restrict__ weights, float idx_scale, const float *__restrict__ grad, int64_t ldg,
     int total_q, int nkt, int ch, int64_t split_stride, float *__restrict__ out) {
@@ -588,8 +593,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DI == 64 ? 
   constexpr int HG = HI < 512 / DI ? HI : 512 / DI;   // heads per step
   constexpr int NG = HI / HG, PB = HG * DI * 2;       // steps per block, bytes per staged row
   constexpr int NCD = DI / 32, NDT = DI / 16;
-  __shared__ __attribute__((aligned(16))) u32x4 qs[2][BWD_TOK * PB / 16];
-  __shared__ __attribute__((aligned(16))) float wsl[2][HI * BWD_TOK];   // [h][token]
+  constexpr int QBLK = BWD_TOK * PB / 16;   // u32x4 of one staged block
+  __shared__ __attribute__((aligned(16))) u32x4 qs[2][2 * QBLK];            // [buffer][block of the pair]
+  __shared__ __attribute__((aligned(16))) float wsl[2][2][HI * BWD_TOK];   // [buffer][block][h][token]
 
   const int seg = blockIdx.x % L.num_seqs;
   const int rest = (int)(blockIdx.x / L.num_seqs);
@@ -637,103 +643,164 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DI == 64 ? 
     return;
   }
 
-  // per block b: fp32(w * s_idx) through registers into wsl[(b - b_lo) & 1] (loaded at
-  // the block before's first step, stored after its last), this lane's G[t0 + 4g + i, jj]
-  // (0 past the segment) likewise one block ahead; per step: the step's q rows by DMA
-  // into qs[step & 1], issued one step ahead
+  // per pair p: fp32(w * s_idx) through registers into wsl[p & 1] (loaded at the pair
+  // before's first step, stored after its last), this lane's G[t0 + 4g + i, jj] of both
+  // blocks (0 past the range or the segment) likewise one pair ahead; per step: the step's
+  // q rows of both blocks by DMA into qs[step & 1], issued one step ahead
+  const int npair = (b_hi - b_lo + 1) / 2;
   constexpr int WPT = (HI * BWD_TOK + 255) / 256;
-  float wreg[WPT];
-  auto load_w = [&](int b) __attribute__((always_inline)) {
+  float wreg[2][WPT];
+  auto load_w = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < WPT; ++k) {
-      const int e = tid + 256 * k, tt = e / HI, h = e - tt * HI;
-      const int t = b * BWD_TOK + tt;
-      wreg[k] = (e < HI * BWD_TOK && t < q_len) ? weights[(int64_t)(q_start + t) * HI + h] : 0.f;
+    for (int bs = 0; bs < 2; ++bs) {
+      const int b = b_lo + 2 * p + bs;
+#pragma unroll
+      for (int k = 0; k < WPT; ++k) {
+        const int e = tid + 256 * k, tt = e / HI, h = e - tt * HI;
+        const int t = b * BWD_TOK + tt;
+        wreg[bs][k] = (e < HI * BWD_TOK && b < b_hi && t < q_len) ? weights[(int64_t)(q_start + t) * HI + h] : 0.f;
+      }
     }
   };
   auto store_w = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < WPT; ++k) {
-      const int e = tid + 256 * k, tt = e / HI, h = e - tt * HI;
-      if (e < HI * BWD_TOK) wsl[buf][h * BWD_TOK + tt] = wreg[k] * idx_scale;
-    }
-  };
-  float gcur[2][4], gnext[2][4];
-  auto load_g = [&](int b, float (&dst)[2][4]) __attribute__((always_inline)) {
+    for (int bs = 0; bs < 2; ++bs)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = b * BWD_TOK + 4 * g + i;
-        dst[u][i] = (t < q_len && jok[u]) ? grad[(int64_t)(q_start + t) * ldg + jj[u]] : 0.f;
+      for (int k = 0; k < WPT; ++k) {
+        const int e = tid + 256 * k, tt = e / HI, h = e - tt * HI;
+        if (e < HI * BWD_TOK) wsl[buf][bs][h * BWD_TOK + tt] = wreg[bs][k] * idx_scale;
       }
+  };
+  float gcur[2][2][4], gnext[2][2][4];   // [block][sub-tile][i]
+  auto load_g = [&](int p, float (&dst)[2][2][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int bs = 0; bs < 2; ++bs) {
+      const int b = b_lo + 2 * p + bs;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = b * BWD_TOK + 4 * g + i;
+          dst[bs][u][i] = (b < b_hi && t < q_len && jok[u]) ? grad[(int64_t)(q_start + t) * ldg + jj[u]] : 0.f;
+        }
+    }
   };
   auto stage_q = [&](int st, int buf) __attribute__((always_inline)) {
-    const int b = b_lo + st / NG, hg = st - (st / NG) * NG;
-    dma_rows<RB, PB>(q_idx, q_start + b * BWD_TOK, total_q, hg * PB, reinterpret_cast<char *>(qs[buf]), w, 4,
-                     lane);
+    const int p = st / NG, hg = st - (st / NG) * NG;
+#pragma unroll
+    for (int bs = 0; bs < 2; ++bs)
+      dma_rows<RB, PB>(q_idx, q_start + (b_lo + 2 * p + bs) * BWD_TOK, total_q, hg * PB,
+                       reinterpret_cast<char *>(qs[buf] + bs * QBLK), w, 4, lane);
+  };
+  // the same loads one at a time (load k of the wave's NSL), spread over a step's heads: a
+  // burst of them holds the issuing wave until the memory pipeline's queue takes them
+  constexpr int RPL = PB >= 1024 ? 1 : 1024 / PB;       // rows per load
+  constexpr int NSL = 2 * (BWD_TOK / RPL) * (PB >= 1024 ? PB / 1024 : 1) / 4;   // the wave's loads per step
+  static_assert(NSL >= 1 && NSL % HG == 0 || HG % NSL == 0, "loads per head");
+  auto stage_q_part = [&](int st, int buf, int k) __attribute__((always_inline)) {
+    const int p = st / NG, hg = st - (st / NG) * NG;
+    constexpr int PERB = NSL / 2;                         // the wave's loads per block
+    const int bs = k / PERB, m = w + 4 * (k - bs * PERB);   // load m of the block (dma_rows' order)
+    const int row0 = q_start + (b_lo + 2 * p + bs) * BWD_TOK;
+    const int rows_left = __builtin_amdgcn_readfirstlane(max(min(BWD_TOK, total_q - row0), 0));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q_idx + (int64_t)row0 * (RB / 2), (uint32_t)(rows_left * RB));
+    char *dst = reinterpret_cast<char *>(qs[buf] + bs * QBLK);
+    constexpr int CPP = PB / 16;
+    if constexpr (PB >= 1024) {
+      constexpr int IPR = PB / 1024;
+      const int r = m / IPR, q0 = (m - r * IPR) * 64;
+      dma16(rq, dst + (size_t)(r * CPP + q0) * 16, (uint32_t)(r * RB + hg * PB + (((q0 + lane) ^ r) << 4)));
+    } else {
+      const int r = m * RPL + lane / CPP, c = lane % CPP;
+      dma16(rq, dst + (size_t)m * 1024, (uint32_t)(r * RB + hg * PB + ((c ^ r) << 4)));
+    }
   };
   stage_q(0, 0);
-  load_w(b_lo);
-  load_g(b_lo, gcur);
+  load_w(0);
+  load_g(0, gcur);
   store_w(0);
-  const int nsteps = (b_hi - b_lo) * NG;
+  const int nsteps = npair * NG;
   const int rr = 4 * g + (r16 >> 2);   // row this lane addresses in the transposing read
   for (int st = 0; st < nsteps; ++st) {
-    const int bi = st / NG, hg = st - bi * NG;
-    const int b = b_lo + bi;
-    const bool more = b + 1 < b_hi;
+    const int p = st / NG, hg = st - p * NG;
+    const bool more = p + 1 < npair;
     wait_vmcnt<0>();
-    __syncthreads();   // step st staged (q rows by DMA; at a block's first step its weights)
-    if (st + 1 < nsteps) stage_q(st + 1, (st + 1) & 1);
+    __syncthreads();   // step st staged (q rows by DMA; at a pair's first step its weights)
     if (hg == 0 && more) {
-      load_w(b + 1);
-      load_g(b + 1, gnext);
+      load_w(p + 1);
+      load_g(p + 1, gnext);
     }
     const char *qb = reinterpret_cast<const char *>(qs[st & 1]);
-    const char *qrow = qb + r16 * PB;
-    const float *wsb = wsl[bi & 1] + hg * HG * BWD_TOK;
 #pragma unroll 2
     for (int hh = 0; hh < HG; ++hh) {
-      // D = Q_h K^T per sub-tile: A = Q_h rows (token r16, piece 4c+g), B = key operand
-      f32x4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      // the next step's q rows, NSL / HG loads per head (or one every HG / NSL heads)
+      if (st + 1 < nsteps) {
+        if constexpr (NSL >= HG) {
 #pragma unroll
-      for (int c = 0; c < NCD; ++c) {
-        const int q = hh * (DI / 8) + 4 * c + g;
-        const u32x4 qa = *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
-        d[0] = mfma16x16x32(qa, kb[0][c], d[0]);
-        d[1] = mfma16x16x32(qa, kb[1][c], d[1]);
+          for (int k = hh * (NSL / HG); k < (hh + 1) * (NSL / HG); ++k) stage_q_part(st + 1, (st + 1) & 1, k);
+        } else if (hh % (HG / NSL) == 0) {
+          stage_q_part(st + 1, (st + 1) & 1, hh / (HG / NSL));
+        }
       }
-      // lane (key r16, group g) holds D[token 4g + i][key] of each sub-tile
-      const f32x4 wv = *reinterpret_cast<const f32x4 *>(wsb + hh * BWD_TOK + 4 * g);
-      uint2 ehi[2], elo[2];
+      // D = Q_h K^T per block and sub-tile: A = Q_h rows (token r16, piece 4c+g), B = key
+      // operand; lane (key r16, group g) holds D[token 4g + i][key]
+      f32x4 d[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+#pragma unroll
+      for (int bs = 0; bs < 2; ++bs) {
+        const char *qrow = qb + bs * BWD_TOK * PB + r16 * PB;
+#pragma unroll
+        for (int c = 0; c < NCD; ++c) {
+          const int q = hh * (DI / 8) + 4 * c + g;
+          const u32x4 qa = *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
+          d[bs][0] = mfma16x16x32(qa, kb[0][c], d[bs][0]);
+          d[bs][1] = mfma16x16x32(qa, kb[1][c], d[bs][1]);
+        }
+      }
+      const int wo = (hg * HG + hh) * BWD_TOK + 4 * g;
+      const f32x4 wv0 = *reinterpret_cast<const f32x4 *>(&wsl[p & 1][0][wo]);
+      const f32x4 wv1 = *reinterpret_cast<const f32x4 *>(&wsl[p & 1][1][wo]);
+      u32x4 ehi[2], elo[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        float e[4];
+        float e[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = d[u][i] > 0.f ? gcur[u][i] * wv[i] : 0.f;
-        split_bf16x4(e, ehi[u], elo[u]);
+        for (int i = 0; i < 4; ++i) {
+          e[i] = d[0][u][i] > 0.f ? gcur[0][u][i] * wv0[i] : 0.f;
+          e[4 + i] = d[1][u][i] > 0.f ? gcur[1][u][i] * wv1[i] : 0.f;
+        }
+        split_bf16x8(e, ehi[u], elo[u]);
       }
-      // Q_h^T operand (dims 16dt + r16 x tokens 4g .. +3) by the transposing read:
-      // lane supplies row 4g + r16/4, dims 16dt + 4(r16%4) .. +3 of head h
+      // Q_h^T operand (dims 16dt + r16 x the pair's tokens) by two transposing reads, one
+      // per block (rows 16 apart: the same swizzle): lane supplies row 4g + r16/4, dims
+      // 16dt + 4(r16%4) .. +3 of head h.  One batch with its own wait: the builtin read
+      // would first wait for the next step's q rows in flight
+      uint32_t ta[NDT];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int col = hh * DI + 16 * dt + 4 * (r16 & 3);   // bf16 column in the staged row
         const int q = col >> 3;                               // 16-byte chunk
-        const uint2 qt = lds_read_tr16(qb + rr * PB + ((q ^ rr) << 4) + 8 * ((col >> 2) & 1));
+        ta[dt] = lds_addr_of(qb + rr * PB + ((q ^ rr) << 4) + 8 * ((col >> 2) & 1));
+      }
+      uint2 tv[2 * NDT];
+      lds_read_tr16_pairs<BWD_TOK * PB, NDT>(tv, ta);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const u32x4 qt = u32x4{tv[2 * dt].x, tv[2 * dt].y, tv[2 * dt + 1].x, tv[2 * dt + 1].y};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          acc[u][dt] = mfma16x16x16(qt, ehi[u], acc[u][dt]);
-          acc[u][dt] = mfma16x16x16(qt, elo[u], acc[u][dt]);
+          acc[u][dt] = mfma16x16x32(qt, ehi[u], acc[u][dt]);
+          acc[u][dt] = mfma16x16x32(qt, elo[u], acc[u][dt]);
         }
       }
     }
     if (hg == NG - 1 && more) {
-      store_w((bi + 1) & 1);   // its last readers (block b - 1) passed the barriers of block b
+      store_w((p + 1) & 1);   // its last readers (pair p - 1) passed the barriers of pair p
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int bs = 0; bs < 2; ++bs)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gcur[u][i] = gnext[u][i];
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gcur[bs][u][i] = gnext[bs][u][i];
     }
     __syncthreads();   // every wave is done with qs[st & 1] before it is restaged
   }
@@ -779,7 +846,12 @@ __global__ __launch_bounds__(256) void idx_bwd_dk_reduce_kernel(LayoutDev L, int
 
 // ---------------------------------------------------------------- launch
 // Chunks of token blocks per key tile: enough workgroups to fill the chip (about 1024),
-// at least 4 blocks per chunk.
+// at least 4 and at most DK_MAX_CHUNK blocks per chunk.  The cap matters for long
+// sequences: causality leaves only about half of the key tile x chunk workgroups with
+// work, each the same length, and with chunks of hundreds of blocks their count lands
+// just above the 512 the chip holds at once (two per CU), so a second round of a few
+// runs on an idle chip; short chunks make it a smaller share of the whole.
+constexpr int DK_MAX_CHUNK = 64;
 void indexer_bwd_dk_split(int num_seqs, int max_seqlen_q, int max_seqlen_k, int *ch, int *ns) {
   const int nqb = (max_seqlen_q + BWD_TOK - 1) / BWD_TOK;
   const int nkt = (max_seqlen_k + DK_TILE - 1) / DK_TILE;
@@ -787,7 +859,7 @@ void indexer_bwd_dk_split(int num_seqs, int max_seqlen_q, int max_seqlen_k, int 
   long long want = (1024 + tiles - 1) / tiles;
   want = std::max(1LL, std::min(want, (long long)(nqb + 3) / 4));
   const int c = (int)((nqb + want - 1) / want);
-  *ch = std::max(c, 1);
+  *ch = std::min(std::max(c, 1), DK_MAX_CHUNK);
   *ns = (nqb + *ch - 1) / *ch;
 }
 

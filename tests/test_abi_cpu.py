@@ -110,6 +110,10 @@ def test_argument_misuse_is_rejected(lib):
     Lb = _layout(ops, total_q=4096, max_seqlen_q=4096, total_k=1024, max_seqlen_k=1024)
     need = lib.csa_indexer_loss_bwd_workspace(B(Lb), 16, 64)
     assert need == 64 * 1024 * 64 * 4
+    # 65,536 tokens, 128 key tiles: 8 chunks would fill the chip, but a chunk holds at most
+    # 64 of the 4,096 token blocks, so 64 chunks of partials (Di = 128)
+    Ll = _layout(ops, total_q=65536, max_seqlen_q=65536, total_k=16384, max_seqlen_k=16384)
+    assert lib.csa_indexer_loss_bwd_workspace(B(Ll), 64, 128) == 64 * 16384 * 128 * 4
     a = list(args); a[0] = B(Lb); a[10] = a[19] = 1024; a[24] = need - 1
     assert bwd(*a) == 1                                                            # workspace too small
     assert "workspace" in lib.csa_last_error().decode()
