@@ -22,8 +22,10 @@ namespace csa {
 constexpr int TK_THREADS = 512;   // 256 and 1,024 measured slower on 16k-key rows
 constexpr int TK_WAVES = TK_THREADS / 64;
 
-// One workgroup per row (rows above 4096 keys).  Wave w owns the contiguous run of keys
-// j = 64 VPT w + 64 v + lane (key[v] of the lane), so every load instruction reads 256
+// One workgroup per row (rows above 4096 keys).  Each lane holds vpt = ceil(n / 512) <= VPT
+// of the row's n visible keys (the rows of one launch differ in length, and every pass
+// below runs over vpt slots, not VPT); wave w owns the contiguous run of keys
+// j = 64 vpt w + 64 v + lane (key[v] of the lane), so every load instruction reads 256
 // bytes of the row contiguously and index order is wave, then v, then lane.  The radix
 // passes stop as soon as the threshold bin is taken whole.  Compaction: each wave counts
 // its keys above the threshold and its ties (ballot popcounts), the waves' totals pass
@@ -48,7 +50,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const RowGeo g = row_geo(L, t);
   const int n = g.n_valid;
-  auto jof = [&](int v) { return 64 * VPT * w + 64 * v + lane; };
+  // slots in use (uniform; the loops below stop at vpt).  At VPT = 64 a run-time bound
+  // leaves the compiler unable to keep key[] in registers, so those rows take all slots
+  const int vpt = VPT >= 64 ? VPT : min(VPT, (n + 64 * TK_WAVES - 1) / (64 * TK_WAVES));
+  auto jof = [&](int v) { return 64 * vpt * w + 64 * v + lane; };
   int32_t *out = ids + (int64_t)t * k_eff;
   float *sout = SEL ? sel + (int64_t)t * k_eff : nullptr;
   const float *row = scores + (int64_t)t * ld;
@@ -67,11 +72,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   uint32_t key[VPT];
 #pragma unroll
   for (int v = 0; v < VPT; ++v)
-    key[v] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rrow, jof(v) * 4, 0, 0);
+    key[v] = v < vpt ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rrow, jof(v) * 4, 0, 0) : 0u;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const bool in = jof(v) < n;
+    const bool in = v < vpt && jof(v) < n;
     key[v] = in ? ordered_key(__uint_as_float(key[v])) : 0u;
     kmin = in ? min(kmin, key[v]) : kmin;
     kmax = in ? max(kmax, key[v]) : kmax;
@@ -101,6 +106,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
+      if (v >= vpt) break;
       const bool in_play = jof(v) < n && (cur >= 32 || (key[v] >> cur) == thr);
       if (in_play) atomicAdd(&hist[(key[v] >> sh) & ((1u << width) - 1u)], 1u);
     }
@@ -149,6 +155,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   int tg = 0, te = 0;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
+    if (v >= vpt) break;
     uint64_t bg, be;
     ballots(v, bg, be);
     tg += __popcll(bg);
@@ -164,6 +171,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayoutDev L, const flo
   }
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
+    if (v >= vpt) break;
     uint64_t bg, be;
     ballots(v, bg, be);
     const int gt_before = og + __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0));
