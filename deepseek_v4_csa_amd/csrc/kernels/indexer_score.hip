@@ -889,18 +889,20 @@ hipError_t launch_indexer_topk(const LaunchLayout &LL, const void *q_idx, const 
 
 // ============================================================================
 // Head-grouped variant for long q_idx rows (bf16, Hi * Di * 2 above what the paired-block
-// kernel stages).  One workgroup (8 waves) = 16 tokens x 512 keys; wave w = the 16 tokens
+// kernel stages).  One workgroup (4 waves) = 16 tokens x 256 keys; wave w = the 16 tokens
 // x 64 keys (64 w), its key fragments in registers for the whole head loop.  The q rows
 // are staged in LDS one head group at a time (HG heads = 512 bytes of each token row,
-// 8 KiB per group: one 1 KiB buffer->LDS load, two rows, per wave), chunk q of token row
+// 8 KiB per group: two 1 KiB buffer->LDS loads, four rows, per wave), chunk q of token row
 // r at slot q ^ r so the 16 lanes of an A-operand read hit 16 bank groups, in a ring of
 // four buffers requested three groups ahead (a group's MFMAs take far less time than its
 // rows take to arrive from L2); fp32(w * s_idx) of every head is staged once.  Per head:
-// Di/32 x 4 MFMAs, then the ReLU x weight accumulate.  Each staged byte of q feeds 512 keys.
+// Di/32 x 4 MFMAs, then the ReLU x weight accumulate.  Each staged byte of q feeds 256
+// keys; four independent workgroups per compute unit (rather than two of 8 waves, which
+// fed 512 keys per byte) overlap one another's group barriers and tile prologues.
 // ============================================================================
 constexpr int HGK_TOK = 16;
-constexpr int HGK_KEYS = 512;
-constexpr int HGK_WAVES = 8;
+constexpr int HGK_KEYS = 256;
+constexpr int HGK_WAVES = 4;
 constexpr int HGK_NBUF = 4;
 // The staged weights [Hi][16 tokens]: token tt of head h sits at h * 16 + (tt ^ wsw(h)).
 // The staging writes go across heads (lane = head), which without the XOR would put 4
@@ -918,7 +920,8 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   constexpr int CPP = PB / 16;        // 16-byte chunks per staged row
   constexpr int NCD = DI / 32;
   constexpr int NTHR = 64 * HGK_WAVES;
-  static_assert(PB == 512 && CPP == 32 && HGK_TOK * PB == HGK_WAVES * 1024, "one 1 KiB load per wave and group");
+  constexpr int NL = HGK_TOK * PB / 1024 / HGK_WAVES;   // 1 KiB loads per wave and group
+  static_assert(PB == 512 && CPP == 32 && NL == 2, "two 1 KiB loads per wave and group");
   __shared__ __attribute__((aligned(16))) u32x4 qs[HGK_NBUF][HGK_TOK * CPP];
   extern __shared__ __attribute__((aligned(16))) float wsl[];   // [Hi][HGK_TOK], tokens XOR wsw(h)
 
@@ -958,11 +961,19 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int rows_left = min(HGK_TOK, total_q - (q_start + t0));
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(q_idx + (int64_t)(q_start + t0) * Hi * DI, (uint32_t)(rows_left * RB));
-  // group grp's rows into buffer grp % NBUF: wave w moves rows 2w and 2w + 1 (lane >> 5)
-  const int srow = 2 * w + (lane >> 5), sc = lane & 31;
-  const uint32_t soff = (uint32_t)(srow * RB + ((sc ^ (srow & 15)) << 4));
+  // group grp's rows into buffer grp % NBUF: load k of wave w moves rows 2(2w + k) and
+  // 2(2w + k) + 1 (lane >> 5), 1 KiB of the buffer at (2w + k) KiB
+  uint32_t soff[NL];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int srow = 2 * (NL * w + k) + (lane >> 5), sc = lane & 31;
+    soff[k] = (uint32_t)(srow * RB + ((sc ^ (srow & 15)) << 4));
+  }
   auto stage = [&](int grp) {
-    dma16(rq, reinterpret_cast<char *>(qs[grp % HGK_NBUF]) + (size_t)w * 1024, soff + (uint32_t)(grp * PB));
+#pragma unroll
+    for (int k = 0; k < NL; ++k)
+      dma16(rq, reinterpret_cast<char *>(qs[grp % HGK_NBUF]) + (size_t)(NL * w + k) * 1024,
+            soff[k] + (uint32_t)(grp * PB));
   };
   const int ngrp = Hi / HG;
 #pragma unroll
@@ -1007,10 +1018,10 @@ __global__ __launch_bounds__(64 * HGK_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int rrow = r16 * PB;
   for (int grp = 0; grp < ngrp; ++grp) {
     // group grp's rows have landed once at most the loads of the groups after it that were
-    // requested (one per wave and group) are outstanding; the barrier publishes every
+    // requested (NL per wave and group) are outstanding; the barrier publishes every
     // wave's rows (and, first time, the weights) and frees the buffer of group grp - 1
-    if (grp + 2 < ngrp) wait_vmcnt<2>();
-    else if (grp + 1 < ngrp) wait_vmcnt<1>();
+    if (grp + 2 < ngrp) wait_vmcnt<2 * NL>();
+    else if (grp + 1 < ngrp) wait_vmcnt<NL>();
     else wait_vmcnt<0>();
     lds_barrier();
     if (grp + HGK_NBUF - 1 < ngrp) stage(grp + HGK_NBUF - 1);

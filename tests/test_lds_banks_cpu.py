@@ -258,6 +258,27 @@ def test_indexer_hg_q_operand_reads():
                 assert cycles_b128(addrs) == 4, (Di, hl, c)
 
 
+def hg_staging(w, k, lane, rows_of=lambda w, k, lane: 2 * (2 * w + k) + (lane >> 5)):
+    """indexer_score_hg_kernel's q staging: load k (of 2) of wave w (of 4) moves 1 KiB to
+    LDS byte (2w + k) KiB + 16 lane, fetching chunk (lane & 31) ^ row of its token row.
+    Returns (row, chunk fetched, LDS slot of 16 bytes)."""
+    row, sc = rows_of(w, k, lane), lane & 31
+    return row, sc ^ (row & 15), (2 * w + k) * 64 + lane
+
+
+def test_indexer_hg_q_staging():
+    """The group's 16 rows x 32 chunks are each staged exactly once, chunk q of row r at
+    slot 32 r + (q ^ r) (where the operand reads above look); the single-load row formula
+    of an 8-wave workgroup (rows 2w, 2w + 1) leaves half the rows unstaged."""
+    def staged(**kw):
+        return [hg_staging(w, k, l, **kw) for w in range(4) for k in range(2) for l in LANES]
+    got = staged()
+    assert sorted((r, q) for r, q, _ in got) == [(r, q) for r in range(16) for q in range(32)]
+    assert all(slot == 32 * r + (q ^ r) for r, q, slot in got)
+    slip = staged(rows_of=lambda w, k, lane: 2 * w + (lane >> 5))
+    assert len({(r, q) for r, q, _ in slip}) < 16 * 32
+
+
 def wsw(h):
     """indexer_score.hip: token XOR of the staged weights of head h."""
     return 4 * ((h >> 2) & 3)
