@@ -1101,7 +1101,7 @@ hipError_t launch_indexer_score(const LaunchLayout &LL, const void *q_idx, const
     if (Di == 64 && Hi == 32) return launch_lds<64, 32>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
     if (Di == 128 && Hi == 4) return launch_lds<128, 4>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
     if (Di == 128 && Hi == 8) return launch_lds<128, 8>(LL, q_idx, k_idx, weights, idx_scale, scores, ld, st);
-    // long rows: head groups staged in LDS (64 tokens x 512 bytes per group)
+    // long rows: head groups staged in LDS (16 tokens x 512 bytes per group)
     if (Di == 64 && Hi >= 64 && Hi % 4 == 0)
       return launch_hg<64>(LL, q_idx, k_idx, weights, Hi, idx_scale, scores, ld, st);
     if (Di == 128 && Hi >= 16 && Hi % 2 == 0)
