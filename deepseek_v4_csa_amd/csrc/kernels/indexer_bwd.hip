@@ -696,7 +696,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   // burst of them holds the issuing wave until the memory pipeline's queue takes them
   constexpr int RPL = PB >= 1024 ? 1 : 1024 / PB;       // rows per load
   constexpr int NSL = 2 * (BWD_TOK / RPL) * (PB >= 1024 ? PB / 1024 : 1) / 4;   // the wave's loads per step
-  static_assert(NSL >= 1 && NSL % HG == 0 || HG % NSL == 0, "loads per head");
+  static_assert(NSL >= 1 && (NSL % HG == 0 || HG % NSL == 0), "loads per head");
   auto stage_q_part = [&](int st, int buf, int k) __attribute__((always_inline)) {
     const int p = st / NG, hg = st - (st / NG) * NG;
     constexpr int PERB = NSL / 2;                         // the wave's loads per block
