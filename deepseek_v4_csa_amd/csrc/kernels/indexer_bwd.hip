@@ -721,6 +721,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
   store_w(0);
   const int nsteps = npair * NG;
   const int rr = 4 * g + (r16 >> 2);   // row this lane addresses in the transposing read
+  // At DI >= 128 a head's 16-byte chunks are a multiple of 16 (DI / 8), so the swizzle (XOR
+  // with a row < 16) leaves the head's part of a chunk index alone: an operand's LDS byte
+  // offset is a per-lane part, the same for every head and step, plus 16 DI / 8 x the head.
+  // Both parts are kept apart so the loop adds one uniform value per head.
+  constexpr bool SPLIT = DI >= 128;
+  uint32_t offq[NCD], offt[NDT];
+#pragma unroll
+  for (int c = 0; c < NCD; ++c) offq[c] = (uint32_t)(r16 * PB + (((4 * c + g) ^ r16) << 4));
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+    offt[dt] = (uint32_t)(rr * PB + (((2 * dt + ((r16 >> 1) & 1)) ^ rr) << 4) + 8 * (r16 & 1));
   for (int st = 0; st < nsteps; ++st) {
     const int p = st / NG, hg = st - p * NG;
     const bool more = p + 1 < npair;
@@ -751,7 +762,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
 #pragma unroll
         for (int c = 0; c < NCD; ++c) {
           const int q = hh * (DI / 8) + 4 * c + g;
-          const u32x4 qa = *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
+          const u32x4 qa = SPLIT ? *reinterpret_cast<const u32x4 *>(qb + bs * BWD_TOK * PB + hh * (2 * DI) + offq[c])
+                                 : *reinterpret_cast<const u32x4 *>(qrow + ((q ^ r16) << 4));
           d[bs][0] = mfma16x16x32(qa, kb[0][c], d[bs][0]);
           d[bs][1] = mfma16x16x32(qa, kb[1][c], d[bs][1]);
         }
@@ -775,11 +787,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
       // 16dt + 4(r16%4) .. +3 of head h.  One batch with its own wait: the builtin read
       // would first wait for the next step's q rows in flight
       uint32_t ta[NDT];
+      const uint32_t tbase = lds_addr_of(qb) + (uint32_t)(hh * (2 * DI));
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int col = hh * DI + 16 * dt + 4 * (r16 & 3);   // bf16 column in the staged row
         const int q = col >> 3;                               // 16-byte chunk
-        ta[dt] = lds_addr_of(qb + rr * PB + ((q ^ rr) << 4) + 8 * ((col >> 2) & 1));
+        ta[dt] = SPLIT ? tbase + offt[dt] : lds_addr_of(qb + rr * PB + ((q ^ rr) << 4) + 8 * ((col >> 2) & 1));
       }
       uint2 tv[2 * NDT];
       lds_read_tr16_pairs<BWD_TOK * PB, NDT>(tv, ta);
